@@ -1,0 +1,18 @@
+"""fp64 CPU oracle of DARKFormer PRF attention: test infrastructure only.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
+this package.  It shares no code with the HIP library and never calls it.
+"""
+from .omega_gen import omega, omega_iid, omega_orthogonal, normals, splitmix64, uniforms  # noqa: F401
+from .prf_oracle import (  # noqa: F401
+    attend_causal_blockwise,
+    attend_noncausal,
+    attention,
+    decode_step,
+    exact_kernel_attention,
+    head_geometry,
+    kv_head,
+    prf_features,
+    project,
+    qk_scale,
+)

@@ -1,0 +1,107 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and show that a pin catches each.
+
+Every mutation below is a mistake a reader of the README's section "Kernel"
+could plausibly make; the pins in oracle_pins must reject all of them.
+"""
+import numpy as np
+import pytest
+
+from oracle import prf_oracle as po
+from tests import oracle_pins as pins
+
+
+def _feat(scale=lambda d: d ** -0.25, sign=1.0, half=0.5, sqrt_m=True, transpose_m=False):
+    def prf_features(X, M_h, omega):
+        omega = np.asarray(omega, np.float64)
+        M_h = np.asarray(M_h, np.float64)
+        Mx = M_h if transpose_m else M_h.T
+        U = scale(X.shape[-1]) * (np.asarray(X, np.float64) @ Mx)
+        E = sign * (U @ omega.T)
+        out = np.exp(E - half * np.sum(U * U, axis=1, keepdims=True))
+        return out / np.sqrt(omega.shape[0]) if sqrt_m else out
+    return prf_features
+
+
+def _causal(strict=False, update_first=False):
+    def attend_causal_blockwise(PQ, PK, V, block=256):
+        L, m = PQ.shape
+        S = np.zeros((m, V.shape[1]))
+        z = np.zeros(m)
+        O = np.zeros((L, V.shape[1]))
+        for s in range(0, L, block):
+            e = min(L, s + block)
+            if update_first:
+                S = S + PK[s:e].T @ V[s:e]
+                z = z + PK[s:e].sum(0)
+            A = np.tril(PQ[s:e] @ PK[s:e].T, -1 if strict else 0)
+            if update_first:
+                A = 0 * A
+            N = PQ[s:e] @ S + A @ V[s:e]
+            D = PQ[s:e] @ z + A.sum(1)
+            ok = D > 0
+            O[s:e][ok] = N[ok] / D[ok, None]
+            if not update_first:
+                S = S + PK[s:e].T @ V[s:e]
+                z = z + PK[s:e].sum(0)
+        return O, S, z
+    return attend_causal_blockwise
+
+
+def _ignore_mask(orig):
+    def attention(q, k, v, M, omega, mask=None, **kw):
+        return orig(q, k, v, M, omega, mask=None, **kw)
+    return attention
+
+
+def _decode_before_update(S, z, q, k, v, M, omega):
+    S = np.asarray(S, np.float64).copy()
+    z = np.asarray(z, np.float64).copy()
+    N, H, d = q.shape
+    H_kv = k.shape[1]
+    o = np.zeros((N, H, d))
+    for h in range(H):
+        g = (h * H_kv) // H
+        M_h = M[h] if np.asarray(M).ndim == 3 else M
+        pq = po.prf_features(np.asarray(q[:, h], np.float64), M_h, omega)
+        pk = po.prf_features(np.asarray(k[:, g], np.float64), M_h, omega)
+        num = np.einsum("nm,nmd->nd", pq, S[:, h])
+        den = np.einsum("nm,nm->n", pq, z[:, h])
+        o[:, h] = num / np.where(den > 0, den, 1.0)[:, None]
+        S[:, h] += pk[:, :, None] * np.asarray(v[:, g], np.float64)[:, None, :]
+        z[:, h] += pk
+    return o, S, z
+
+
+MUTATIONS = {
+    "scale_d^-1/2": ("prf_features", _feat(scale=lambda d: d ** -0.5)),
+    "no_scale": ("prf_features", _feat(scale=lambda d: 1.0)),
+    "exponent_sign": ("prf_features", _feat(sign=-1.0)),
+    "no_half_norm": ("prf_features", _feat(half=0.0)),
+    "full_norm": ("prf_features", _feat(half=1.0)),
+    "no_1/sqrt_m": ("prf_features", _feat(sqrt_m=False)),
+    "M_transposed": ("prf_features", _feat(transpose_m=True)),
+    "causal_strict": ("attend_causal_blockwise", _causal(strict=True)),
+    "causal_update_first": ("attend_causal_blockwise", _causal(update_first=True)),
+    "mask_ignored": ("attention", None),
+    "gqa_modulo": ("kv_head", lambda h, H, H_kv: h % H_kv),
+    "decode_pre_update": ("decode_step", _decode_before_update),
+    "eps_denominator": ("_ratio", lambda N, D: N / (D + 1e-8)[:, None]),
+}
+
+QUICK = pins.ALL_CHECKS + [pins.check_mc_kernel]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name, monkeypatch):
+    attr, repl = MUTATIONS[name]
+    if name == "mask_ignored":
+        repl = _ignore_mask(po.attention)
+    monkeypatch.setattr(po, attr, repl)
+    caught = []
+    for check in QUICK:
+        try:
+            kw = {"ms": (2 ** 8, 2 ** 12)} if check is pins.check_mc_kernel else {}
+            check(**kw)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(check.__name__)
+    assert caught, f"no pin caught mutation {name}"

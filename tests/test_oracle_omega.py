@@ -1,0 +1,89 @@
+"""The oracle's Omega generator against its published definitions and laws."""
+import os
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from oracle import omega_gen as oo
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "splitmix64_kat.txt")
+
+
+def _kat():
+    rows = []
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                seed, idx, val = line.split()
+                rows.append((int(seed), int(idx), int(val, 16)))
+    return rows
+
+
+def test_splitmix64_known_answers():
+    rows = _kat()
+    assert len(rows) >= 7
+    for seed, idx, val in rows:
+        assert int(oo.splitmix64(seed, idx, 1)[0]) == val, (seed, idx)
+
+
+def test_uniforms_in_half_open_unit_interval():
+    u = oo.uniforms(3, 0, 1 << 16)
+    assert np.all(u > 0.0) and np.all(u <= 1.0)
+    assert abs(u.mean() - 0.5) < 5 * np.sqrt(1 / 12 / u.size)
+
+
+def test_normals_moments_and_ks():
+    x = oo.normals(7, 0, 1 << 20)
+    n = x.size
+    assert abs(x.mean()) < 5 / np.sqrt(n)
+    assert abs(x.var() - 1.0) < 5 * np.sqrt(2.0 / n)
+    assert stats.kstest(x, "norm").pvalue > 1e-4
+    # any window of the stream equals the same slice of a longer draw
+    assert np.array_equal(oo.normals(7, 5, 100), x[5:105])
+
+
+def test_iid_is_the_normal_stream():
+    om = oo.omega_iid(11, 32, 16)
+    assert om.shape == (32, 16)
+    assert np.array_equal(om.reshape(-1), oo.normals(11, 0, 32 * 16))
+
+
+@pytest.mark.parametrize("m,r", [(256, 64), (100, 16), (16, 16), (40, 8)])
+def test_orthogonal_blocks(m, r):
+    om = oo.omega_orthogonal(123, m, r)
+    assert om.shape == (m, r)
+    for b in range(0, m, r):
+        blk = om[b:b + r]
+        gram = blk @ blk.T
+        off = gram - np.diag(np.diag(gram))
+        assert np.max(np.abs(off)) <= 1e-12 * np.max(np.diag(gram))
+        # rows are ||Hn_a|| * Q[a, :] with Q the sign-fixed (Haar) QR factor of G
+        base = 2 * (b // r) * r * r
+        G = oo.normals(123, base, r * r).reshape(r, r)
+        Hn = oo.normals(123, base + r * r, r * r).reshape(r, r)
+        norms = np.sqrt((Hn * Hn).sum(1))[: blk.shape[0]]
+        assert np.allclose(np.sqrt((blk * blk).sum(1)), norms, rtol=1e-12)
+        Q = blk / norms[:, None]
+        if blk.shape[0] == r:
+            R = Q.T @ G          # G = Q R  =>  R = Q^T G: upper triangular, positive diagonal
+            assert np.allclose(np.tril(R, -1), 0.0, atol=1e-10)
+            assert np.all(np.diag(R) > 0)
+
+
+def test_orthogonal_row_norms_are_chi_r():
+    r = 8
+    sq = np.concatenate([(oo.omega_orthogonal(s, 64, r) ** 2).sum(1) for s in range(40)])
+    assert stats.kstest(sq, stats.chi2(r).cdf).pvalue > 1e-4
+    assert abs(sq.mean() - r) < 5 * np.sqrt(2 * r / sq.size)
+
+
+def test_determinism_and_seed_sensitivity():
+    for orth in (False, True):
+        a = oo.omega(99, 64, 16, orth)
+        b = oo.omega(99, 64, 16, orth)
+        c = oo.omega(100, 64, 16, orth)
+        assert a.dtype == np.float32
+        assert np.array_equal(a, b)
+        assert not np.array_equal(a, c)
