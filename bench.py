@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Throughput of the DARKFormer PRF-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one dark_prf_fwd call over one batch (every kernel of the path:
+operand preparation, key-side state, state sum / prefix scan, query-side
+output), on seeded synthetic inputs already resident in HBM.  The timed region
+replays a HIP graph of back-to-back forwards that rotate over enough input
+copies to touch more memory than the 256 MB Infinity Cache holds.  Prints one
+JSON line.  The default workload is the causal L=2048 attention core
+(B=2, H=8, d_h=64, m=256, r=64); the L=64K non-causal workload
+(B=1, H=8, d_h=64, m=1024, r=16) is measured in the same run and reported
+under "secondary".  `--workload c4_gqa_L8192` or `c5_decode` prints the line
+for those workloads instead.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (matrix and vector)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "fwd tokens/sec (all heads) at L=2048 and L=64K; % bf16 MFMA/HBM roofline"
+MALL_BYTES = 256 << 20
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work per kernel (method steps only; no recomputation counted)
+# ---------------------------------------------------------------------------
+def kernel_flops(w, chunk: int) -> dict:
+    """Algorithmic flops per launch of each kernel, from the method's steps:
+    projection 2 r d_h and exponent 2 r m per token and tensor, state and output
+    contractions 2 m (d_h + 1) per token, and for the causal form the masked
+    intra-chunk block 2 C (m + d_h + 1) per token (C = chunk length)."""
+    th = w.B * w.H * w.L
+    proj = 2 * w.r * w.d_h
+    expo = 2 * w.r * w.m
+    contr = 2 * w.m * (w.d_h + 1)
+    intra = 2 * chunk * (w.m + w.d_h + 1) if w.causal else 0
+    return {"kstate": th * (proj + expo + contr), "qout": th * (proj + expo + contr + intra)}
+
+
+def io_bytes(w) -> int:
+    e = 2 if w.dtype == "bf16" else 4
+    tok = w.B * w.L * w.d_h * e
+    return tok * (2 * w.H + 2 * w.hkv)
+
+
+def nominal_flops(w) -> int:
+    return 8 * w.B * w.H * w.L * w.m * w.d_h
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "random_feature_linear_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        ent = rec.get(workload, {}).get(kernel)
+        if ent and ent.get("source_digest") == source_digest():
+            return ent.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+    return None
+
+
+# ---------------------------------------------------------------------------
+# device-side forward
+# ---------------------------------------------------------------------------
+class Forward:
+    """Device inputs (several copies), output and workspace for one workload."""
+
+    def __init__(self, w, copies: int):
+        import torch
+
+        from random_feature_linear_amd import binding as bd
+        from random_feature_linear_amd.workloads import make_inputs
+        self.bd, self.w = bd, w
+        dt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+        inp = make_inputs(w)
+        self.M = torch.from_numpy(inp["M"]).to("cuda:0")
+        self.omega = torch.from_numpy(bd.dark_prf_omega(w.seed, w.m, w.r, w.orthogonal)).to("cuda:0")
+        base = {n: torch.from_numpy(inp[n]).to(dt).to("cuda:0") for n in ("q", "k", "v")}
+        mask = torch.from_numpy(inp["mask"]).to("cuda:0") if inp["mask"] is not None else None
+        self.copies = []
+        for _ in range(copies):
+            c = {n: base[n].clone() for n in base}
+            c["mask"] = mask.clone() if mask is not None else None
+            c["out"] = torch.empty_like(c["q"])
+            self.copies.append(c)
+        self.tag = bd.dark_prf_proj_tag(w.seed, w.m, w.r, w.orthogonal)
+        c0 = self.copies[0]
+        self.desc = bd.make_desc(c0["q"], c0["k"], c0["v"], c0["out"], self.M, self.omega, w.causal, self.tag)
+        self.ws_bytes = bd.dark_prf_workspace_bytes(self.desc)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device="cuda:0")
+        self.args = [(c["q"].data_ptr(), c["k"].data_ptr(), c["v"].data_ptr(),
+                      c["mask"].data_ptr() if c["mask"] is not None else 0, c["out"].data_ptr())
+                     for c in self.copies]
+
+    def __call__(self, i: int) -> None:
+        import torch
+        q, k, v, mk, out = self.args[i % len(self.args)]
+        st = self.bd.dark_prf_fwd(self.desc, q, k, v, self.M.data_ptr(), self.omega.data_ptr(), mk,
+                                  out, 0, 0, self.ws.data_ptr(), self.ws_bytes,
+                                  torch.cuda.current_stream().cuda_stream)
+        if st != self.bd.DARK_OK:
+            raise self.bd.DarkPrfError(st, "dark_prf_fwd")
+
+
+def chunk_len(w) -> int:
+    """Causal chunk the library plans for this workload (64 or 128 tokens)."""
+    if not w.causal:
+        return 0
+    chunks64 = w.B * w.H * -(-w.L // 64)
+    e = 2 if w.dtype == "bf16" else 4
+    lds2 = (w.d_h * (128 + 8) + 2 * 4 * 2 * 64 * 8) * e
+    return 128 if ((chunks64 > 8192 or w.d_h >= 128) and lds2 <= 160 * 1024) else 64
+
+
+def measure(w, steps: int, warmup: int) -> dict:
+    import torch
+    per_copy = io_bytes(w)
+    copies = max(2, min(32, -(-(MALL_BYTES + (64 << 20)) // per_copy)))
+    fwd = Forward(w, copies)
+    log(f"[bench] {w.name}: {copies} input copies of {per_copy / 1e6:.1f} MB, workspace "
+        f"{fwd.ws_bytes / 1e6:.1f} MB")
+    for i in range(warmup):
+        fwd(i)
+    torch.cuda.synchronize()
+    # one graph = one pass over the copies; replay it until `steps` forwards ran
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for i in range(copies):
+                fwd(i)
+    torch.cuda.synchronize()
+    reps = max(1, -(-steps // copies))
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    n_fwd = reps * copies
+    ms = t0.elapsed_time(t1) / n_fwd
+    # eager pass with per-kernel events (timing hooks on)
+    n_t = min(max(steps, 20), 200)
+    fwd.bd.dark_prf_timing_begin()
+    for i in range(n_t):
+        fwd(i)
+    per = fwd.bd.dark_prf_timing_end()
+    torch.cuda.synchronize()
+    kern = {k: {"avg_us": 1e3 * v[0] / v[1], "launches": v[1]} for k, v in per.items() if v[1] > 0}
+    return {"ms": ms, "n_fwd": n_fwd, "copies": copies, "kernels": kern}
+
+
+def roofline(w, res: dict) -> dict:
+    """Roofline of the dominant kernel (largest average duration)."""
+    C = chunk_len(w)
+    flops = kernel_flops(w, C)
+    dom = max(res["kernels"], key=lambda k: res["kernels"][k]["avg_us"])
+    avg_s = res["kernels"][dom]["avg_us"] * 1e-6
+    traffic = traffic_from_profiles(dom, w.name)
+    if dom in flops:
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        ach = flops[dom] / avg_s / 1e12
+        return {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
+                "flops_per_launch": flops[dom], "avg_launch_us": round(res["kernels"][dom]["avg_us"], 3)}
+    return {"bound": "hbm", "kernel": dom, "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": None, "traffic": traffic, "avg_launch_us": round(res["kernels"][dom]["avg_us"], 3)}
+
+
+def cpu_baseline(w, max_heads=None) -> dict:
+    """The fp64 oracle on the host cores, on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from random_feature_linear_amd.workloads import make_inputs
+    inp = make_inputs(w)
+    om = oracle.omega(w.seed, w.m, w.r, w.orthogonal)
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    if max_heads is not None:
+        pairs = pairs[:max_heads]
+    t = time.perf_counter()
+    oracle.attention(inp["q"], inp["k"], inp["v"], inp["M"], om, mask=inp["mask"], causal=w.causal,
+                     heads=pairs)
+    dt = time.perf_counter() - t
+    frac = len(pairs) / (w.B * w.H)
+    tok_s = w.B * w.L * frac / dt
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("internal_api") in
+                   ("openblas", "mkl", "blis")] or [1])
+    return {"value": round(tok_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(pairs)} of {w.B * w.H} (batch, head) slices, full length, fp64, "
+                      f"{dt:.2f} s", "blas": "openblas",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def line_for(w, res: dict, steps: int, warmup: int) -> dict:
+    tokens = w.B * w.L
+    value = tokens / (res["ms"] * 1e-3)
+    nom = nominal_flops(w) / (res["ms"] * 1e-3) / 1e12
+    return {
+        "value": round(value, 1), "ms_per_step": round(res["ms"], 6),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.hkv, "L": w.L, "d_h": w.d_h,
+                   "m": w.m, "r": w.r, "causal": w.causal, "mask": w.mask_kind,
+                   "launch": "hipGraph of %d forwards over rotating input copies" % res["copies"]},
+        "roofline": roofline(w, res),
+        "nominal_tflops": round(nom, 2), "nominal_frac_bf16": round(nom / PEAK_BF16_TFLOPS, 4),
+        "io_GBps": round(io_bytes(w) / (res["ms"] * 1e-3) / 1e9, 1),
+        "kernels_us": {k: round(v["avg_us"], 3) for k, v in res["kernels"].items()},
+    }
+
+
+def decode_line(steps: int) -> dict:
+    """Workload 5: 512 one-token steps over 256 sequences x 8 heads (fp32 state)."""
+    import torch
+
+    from random_feature_linear_amd import binding as bd
+    from random_feature_linear_amd.workloads import CONFIGS, make_decode_tokens
+    w = CONFIGS["c5_decode"]
+    g = torch.Generator(device="cuda:0").manual_seed(w.seed)
+    dt = torch.bfloat16
+    S = torch.randn((w.B, w.H, w.m, w.d_h), generator=g, device="cuda:0", dtype=torch.float32)
+    z = torch.rand((w.B, w.H, w.m), generator=g, device="cuda:0", dtype=torch.float32) * 4096
+    tok = make_decode_tokens(w, steps)
+    tq, tk, tv = (torch.from_numpy(tok[n]).to(dt).to("cuda:0") for n in ("q", "k", "v"))
+    from random_feature_linear_amd.workloads import make_inputs
+    M = torch.from_numpy(make_inputs(w.with_(B=1, L=1))["M"]).to("cuda:0")
+    om = torch.from_numpy(bd.dark_prf_omega(w.seed, w.m, w.r, w.orthogonal)).to("cuda:0")
+    tag = bd.dark_prf_proj_tag(w.seed, w.m, w.r, w.orthogonal)
+    out = torch.empty_like(tq[0])
+    for t in range(4):
+        bd.decode_step(tq[t], tk[t], tv[t], M, om, S, z, tag, tag, out=out)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for t in range(steps):
+        bd.decode_step(tq[t], tk[t], tv[t], M, om, S, z, tag, tag, out=out)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    bd.dark_prf_timing_begin()
+    for t in range(min(steps, 64)):
+        bd.decode_step(tq[t], tk[t], tv[t], M, om, S, z, tag, tag, out=out)
+    per = bd.dark_prf_timing_end()
+    avg_us = 1e3 * per["decode"][0] / per["decode"][1]
+    state_bytes = 2 * (w.B * w.H * w.m * (w.d_h + 1) * 4)
+    ach = state_bytes / (avg_us * 1e-6) / 1e9
+    return {"value": round(w.B / (ms * 1e-3), 1), "ms_per_step": round(ms, 6), "unit": "tokens/s",
+            "config": {"workload": w.name, "N": w.B, "H": w.H, "d_h": w.d_h, "m": w.m, "r": w.r,
+                       "steps": steps, "launch": "eager, one launch per step"},
+            "roofline": {"bound": "hbm", "kernel": "decode", "achieved": round(ach, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                         "traffic": traffic_from_profiles("decode", w.name),
+                         "bytes_per_launch": state_bytes, "avg_launch_us": round(avg_us, 3)}}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2_causal_L2048")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the L=64K measurement")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path, so --gpus must be 1",
+              file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    from random_feature_linear_amd import binding as bd
+    from random_feature_linear_amd.workloads import CONFIGS
+    bd.lib()
+    torch.cuda.synchronize()
+    if args.workload == "c5_decode":
+        rec = decode_line(min(args.steps, 512))
+        rec.update({"metric": "decode tokens/sec (256 sequences x 8 heads, one token each)",
+                    "n_gpus": 1, "steps": min(args.steps, 512), "warmup": 4, "higher_is_better": True,
+                    "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"})
+        print(json.dumps(rec), flush=True)
+        return 0
+    w = CONFIGS[args.workload]
+    res = measure(w, args.steps, args.warmup)
+    main_line = line_for(w, res, args.steps, args.warmup)
+    rec = {"metric": METRIC, "value": main_line["value"], "unit": "tokens/s", "n_gpus": 1,
+           "steps": res["n_fwd"], "warmup": args.warmup, "ms_per_step": main_line["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": w.dtype, "data": "synthetic (seeded Gaussian inputs of the workload's shape)"}
+    rec.update({k: v for k, v in main_line.items() if k not in ("value", "ms_per_step")})
+    if not args.no_cpu and torch.cuda.current_device() == 0:
+        log("[bench] timing the fp64 oracle on the host")
+        rec["cpu_baseline"] = cpu_baseline(w)
+    if args.workload == "c2_causal_L2048" and not args.no_secondary:
+        w3 = CONFIGS["c3_long_L64K"]
+        res3 = measure(w3, max(20, args.steps // 8), min(args.warmup, 5))
+        sec = line_for(w3, res3, args.steps, args.warmup)
+        if not args.no_cpu:
+            log("[bench] timing the fp64 oracle on one head of the L=64K workload")
+            sec["cpu_baseline"] = cpu_baseline(w3, max_heads=1)
+        sec["steps"] = res3["n_fwd"]
+        rec["secondary"] = sec
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

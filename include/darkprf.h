@@ -1,0 +1,180 @@
+/*
+ * darkprf.h - C ABI of the MI355X (gfx950) DARKFormer positive-random-feature
+ * attention forward pass.
+ *
+ * What is computed (package README "Data-Aware Random Feature Kernels for
+ * Transformers (DARKformer)", darkformer-pytorch 0.1.0):
+ *   - section "Kernel", scaled-kernel equation: q and k are scaled by
+ *     d_h^(-1/4) inside the library; callers pass unscaled tensors;
+ *   - section "Kernel", feature-map equation: for a scaled row x,
+ *     phi(x)_j = exp(omega_j^T M x - x^T M^T M x / 2) / sqrt(m);
+ *   - section "Kernel", attention equation: out = Phi(Q)(Phi(K)^T V) /
+ *     Phi(Q)(Phi(K)^T 1), evaluated associatively;
+ *   - section "Self-attention": a boolean key mask (nonzero = valid token),
+ *     combined with the causal constraint when causal;
+ *   - section "Encoder-decoder model and generation": recurrent statistics
+ *     S = sum phi(k) v^T and z = sum phi(k), updated per appended token; a
+ *     state is tied to the projection that produced it and a redraw is
+ *     rejected;
+ *   - section "Mixed precision": reductions accumulate in fp32 and results are
+ *     returned in the input dtype.
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: every pointer is owned by the caller.  Device pointers must
+ *     stay valid until the work queued on `stream` has finished.  The library
+ *     allocates no device memory and keeps no state between calls; it is safe
+ *     to call from several host threads on different streams.
+ *   - Asynchrony: compute calls only queue kernels on `stream` (a hipStream_t;
+ *     NULL = the default stream) and never synchronise.
+ *   - Errors: argument errors are detected on the host, before anything is
+ *     queued, and returned as a status; nothing is launched in that case.  A
+ *     failed launch is reported as DARK_ERR_HIP.  Nothing throws or aborts.
+ *   - Layout: q, k, v and out are addressed as base + b*str[0] + h*str[1] +
+ *     l*str[2] + e (elements, e = 0..d_h-1 contiguous).  Device pointers and
+ *     every stride must give 16-byte aligned rows.
+ *   - dtype: q, k, v and out share desc->dtype.  M, omega and the recurrent
+ *     state are fp32.
+ */
+#ifndef DARKPRF_H
+#define DARKPRF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DARK_OK = 0,
+  DARK_ERR_INVALID_ARG = 1,  /* a pointer, size, stride or alignment is wrong */
+  DARK_ERR_UNSUPPORTED = 2,  /* a valid combination this build does not serve */
+  DARK_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  DARK_ERR_STALE_STATE = 4,  /* recurrent state made with another projection */
+  DARK_ERR_HIP = 5           /* the HIP runtime reported an error */
+} dark_status;
+
+typedef enum { DARK_F32 = 0, DARK_BF16 = 1 } dark_dtype;
+
+typedef struct {
+  int32_t B;          /* batch (number of sequences) */
+  int32_t H;          /* query heads */
+  int32_t H_kv;       /* key/value heads; H % H_kv == 0; query head h reads kv head h*H_kv/H */
+  int32_t L;          /* sequence length (1 for a decode step) */
+  int32_t d_h;        /* head dimension: 16, 32, 64, 128 or 256 */
+  int32_t m;          /* number of random features, a positive multiple of 16 */
+  int32_t r;          /* geometry rank (rows of M, width of omega), 1..256 */
+  int32_t dtype;      /* dark_dtype of q, k, v and out */
+  int32_t causal;     /* 0: every valid key is visible; 1: key j visible to query t iff j <= t */
+  int32_t m_per_head; /* 1: M is [H][r][d_h]; 0: one M [r][d_h] shared by all heads */
+  int64_t q_str[3];   /* element strides of q over (b, h, l) */
+  int64_t k_str[3];   /* element strides of k over (b, h_kv, l) */
+  int64_t v_str[3];   /* element strides of v over (b, h_kv, l) */
+  int64_t o_str[3];   /* element strides of out over (b, h, l) */
+  uint64_t proj_tag;  /* identifies omega; see dark_prf_proj_tag */
+} dark_prf_desc;
+
+/*
+ * dark_prf_omega - the random projection omega [m][r] (fp32, row-major, host
+ * memory) for a seed.  README section "Kernel" (each omega_j standard
+ * Gaussian), section "Self-attention" (orthogonal Gaussian blocks by default,
+ * independent Gaussian features otherwise) and section "Projection lifecycle"
+ * (a seed makes the projection reproducible).
+ *   orthogonal == 0: i.i.d. N(0, 1) entries.
+ *   orthogonal != 0: ceil(m / r) blocks of r rows; each block is a Haar
+ *     rotation (QR of a Gaussian r x r matrix with the sign of diag(R) moved
+ *     into Q) whose rows are rescaled by the norms of independent Gaussian
+ *     r-vectors; the last block keeps its first m - r*(blocks-1) rows.
+ * Gaussians come from Box-Muller over the SplitMix64 stream of `seed`; the
+ * arithmetic is fp64 and the result is rounded once to fp32.  Deterministic
+ * for a seed on any machine with IEEE fp64 libm.  Returns
+ * DARK_ERR_INVALID_ARG for m < 1, r < 1 or omega_host == NULL.
+ */
+dark_status dark_prf_omega(uint64_t seed, int32_t m, int32_t r, int32_t orthogonal,
+                           float* omega_host);
+
+/*
+ * dark_prf_proj_tag - a 64-bit tag naming the projection (seed, m, r,
+ * orthogonal).  Store it in desc->proj_tag; states exported by dark_prf_fwd
+ * are valid only for calls that carry the same tag.
+ */
+uint64_t dark_prf_proj_tag(uint64_t seed, int32_t m, int32_t r, int32_t orthogonal);
+
+/*
+ * dark_prf_workspace_bytes - device workspace that dark_prf_fwd needs for this
+ * descriptor (0 if the descriptor is invalid).  The workspace holds the
+ * bf16/fp32 operand copies of M and omega and the partial or per-chunk
+ * feature-space states; its contents need no initialisation.
+ */
+size_t dark_prf_workspace_bytes(const dark_prf_desc* desc);
+
+/*
+ * dark_prf_fwd - linear-mode attention over a whole sequence (README section
+ * "Kernel", attention equation; section "Self-attention" for mask and causal).
+ *   q     [B][H][L][d_h]     (strides q_str), dtype
+ *   k, v  [B][H_kv][L][d_h]  (strides k_str, v_str), dtype
+ *   M     fp32 [H][r][d_h] when m_per_head, else [r][d_h], contiguous
+ *   omega fp32 [m][r], contiguous (e.g. from dark_prf_omega)
+ *   mask  uint8 [B][L] contiguous, nonzero = valid key, or NULL (all valid);
+ *         masked positions are removed as keys; their query rows are still
+ *         computed
+ *   out   [B][H][L][d_h] (strides o_str), dtype; a row with no visible valid
+ *         key is 0
+ *   S_out fp32 [B][H][m][d_h] contiguous or NULL; z_out fp32 [B][H][m]
+ *         contiguous or NULL: the recurrent state after the last token
+ *         (causal only; either both or neither), i.e. S = sum_j phi(k_j) v_j^T
+ *         and z = sum_j phi(k_j) over valid keys, ready for
+ *         dark_prf_decode_step
+ *   workspace, ws_bytes: device scratch of at least dark_prf_workspace_bytes
+ * All device pointers are read or written on `stream` only.
+ */
+dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k,
+                         const void* v, const float* M, const float* omega,
+                         const uint8_t* mask, void* out, float* S_out, float* z_out,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dark_prf_decode_step - append one token to every sequence and emit its
+ * output (README section "Encoder-decoder model and generation": recurrent
+ * statistics updated per appended token).  desc->B = N sequences, desc->L = 1,
+ * desc->causal = 1.
+ *   q [N][H][d_h], k, v [N][H_kv][d_h] (strides q_str/k_str/v_str over
+ *     (n, h, -); the l-stride is unused), dtype
+ *   S fp32 [N][H][m][d_h], z fp32 [N][H][m]: updated in place,
+ *     S += phi(k) v^T, z += phi(k); the output reads the updated state:
+ *     out = phi(q)^T S / phi(q)^T z (0 when the denominator is 0)
+ *   state_tag: the proj_tag the state was made with; it must equal
+ *     desc->proj_tag, else DARK_ERR_STALE_STATE and nothing is queued
+ *   out [N][H][d_h] (strides o_str), dtype
+ */
+dark_status dark_prf_decode_step(const dark_prf_desc* desc, const void* q, const void* k,
+                                 const void* v, const float* M, const float* omega,
+                                 float* S, float* z, uint64_t state_tag, void* out,
+                                 void* stream);
+
+/* dark_prf_status_str - a static, human-readable name of a status. */
+const char* dark_prf_status_str(dark_status status);
+
+/*
+ * Diagnostics: GPU time of each kernel the library launches, taken with HIP
+ * events recorded on the caller's stream around every launch.  Not needed for
+ * computation and off by default; while on, each launch costs two event
+ * records.  Process-wide; the two calls are serialised by a lock.
+ *   dark_prf_timing_begin: start recording (drops anything recorded before).
+ *   dark_prf_timing_end: wait for the recorded events, write the summed
+ *     milliseconds and the launch count of every kernel kind into
+ *     ms[DARK_KERNEL_KINDS] and launches[DARK_KERNEL_KINDS] (host arrays),
+ *     and stop recording.  Returns DARK_ERR_INVALID_ARG for NULL arrays and
+ *     DARK_ERR_HIP if an event failed.
+ * Kernel kinds: 0 operand preparation of M and omega, 1 key-side feature
+ * state, 2 state sum / prefix scan, 3 query-side output, 4 decode step.
+ */
+#define DARK_KERNEL_KINDS 5
+dark_status dark_prf_timing_begin(void);
+dark_status dark_prf_timing_end(double* ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DARKPRF_H */

@@ -1,0 +1,220 @@
+"""ctypes binding of libdarkprf.so (the C ABI in include/darkprf.h).
+
+Argument marshalling only: every step of the attention runs in the library's
+HIP kernels.  torch supplies device memory and the current HIP stream.  There
+is no fallback: if the library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdarkprf.so")
+
+DARK_OK = 0
+DARK_ERR_INVALID_ARG = 1
+DARK_ERR_UNSUPPORTED = 2
+DARK_ERR_WORKSPACE = 3
+DARK_ERR_STALE_STATE = 4
+DARK_ERR_HIP = 5
+DARK_F32 = 0
+DARK_BF16 = 1
+
+
+class DarkPrfDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("H_kv", ctypes.c_int32),
+        ("L", ctypes.c_int32), ("d_h", ctypes.c_int32), ("m", ctypes.c_int32),
+        ("r", ctypes.c_int32), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("m_per_head", ctypes.c_int32),
+        ("q_str", ctypes.c_int64 * 3), ("k_str", ctypes.c_int64 * 3),
+        ("v_str", ctypes.c_int64 * 3), ("o_str", ctypes.c_int64 * 3),
+        ("proj_tag", ctypes.c_uint64),
+    ]
+
+
+class DarkPrfError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdarkprf.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(
+                f"{LIB_PATH} is missing: build it with random_feature_linear_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        L.dark_prf_omega.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
+        L.dark_prf_omega.restype = ctypes.c_int
+        L.dark_prf_proj_tag.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+        L.dark_prf_proj_tag.restype = ctypes.c_uint64
+        L.dark_prf_workspace_bytes.argtypes = [ctypes.POINTER(DarkPrfDesc)]
+        L.dark_prf_workspace_bytes.restype = ctypes.c_size_t
+        L.dark_prf_fwd.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P, P, P, P,
+                                   ctypes.c_size_t, P]
+        L.dark_prf_fwd.restype = ctypes.c_int
+        L.dark_prf_decode_step.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P,
+                                           ctypes.c_uint64, P, P]
+        L.dark_prf_decode_step.restype = ctypes.c_int
+        L.dark_prf_status_str.argtypes = [ctypes.c_int]
+        L.dark_prf_status_str.restype = ctypes.c_char_p
+        L.dark_prf_timing_begin.argtypes = []
+        L.dark_prf_timing_begin.restype = ctypes.c_int
+        L.dark_prf_timing_end.argtypes = [P, P]
+        L.dark_prf_timing_end.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+# ---- the C entry points, same names ------------------------------------------
+def dark_prf_status_str(status: int) -> str:
+    return lib().dark_prf_status_str(int(status)).decode()
+
+
+status_str = dark_prf_status_str
+
+
+def dark_prf_omega(seed: int, m: int, r: int, orthogonal: bool) -> np.ndarray:
+    out = np.empty((m, r), dtype=np.float32)
+    st = lib().dark_prf_omega(ctypes.c_uint64(seed), m, r, int(bool(orthogonal)),
+                              out.ctypes.data_as(ctypes.c_void_p))
+    if st != DARK_OK:
+        raise DarkPrfError(st, "dark_prf_omega")
+    return out
+
+
+def dark_prf_proj_tag(seed: int, m: int, r: int, orthogonal: bool) -> int:
+    return int(lib().dark_prf_proj_tag(ctypes.c_uint64(seed), m, r, int(bool(orthogonal))))
+
+
+def dark_prf_workspace_bytes(desc: DarkPrfDesc) -> int:
+    return int(lib().dark_prf_workspace_bytes(ctypes.byref(desc)))
+
+
+def dark_prf_fwd(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, omega: int, mask: int,
+                 out: int, S_out: int, z_out: int, workspace: int, ws_bytes: int,
+                 stream: int) -> int:
+    """Raw call with integer device addresses (0 = NULL); returns the status."""
+    return lib().dark_prf_fwd(ctypes.byref(desc), q or None, k or None, v or None, M or None,
+                              omega or None, mask or None, out or None, S_out or None,
+                              z_out or None, workspace or None, ws_bytes, stream or None)
+
+
+def dark_prf_decode_step(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, omega: int, S: int,
+                         z: int, state_tag: int, out: int, stream: int) -> int:
+    return lib().dark_prf_decode_step(ctypes.byref(desc), q or None, k or None, v or None,
+                                      M or None, omega or None, S or None, z or None,
+                                      ctypes.c_uint64(state_tag), out or None, stream or None)
+
+
+KERNEL_KINDS = ("prep", "kstate", "scan", "qout", "decode")
+
+
+def dark_prf_timing_begin() -> None:
+    st = lib().dark_prf_timing_begin()
+    if st != DARK_OK:
+        raise DarkPrfError(st, "dark_prf_timing_begin")
+
+
+def dark_prf_timing_end() -> dict:
+    """{kind: (total_ms, launches)} for every kernel kind."""
+    ms = (ctypes.c_double * len(KERNEL_KINDS))()
+    n = (ctypes.c_int32 * len(KERNEL_KINDS))()
+    st = lib().dark_prf_timing_end(ctypes.cast(ms, ctypes.c_void_p), ctypes.cast(n, ctypes.c_void_p))
+    if st != DARK_OK:
+        raise DarkPrfError(st, "dark_prf_timing_end")
+    return {k: (float(ms[i]), int(n[i])) for i, k in enumerate(KERNEL_KINDS)}
+
+
+# ---- torch-tensor conveniences (marshalling only) -----------------------------
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DARK_BF16
+    if t.dtype == torch.float32:
+        return DARK_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def make_desc(q, k, v, out, M, omega, causal: bool, proj_tag: int = 0) -> DarkPrfDesc:
+    """Descriptor for q [B][H][L][d_h], k/v [B][H_kv][L][d_h] (any strides, d_h contiguous)."""
+    B, H, L, d_h = q.shape
+    d = DarkPrfDesc()
+    d.B, d.H, d.H_kv, d.L, d.d_h = B, H, k.shape[1], L, d_h
+    d.m, d.r = omega.shape[0], omega.shape[1]
+    d.dtype = _dtype_code(q)
+    d.causal = int(bool(causal))
+    d.m_per_head = int(M.dim() == 3)
+    for name, t in (("q_str", q), ("k_str", k), ("v_str", v), ("o_str", out)):
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name}: the last dimension must be contiguous")
+        getattr(d, name)[:] = list(t.stride()[:3])
+    d.proj_tag = proj_tag
+    return d
+
+
+def prf_attention(q, k, v, M, omega, mask=None, causal: bool = False, return_state: bool = False,
+                  proj_tag: int = 0, out=None, workspace=None):
+    """dark_prf_fwd on torch device tensors; returns out (and S, z when return_state)."""
+    import torch
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    desc = make_desc(q, k, v, out, M, omega, causal, proj_tag)
+    nbytes = dark_prf_workspace_bytes(desc)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    S = z = None
+    if return_state:
+        B, H = q.shape[0], q.shape[1]
+        S = torch.empty((B, H, desc.m, desc.d_h), dtype=torch.float32, device=q.device)
+        z = torch.empty((B, H, desc.m), dtype=torch.float32, device=q.device)
+    mask_ptr = 0
+    if mask is not None:
+        if mask.dtype != torch.uint8 or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous uint8 [B][L] tensor")
+        mask_ptr = mask.data_ptr()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = dark_prf_fwd(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), M.data_ptr(),
+                      omega.data_ptr(), mask_ptr, out.data_ptr(),
+                      S.data_ptr() if S is not None else 0, z.data_ptr() if z is not None else 0,
+                      workspace.data_ptr(), workspace.numel(), stream)
+    if st != DARK_OK:
+        raise DarkPrfError(st, "dark_prf_fwd")
+    return (out, S, z) if return_state else out
+
+
+def decode_step(q, k, v, M, omega, S, z, state_tag: int, proj_tag: int, out=None):
+    """dark_prf_decode_step: q [N][H][d_h], k/v [N][H_kv][d_h]; S, z updated in place."""
+    import torch
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    N, H, d_h = q.shape
+    d = DarkPrfDesc()
+    d.B, d.H, d.H_kv, d.L, d.d_h = N, H, k.shape[1], 1, d_h
+    d.m, d.r = omega.shape[0], omega.shape[1]
+    d.dtype = _dtype_code(q)
+    d.causal = 1
+    d.m_per_head = int(M.dim() == 3)
+    for name, t in (("q_str", q), ("k_str", k), ("v_str", v), ("o_str", out)):
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name}: the last dimension must be contiguous")
+        getattr(d, name)[:] = [t.stride(0), t.stride(1), 0]
+    d.proj_tag = proj_tag
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = dark_prf_decode_step(d, q.data_ptr(), k.data_ptr(), v.data_ptr(), M.data_ptr(),
+                              omega.data_ptr(), S.data_ptr(), z.data_ptr(), state_tag,
+                              out.data_ptr(), stream)
+    if st != DARK_OK:
+        raise DarkPrfError(st, "dark_prf_decode_step")
+    return out

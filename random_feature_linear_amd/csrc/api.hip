@@ -1,0 +1,432 @@
+// C ABI of the darkprf library: argument validation, planning and dispatch.
+// Every check happens on the host before anything is queued; see darkprf.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "common.h"
+
+namespace dk {
+
+// launchers defined in the instantiation units
+#define DK_DECL(dt, dh)                                                                                \
+  dark_status fwd_##dt##_d##dh##_r1(const FwdArgs&, const Plan&, void*, void*);                       \
+  dark_status fwd_##dt##_d##dh##_r2(const FwdArgs&, const Plan&, void*, void*);                       \
+  dark_status fwd_##dt##_d##dh##_r4(const FwdArgs&, const Plan&, void*, void*);                       \
+  dark_status fwd_##dt##_d##dh##_r8(const FwdArgs&, const Plan&, void*, void*);                       \
+  dark_status fwd_##dt##_d##dh##_r16(const FwdArgs&, const Plan&, void*, void*);                      \
+  dark_status dec_##dt##_d##dh(const dark_prf_desc&, const void*, const void*, const void*,            \
+                               const float*, const float*, float*, float*, void*, void*);
+DK_DECL(bf16, 16)
+DK_DECL(bf16, 32)
+DK_DECL(bf16, 64)
+DK_DECL(bf16, 128)
+DK_DECL(bf16, 256)
+DK_DECL(f32, 16)
+DK_DECL(f32, 32)
+DK_DECL(f32, 64)
+DK_DECL(f32, 128)
+DK_DECL(f32, 256)
+#undef DK_DECL
+
+static int dh_index(int d_h) {
+  switch (d_h) {
+    case 16: return 0;
+    case 32: return 1;
+    case 64: return 2;
+    case 128: return 3;
+    case 256: return 4;
+    default: return -1;
+  }
+}
+static int r16_index(int r16) {
+  switch (r16) {
+    case 1: return 0;
+    case 2: return 1;
+    case 4: return 2;
+    case 8: return 3;
+    case 16: return 4;
+    default: return -1;
+  }
+}
+
+#define DK_ROW(dt, dh) {fwd_##dt##_d##dh##_r1, fwd_##dt##_d##dh##_r2, fwd_##dt##_d##dh##_r4, fwd_##dt##_d##dh##_r8, fwd_##dt##_d##dh##_r16}
+static const fwd_launcher kFwd[2][5][5] = {
+    {DK_ROW(f32, 16), DK_ROW(f32, 32), DK_ROW(f32, 64), DK_ROW(f32, 128), DK_ROW(f32, 256)},
+    {DK_ROW(bf16, 16), DK_ROW(bf16, 32), DK_ROW(bf16, 64), DK_ROW(bf16, 128), DK_ROW(bf16, 256)}};
+#undef DK_ROW
+static const decode_launcher kDec[2][5] = {
+    {dec_f32_d16, dec_f32_d32, dec_f32_d64, dec_f32_d128, dec_f32_d256},
+    {dec_bf16_d16, dec_bf16_d32, dec_bf16_d64, dec_bf16_d128, dec_bf16_d256}};
+
+fwd_launcher find_fwd_launcher(int dtype, int d_h, int r16) {
+  const int i = dh_index(d_h), j = r16_index(r16);
+  if (dtype < 0 || dtype > 1 || i < 0 || j < 0) return nullptr;
+  return kFwd[dtype][i][j];
+}
+decode_launcher find_decode_launcher(int dtype, int d_h) {
+  const int i = dh_index(d_h);
+  if (dtype < 0 || dtype > 1 || i < 0) return nullptr;
+  return kDec[dtype][i];
+}
+
+static int rank_blocks(int r) { return r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : r <= 128 ? 8 : 16; }
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+
+// Features per wave in the key-side kernel (must match the instantiation units).
+static int features_per_wave(int d_h) { return d_h <= 64 ? 64 : 32; }
+
+static void make_plan(const dark_prf_desc& d, Plan& p) {
+  memset(&p, 0, sizeof(p));
+  p.DH = d.d_h;
+  p.R16 = rank_blocks(d.r);
+  p.KD = (d.d_h + 31) / 32;
+  p.RK = (p.R16 + 1) / 2;
+  p.FB = d.m / 16;
+  p.PM = (d.m + 31) / 32;
+  p.HM = d.m_per_head ? d.H : 1;
+  p.BH = d.B * d.H;
+  p.elem = d.dtype == DARK_BF16 ? 2 : 4;
+  p.FW = features_per_wave(d.d_h);
+  p.NF = cdiv(p.FB, 4 * (p.FW / 16));
+  const int L = d.L > 0 ? d.L : 1;
+  if (d.causal) {
+    // chunk = 64 NQB tokens: the key-side unit, the query-side tile and the
+    // granularity of the materialised chunk states
+    const long chunks64 = (long)p.BH * cdiv(L, 64);
+    const size_t lds2 = (size_t)(d.d_h * (128 + 8) + 2 * 4 * 2 * 64 * 8) * p.elem;
+    p.NQB = ((chunks64 > 8192 || d.d_h >= 128) && lds2 <= 160 * 1024) ? 2 : 1;
+    p.tile2 = 64 * p.NQB;
+    p.span1 = p.tile2;
+    p.NU = cdiv(L, p.span1);
+    p.NT2 = p.NU;
+  } else {
+    p.NQB = d.d_h <= 64 ? 4 : 1;
+    p.tile2 = 64 * p.NQB;
+    p.NT2 = cdiv(L, p.tile2);
+    int splits = cdiv(512, (long)p.BH * p.NF);
+    splits = splits < 1 ? 1 : splits;
+    const int max_splits = cdiv(L, 64);
+    if (splits > max_splits) splits = max_splits;
+    p.span1 = cdiv(cdiv(L, splits), 64) * 64;
+    p.NU = cdiv(L, p.span1);
+  }
+  // operand copies of M' and omega' (bf16: hi and lo parts; see prf_kernels.cuh)
+  const bool split = d.dtype == DARK_BF16;
+  const int NM = split ? 2 : 1;
+  const int NO = !split ? p.RK : (p.R16 == 1 ? 2 : 2 * p.RK);
+  size_t off = 0;
+  p.off_mfrag = off;
+  off = align256(off + (size_t)p.HM * p.R16 * p.KD * NM * 64 * 8 * p.elem);
+  p.off_ofrag = off;
+  off = align256(off + (size_t)p.FB * NO * 64 * 8 * p.elem);
+  p.off_spart = off;
+  off = align256(off + (size_t)p.BH * p.NU * (d.d_h + 1) * (size_t)d.m * sizeof(float));
+  p.off_sfrag = off;
+  off = align256(off + (size_t)p.BH * (d.causal ? p.NU : 1) * (d.d_h / 16 + 1) * p.PM * 64 * 8 * p.elem);
+  p.total = off;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Shape and stride checks shared by the forward and decode entry points.
+static dark_status check_desc(const dark_prf_desc* d, bool decode) {
+  if (!d) return DARK_ERR_INVALID_ARG;
+  if (d->B < 0 || d->L < 0 || d->H < 1 || d->H_kv < 1 || d->H % d->H_kv != 0) return DARK_ERR_INVALID_ARG;
+  if (dh_index(d->d_h) < 0) return DARK_ERR_INVALID_ARG;
+  if (d->m < 16 || d->m % 16 != 0) return DARK_ERR_INVALID_ARG;
+  if (d->r < 1 || d->r > 256) return DARK_ERR_INVALID_ARG;
+  if (d->dtype != DARK_F32 && d->dtype != DARK_BF16) return DARK_ERR_INVALID_ARG;
+  if (d->causal != 0 && d->causal != 1) return DARK_ERR_INVALID_ARG;
+  if (d->m_per_head != 0 && d->m_per_head != 1) return DARK_ERR_INVALID_ARG;
+  if (decode && (d->L != 1 || d->causal != 1)) return DARK_ERR_INVALID_ARG;
+  const int64_t elem = d->dtype == DARK_BF16 ? 2 : 4;
+  const int64_t* strides[4] = {d->q_str, d->k_str, d->v_str, d->o_str};
+  for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 3; ++i) {
+      if (decode && i == 2) continue;
+      if (strides[t][i] < 0 || (strides[t][i] * elem) % 16 != 0) return DARK_ERR_INVALID_ARG;
+    }
+  if (!decode) {
+    for (int t = 0; t < 4; ++t)
+      if (d->L > 1 && strides[t][2] < d->d_h) return DARK_ERR_INVALID_ARG;
+  }
+  // element offsets are formed in 64-bit; the grid is formed in 32-bit
+  if ((int64_t)d->B * d->H * ((int64_t)d->L + 255) > (int64_t)1 << 31) return DARK_ERR_UNSUPPORTED;
+  return DARK_OK;
+}
+
+// ---- Omega: SplitMix64 + Box-Muller; Householder QR with the sign of R ----
+static inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+static inline double uniform_at(uint64_t seed, uint64_t i) {
+  const uint64_t x = mix64(seed + (i + 1) * 0x9E3779B97F4A7C15ULL);
+  return ((double)(x >> 11) + 1.0) * 0x1.0p-53;
+}
+static double normal_at(uint64_t seed, uint64_t k) {
+  const uint64_t p = k >> 1;
+  const double u1 = uniform_at(seed, 2 * p);
+  const double u2 = uniform_at(seed, 2 * p + 1);
+  const double rad = sqrt(-2.0 * log(u1));
+  const double ang = 2.0 * M_PI * u2;
+  return (k & 1) ? rad * sin(ang) : rad * cos(ang);
+}
+
+// Q of G = Q R (n x n, row-major, overwritten) by Householder reflections,
+// with column j of Q multiplied by the sign of R[j][j] so that Q is Haar.
+static void haar_q(std::vector<double>& G, int n, std::vector<double>& Q) {
+  std::vector<double> V((size_t)n * n, 0.0);   // reflector k in column k (rows k..n-1)
+  std::vector<double> vn2(n, 0.0), diag(n, 0.0);
+  for (int k = 0; k < n; ++k) {
+    double norm = 0.0;
+    for (int i = k; i < n; ++i) norm += G[(size_t)i * n + k] * G[(size_t)i * n + k];
+    norm = sqrt(norm);
+    const double alpha = G[(size_t)k * n + k] >= 0.0 ? -norm : norm;
+    for (int i = k; i < n; ++i) {
+      const double vi = G[(size_t)i * n + k] - (i == k ? alpha : 0.0);
+      V[(size_t)i * n + k] = vi;
+      vn2[k] += vi * vi;
+    }
+    if (vn2[k] > 0.0) {
+      for (int j = k; j < n; ++j) {
+        double dot = 0.0;
+        for (int i = k; i < n; ++i) dot += V[(size_t)i * n + k] * G[(size_t)i * n + j];
+        const double f = 2.0 * dot / vn2[k];
+        for (int i = k; i < n; ++i) G[(size_t)i * n + j] -= f * V[(size_t)i * n + k];
+      }
+    }
+    diag[k] = G[(size_t)k * n + k];
+  }
+  Q.assign((size_t)n * n, 0.0);
+  for (int i = 0; i < n; ++i) Q[(size_t)i * n + i] = 1.0;
+  // Q = H_0 H_1 ... H_{n-1} applied to the identity, right to left
+  for (int k = n - 1; k >= 0; --k) {
+    if (vn2[k] <= 0.0) continue;
+    for (int j = 0; j < n; ++j) {
+      double dot = 0.0;
+      for (int i = k; i < n; ++i) dot += V[(size_t)i * n + k] * Q[(size_t)i * n + j];
+      const double f = 2.0 * dot / vn2[k];
+      for (int i = k; i < n; ++i) Q[(size_t)i * n + j] -= f * V[(size_t)i * n + k];
+    }
+  }
+  for (int j = 0; j < n; ++j)
+    if (diag[j] < 0.0)
+      for (int i = 0; i < n; ++i) Q[(size_t)i * n + j] = -Q[(size_t)i * n + j];
+}
+
+// ---- optional per-kernel timing ----
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> recs;
+};
+static TimingState& timing() {
+  static TimingState t;
+  return t;
+}
+
+KernelTimer::KernelTimer(int k, void* s) : kind(k), stream(s), ev0(nullptr), ev1(nullptr) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (!t.on) return;
+  hipEvent_t a, b;
+  if (hipEventCreate(&a) != hipSuccess) return;
+  if (hipEventCreate(&b) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return;
+  }
+  (void)hipEventRecord(a, reinterpret_cast<hipStream_t>(s));
+  ev0 = a;
+  ev1 = b;
+}
+
+KernelTimer::~KernelTimer() {
+  if (!ev0) return;
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev1), reinterpret_cast<hipStream_t>(stream));
+  t.recs.push_back({kind, {reinterpret_cast<hipEvent_t>(ev0), reinterpret_cast<hipEvent_t>(ev1)}});
+}
+
+static void drop_records(TimingState& t) {
+  for (auto& r : t.recs) {
+    (void)hipEventDestroy(r.second.first);
+    (void)hipEventDestroy(r.second.second);
+  }
+  t.recs.clear();
+}
+
+}  // namespace dk
+
+using namespace dk;
+
+extern "C" {
+
+const char* dark_prf_status_str(dark_status s) {
+  switch (s) {
+    case DARK_OK: return "DARK_OK";
+    case DARK_ERR_INVALID_ARG: return "DARK_ERR_INVALID_ARG";
+    case DARK_ERR_UNSUPPORTED: return "DARK_ERR_UNSUPPORTED";
+    case DARK_ERR_WORKSPACE: return "DARK_ERR_WORKSPACE";
+    case DARK_ERR_STALE_STATE: return "DARK_ERR_STALE_STATE";
+    case DARK_ERR_HIP: return "DARK_ERR_HIP";
+    default: return "DARK_ERR_UNKNOWN";
+  }
+}
+
+uint64_t dark_prf_proj_tag(uint64_t seed, int32_t m, int32_t r, int32_t orthogonal) {
+  const uint64_t shape = ((uint64_t)(uint32_t)m << 32) ^ ((uint64_t)(uint32_t)r << 1) ^ (orthogonal ? 1u : 0u);
+  return mix64(mix64(seed + 0x9E3779B97F4A7C15ULL) ^ mix64(shape + 0x632BE59BD9B4E019ULL));
+}
+
+dark_status dark_prf_omega(uint64_t seed, int32_t m, int32_t r, int32_t orthogonal, float* omega_host) {
+  if (m < 1 || r < 1 || omega_host == nullptr) return DARK_ERR_INVALID_ARG;
+  if (!orthogonal) {
+    for (int64_t i = 0; i < (int64_t)m * r; ++i) omega_host[i] = (float)normal_at(seed, (uint64_t)i);
+    return DARK_OK;
+  }
+  const int blocks = (m + r - 1) / r;
+  std::vector<double> G((size_t)r * r), Q;
+  for (int b = 0; b < blocks; ++b) {
+    const uint64_t base = 2ull * (uint64_t)b * r * r;
+    for (int i = 0; i < r * r; ++i) G[i] = normal_at(seed, base + i);
+    haar_q(G, r, Q);
+    const int keep = (m - b * r) < r ? (m - b * r) : r;
+    for (int a = 0; a < keep; ++a) {
+      double nn = 0.0;
+      for (int c = 0; c < r; ++c) {
+        const double x = normal_at(seed, base + (uint64_t)r * r + (uint64_t)a * r + c);
+        nn += x * x;
+      }
+      const double norm = sqrt(nn);
+      for (int c = 0; c < r; ++c) omega_host[((int64_t)b * r + a) * r + c] = (float)(norm * Q[(size_t)a * r + c]);
+    }
+  }
+  return DARK_OK;
+}
+
+size_t dark_prf_workspace_bytes(const dark_prf_desc* desc) {
+  if (check_desc(desc, false) != DARK_OK) return 0;
+  Plan p;
+  make_plan(*desc, p);
+  return p.total;
+}
+
+__global__ void dk_fill_zero(float* p, long n) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) p[i] = 0.f;
+}
+
+dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k, const void* v,
+                         const float* M, const float* omega, const uint8_t* mask, void* out, float* S_out,
+                         float* z_out, void* workspace, size_t ws_bytes, void* stream) {
+  dark_status st = check_desc(desc, false);
+  if (st != DARK_OK) return st;
+  const dark_prf_desc& d = *desc;
+  if ((S_out == nullptr) != (z_out == nullptr)) return DARK_ERR_INVALID_ARG;
+  if (S_out && !d.causal) return DARK_ERR_INVALID_ARG;
+  if (d.B == 0) return DARK_OK;
+  if (d.L == 0) {
+    if (S_out) {
+      hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+      const long nS = (long)d.B * d.H * d.m * d.d_h, nz = (long)d.B * d.H * d.m;
+      hipLaunchKernelGGL(dk_fill_zero, dim3(256), dim3(256), 0, s, S_out, nS);
+      hipLaunchKernelGGL(dk_fill_zero, dim3(64), dim3(256), 0, s, z_out, nz);
+      return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
+    }
+    return DARK_OK;
+  }
+  if (!q || !k || !v || !M || !omega || !out) return DARK_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return DARK_ERR_INVALID_ARG;
+  if (!aligned16(M) || !aligned16(omega)) return DARK_ERR_INVALID_ARG;
+  if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return DARK_ERR_INVALID_ARG;
+  Plan p;
+  make_plan(d, p);
+  if (workspace == nullptr || ws_bytes < p.total) return DARK_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DARK_ERR_INVALID_ARG;
+  fwd_launcher fn = find_fwd_launcher(d.dtype, d.d_h, p.R16);
+  if (!fn) return DARK_ERR_UNSUPPORTED;
+  FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = d.q_str[i];
+    a.ks[i] = d.k_str[i];
+    a.vs[i] = d.v_str[i];
+    a.os[i] = d.o_str[i];
+  }
+  a.mask = mask;
+  a.M = M;
+  a.omega = omega;
+  a.S_out = S_out;
+  a.z_out = z_out;
+  a.B = d.B;
+  a.H = d.H;
+  a.H_kv = d.H_kv;
+  a.L = d.L;
+  a.m = d.m;
+  a.r = d.r;
+  a.causal = d.causal;
+  a.m_per_head = d.m_per_head;
+  return fn(a, p, workspace, stream);
+}
+
+dark_status dark_prf_decode_step(const dark_prf_desc* desc, const void* q, const void* k, const void* v,
+                                 const float* M, const float* omega, float* S, float* z, uint64_t state_tag,
+                                 void* out, void* stream) {
+  dark_status st = check_desc(desc, true);
+  if (st != DARK_OK) return st;
+  const dark_prf_desc& d = *desc;
+  if (state_tag != d.proj_tag) return DARK_ERR_STALE_STATE;
+  if (d.B == 0) return DARK_OK;
+  if (!q || !k || !v || !M || !omega || !S || !z || !out) return DARK_ERR_INVALID_ARG;
+  if (!aligned16(S) || !aligned16(z) || !aligned16(M) || !aligned16(omega)) return DARK_ERR_INVALID_ARG;
+  decode_launcher fn = find_decode_launcher(d.dtype, d.d_h);
+  if (!fn) return DARK_ERR_UNSUPPORTED;
+  return fn(d, q, k, v, M, omega, S, z, out, stream);
+}
+
+dark_status dark_prf_timing_begin(void) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  drop_records(t);
+  t.on = true;
+  return DARK_OK;
+}
+
+dark_status dark_prf_timing_end(double* ms, int32_t* launches) {
+  if (!ms || !launches) return DARK_ERR_INVALID_ARG;
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  for (int i = 0; i < DARK_KERNEL_KINDS; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  dark_status st = DARK_OK;
+  for (auto& r : t.recs) {
+    float e = 0.f;
+    if (hipEventSynchronize(r.second.second) != hipSuccess ||
+        hipEventElapsedTime(&e, r.second.first, r.second.second) != hipSuccess) {
+      st = DARK_ERR_HIP;
+      continue;
+    }
+    if (r.first >= 0 && r.first < DARK_KERNEL_KINDS) {
+      ms[r.first] += e;
+      launches[r.first] += 1;
+    }
+  }
+  drop_records(t);
+  t.on = false;
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Shared host/device definitions of the darkprf HIP library (gfx950).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/darkprf.h"
+
+namespace dk {
+
+// Arguments of one dark_prf_fwd call after validation.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  const uint8_t* mask;
+  const float* M;
+  const float* omega;
+  float* S_out;
+  float* z_out;
+  int B, H, H_kv, L, m, r, causal, m_per_head;
+};
+
+// How one call is cut into kernels; all sizes derived on the host.
+struct Plan {
+  int DH;      // head dimension (template value)
+  int R16;     // geometry rank rounded up to 16, in 16-row blocks (1, 2, 4, 8, 16)
+  int KD;      // 32-wide K-steps over d_h for the projection u = s M x
+  int RK;      // 32-wide K-steps over r for the feature exponent
+  int FB;      // 16-feature blocks (m / 16)
+  int PM;      // 32-feature K-steps (ceil(m / 32))
+  int HM;      // number of geometry matrices (H or 1)
+  int BH;      // B * H
+  // key-side state kernel
+  int span1;   // tokens per unit (a chunk when causal, an L-split otherwise)
+  int NU;      // units per (b, h)
+  int FW;      // features per wave
+  int NF;      // feature slices per unit (each slice = 4 waves * FW features)
+  // query-side output kernel
+  int NQB;     // 16-token query blocks per wave
+  int tile2;   // queries per workgroup (4 waves * 16 * NQB); equals span1 when causal
+  int NT2;     // query tiles per (b, h)
+  // workspace (bytes from the base pointer)
+  size_t off_mfrag, off_ofrag, off_spart, off_sfrag, total;
+  int elem;    // bytes per element of q/k/v (2 or 4)
+};
+
+// Optional per-kernel timing (dark_prf_timing_begin / _end): records a HIP
+// event pair on `stream` around one launch while timing is on.
+enum KernelKind { kPrep = 0, kKState = 1, kScan = 2, kQOut = 3, kDecode = 4 };
+struct KernelTimer {
+  KernelTimer(int kind, void* stream);
+  ~KernelTimer();
+  int kind;
+  void* stream;
+  void* ev0;
+  void* ev1;
+};
+
+// One launcher per (element type, head dimension, rank blocks); defined in the
+// instantiation units.
+typedef dark_status (*fwd_launcher)(const FwdArgs&, const Plan&, void* ws, void* stream);
+fwd_launcher find_fwd_launcher(int dtype, int d_h, int r16);
+
+typedef dark_status (*decode_launcher)(const dark_prf_desc&, const void* q, const void* k,
+                                       const void* v, const float* M, const float* omega,
+                                       float* S, float* z, void* out, void* stream);
+decode_launcher find_decode_launcher(int dtype, int d_h);
+
+}  // namespace dk

@@ -1,0 +1,15 @@
+// Instantiation unit: element type bf16, head dimension 256.
+#include "prf_kernels.cuh"
+#include "decode_kernels.cuh"
+
+namespace dk {
+dark_status fwd_bf16_d256_r1(const FwdArgs& a, const Plan& p, void* ws, void* s) { return launch_fwd_impl<bf16, 256, 1, 32>(a, p, ws, s); }
+dark_status fwd_bf16_d256_r2(const FwdArgs& a, const Plan& p, void* ws, void* s) { return launch_fwd_impl<bf16, 256, 2, 32>(a, p, ws, s); }
+dark_status fwd_bf16_d256_r4(const FwdArgs& a, const Plan& p, void* ws, void* s) { return launch_fwd_impl<bf16, 256, 4, 32>(a, p, ws, s); }
+dark_status fwd_bf16_d256_r8(const FwdArgs& a, const Plan& p, void* ws, void* s) { return launch_fwd_impl<bf16, 256, 8, 32>(a, p, ws, s); }
+dark_status fwd_bf16_d256_r16(const FwdArgs& a, const Plan& p, void* ws, void* s) { return launch_fwd_impl<bf16, 256, 16, 32>(a, p, ws, s); }
+dark_status dec_bf16_d256(const dark_prf_desc& d, const void* q, const void* k, const void* v, const float* M,
+                         const float* om, float* S, float* z, void* out, void* s) {
+  return launch_decode_impl<bf16, 256>(d, q, k, v, M, om, S, z, out, s);
+}
+}  // namespace dk

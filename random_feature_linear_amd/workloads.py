@@ -125,8 +125,8 @@ def _haar(rng: np.random.Generator, n: int) -> np.ndarray:
 
 def _tokens(w: Workload, rng: np.random.Generator, heads: int, L: int, kind: str,
             ctx: dict) -> np.ndarray:
-    """One q/k/v tensor [B][heads][L][d_h] in float64 before rounding."""
-    shape = (w.B, heads, L, w.d_h)
+    """One batch row of a q/k/v tensor: [heads][L][d_h] in float64 before rounding."""
+    shape = (heads, L, w.d_h)
     if kind == "iid":
         return rng.standard_normal(shape)
     if kind == "aniso":
@@ -137,7 +137,7 @@ def _tokens(w: Workload, rng: np.random.Generator, heads: int, L: int, kind: str
         # N(0, I) plus U c with U an orthonormal d_h x 8 basis shared by q, k and all
         # heads, and c ~ N(0, 3^2 I_8) drawn per token, head and tensor
         base = rng.standard_normal(shape)
-        c = 3.0 * rng.standard_normal((w.B, heads, L, 8))
+        c = 3.0 * rng.standard_normal((heads, L, 8))
         return base + c @ ctx["spike_basis"].T
     if kind == "cov":
         # N(0, C) with C = R diag(lam) R^T, lam_i = (1+i)^-1.5
@@ -146,15 +146,8 @@ def _tokens(w: Workload, rng: np.random.Generator, heads: int, L: int, kind: str
     raise ValueError(kind)
 
 
-def make_inputs(w: Workload, L: Optional[int] = None) -> dict:
-    """Draw M, q, k, v and the key mask for one workload.
-
-    Draw order is fixed: extras (spike basis / covariance rotation), M, q, k, v,
-    mask padding.  Returns float32 arrays (bf16-exact when w.dtype == "bf16") in
-    [B][H][L][d_h] layout for q and [B][H_kv][L][d_h] for k and v, a uint8 mask
-    [B][L] (1 = valid key) or None, and M.
-    """
-    L = w.L if L is None else L
+def _shared(w: Workload):
+    """Draws shared by every batch row: extras, then M (stream PCG64(seed))."""
     rng = np.random.Generator(np.random.PCG64(w.seed))
     ctx: dict = {}
     if w.x_kind == "spike":
@@ -162,7 +155,12 @@ def make_inputs(w: Workload, L: Optional[int] = None) -> dict:
     if w.x_kind == "cov":
         ctx["cov_rot"] = _haar(rng, w.d_h)
         ctx["cov_sqrt_lam"] = (1.0 + np.arange(w.d_h)) ** -0.75
-    M = _geometry(w, rng)
+    return ctx, _geometry(w, rng)
+
+
+def _row(w: Workload, ctx: dict, b: int, L: int):
+    """q, k, v and mask of batch row b (stream PCG64([seed, b + 1]))."""
+    rng = np.random.Generator(np.random.PCG64([w.seed, b + 1]))
     qk_kind = w.x_kind
     v_kind = "iid" if w.x_kind in ("spike", "cov") else w.x_kind
     q = round_to(_tokens(w, rng, w.H, L, qk_kind, ctx), w.dtype)
@@ -170,24 +168,51 @@ def make_inputs(w: Workload, L: Optional[int] = None) -> dict:
     v = round_to(_tokens(w, rng, w.hkv, L, v_kind, ctx), w.dtype)
     mask = None
     if w.mask_kind == "ones":
-        mask = np.ones((w.B, L), dtype=np.uint8)
+        mask = np.ones(L, dtype=np.uint8)
     elif w.mask_kind == "tail":
-        pads = rng.integers(0, w.max_pad + 1, size=w.B)
-        mask = np.ones((w.B, L), dtype=np.uint8)
-        for b in range(w.B):
-            if pads[b] > 0:
-                mask[b, L - min(int(pads[b]), L):] = 0
+        pad = int(rng.integers(0, w.max_pad + 1))
+        mask = np.ones(L, dtype=np.uint8)
+        if pad > 0:
+            mask[L - min(pad, L):] = 0
     elif w.mask_kind == "random":
-        mask = (rng.random((w.B, L)) < 0.7).astype(np.uint8)
+        mask = (rng.random(L) < 0.7).astype(np.uint8)
     elif w.mask_kind != "none":
         raise ValueError(w.mask_kind)
-    return {"q": q, "k": k, "v": v, "M": M, "mask": mask}
+    return q, k, v, mask
 
 
-def make_decode_tokens(w: Workload, steps: int, seed_offset: int = 77) -> dict:
-    """q, k, v for `steps` one-token decode steps: [steps][B][H][d_h] each (N(0,1))."""
-    rng = np.random.Generator(np.random.PCG64(w.seed + seed_offset))
-    out = {}
-    for name, heads in (("q", w.H), ("k", w.hkv), ("v", w.hkv)):
-        out[name] = round_to(rng.standard_normal((steps, w.B, heads, w.d_h)), w.dtype)
-    return out
+def make_inputs(w: Workload, L: Optional[int] = None, rows: Optional[list] = None) -> dict:
+    """Draw M, q, k, v and the key mask for one workload.
+
+    M (and any shared basis) comes from the stream PCG64(seed); batch row b draws
+    q, k, v and its mask padding, in that order, from PCG64([seed, b + 1]), so any
+    subset of rows can be regenerated alone (`rows`).  Returns float32 arrays
+    (bf16-exact when w.dtype == "bf16"): q [B][H][L][d_h], k and v
+    [B][H_kv][L][d_h], mask uint8 [B][L] (1 = valid key) or None, and M.
+    """
+    L = w.L if L is None else L
+    rows = list(range(w.B)) if rows is None else list(rows)
+    ctx, M = _shared(w)
+    qs, ks, vs, ms = [], [], [], []
+    for b in rows:
+        q, k, v, mk = _row(w, ctx, b, L)
+        qs.append(q)
+        ks.append(k)
+        vs.append(v)
+        ms.append(mk)
+    mask = None if ms[0] is None else np.stack(ms)
+    return {"q": np.stack(qs), "k": np.stack(ks), "v": np.stack(vs), "M": M, "mask": mask}
+
+
+def make_decode_tokens(w: Workload, steps: int, rows: Optional[list] = None) -> dict:
+    """q, k, v for `steps` one-token decode steps: [steps][len(rows)][heads][d_h], N(0,1).
+
+    Batch row b draws from PCG64([seed, 100000 + b]) (q, then k, then v).
+    """
+    rows = list(range(w.B)) if rows is None else list(rows)
+    out = {"q": [], "k": [], "v": []}
+    for b in rows:
+        rng = np.random.Generator(np.random.PCG64([w.seed, 100000 + b]))
+        for name, heads in (("q", w.H), ("k", w.hkv), ("v", w.hkv)):
+            out[name].append(round_to(rng.standard_normal((steps, heads, w.d_h)), w.dtype))
+    return {k2: np.stack(v2, axis=1) for k2, v2 in out.items()}

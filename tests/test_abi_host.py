@@ -1,0 +1,154 @@
+"""Host-side tests of the C ABI: symbols, validation, workspace sizing, Omega.
+
+No kernel runs here: every call below returns before anything is queued.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import omega_gen as oo
+from random_feature_linear_amd import binding as bd
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "darkprf.h")
+FAKE = 1 << 20          # an aligned, never dereferenced stand-in for a device address
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dark_prf_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) == 8, names
+    L = bd.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _desc(**kw):
+    d = bd.DarkPrfDesc()
+    base = dict(B=2, H=8, H_kv=8, L=256, d_h=64, m=256, r=64, dtype=bd.DARK_BF16, causal=1, m_per_head=1)
+    base.update(kw)
+    for k, v in base.items():
+        if not k.endswith("_str"):
+            setattr(d, k, v)
+    L, dh, H = base["L"], base["d_h"], base["H"]
+    for name, heads in (("q_str", H), ("k_str", base["H_kv"]), ("v_str", base["H_kv"]), ("o_str", H)):
+        getattr(d, name)[:] = kw.get(name, [heads * L * dh, L * dh, dh])
+    return d
+
+
+def _fwd(d, ws_bytes=None, S=0, z=0, mask=0, ws=FAKE):
+    nb = bd.dark_prf_workspace_bytes(d) if ws_bytes is None else ws_bytes
+    return bd.dark_prf_fwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, mask, FAKE, S, z, ws, nb, 0)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(H=8, H_kv=3), dict(d_h=48), dict(d_h=512), dict(m=24), dict(m=0), dict(r=0), dict(r=257),
+    dict(dtype=7), dict(causal=2), dict(m_per_head=3), dict(B=-1), dict(H=0),
+    dict(q_str=[8 * 256 * 64, 256 * 64, 60]),      # rows overlap
+    dict(k_str=[8 * 256 * 64, 256 * 64, 68]),      # 136-byte rows: not 16-byte aligned
+])
+def test_invalid_descriptors(kw):
+    d = _desc(**kw)
+    assert _fwd(d, ws_bytes=1 << 40) == bd.DARK_ERR_INVALID_ARG
+    assert bd.dark_prf_workspace_bytes(d) == 0
+
+
+def test_null_and_misaligned_pointers():
+    d = _desc()
+    nb = bd.dark_prf_workspace_bytes(d)
+    assert bd.dark_prf_fwd(d, 0, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0, 0, FAKE, nb, 0) == bd.DARK_ERR_INVALID_ARG
+    assert bd.dark_prf_fwd(d, FAKE + 2, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0, 0, FAKE, nb, 0) == bd.DARK_ERR_INVALID_ARG
+    assert bd.dark_prf_fwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, 0, FAKE, nb, 0) == bd.DARK_ERR_INVALID_ARG
+
+
+def test_workspace_checks():
+    d = _desc()
+    nb = bd.dark_prf_workspace_bytes(d)
+    assert nb > 0
+    assert _fwd(d, ws_bytes=nb - 1) == bd.DARK_ERR_WORKSPACE
+    assert _fwd(d, ws=0) == bd.DARK_ERR_WORKSPACE
+    # more tokens never need less workspace
+    assert bd.dark_prf_workspace_bytes(_desc(L=4096)) >= nb
+
+
+def test_state_export_rules():
+    assert _fwd(_desc(causal=0), S=FAKE, z=FAKE) == bd.DARK_ERR_INVALID_ARG
+    assert _fwd(_desc(causal=1), S=FAKE, z=0) == bd.DARK_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op():
+    assert _fwd(_desc(B=0), ws=0, ws_bytes=0) == bd.DARK_OK
+
+
+def _dec_desc(**kw):
+    kw.setdefault("L", 1)
+    return _desc(**kw)
+
+
+def test_decode_rejects_stale_state():
+    d = _dec_desc()
+    d.proj_tag = bd.dark_prf_proj_tag(7, 256, 64, True)
+    other = bd.dark_prf_proj_tag(8, 256, 64, True)
+    st = bd.dark_prf_decode_step(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, other, FAKE, 0)
+    assert st == bd.DARK_ERR_STALE_STATE
+
+
+def test_decode_argument_checks():
+    d = _dec_desc(L=2)
+    assert bd.dark_prf_decode_step(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0) == bd.DARK_ERR_INVALID_ARG
+    d = _dec_desc()
+    d.causal = 0
+    assert bd.dark_prf_decode_step(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0) == bd.DARK_ERR_INVALID_ARG
+    d = _dec_desc()
+    assert bd.dark_prf_decode_step(d, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0, FAKE, 0) == bd.DARK_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    assert bd.dark_prf_status_str(bd.DARK_OK) == "DARK_OK"
+    assert bd.dark_prf_status_str(bd.DARK_ERR_STALE_STATE) == "DARK_ERR_STALE_STATE"
+    assert bd.dark_prf_status_str(99) == "DARK_ERR_UNKNOWN"
+
+
+def test_proj_tag():
+    a = bd.dark_prf_proj_tag(5, 256, 64, True)
+    assert a == bd.dark_prf_proj_tag(5, 256, 64, True)
+    others = {bd.dark_prf_proj_tag(6, 256, 64, True), bd.dark_prf_proj_tag(5, 512, 64, True),
+              bd.dark_prf_proj_tag(5, 256, 32, True), bd.dark_prf_proj_tag(5, 256, 64, False)}
+    assert a not in others and len(others) == 4
+
+
+def test_omega_argument_checks():
+    buf = np.empty(4, np.float32)
+    L = bd.lib()
+    assert L.dark_prf_omega(1, 0, 2, 0, buf.ctypes.data_as(ctypes.c_void_p)) == bd.DARK_ERR_INVALID_ARG
+    assert L.dark_prf_omega(1, 2, 2, 0, None) == bd.DARK_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("seed,m,r,orth", [
+    (1001, 32, 16, False), (1002, 256, 64, True), (1003, 1024, 16, False), (1004, 512, 256, True),
+    (1005, 256, 64, True), (42, 100, 16, True), (7, 48, 64, True)])
+def test_library_omega_matches_oracle(seed, m, r, orth):
+    """The C++ and the numpy generators implement the same published stream."""
+    lib_om = bd.dark_prf_omega(seed, m, r, orth)
+    ref = oo.omega(seed, m, r, orth)
+    assert lib_om.shape == ref.shape and lib_om.dtype == np.float32
+    same = np.mean(lib_om == ref)
+    ulp = np.spacing(np.abs(ref).astype(np.float32))
+    assert same >= 0.999, same
+    assert np.all(np.abs(lib_om - ref) <= ulp), np.max(np.abs(lib_om - ref) / ulp)
+
+
+def test_timing_end_without_records():
+    import ctypes as ct
+    L = bd.lib()
+    assert L.dark_prf_timing_end(None, None) == bd.DARK_ERR_INVALID_ARG
+    bd.dark_prf_timing_begin()
+    res = bd.dark_prf_timing_end()
+    assert set(res) == set(bd.KERNEL_KINDS) and all(v == (0.0, 0) for v in res.values())
