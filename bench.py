@@ -135,13 +135,8 @@ class Forward:
 
 
 def chunk_len(w) -> int:
-    """Causal chunk the library plans for this workload (64 or 128 tokens)."""
-    if not w.causal:
-        return 0
-    chunks64 = w.B * w.H * -(-w.L // 64)
-    e = 2 if w.dtype == "bf16" else 4
-    lds2 = (w.d_h * (128 + 8) + 2 * 4 * 2 * 64 * 8) * e
-    return 128 if ((chunks64 > 8192 or w.d_h >= 128) and lds2 <= 160 * 1024) else 64
+    """Causal chunk the library plans (the query-side tile): 128 tokens."""
+    return 128 if w.causal else 0
 
 
 def measure(w, steps: int, warmup: int) -> dict:

@@ -53,6 +53,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise FileNotFoundError(
                 f"{LIB_PATH} is missing: build it with random_feature_linear_amd.build.build()")
+        # torch ships its own HIP runtime (SONAME libamdhip64.so.7).  Loading it
+        # first makes this library bind to that same runtime; loading this
+        # library first would put a second HIP runtime in the process, and
+        # torch's streams and memory would be foreign to it.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         P = ctypes.c_void_p
         L.dark_prf_omega.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]

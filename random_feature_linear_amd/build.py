@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -27,11 +28,23 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
+# MFMA results in ordinary VGPRs (no accumulator-register copies around the exp)
+# for the instantiations whose registers fit in 256 VGPRs; the others keep the
+# accumulator registers.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+_UNIT = re.compile(r"fwd_(bf16|f32)_d(\d+)_r(\d+)\.hip$")
+
+
+def _unit_flags(src: str) -> list:
+    m = _UNIT.search(os.path.basename(src))
+    if m and int(m.group(2)) <= 128 and int(m.group(3)) <= 4:
+        return VGPR_FORM
+    return []
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *_unit_flags(src), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr[-6000:]}")
@@ -41,7 +54,7 @@ def _compile(src: str) -> str:
 def build(jobs: int | None = None, verbose: bool = True) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
-    jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    jobs = jobs or max(1, min(16, os.cpu_count() or 1))
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"

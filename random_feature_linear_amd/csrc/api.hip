@@ -78,57 +78,56 @@ static int rank_blocks(int r) { return r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 :
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
-// Features per wave in the key-side kernel (must match the instantiation units).
-static int features_per_wave(int d_h) { return d_h <= 64 ? 64 : 32; }
+// 32-feature blocks per wave in the key-side kernel (must match the instantiation units).
+static int feature_blocks_per_wave(int d_h) { return d_h <= 64 ? 2 : 1; }
 
 static void make_plan(const dark_prf_desc& d, Plan& p) {
   memset(&p, 0, sizeof(p));
   p.DH = d.d_h;
   p.R16 = rank_blocks(d.r);
-  p.KD = (d.d_h + 31) / 32;
-  p.RK = (p.R16 + 1) / 2;
-  p.FB = d.m / 16;
-  p.PM = (d.m + 31) / 32;
+  p.FB = cdiv(d.m, 32);
   p.HM = d.m_per_head ? d.H : 1;
   p.BH = d.B * d.H;
   p.elem = d.dtype == DARK_BF16 ? 2 : 4;
-  p.FW = features_per_wave(d.d_h);
-  p.NF = cdiv(p.FB, 4 * (p.FW / 16));
+  p.FBW = feature_blocks_per_wave(d.d_h);
+  p.NF = cdiv(p.FB, 4 * p.FBW);
   const int L = d.L > 0 ? d.L : 1;
+  const int tile1 = 128;                 // key-side tile: 4 waves x 32 tokens
   if (d.causal) {
-    // chunk = 64 NQB tokens: the key-side unit, the query-side tile and the
+    // chunk = 128 tokens: the key-side unit, the query-side tile and the
     // granularity of the materialised chunk states
-    const long chunks64 = (long)p.BH * cdiv(L, 64);
-    const size_t lds2 = (size_t)(d.d_h * (128 + 8) + 2 * 4 * 2 * 64 * 8) * p.elem;
-    p.NQB = ((chunks64 > 8192 || d.d_h >= 128) && lds2 <= 160 * 1024) ? 2 : 1;
-    p.tile2 = 64 * p.NQB;
+    p.NQB = 1;
+    p.tile2 = 128;
     p.span1 = p.tile2;
     p.NU = cdiv(L, p.span1);
     p.NT2 = p.NU;
   } else {
-    p.NQB = d.d_h <= 64 ? 4 : 1;
-    p.tile2 = 64 * p.NQB;
+    p.NQB = d.d_h <= 64 ? 2 : 1;
+    p.tile2 = 128 * p.NQB;
     p.NT2 = cdiv(L, p.tile2);
     int splits = cdiv(512, (long)p.BH * p.NF);
     splits = splits < 1 ? 1 : splits;
-    const int max_splits = cdiv(L, 64);
+    const int max_splits = cdiv(L, tile1);
     if (splits > max_splits) splits = max_splits;
-    p.span1 = cdiv(cdiv(L, splits), 64) * 64;
+    p.span1 = cdiv(cdiv(L, splits), tile1) * tile1;
     p.NU = cdiv(L, p.span1);
   }
   // operand copies of M' and omega' (bf16: hi and lo parts; see prf_kernels.cuh)
-  const bool split = d.dtype == DARK_BF16;
-  const int NM = split ? 2 : 1;
-  const int NO = !split ? p.RK : (p.R16 == 1 ? 2 : 2 * p.RK);
+  const int NM = d.dtype == DARK_BF16 ? 2 : 1;
+  const int R32 = (p.R16 + 1) / 2;
+  const int DB = (d.d_h + 1 + 31) / 32;  // 32-column blocks of [V, 1]
+  const size_t frag = 64 * 8;            // elements per operand fragment
+  const size_t state_frags = (size_t)DB * 2 * p.FB;   // fragments of one unit state [S, z]
+  const int nout = d.causal ? p.NU : 1;
   size_t off = 0;
   p.off_mfrag = off;
-  off = align256(off + (size_t)p.HM * p.R16 * p.KD * NM * 64 * 8 * p.elem);
+  off = align256(off + (size_t)p.HM * R32 * (d.d_h / 16) * NM * frag * p.elem);
   p.off_ofrag = off;
-  off = align256(off + (size_t)p.FB * NO * 64 * 8 * p.elem);
-  p.off_spart = off;
-  off = align256(off + (size_t)p.BH * p.NU * (d.d_h + 1) * (size_t)d.m * sizeof(float));
+  off = align256(off + (size_t)p.FB * p.R16 * NM * frag * p.elem);
+  p.off_sdelta = off;
+  off = align256(off + (size_t)p.BH * p.NU * state_frags * frag * p.elem);
   p.off_sfrag = off;
-  off = align256(off + (size_t)p.BH * (d.causal ? p.NU : 1) * (d.d_h / 16 + 1) * p.PM * 64 * 8 * p.elem);
+  off = align256(off + (size_t)p.BH * nout * state_frags * frag * p.elem);
   p.total = off;
 }
 
@@ -335,6 +334,7 @@ dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k
   if (d.B == 0) return DARK_OK;
   if (d.L == 0) {
     if (S_out) {
+      (void)hipGetLastError();
       hipStream_t s = reinterpret_cast<hipStream_t>(stream);
       const long nS = (long)d.B * d.H * d.m * d.d_h, nz = (long)d.B * d.H * d.m;
       hipLaunchKernelGGL(dk_fill_zero, dim3(256), dim3(256), 0, s, S_out, nS);
@@ -353,6 +353,7 @@ dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k
   if (!aligned16(workspace)) return DARK_ERR_INVALID_ARG;
   fwd_launcher fn = find_fwd_launcher(d.dtype, d.d_h, p.R16);
   if (!fn) return DARK_ERR_UNSUPPORTED;
+  (void)hipGetLastError();   // launch errors below are ours, not an earlier caller's
   FwdArgs a;
   a.q = q;
   a.k = k;
@@ -392,6 +393,7 @@ dark_status dark_prf_decode_step(const dark_prf_desc* desc, const void* q, const
   if (!aligned16(S) || !aligned16(z) || !aligned16(M) || !aligned16(omega)) return DARK_ERR_INVALID_ARG;
   decode_launcher fn = find_decode_launcher(d.dtype, d.d_h);
   if (!fn) return DARK_ERR_UNSUPPORTED;
+  (void)hipGetLastError();   // launch errors below are ours, not an earlier caller's
   return fn(d, q, k, v, M, omega, S, z, out, stream);
 }
 

@@ -25,24 +25,21 @@ struct FwdArgs {
 // How one call is cut into kernels; all sizes derived on the host.
 struct Plan {
   int DH;      // head dimension (template value)
-  int R16;     // geometry rank rounded up to 16, in 16-row blocks (1, 2, 4, 8, 16)
-  int KD;      // 32-wide K-steps over d_h for the projection u = s M x
-  int RK;      // 32-wide K-steps over r for the feature exponent
-  int FB;      // 16-feature blocks (m / 16)
-  int PM;      // 32-feature K-steps (ceil(m / 32))
+  int R16;     // geometry rank in 16-wide blocks, rounded up to 1, 2, 4, 8 or 16
+  int FB;      // 32-feature blocks (ceil(m / 32))
   int HM;      // number of geometry matrices (H or 1)
   int BH;      // B * H
   // key-side state kernel
   int span1;   // tokens per unit (a chunk when causal, an L-split otherwise)
   int NU;      // units per (b, h)
-  int FW;      // features per wave
-  int NF;      // feature slices per unit (each slice = 4 waves * FW features)
+  int FBW;     // 32-feature blocks per wave
+  int NF;      // feature slices per unit (each slice = 4 waves * FBW blocks)
   // query-side output kernel
-  int NQB;     // 16-token query blocks per wave
-  int tile2;   // queries per workgroup (4 waves * 16 * NQB); equals span1 when causal
+  int NQB;     // 32-token query blocks per wave
+  int tile2;   // queries per workgroup (4 waves * 32 * NQB); equals span1 when causal
   int NT2;     // query tiles per (b, h)
   // workspace (bytes from the base pointer)
-  size_t off_mfrag, off_ofrag, off_spart, off_sfrag, total;
+  size_t off_mfrag, off_ofrag, off_sdelta, off_sfrag, total;
   int elem;    // bytes per element of q/k/v (2 or 4)
 };
 

@@ -1,0 +1,10 @@
+// Decode instantiation: element type bf16, head dimension 16.
+#include "prf_kernels.cuh"
+#include "decode_kernels.cuh"
+
+namespace dk {
+dark_status dec_bf16_d16(const dark_prf_desc& d, const void* q, const void* k, const void* v, const float* M,
+                         const float* om, float* S, float* z, void* out, void* s) {
+  return launch_decode_impl<bf16, 16>(d, q, k, v, M, om, S, z, out, s);
+}
+}  // namespace dk

@@ -1,0 +1,10 @@
+// Decode instantiation: element type float, head dimension 32.
+#include "prf_kernels.cuh"
+#include "decode_kernels.cuh"
+
+namespace dk {
+dark_status dec_f32_d32(const dark_prf_desc& d, const void* q, const void* k, const void* v, const float* M,
+                         const float* om, float* S, float* z, void* out, void* s) {
+  return launch_decode_impl<float, 32>(d, q, k, v, M, om, S, z, out, s);
+}
+}  // namespace dk

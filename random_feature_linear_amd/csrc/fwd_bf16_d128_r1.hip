@@ -1,0 +1,8 @@
+// Forward instantiation: element type bf16, head dimension 128, rank blocks 1.
+#include "prf_kernels.cuh"
+
+namespace dk {
+dark_status fwd_bf16_d128_r1(const FwdArgs& a, const Plan& p, void* ws, void* s) {
+  return launch_fwd_impl<bf16, 128, 1, 1>(a, p, ws, s);
+}
+}  // namespace dk

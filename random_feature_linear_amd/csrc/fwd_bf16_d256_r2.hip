@@ -1,0 +1,8 @@
+// Forward instantiation: element type bf16, head dimension 256, rank blocks 2.
+#include "prf_kernels.cuh"
+
+namespace dk {
+dark_status fwd_bf16_d256_r2(const FwdArgs& a, const Plan& p, void* ws, void* s) {
+  return launch_fwd_impl<bf16, 256, 2, 1>(a, p, ws, s);
+}
+}  // namespace dk

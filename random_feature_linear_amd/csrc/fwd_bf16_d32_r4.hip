@@ -1,0 +1,8 @@
+// Forward instantiation: element type bf16, head dimension 32, rank blocks 4.
+#include "prf_kernels.cuh"
+
+namespace dk {
+dark_status fwd_bf16_d32_r4(const FwdArgs& a, const Plan& p, void* ws, void* s) {
+  return launch_fwd_impl<bf16, 32, 4, 2>(a, p, ws, s);
+}
+}  // namespace dk

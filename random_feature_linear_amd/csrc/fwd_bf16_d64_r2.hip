@@ -1,0 +1,8 @@
+// Forward instantiation: element type bf16, head dimension 64, rank blocks 2.
+#include "prf_kernels.cuh"
+
+namespace dk {
+dark_status fwd_bf16_d64_r2(const FwdArgs& a, const Plan& p, void* ws, void* s) {
+  return launch_fwd_impl<bf16, 64, 2, 2>(a, p, ws, s);
+}
+}  // namespace dk

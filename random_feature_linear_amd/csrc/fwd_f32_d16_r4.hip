@@ -1,0 +1,8 @@
+// Forward instantiation: element type float, head dimension 16, rank blocks 4.
+#include "prf_kernels.cuh"
+
+namespace dk {
+dark_status fwd_f32_d16_r4(const FwdArgs& a, const Plan& p, void* ws, void* s) {
+  return launch_fwd_impl<float, 16, 4, 2>(a, p, ws, s);
+}
+}  // namespace dk

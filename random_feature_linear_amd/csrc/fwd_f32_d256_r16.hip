@@ -1,0 +1,8 @@
+// Forward instantiation: element type float, head dimension 256, rank blocks 16.
+#include "prf_kernels.cuh"
+
+namespace dk {
+dark_status fwd_f32_d256_r16(const FwdArgs& a, const Plan& p, void* ws, void* s) {
+  return launch_fwd_impl<float, 256, 16, 1>(a, p, ws, s);
+}
+}  // namespace dk

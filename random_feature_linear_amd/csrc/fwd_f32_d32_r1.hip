@@ -1,0 +1,8 @@
+// Forward instantiation: element type float, head dimension 32, rank blocks 1.
+#include "prf_kernels.cuh"
+
+namespace dk {
+dark_status fwd_f32_d32_r1(const FwdArgs& a, const Plan& p, void* ws, void* s) {
+  return launch_fwd_impl<float, 32, 1, 2>(a, p, ws, s);
+}
+}  // namespace dk
