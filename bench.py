@@ -139,7 +139,7 @@ def chunk_len(w) -> int:
     return 128 if w.causal else 0
 
 
-def measure(w, steps: int, warmup: int) -> dict:
+def measure(w, steps: int, warmup: int, eager: bool = False) -> dict:
     import torch
     per_copy = io_bytes(w)
     copies = max(2, min(32, -(-(MALL_BYTES + (64 << 20)) // per_copy)))
@@ -149,6 +149,15 @@ def measure(w, steps: int, warmup: int) -> dict:
     for i in range(warmup):
         fwd(i)
     torch.cuda.synchronize()
+    if eager:   # plain launches (for profilers that follow kernel dispatches)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            fwd(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return {"ms": t0.elapsed_time(t1) / steps, "n_fwd": steps, "copies": copies, "kernels": {},
+                "launch": "eager"}
     # one graph = one pass over the copies; replay it until `steps` forwards ran
     graph = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -292,6 +301,8 @@ def main() -> int:
     ap.add_argument("--workload", default="c2_causal_L2048")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-secondary", action="store_true", help="skip the L=64K measurement")
+    ap.add_argument("--eager", action="store_true",
+                    help="plain launches instead of a HIP graph, no per-kernel timing (for profilers)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path, so --gpus must be 1",
@@ -313,6 +324,11 @@ def main() -> int:
         print(json.dumps(rec), flush=True)
         return 0
     w = CONFIGS[args.workload]
+    if args.eager:
+        res = measure(w, args.steps, args.warmup, eager=True)
+        print(json.dumps({"workload": w.name, "ms_per_step": res["ms"], "steps": res["n_fwd"],
+                          "launch": "eager"}), flush=True)
+        return 0
     res = measure(w, args.steps, args.warmup)
     main_line = line_for(w, res, args.steps, args.warmup)
     rec = {"metric": METRIC, "value": main_line["value"], "unit": "tokens/s", "n_gpus": 1,

@@ -288,11 +288,38 @@ template <typename T, int DH, int TT, int VST>
 __device__ __forceinline__ void stage_vt(T* s_vt, const T* vb, int64_t vstride, int t0, int t_end, int tid) {
   typedef typename FragOf<T>::type F;
   for (int e = tid; e < TT * (DH / 8); e += kThreads) {
-    const int tl = e / (DH / 8), d8 = (e % (DH / 8)) * 8;
+    const int tl = e % TT, d8 = (e / TT) * 8;   // consecutive lanes: consecutive tokens
     const int t = t0 + tl;
     const F x = (t < t_end) ? ld8(vb + (long)t * vstride + d8) : zero_frag<F>();
 #pragma unroll
     for (int i = 0; i < 8; ++i) s_vt[(d8 + i) * VST + tl] = x[i];
+  }
+}
+
+// The same staging in two halves: global loads into registers (issued a tile
+// ahead of their use) and the transposed LDS stores.
+template <int DH, int TT> constexpr int vloads_per_thread() { return (TT * (DH / 8) + kThreads - 1) / kThreads; }
+template <typename T, int DH, int TT>
+__device__ __forceinline__ void load_v(typename FragOf<T>::type* vr, const T* vb, int64_t vstride, int t0, int t_end,
+                                       int tid) {
+  typedef typename FragOf<T>::type F;
+#pragma unroll
+  for (int p = 0; p < vloads_per_thread<DH, TT>(); ++p) {
+    const int e = tid + p * kThreads;
+    const int tl = e % TT, d8 = (e / TT) * 8;   // consecutive lanes: consecutive tokens
+    const int t = t0 + tl;
+    vr[p] = (e < TT * (DH / 8) && t < t_end) ? ld8(vb + (long)t * vstride + d8) : zero_frag<F>();
+  }
+}
+template <typename T, int DH, int TT, int VST>
+__device__ __forceinline__ void store_vt(T* s_vt, const typename FragOf<T>::type* vr, int tid) {
+#pragma unroll
+  for (int p = 0; p < vloads_per_thread<DH, TT>(); ++p) {
+    const int e = tid + p * kThreads;
+    if (e >= TT * (DH / 8)) break;
+    const int tl = e % TT, d8 = (e / TT) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_vt[(d8 + i) * VST + tl] = vr[p][i];
   }
 }
 
@@ -333,11 +360,14 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
   constexpr int NM = kParts<T>;
   constexpr int DB = vblocks<DH>();
   constexpr int TT = kTile;
-  constexpr int VST = TT + 8;
+  constexpr int VST = TT + 4;   // 4 x odd: 8-byte rows of V^T fall in distinct LDS banks
 
+  constexpr int MFR = ((R16 + 1) / 2) * KD * NM;   // fragments of M' (one head)
+  constexpr int VPT = vloads_per_thread<DH, TT>();
   __shared__ __attribute__((aligned(16))) T s_u[kWaves][NM][R16][64 * 8];
   __shared__ __attribute__((aligned(16))) float s_init[TT];
   __shared__ __attribute__((aligned(16))) T s_vt[DH * VST];
+  __shared__ __attribute__((aligned(16))) T s_m[MFR * 64 * 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
@@ -375,13 +405,24 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
     }
   }
 
+  // M' of this head in LDS: every token block of every tile reads it
+  for (int i = tid; i < MFR * 64; i += kThreads) st8(s_m + i * 8, ld8(mf + (long)i * 8));
+  // K rows of block w and the V rows of a tile are loaded one tile ahead of their use
+  F xpre[KD], vpre[VPT];
+  auto prefetch = [&](int tt) {
+    const int t = tt + 32 * w + c;
+    load_rows<T, DH>(xpre, kbase + (long)t * a.ks[2], t < t_end, g);
+    load_v<T, DH, TT>(vpre, vbase, a.vs[2], tt, t_end, tid);
+  };
+  prefetch(t_begin);
+  __syncthreads();
+
   for (int t0 = t_begin; t0 < t_end; t0 += TT) {
     {  // projection of token block w
       const int t = t0 + 32 * w + c;
       const bool ok = t < t_end;
-      F xf[KD], uhi[R16], ulo[R16];
-      load_rows<T, DH>(xf, kbase + (long)t * a.ks[2], ok, g);
-      const float shift = project_block<T, DH, R16>(uhi, ulo, xf, mf, lane, half_log2m);
+      F uhi[R16], ulo[R16];
+      const float shift = project_block<T, DH, R16>(uhi, ulo, xpre, s_m, lane, half_log2m);
 #pragma unroll
       for (int k = 0; k < R16; ++k) {
         st8(&s_u[w][0][k][lane * 8], uhi[k]);
@@ -390,8 +431,9 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
       const bool valid = ok && (mrow == nullptr || mrow[t] != 0);
       if (g == 0) s_init[32 * w + c] = valid ? -shift : -INFINITY;
     }
-    stage_vt<T, DH, TT, VST>(s_vt, vbase, a.vs[2], t0, t_end, tid);
+    store_vt<T, DH, TT, VST>(s_vt, vpre, tid);
     __syncthreads();
+    if (t0 + TT < t_end) prefetch(t0 + TT);
 
 #pragma unroll
     for (int tb = 0; tb < kWaves; ++tb) {
@@ -476,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
   constexpr int NM = kParts<T>;
   constexpr int DB = vblocks<DH>();
   constexpr int R32 = (R16 + 1) / 2;
-  constexpr int VST = 32 + 8;
+  constexpr int VST = 32 + 4;
 
   __shared__ __attribute__((aligned(16))) T s_u[NM][R16][64 * 8];
   __shared__ __attribute__((aligned(16))) float s_ss[kWaves][32];
@@ -676,14 +718,25 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   constexpr int DB = vblocks<DH>();
   constexpr int NB = kWaves * NQB;         // 32-token blocks per tile
   constexpr int TT = 32 * NB;              // tokens per tile
-  constexpr int VST = TT + 8;
-  // key-feature exchange buffers: two (one barrier per feature step) unless LDS is short
-  constexpr int KBUF = (DH * VST + 2 * NB * 2 * 64 * 8) * sizeof(T) <= 160 * 1024 ? 2 : 1;
+  constexpr int VST = TT + 4;
+  constexpr int NOF = R16 * NM;            // omega' fragments per feature step
+  constexpr int NSTEP = NOF + 2 * DB;      // plus state fragments
+  constexpr int PERW = (NSTEP + kWaves - 1) / kWaves;
   constexpr int VT_ELEMS = CAUSAL ? DH * VST : 8;
+  constexpr size_t kBase = (size_t)VT_ELEMS * sizeof(T);
+  constexpr size_t kOpStep = (size_t)NSTEP * 64 * 8 * sizeof(T);
+  constexpr size_t kKfStep = CAUSAL ? (size_t)NB * 2 * 64 * 8 * sizeof(T) : 0;
+  // Operands staged in LDS when one step buffer fits beside the V^T tile (else
+  // each wave reads them from L2 itself); double buffers (one barrier per
+  // feature step) unless LDS is short.
+  constexpr bool STAGE = kBase + kOpStep + kKfStep <= 160 * 1024;
+  constexpr int OPB = !STAGE ? 0 : kBase + 2 * kOpStep + 2 * kKfStep <= 160 * 1024 ? 2 : 1;
+  constexpr int KBUF = kBase + OPB * kOpStep + 2 * kKfStep <= 160 * 1024 ? 2 : 1;
   constexpr int KF_ELEMS = CAUSAL ? KBUF * NB * 2 * 64 * 8 : 8;
 
   __shared__ __attribute__((aligned(16))) T s_vt[VT_ELEMS];
   __shared__ __attribute__((aligned(16))) T s_kf[KF_ELEMS];
+  __shared__ __attribute__((aligned(16))) T s_op[STAGE ? OPB * NSTEP * 64 * 8 : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
@@ -737,26 +790,46 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
       for (int kb2 = 0; kb2 < NB; ++kb2) at[j][kb2] = zero16();
   }
 
-  // operands of one 32-feature step: omega' (hi, lo) and the state fragments
-  struct Step {
-    F ohi[R16], olo[R16];
-    F s[DB][2];
+  // Operands of one 32-feature step (omega' hi/lo fragments, then the state
+  // fragments) are the same for the four waves: each wave fetches a quarter of
+  // them from L2 one step ahead, and all read them from LDS.
+  auto gsrc = [&](int fb, int f) -> const T* {
+    if (f < NOF) return ofrag + (((long)(fb * R16 + f / NM) * NM + f % NM) * 64 + lane) * 8;
+    f -= NOF;
+    return sf + (((f >> 1) * FK + 2 * fb + (f & 1)) * 64 + lane) * 8;
   };
-  auto fetch = [&](int fb, Step& o) {
+  F pre[STAGE ? PERW : 1];
+  auto load_step = [&](int fb) {
+    if constexpr (STAGE) {
+#pragma unroll
+      for (int q = 0; q < PERW; ++q) {
+        const int f = w + kWaves * q;
+        if (f < NSTEP) pre[q] = ld8(gsrc(fb, f));
+      }
+    }
+  };
+  auto store_step = [&](int buf) {
+    if constexpr (STAGE) {
+#pragma unroll
+      for (int q = 0; q < PERW; ++q) {
+        const int f = w + kWaves * q;
+        if (f < NSTEP) st8(s_op + ((buf * NSTEP + f) * 64 + lane) * 8, pre[q]);
+      }
+    }
+  };
+  auto op = [&](int fb, int buf, int f) {
+    if constexpr (STAGE) return ld8(s_op + ((buf * NSTEP + f) * 64 + lane) * 8);
+    else return ld8(gsrc(fb, f));
+  };
+
+  // one 32-feature step; the operands of the next step are fetched before it runs
+  auto step = [&](int fb, int buf) {
+    F ohi[R16], olo[R16];
 #pragma unroll
     for (int k = 0; k < R16; ++k) {
-      o.ohi[k] = ld8(ofrag + (((long)(fb * R16 + k) * NM) * 64 + lane) * 8);
-      o.olo[k] = ld8(ofrag + (((long)(fb * R16 + k) * NM + NM - 1) * 64 + lane) * 8);
+      ohi[k] = op(fb, buf, k * NM);
+      olo[k] = op(fb, buf, k * NM + NM - 1);
     }
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int k = 0; k < 2; ++k) o.s[db][k] = ld8(sf + ((db * FK + 2 * fb + k) * 64 + lane) * 8);
-  };
-  // one 32-feature step; the operands of the next step are fetched before it runs
-  auto step = [&](int fb, const Step& cur) {
-    const F* ohi = cur.ohi;
-    const F* olo = cur.olo;
     const bool partial = PAD && (fb + 1) * 32 > a.m;   // the last block may hold padding features
     F pq[NQB][2];
 #pragma unroll
@@ -777,9 +850,11 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
+      for (int k = 0; k < 2; ++k) {
+        const F sv = op(fb, buf, NOF + 2 * db + k);
 #pragma unroll
-        for (int j = 0; j < NQB; ++j) acc[j][db] = mma(pq[j][k], cur.s[db][k], acc[j][db]);
+        for (int j = 0; j < NQB; ++j) acc[j][db] = mma(pq[j][k], sv, acc[j][db]);
+      }
     if constexpr (CAUSAL) {
       T* kbuf = s_kf + (KBUF == 2 ? (fb & 1) : 0) * NB * 2 * 64 * 8;
 #pragma unroll
@@ -810,14 +885,20 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
       if constexpr (KBUF == 1) __syncthreads();   // the buffer is rewritten by the next step
     }
   };
-  Step sa, sb;   // two named buffers (an indexed array would live in scratch memory)
-  fetch(0, sa);
-  for (int fb = 0; fb < pl.FB; fb += 2) {
-    if (fb + 1 < pl.FB) fetch(fb + 1, sb);
-    step(fb, sa);
-    if (fb + 1 >= pl.FB) break;
-    if (fb + 2 < pl.FB) fetch(fb + 2, sa);
-    step(fb + 1, sb);
+  load_step(0);
+  store_step(0);
+  __syncthreads();
+  for (int fb = 0; fb < pl.FB; ++fb) {
+    const int buf = OPB == 2 ? (fb & 1) : 0;
+    if (fb + 1 < pl.FB) load_step(fb + 1);
+    step(fb, buf);
+    if constexpr (STAGE) {
+      if (fb + 1 < pl.FB) {
+        if constexpr (OPB == 1) __syncthreads();   // one buffer: everyone is done reading it
+        store_step(OPB == 2 ? ((fb + 1) & 1) : 0);
+      }
+      __syncthreads();
+    }
   }
 
   if constexpr (CAUSAL) {
@@ -871,11 +952,14 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
 constexpr size_t kMaxLds = 160 * 1024;
 // LDS of the tiled key-side kernel: u fragments of four blocks, shifts, the V^T tile
 template <typename T, int DH, int R16> constexpr size_t kstate_tile_lds_bytes() {
-  return (size_t)(kWaves * kParts<T> * R16 * 64 * 8 + DH * (kTile + 8)) * sizeof(T) + kTile * sizeof(float);
+  return (size_t)(kWaves * kParts<T> * R16 * 64 * 8 + DH * (kTile + 8) + ((R16 + 1) / 2) * (DH / 16) * kParts<T> * 64 * 8) *
+             sizeof(T) +
+         kTile * sizeof(float);
 }
-// LDS of the causal query-side kernel: the V^T tile, one key-feature buffer, the denominators
-template <typename T, int DH, int NQB> constexpr size_t causal_lds_bytes() {
-  return (size_t)(DH * (128 * NQB + 8) + 4 * NQB * 2 * 64 * 8) * sizeof(T);
+// Least LDS of the causal query-side kernel: the V^T tile and one key-feature
+// buffer (the operand staging buffers are added only where they fit).
+template <typename T, int DH, int R16, int NQB> constexpr size_t causal_lds_bytes() {
+  return (size_t)(DH * (128 * NQB + 4) + 4 * NQB * 2 * 64 * 8) * sizeof(T);
 }
 
 template <typename T, int DH, int R16, int FBW, bool PAD>
@@ -913,7 +997,7 @@ dark_status launch_fwd_pad(const FwdArgs& a, const Plan& pl, void* ws, void* str
   const dim3 grid(pl.BH * pl.NT2);
   KernelTimer tm(kQOut, stream);
   if (a.causal) {
-    if constexpr (causal_lds_bytes<T, DH, 1>() <= kMaxLds) {
+    if constexpr (causal_lds_bytes<T, DH, R16, 1>() <= kMaxLds) {
       if (pl.NQB != 1) return DARK_ERR_UNSUPPORTED;
       hipLaunchKernelGGL((qout_kernel<T, DH, R16, 1, true, PAD>), grid, dim3(kThreads), 0, st, a, pl, mfrag, ofrag,
                          sfrag);
