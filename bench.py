@@ -158,36 +158,39 @@ def measure(w, steps: int, warmup: int, eager: bool = False) -> dict:
         torch.cuda.synchronize()
         return {"ms": t0.elapsed_time(t1) / steps, "n_fwd": steps, "copies": copies, "kernels": {},
                 "launch": "eager"}
-    # one graph = one pass over the copies; replay it until `steps` forwards ran
-    graph = torch.cuda.CUDAGraph()
+    # Timed region: one HIP graph of `steps` forwards that rotate over the input
+    # copies, replayed once after an untimed first replay.
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
-        with torch.cuda.graph(graph, stream=s):
-            for i in range(copies):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
                 fwd(i)
     torch.cuda.synchronize()
-    reps = max(1, -(-steps // copies))
-    for _ in range(2):
-        graph.replay()
+    g.replay()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
-    for _ in range(reps):
-        graph.replay()
+    g.replay()
     t1.record()
-    torch.cuda.synchronize()
-    n_fwd = reps * copies
-    ms = t0.elapsed_time(t1) / n_fwd
-    # eager pass with per-kernel events (timing hooks on)
-    n_t = min(max(steps, 20), 200)
+    # Per-kernel times: the same `steps` forwards launched one by one right behind
+    # the replay (the GPU stays busy), with the library's HIP events recorded
+    # around every kernel launch on the stream the kernel runs on.
     fwd.bd.dark_prf_timing_begin()
-    for i in range(n_t):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
         fwd(i)
+    e1.record()
     per = fwd.bd.dark_prf_timing_end()
     torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    ms_eager = e0.elapsed_time(e1) / steps
+    del g
     kern = {k: {"avg_us": 1e3 * v[0] / v[1], "launches": v[1]} for k, v in per.items() if v[1] > 0}
-    return {"ms": ms, "n_fwd": n_fwd, "copies": copies, "kernels": kern}
+    n_fwd = steps
+    return {"ms": ms, "ms_eager": ms_eager, "n_fwd": n_fwd, "copies": copies, "kernels": kern}
 
 
 def roofline(w, res: dict) -> dict:
@@ -207,9 +210,10 @@ def roofline(w, res: dict) -> dict:
             "frac": None, "traffic": traffic, "avg_launch_us": round(res["kernels"][dom]["avg_us"], 3)}
 
 
-def cpu_baseline(w, max_heads=None) -> dict:
-    """The fp64 oracle on the host cores, on a bounded sample of the same workload."""
-    import numpy as np
+def cpu_baseline(w, max_heads=None, min_seconds: float = 10.0) -> dict:
+    """The fp64 oracle on the host cores, on a bounded sample of the same workload:
+    `max_heads` (batch, head) slices at full length, repeated until at least
+    `min_seconds` of wall time have passed."""
     from threadpoolctl import threadpool_info
 
     import oracle
@@ -219,18 +223,34 @@ def cpu_baseline(w, max_heads=None) -> dict:
     pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
     if max_heads is not None:
         pairs = pairs[:max_heads]
-    t = time.perf_counter()
-    oracle.attention(inp["q"], inp["k"], inp["v"], inp["M"], om, mask=inp["mask"], causal=w.causal,
-                     heads=pairs)
-    dt = time.perf_counter() - t
+    reps, t = 0, time.perf_counter()
+    while True:
+        oracle.attention(inp["q"], inp["k"], inp["v"], inp["M"], om, mask=inp["mask"],
+                         causal=w.causal, heads=pairs)
+        reps += 1
+        dt = time.perf_counter() - t
+        if dt >= min_seconds:
+            break
     frac = len(pairs) / (w.B * w.H)
-    tok_s = w.B * w.L * frac / dt
+    tok_s = reps * w.B * w.L * frac / dt
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("internal_api") in
                    ("openblas", "mkl", "blis")] or [1])
     return {"value": round(tok_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(pairs)} of {w.B * w.H} (batch, head) slices, full length, fp64, "
-                      f"{dt:.2f} s", "blas": "openblas",
+            "sample": f"{len(pairs)} of {w.B * w.H} (batch, head) slices at full length, fp64, "
+                      f"{reps} repetitions in {dt:.1f} s", "blas": "openblas",
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 4) -> None:
+    """Plain device-to-device copies of `nbytes` (for scaling HBM byte counters)."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def line_for(w, res: dict, steps: int, warmup: int) -> dict:
@@ -241,11 +261,13 @@ def line_for(w, res: dict, steps: int, warmup: int) -> dict:
         "value": round(value, 1), "ms_per_step": round(res["ms"], 6),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.hkv, "L": w.L, "d_h": w.d_h,
                    "m": w.m, "r": w.r, "causal": w.causal, "mask": w.mask_kind,
-                   "launch": "hipGraph of %d forwards over rotating input copies" % res["copies"]},
+                   "launch": "one hipGraph of %d forwards over %d rotating input copies" % (res["n_fwd"], res["copies"])},
         "roofline": roofline(w, res),
         "nominal_tflops": round(nom, 2), "nominal_frac_bf16": round(nom / PEAK_BF16_TFLOPS, 4),
         "io_GBps": round(io_bytes(w) / (res["ms"] * 1e-3) / 1e9, 1),
         "kernels_us": {k: round(v["avg_us"], 3) for k, v in res["kernels"].items()},
+        "kernel_timing": "HIP events around each launch, eager pass of the same forwards "
+                         "right behind the timed replay (%.4f ms per forward)" % res["ms_eager"],
     }
 
 
@@ -303,6 +325,8 @@ def main() -> int:
     ap.add_argument("--no-secondary", action="store_true", help="skip the L=64K measurement")
     ap.add_argument("--eager", action="store_true",
                     help="plain launches instead of a HIP graph, no per-kernel timing (for profilers)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 1 GiB device copies (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path, so --gpus must be 1",
@@ -314,6 +338,9 @@ def main() -> int:
         return 2
     from random_feature_linear_amd import binding as bd
     from random_feature_linear_amd.workloads import CONFIGS
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
     bd.lib()
     torch.cuda.synchronize()
     if args.workload == "c5_decode":
