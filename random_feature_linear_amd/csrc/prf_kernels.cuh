@@ -40,6 +40,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace dk {
@@ -459,8 +461,10 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
         for (int k = 0; k < 2; ++k) vf[db][k] = v_frag<T, DH, VST>(s_vt, db, 32 * tb, k, c, g);
 #pragma unroll
       for (int f = 0; f < FBW; ++f) {
+        // a block past the last one (last slice only) runs on clamped operands
+        // and is never stored: no branch in the loop
         const int fb = fb0 + f;
-        if (fb >= pl.FB) continue;
+        const int fbc = min(fb, pl.FB - 1);
         F ohi[R16], olo[R16];
 #pragma unroll
         for (int k = 0; k < R16; ++k) {
@@ -468,8 +472,8 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
             ohi[k] = ohr[f][k];
             olo[k] = olr[f][k];
           } else {
-            ohi[k] = ld8(ofrag + (((long)(fb * R16 + k) * NM) * 64 + lane) * 8);
-            olo[k] = ld8(ofrag + (((long)(fb * R16 + k) * NM + NM - 1) * 64 + lane) * 8);
+            ohi[k] = ld8(ofrag + (((long)(fbc * R16 + k) * NM) * 64 + lane) * 8);
+            olo[k] = ld8(ofrag + (((long)(fbc * R16 + k) * NM + NM - 1) * 64 + lane) * 8);
           }
         }
         f32x16 e = ini;
@@ -595,12 +599,12 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
 #pragma unroll
     for (int f = 0; f < FBW; ++f) {
       const int fb = fb0 + f;
-      if (fb >= pl.FB) continue;
+      const int fbc = min(fb, pl.FB - 1);   // past the last block: clamped, never stored
       F ohi[R16], olo[R16];
 #pragma unroll
       for (int k = 0; k < R16; ++k) {
-        ohi[k] = ld8(ofrag + (((long)(fb * R16 + k) * NM) * 64 + lane) * 8);
-        olo[k] = ld8(ofrag + (((long)(fb * R16 + k) * NM + NM - 1) * 64 + lane) * 8);
+        ohi[k] = ld8(ofrag + (((long)(fbc * R16 + k) * NM) * 64 + lane) * 8);
+        olo[k] = ld8(ofrag + (((long)(fbc * R16 + k) * NM + NM - 1) * 64 + lane) * 8);
       }
       f32x16 e = ini;
       if constexpr (PAD)
