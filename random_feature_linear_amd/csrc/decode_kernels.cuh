@@ -37,29 +37,74 @@ __device__ __forceinline__ float ld_elem(const float* p, int i) { return p[i]; }
 __device__ __forceinline__ void st_elem(__bf16* p, int i, float x) { p[i] = (__bf16)x; }
 __device__ __forceinline__ void st_elem(float* p, int i, float x) { p[i] = x; }
 
-// Workgroup: 256 threads, one query head, NS consecutive sequences.
-// Dynamic LDS: x[3][NS][DH] (q, k, v), u[2][NS][256], ph[2][NS][m], red[256][4], nrm[2][NS], den[NS]
-template <typename T, int DH>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+// Workgroup: 256 threads, one query head h, NS consecutive sequences.  The
+// state is streamed in slices of 256 x kDecVec float4 per sequence: a thread
+// owns the columns d0 .. d0 + 3 (d0 = 4 (tid % (DH / 4))) of rows
+// j = tid / (DH / 4) + i 256 / (DH / 4).  All loads of a slice are issued
+// before any of its stores, and the first slice is requested before the
+// feature maps are computed, so HBM latency overlaps the arithmetic.
+// Dynamic LDS (dec_lds_bytes): x[3][NS][DH] (q, k, v), u[2 NS][r], nrm[2 NS],
+// ph[2 NS][m], red[NS][256][4], dred[NS][4].
+constexpr int kDecThreads = 256;
+constexpr int kDecVec = 16;   // float4 per thread per sequence and slice
+
+// LDS carve-up in floats, each array starting on a 16-byte boundary
+__host__ __device__ constexpr int dec_align4(int n) { return (n + 3) & ~3; }
+__host__ constexpr size_t dec_lds_bytes(int ns, int dh, int r, int m) {
+  return (size_t)(3 * ns * dh + dec_align4(2 * ns * r) + dec_align4(2 * ns) + dec_align4(2 * ns * m) +
+                  ns * kDecThreads * 4 + ns * 4) *
+         sizeof(float);
+}
+
+template <int DH> __device__ __forceinline__ void dec_rows(int tid, int i, int& j, int& d0) {
+  constexpr int Q4 = DH / 4;
+  j = tid / Q4 + i * (kDecThreads / Q4);
+  d0 = (tid % Q4) * 4;
+}
+
+template <typename T, int DH, int NS>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
-  const int NS = a.NS;
-  float* xs = smem;                          // [3][NS][DH]
-  float* us = xs + 3 * NS * DH;              // [2][NS][256]
-  float* ph = us + 2 * NS * 256;             // [2][NS][m]
-  float* red = ph + 2 * NS * a.m;            // [256][4]
-  float* nrm = red + 256 * 4;                // [2][NS]
-  float* den = nrm + 2 * NS;                 // [NS]
+  constexpr int Q4 = DH / 4;
+  constexpr int RPS = kDecThreads / Q4;   // rows per slice step
+  float* xs = smem;                                 // [3][NS][DH]
+  float* us = xs + 3 * NS * DH;                     // [2 NS][r]
+  float* nrm = us + dec_align4(2 * NS * a.r);       // [2 NS]
+  float* ph = nrm + dec_align4(2 * NS);             // [2 NS][m]
+  float* red = ph + dec_align4(2 * NS * a.m);       // [NS][256][4] (16-byte aligned)
+  float* dred = red + NS * kDecThreads * 4;         // [NS][4]
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int h = blockIdx.x % a.H;
   const int n0 = (blockIdx.x / a.H) * NS;
   const int hk = (h * a.H_kv) / a.H;
   const int ns = min(NS, a.N - n0);
   const float s = powf((float)DH, -0.25f);
   const float* Mh = a.M + (long)(a.m_per_head ? h : 0) * a.r * DH;
+  const int nrows_slice = RPS * kDecVec;            // state rows per slice
+  const int nslices = (a.m + nrows_slice - 1) / nrows_slice;
+
+  // ---- request the first state slice of every sequence ----
+  float4 sreg[NS][kDecVec];
+  auto load_slice = [&](int sl) {
+#pragma unroll
+    for (int sq = 0; sq < NS; ++sq) {
+      const float* Sb = a.S + ((long)(n0 + sq) * a.H + h) * (long)a.m * DH;
+#pragma unroll
+      for (int i = 0; i < kDecVec; ++i) {
+        int j, d0;
+        dec_rows<DH>(tid, i, j, d0);
+        j += sl * nrows_slice;
+        sreg[sq][i] = (sq < ns && j < a.m) ? *reinterpret_cast<const float4*>(Sb + (long)j * DH + d0)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  load_slice(0);
 
   // ---- token rows to LDS (fp32) ----
-  for (int e = tid; e < 3 * NS * DH; e += 256) {
+  for (int e = tid; e < 3 * NS * DH; e += kDecThreads) {
     const int which = e / (NS * DH), sq = (e / DH) % NS, d = e % DH;
     float x = 0.f;
     if (sq < ns) {
@@ -72,98 +117,141 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // ---- u = s M x for q and k; thread `row` owns one rank index ----
-  for (int row = tid; row < a.r; row += 256) {
+  // ---- u = s M x for q and k of every sequence (vector vi: 2 sq + {0: q, 1: k}) ----
+  for (int p = tid; p < 2 * NS * a.r; p += kDecThreads) {
+    const int row = p % a.r, vi = p / a.r;
+    const float* xr = xs + ((vi & 1) * NS + (vi >> 1)) * DH;
     const float* mr = Mh + (long)row * DH;
-    for (int sq = 0; sq < NS; ++sq) {
-      float uq = 0.f, uk = 0.f;
-      for (int d = 0; d < DH; ++d) {
-        const float mv = mr[d];
-        uq += mv * xs[sq * DH + d];
-        uk += mv * xs[(NS + sq) * DH + d];
-      }
-      us[sq * 256 + row] = s * uq;
-      us[(NS + sq) * 256 + row] = s * uk;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int d = 0; d < DH; d += 4) {
+      const float4 mv = *reinterpret_cast<const float4*>(mr + d);
+      acc += mv.x * xr[d] + mv.y * xr[d + 1] + mv.z * xr[d + 2] + mv.w * xr[d + 3];
     }
+    us[vi * a.r + row] = s * acc;
   }
   __syncthreads();
-  if (tid < 2 * NS) {
-    const float* u = us + tid * 256;
+  // |u|^2 / 2 of each vector: one wave per vector, lanes over the rank index
+  for (int vi = wv; vi < 2 * NS; vi += kDecThreads / 64) {
     float acc = 0.f;
-    for (int i = 0; i < a.r; ++i) acc += u[i] * u[i];
-    nrm[tid] = 0.5f * acc;
+    for (int i = lane; i < a.r; i += 64) acc += us[vi * a.r + i] * us[vi * a.r + i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) nrm[vi] = 0.5f * acc;
   }
   __syncthreads();
 
-  // ---- phi_j = exp(omega_j . u - |u|^2 / 2) / sqrt(m) ----
-  const float inv_sqrt_m = 1.0f / sqrtf((float)a.m);
-  for (int j = tid; j < a.m; j += 256) {
+  // ---- phi_j = exp(omega_j . u - |u|^2 / 2) / sqrt(m) for every vector ----
+  const float half_log2m = 0.5f * log2f((float)a.m);
+  for (int j = tid; j < a.m; j += kDecThreads) {
     const float* om = a.omega + (long)j * a.r;
-    for (int sq = 0; sq < NS; ++sq) {
-      float eq = 0.f, ek = 0.f;
+    float e[2 * NS];
+#pragma unroll
+    for (int vi = 0; vi < 2 * NS; ++vi) e[vi] = 0.f;
+    if (a.r % 4 == 0) {   // rows of omega are 16-byte aligned
+      for (int i = 0; i < a.r; i += 4) {
+        const float4 w = *reinterpret_cast<const float4*>(om + i);
+#pragma unroll
+        for (int vi = 0; vi < 2 * NS; ++vi) {
+          const float* u = us + vi * a.r + i;
+          e[vi] += w.x * u[0] + w.y * u[1] + w.z * u[2] + w.w * u[3];
+        }
+      }
+    } else {
       for (int i = 0; i < a.r; ++i) {
         const float w = om[i];
-        eq += w * us[sq * 256 + i];
-        ek += w * us[(NS + sq) * 256 + i];
+#pragma unroll
+        for (int vi = 0; vi < 2 * NS; ++vi) e[vi] += w * us[vi * a.r + i];
       }
-      ph[sq * a.m + j] = exp2f(kLog2eDec * (eq - nrm[sq])) * inv_sqrt_m;
-      ph[(NS + sq) * a.m + j] = exp2f(kLog2eDec * (ek - nrm[NS + sq])) * inv_sqrt_m;
     }
+#pragma unroll
+    for (int vi = 0; vi < 2 * NS; ++vi)
+      ph[vi * a.m + j] = exp2f(kLog2eDec * (e[vi] - nrm[vi]) - half_log2m);
   }
   __syncthreads();
 
-  for (int sq = 0; sq < ns; ++sq) {
-    const int n = n0 + sq;
-    const long st = ((long)n * a.H + h);
-    const float* pq = ph + sq * a.m;
-    const float* pk = ph + (NS + sq) * a.m;
-    const float* vv = xs + (2 * NS + sq) * DH;
-    // z and the denominator
-    float dp = 0.f;
-    for (int j = tid; j < a.m; j += 256) {
+  // ---- z += phi(k); denominator phi(q) . z ----
+  float dp[NS];
+#pragma unroll
+  for (int sq = 0; sq < NS; ++sq) {
+    dp[sq] = 0.f;
+    if (sq >= ns) continue;
+    const long st = (long)(n0 + sq) * a.H + h;
+    const float* pq = ph + (2 * sq) * a.m;
+    const float* pk = ph + (2 * sq + 1) * a.m;
+    for (int j = tid; j < a.m; j += kDecThreads) {
       const float zj = a.z[st * a.m + j] + pk[j];
       a.z[st * a.m + j] = zj;
-      dp += pq[j] * zj;
+      dp[sq] += pq[j] * zj;
     }
-    red[tid] = dp;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-      if (tid < off) red[tid] += red[tid + off];
-      __syncthreads();
+  }
+
+  // ---- S += phi(k) v^T and the numerator phi(q)^T S, slice by slice ----
+  float np[NS][4];
+#pragma unroll
+  for (int sq = 0; sq < NS; ++sq)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) np[sq][c] = 0.f;
+  for (int sl = 0; sl < nslices; ++sl) {
+    if (sl > 0) load_slice(sl);
+#pragma unroll
+    for (int sq = 0; sq < NS; ++sq) {
+      if (sq >= ns) continue;
+      float* Sb = a.S + ((long)(n0 + sq) * a.H + h) * (long)a.m * DH;
+      const float* pq = ph + (2 * sq) * a.m;
+      const float* pk = ph + (2 * sq + 1) * a.m;
+      const float* vv = xs + (2 * NS + sq) * DH;
+      int j0, d0;
+      dec_rows<DH>(tid, 0, j0, d0);
+      const float4 v4 = *reinterpret_cast<const float4*>(vv + d0);
+#pragma unroll
+      for (int i = 0; i < kDecVec; ++i) {
+        const int j = j0 + i * RPS + sl * nrows_slice;
+        if (j >= a.m) break;
+        const float kj = pk[j], qj = pq[j];
+        float4 s4 = sreg[sq][i];
+        s4.x += kj * v4.x;
+        s4.y += kj * v4.y;
+        s4.z += kj * v4.z;
+        s4.w += kj * v4.w;
+        *reinterpret_cast<float4*>(Sb + (long)j * DH + d0) = s4;
+        np[sq][0] += qj * s4.x;
+        np[sq][1] += qj * s4.y;
+        np[sq][2] += qj * s4.z;
+        np[sq][3] += qj * s4.w;
+      }
     }
-    if (tid == 0) den[sq] = red[0];
-    __syncthreads();
-    // S and the numerator; thread owns columns d0 .. d0 + 3
-    constexpr int Q4 = DH / 4;
-    const int d0 = (tid % Q4) * 4;
-    float np[4] = {0.f, 0.f, 0.f, 0.f};
-    float* Sb = a.S + st * (long)a.m * DH;
-    for (int e = tid; e < a.m * Q4; e += 256) {
-      const int j = e / Q4;
-      float4 s4 = *reinterpret_cast<float4*>(Sb + (long)j * DH + d0);
-      const float kj = pk[j], qj = pq[j];
-      s4.x += kj * vv[d0];
-      s4.y += kj * vv[d0 + 1];
-      s4.z += kj * vv[d0 + 2];
-      s4.w += kj * vv[d0 + 3];
-      *reinterpret_cast<float4*>(Sb + (long)j * DH + d0) = s4;
-      np[0] += qj * s4.x;
-      np[1] += qj * s4.y;
-      np[2] += qj * s4.z;
-      np[3] += qj * s4.w;
+  }
+
+  // ---- reductions: numerator over the row groups, denominator over all threads ----
+#pragma unroll
+  for (int sq = 0; sq < NS; ++sq) {
+    *reinterpret_cast<float4*>(red + (sq * kDecThreads + tid) * 4) =
+        make_float4(np[sq][0], np[sq][1], np[sq][2], np[sq][3]);
+    float x = dp[sq];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    if (lane == 0) dred[sq * 4 + wv] = x;
+  }
+  __syncthreads();
+  for (int p = tid; p < NS * Q4; p += kDecThreads) {
+    const int sq = p / Q4, cg = p % Q4;
+    if (sq >= ns) continue;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int grp = 0; grp < RPS; ++grp) {
+      const float4 x = *reinterpret_cast<const float4*>(red + (sq * kDecThreads + grp * Q4 + cg) * 4);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
     }
-    for (int i = 0; i < 4; ++i) red[tid * 4 + i] = np[i];
-    __syncthreads();
-    if (tid < Q4) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int grp = tid; grp < 256; grp += Q4)
-        for (int i = 0; i < 4; ++i) acc[i] += red[grp * 4 + i];
-      const float dd = den[sq];
-      const float inv = dd > 0.f ? 1.0f / dd : 0.f;
-      T* o = reinterpret_cast<T*>(a.out) + n * a.os[0] + h * a.os[1];
-      for (int i = 0; i < 4; ++i) st_elem(o, d0 + i, acc[i] * inv);
-    }
-    __syncthreads();
+    const float dd = dred[sq * 4] + dred[sq * 4 + 1] + dred[sq * 4 + 2] + dred[sq * 4 + 3];
+    const float inv = dd > 0.f ? 1.0f / dd : 0.f;
+    T* o = reinterpret_cast<T*>(a.out) + (n0 + sq) * a.os[0] + h * a.os[1];
+    st_elem(o, 4 * cg, acc.x * inv);
+    st_elem(o, 4 * cg + 1, acc.y * inv);
+    st_elem(o, 4 * cg + 2, acc.z * inv);
+    st_elem(o, 4 * cg + 3, acc.w * inv);
   }
 }
 
@@ -190,17 +278,19 @@ dark_status launch_decode_impl(const dark_prf_desc& d, const void* q, const void
   a.m = d.m;
   a.r = d.r;
   a.m_per_head = d.m_per_head;
-  int NS = 4;
-  auto lds = [&](int ns) {
-    return (size_t)(3 * ns * DH + 2 * ns * 256 + 2 * ns * d.m + 256 * 4 + 3 * ns) * sizeof(float);
-  };
-  while (NS > 1 && lds(NS) > 64 * 1024) NS >>= 1;
+  auto lds = [&](int ns) { return dec_lds_bytes(ns, DH, d.r, d.m); };
+  // two sequences per workgroup (the feature maps share the M and omega reads)
+  // when there are enough of them and the LDS allows it
+  int NS = (d.B >= 64 && lds(2) <= 64 * 1024) ? 2 : 1;
   if (lds(NS) > 64 * 1024) return DARK_ERR_UNSUPPORTED;
   a.NS = NS;
   const int groups = (d.B + NS - 1) / NS;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   KernelTimer tm(kDecode, stream);
-  hipLaunchKernelGGL((decode_kernel<T, DH>), dim3(groups * d.H), dim3(256), lds(NS), st, a);
+  if (NS == 2)
+    hipLaunchKernelGGL((decode_kernel<T, DH, 2>), dim3(groups * d.H), dim3(kDecThreads), lds(NS), st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, DH, 1>), dim3(groups * d.H), dim3(kDecThreads), lds(NS), st, a);
   return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
 }
 

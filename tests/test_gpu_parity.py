@@ -198,6 +198,34 @@ def test_decode_small(dt):
     assert normwise_rel_err(z, z_ref, axes=(-1,)) <= TOL[dt]
 
 
+DECODE_SHAPES = {
+    # two sequences per workgroup with a ragged last group, a rank that is not a
+    # multiple of 4 and m not a multiple of 32
+    "bf16_d16_B65_r7_m48": dict(B=65, H=2, H_kv=1, d_h=16, m=48, r=7, dtype="bf16"),
+    # d_h = 256: the state is streamed in three 64-row slices, the last one partial
+    "bf16_d256_B70_m160": dict(B=70, H=2, H_kv=2, d_h=256, m=160, r=40, dtype="bf16"),
+    "f32_d128_B66_m96": dict(B=66, H=1, H_kv=1, d_h=128, m=96, r=100, dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DECODE_SHAPES))
+def test_decode_shapes(name):
+    cfg = DECODE_SHAPES[name]
+    w = Workload(name="dec_" + name, L=0, causal=True, seed=93, m_kind="eye_noise", m_noise=0.3,
+                 **cfg)
+    rows = [0, 33, w.B - 1]
+    say(f"[decode] {name}: B={w.B} H={w.H} d={w.d_h} m={w.m} r={w.r}; oracle on rows {rows}")
+    P, T = 20, 3
+    inp, tok, o, S, z = _decode_run(w, P, T, rows)
+    heads = [(i, h) for i in range(len(rows)) for h in range(w.H)]
+    ref, S_ref, z_ref = _decode_ref(w, inp, tok, heads)
+    err_o = normwise_rel_err(o, ref[:, :, P:])
+    say(f"[decode] {name}: output err {err_o:.3e}")
+    assert err_o <= TOL[w.dtype]
+    assert normwise_rel_err(S, S_ref) <= TOL[w.dtype]
+    assert normwise_rel_err(z, z_ref, axes=(-1,)) <= TOL[w.dtype]
+
+
 def test_c5_decode_sampled():
     """Workload 5 in its launch shape: 256 sequences x 8 heads, 4096-token prefill with state
     export, then 512 decode steps; sequences 0, 77 and 255 are checked against the oracle."""
