@@ -87,6 +87,7 @@ static void make_plan(const dark_prf_desc& d, Plan& p) {
   p.R16 = rank_blocks(d.r);
   p.FB = cdiv(d.m, 32);
   p.HM = d.m_per_head ? d.H : 1;
+  p.fold = fold_exponent(d.dtype == DARK_BF16 ? 2 : 4, d.d_h, p.R16);
   p.BH = d.B * d.H;
   p.elem = d.dtype == DARK_BF16 ? 2 : 4;
   p.FBW = feature_blocks_per_wave(d.d_h);
@@ -123,11 +124,19 @@ static void make_plan(const dark_prf_desc& d, Plan& p) {
   p.off_mfrag = off;
   off = align256(off + (size_t)p.HM * R32 * (d.d_h / 16) * NM * frag * p.elem);
   p.off_ofrag = off;
-  off = align256(off + (size_t)p.FB * p.R16 * NM * frag * p.elem);
+  if (p.fold)   // W' fragments per geometry matrix, K-steps over d_h
+    off = align256(off + (size_t)p.HM * p.FB * (d.d_h / 16) * NM * frag * p.elem);
+  else          // omega' fragments, K-steps over the rank
+    off = align256(off + (size_t)p.FB * p.R16 * NM * frag * p.elem);
   p.off_sdelta = off;
   off = align256(off + (size_t)p.BH * p.NU * state_frags * frag * p.elem);
   p.off_sfrag = off;
   off = align256(off + (size_t)p.BH * nout * state_frags * frag * p.elem);
+  // keys and queries are projected once up front (for |u|^2) when several
+  // feature slices, or the causal query side, would otherwise repeat it
+  p.kshift = p.fold && (p.NF > 1 || (d.causal && d.d_h >= 128));
+  p.off_kshift = off;
+  if (p.kshift) off = align256(off + 2 * (size_t)p.BH * L * sizeof(float));   // key, then query shifts
   p.total = off;
 }
 
@@ -370,6 +379,8 @@ dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k
   a.omega = omega;
   a.S_out = S_out;
   a.z_out = z_out;
+  a.kshift = nullptr;   // set by the launcher from the workspace
+  a.qshift = nullptr;
   a.B = d.B;
   a.H = d.H;
   a.H_kv = d.H_kv;

@@ -19,8 +19,17 @@ struct FwdArgs {
   const float* omega;
   float* S_out;
   float* z_out;
+  float* kshift;   // per-key shifts in the workspace (folded path), or null
+  float* qshift;   // per-query shifts, likewise
   int B, H, H_kv, L, m, r, causal, m_per_head;
 };
+
+// The exponent omega_j . u of a feature can be formed from the projected token
+// u = M' x (r-dimensional), or with the projection folded into omega, as
+// W'_j . x with W' = omega' M' (m x d_h, one per geometry matrix).  With hi/lo
+// bf16 operands the folded form costs 4 m d_h flops per token (plus 4 r d_h
+// for |u|^2) against 4 r d_h + 6 r m, so it is taken when d_h < 1.5 r.
+constexpr bool fold_exponent(int elem_bytes, int d_h, int r16) { return elem_bytes == 2 && 2 * d_h < 3 * 16 * r16; }
 
 // How one call is cut into kernels; all sizes derived on the host.
 struct Plan {
@@ -28,6 +37,8 @@ struct Plan {
   int R16;     // geometry rank in 16-wide blocks, rounded up to 1, 2, 4, 8 or 16
   int FB;      // 32-feature blocks (ceil(m / 32))
   int HM;      // number of geometry matrices (H or 1)
+  int fold;    // exponent from W' x (see fold_exponent)
+  int kshift;  // folded path with per-key shifts precomputed once (kshift_kernel)
   int BH;      // B * H
   // key-side state kernel
   int span1;   // tokens per unit (a chunk when causal, an L-split otherwise)
@@ -39,7 +50,7 @@ struct Plan {
   int tile2;   // queries per workgroup (4 waves * 32 * NQB); equals span1 when causal
   int NT2;     // query tiles per (b, h)
   // workspace (bytes from the base pointer)
-  size_t off_mfrag, off_ofrag, off_sdelta, off_sfrag, total;
+  size_t off_mfrag, off_ofrag, off_sdelta, off_sfrag, off_kshift, total;
   int elem;    // bytes per element of q/k/v (2 or 4)
 };
 

@@ -196,32 +196,35 @@ __device__ __forceinline__ float project_block(typename FragOf<T>::type (&uhi)[R
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       if (2 * rb + h < R16) acc_frag_split<T>(acc, h, uhi[2 * rb + h], ulo[2 * rb + h]);
+    if constexpr (KD * NM > 8) __builtin_amdgcn_sched_barrier(0);
   }
   ss += __shfl_xor(ss, 32);
   return 0.5f * kLog2e * ss + half_log2m;
 }
 
-// e += u . omega' over the rank index: u_hi omega'_hi + u_lo omega'_hi +
-// u_hi omega'_lo (bf16), or one fp32 product.  U_IS_A: the u fragments are the
-// A operand (result rows = tokens, columns = features); otherwise omega' is
-// (result rows = features, columns = tokens).
-template <typename T, int R16, bool U_IS_A>
+// e += u . omega' over the K-steps of the exponent: u_hi omega'_hi + u_lo
+// omega'_hi + u_hi omega'_lo (bf16), or one fp32 product.  In the folded form
+// (see fold_exponent) u is the token row x itself, which is exact in bf16
+// (ULO false, no u_lo term), and omega' is W'.  U_IS_A: the u fragments are
+// the A operand (result rows = tokens, columns = features); otherwise omega'
+// is (result rows = features, columns = tokens).
+template <typename T, int NK, bool U_IS_A, bool ULO = true>
 __device__ __forceinline__ f32x16 exponent(const typename FragOf<T>::type* uhi,
                                            const typename FragOf<T>::type* ulo,
                                            const typename FragOf<T>::type* ohi,
                                            const typename FragOf<T>::type* olo, f32x16 e) {
 #pragma unroll
-  for (int k = 0; k < R16; ++k) {
+  for (int k = 0; k < NK; ++k) {
     if constexpr (U_IS_A) {
       e = mma(uhi[k], ohi[k], e);
       if constexpr (kParts<T> == 2) {
-        e = mma(ulo[k], ohi[k], e);
+        if constexpr (ULO) e = mma(ulo[k], ohi[k], e);
         e = mma(uhi[k], olo[k], e);
       }
     } else {
       e = mma(ohi[k], uhi[k], e);
       if constexpr (kParts<T> == 2) {
-        e = mma(ohi[k], ulo[k], e);
+        if constexpr (ULO) e = mma(ohi[k], ulo[k], e);
         e = mma(olo[k], uhi[k], e);
       }
     }
@@ -229,43 +232,174 @@ __device__ __forceinline__ f32x16 exponent(const typename FragOf<T>::type* uhi,
   return e;
 }
 
+// The same sum with the operands fetched step by step: uload(k, part) and
+// oload(k, part) return fragment k of the token operand and of omega' (W').
+// Long sums (more than 8 K-steps, d_h = 256 folded) run in chunks of 2 steps
+// whose operands are fetched one chunk ahead, with scheduling fences between
+// chunks so that at most two chunks of operands are live in registers.
+template <typename T, int NK, bool U_IS_A, bool ULO, typename UL, typename OL>
+__device__ __forceinline__ f32x16 exponent_stream(UL uload, OL oload, f32x16 e) {
+  typedef typename FragOf<T>::type F;
+  if constexpr (NK <= 8) {
+    F uh[NK], ul[NK], oh[NK], ol[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      uh[k] = uload(k, 0);
+      if constexpr (ULO) ul[k] = uload(k, 1);
+      oh[k] = oload(k, 0);
+      ol[k] = oload(k, 1);
+    }
+    return exponent<T, NK, U_IS_A, ULO>(uh, ul, oh, ol, e);
+  } else {
+    constexpr int CH = 2;
+    static_assert(NK % CH == 0, "chunked exponent");
+    F uh[2][CH], ul[2][ULO ? CH : 1], oh[2][CH], ol[2][CH];
+    auto fetch = [&](int b, int k0) {
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        uh[b][k] = uload(k0 + k, 0);
+        if constexpr (ULO) ul[b][k] = uload(k0 + k, 1);
+        oh[b][k] = oload(k0 + k, 0);
+        ol[b][k] = oload(k0 + k, 1);
+      }
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int c0 = 0; c0 < NK / CH; ++c0) {
+      if (c0 + 1 < NK / CH) fetch((c0 + 1) & 1, (c0 + 1) * CH);
+      __builtin_amdgcn_sched_barrier(0);
+      e = exponent<T, CH, U_IS_A, ULO>(uh[c0 & 1], ul[c0 & 1], oh[c0 & 1], ol[c0 & 1], e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return e;
+  }
+}
+
+// Only the exp2-domain shift log2(e) |u|^2 / 2 + log2(m) / 2 of token c of a
+// 32-token block (the folded exponent does not need u itself).
+template <typename T, int DH, int R16>
+__device__ __forceinline__ float project_shift(const typename FragOf<T>::type (&xf)[DH / 16], const T* mfrag,
+                                               int lane, float half_log2m) {
+  constexpr int KD = DH / 16;
+  constexpr int R32 = (R16 + 1) / 2;
+  constexpr int NM = kParts<T>;
+  float ss = 0.f;
+#pragma unroll
+  for (int rb = 0; rb < R32; ++rb) {
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd)
+#pragma unroll
+      for (int part = 0; part < NM; ++part)
+        acc = mma(ld8(mfrag + (((rb * KD + kd) * NM + part) * 64 + lane) * 8), xf[kd], acc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ss += acc[i] * acc[i];
+    // large M' (d_h = 256): one 32-row slice of operands in flight at a time
+    if constexpr (KD * NM > 8) __builtin_amdgcn_sched_barrier(0);
+  }
+  ss += __shfl_xor(ss, 32);
+  return 0.5f * kLog2e * ss + half_log2m;
+}
+
+// Fragment lane idx of M' = s M (bf16: hi and lo parts; see prep_kernel).
+template <typename T>
+__device__ __forceinline__ void mfrag_lane(long idx, const float* __restrict__ M, T* __restrict__ mfrag, int r,
+                                           int d_h, int R16, float s) {
+  constexpr int NM = kParts<T>;
+  const int R32 = (R16 + 1) / 2;
+  const int KD = d_h / 16;
+  const int lane = (int)(idx & 63), c = lane & 31, g = lane >> 5;
+  const long f = idx >> 6;
+  const int part = (int)(f % NM);
+  const int kd = (int)((f / NM) % KD);
+  const int rb = (int)((f / ((long)NM * KD)) % R32);
+  const int hm = (int)(f / ((long)NM * KD * R32));
+  const int row = rb * 32 + c;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int col = kd * 16 + 8 * g + e;
+    const float x = (row < r) ? s * M[((long)hm * r + row) * d_h + col] : 0.f;
+    const float hi = NM == 2 ? bf16_hi(x) : x;
+    v[e] = part == 0 ? hi : x - hi;
+  }
+  typename FragOf<T>::type fr;
+  make_frag(fr, v);
+  st8(mfrag + idx * 8, fr);
+}
+
 // ---------------------------------------------------------------------------
 // Preparation: M' = d_h^(-1/4) M and omega' = log2(e) omega in fragment order.
 //   mfrag[hm][rb][kd][part][lane][8]: row 32 rb + c of M', columns 16 kd + 8g + e
 //   ofrag[fb][k][part][lane][8]: row 32 fb + c of omega', rank index
 //                                16k + 8 (e / 4) + 4g + e % 4
+// or, folded, W'_hm = omega' M'_hm:
+//   ofrag[hm][fb][kd][part][lane][8]: row 32 fb + c of W', columns 16 kd + 8g + e
 // part 0 is the bf16-rounded value, part 1 the rounded remainder (bf16 path).
+// The M' and omega' ranges take one thread per fragment lane and part; the W'
+// range one thread per fragment lane (both parts, r products each).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict__ omega,
                             T* __restrict__ mfrag, T* __restrict__ ofrag, int HM, int r, int d_h, int m,
-                            int R16, int FB, float s) {
+                            int R16, int FB, float s, int fold) {
   constexpr int NM = kParts<T>;
   const int R32 = (R16 + 1) / 2;
   const int KD = d_h / 16;
   const long nM = (long)HM * R32 * KD * NM * 64;
-  const long nO = (long)FB * R16 * NM * 64;
+  // fold: 0 omega' fragments, 1 W' fragments here, 2 W' fragments by fold_kernel
+  const long nO = fold == 2 ? 0 : fold ? (long)HM * FB * KD * 64 : (long)FB * R16 * NM * 64;
   for (long idx = blockIdx.x * (long)blockDim.x + threadIdx.x; idx < nM + nO;
        idx += (long)gridDim.x * blockDim.x) {
     float v[8];
+    typename FragOf<T>::type fr;
     const bool m_side = idx < nM;
     const long j = m_side ? idx : idx - nM;
     const int lane = (int)(j & 63);
     const long f = j >> 6;
-    const int part = (int)(f % NM);
     const int c = lane & 31, g = lane >> 5;
-    if (m_side) {
-      const int kd = (int)((f / NM) % KD);
-      const int rb = (int)((f / ((long)NM * KD)) % R32);
-      const int hm = (int)(f / ((long)NM * KD * R32));
-      const int row = rb * 32 + c;
+    if (!m_side && fold) {
+      const int kd = (int)(f % KD);
+      const int fb = (int)((f / KD) % FB);
+      const int hm = (int)(f / ((long)KD * FB));
+      const int row = fb * 32 + c;
+      const int col0 = kd * 16 + 8 * g;
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (row < m) {
+        const float* orow = omega + (long)row * r;
+        const float* Mh = M + (long)hm * r * d_h + col0;
+        for (int a = 0; a < r; ++a) {
+          const float w = orow[a];
+          const float4 m0 = *reinterpret_cast<const float4*>(Mh + (long)a * d_h);
+          const float4 m1 = *reinterpret_cast<const float4*>(Mh + (long)a * d_h + 4);
+          acc[0] += w * m0.x;
+          acc[1] += w * m0.y;
+          acc[2] += w * m0.z;
+          acc[3] += w * m0.w;
+          acc[4] += w * m1.x;
+          acc[5] += w * m1.y;
+          acc[6] += w * m1.z;
+          acc[7] += w * m1.w;
+        }
+      }
+      float lo[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int col = kd * 16 + 8 * g + e;
-        const float x = (row < r) ? s * M[((long)hm * r + row) * d_h + col] : 0.f;
-        const float hi = NM == 2 ? bf16_hi(x) : x;
-        v[e] = part == 0 ? hi : x - hi;
+        const float x = kLog2e * s * acc[e];
+        v[e] = bf16_hi(x);
+        lo[e] = x - v[e];
       }
+      const long base = f * NM * 64 + lane;   // fragment (f, part 0)
+      make_frag(fr, v);
+      st8(ofrag + base * 8, fr);
+      make_frag(fr, lo);
+      st8(ofrag + (base + 64) * 8, fr);
+      continue;
+    }
+    const int part = (int)(f % NM);
+    if (m_side) {
+      mfrag_lane<T>(j, M, mfrag, r, d_h, R16, s);
+      continue;
     } else {
       const int k = (int)((f / NM) % R16);
       const int fb = (int)(f / ((long)NM * R16));
@@ -278,25 +412,202 @@ __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict
         v[e] = part == 0 ? hi : x - hi;
       }
     }
-    typename FragOf<T>::type fr;
     make_frag(fr, v);
     st8((m_side ? mfrag : ofrag) + j * 8, fr);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Folded operand W'_hm = omega' M'_hm (m x d_h) for the bf16 path, with fp32
+// matrix products (32x32x2) so that the hi/lo split sees the exact product.
+// Workgroup: 4 waves, one 32-feature block and up to four 32-column tiles (one
+// per wave).  The rank index runs in chunks of 64: the chunk's M columns and
+// omega rows are fetched into registers one chunk ahead (all loads of a chunk
+// in flight together) and staged in LDS.  Each wave's transposed tile
+// W'^T = M'^T omega'^T (features in the lane index) goes back through LDS to
+// the fragment order of prep_kernel's folded layout.
+// ---------------------------------------------------------------------------
+constexpr int kFoldRC = 64;   // rank indices per chunk
+template <typename T>
+__global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict__ M, const float* __restrict__ omega,
+                                                        T* __restrict__ ofrag, T* __restrict__ mfrag, int HM, int R16,
+                                                        int r, int d_h, int m, int FB, float s, float scale) {
+  static_assert(sizeof(T) == 2, "the folded operands are bf16");
+  {  // blocks past the W' tiles write the M' fragments (used for |u|^2)
+    const int nW = HM * FB * ((d_h / 32 + 3) / 4);
+    if ((int)blockIdx.x >= nW) {
+      const long nM = (long)HM * ((R16 + 1) / 2) * (d_h / 16) * kParts<T> * 64;
+      const long idx = (long)(blockIdx.x - nW) * kThreads + threadIdx.x;
+      if (idx < nM) mfrag_lane<T>(idx, M, mfrag, r, d_h, R16, s);
+      return;
+    }
+  }
+  __shared__ float s_m[kFoldRC][4 * 32 + 1];   // M[a][col], 128 columns of the group
+  __shared__ float s_o[32][kFoldRC + 1];       // omega[32 fb + row][a]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
+  const int DT = d_h / 32;
+  const int NG = (DT + 3) / 4;                 // groups of four column tiles
+  const int grp = blockIdx.x % NG;
+  const int fb = (blockIdx.x / NG) % FB;
+  const int hm = blockIdx.x / (NG * FB);
+  const int col0 = grp * 128;                  // first column of the group
+  const float* Mh = M + (long)hm * r * d_h;
+  // this thread's loads of one chunk: 8 float4 of M (row a, 4 columns), 2 float4 of omega
+  float4 vm[8], vo[2];
+  auto fetch = [&](int a0) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int e = tid + p * kThreads;        // 0 .. 2047: row e / 32, float4 column e % 32
+      const int a = a0 + (e >> 5), cc = col0 + 4 * (e & 31);
+      const float4 x = *reinterpret_cast<const float4*>(Mh + (long)min(a, r - 1) * d_h + min(cc, d_h - 4));
+      vm[p] = (a < r && cc < d_h) ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int e = tid + p * kThreads;        // 0 .. 511: row e / 16, four rank indices 4 (e % 16)
+      const int row = e >> 4, a = a0 + 4 * (e & 15);
+      const int j = min(fb * 32 + row, m - 1);
+      float4 x;
+      if ((r & 3) == 0) {
+        x = *reinterpret_cast<const float4*>(omega + (long)j * r + min(a, r - 4));
+      } else {   // rows of omega are not 16-byte aligned
+        const float* o = omega + (long)j * r;
+        x = make_float4(o[min(a, r - 1)], o[min(a + 1, r - 1)], o[min(a + 2, r - 1)], o[min(a + 3, r - 1)]);
+      }
+      const bool okr = fb * 32 + row < m;
+      vo[p] = make_float4(okr && a < r ? x.x : 0.f, okr && a + 1 < r ? x.y : 0.f, okr && a + 2 < r ? x.z : 0.f,
+                          okr && a + 3 < r ? x.w : 0.f);
+    }
+  };
+  f32x16 acc = zero16();
+  fetch(0);
+  for (int a0 = 0; a0 < r; a0 += kFoldRC) {
+    __syncthreads();   // the previous chunk is no longer read
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int e = tid + p * kThreads, row = e >> 5, cc = 4 * (e & 31);
+      s_m[row][cc] = vm[p].x;
+      s_m[row][cc + 1] = vm[p].y;
+      s_m[row][cc + 2] = vm[p].z;
+      s_m[row][cc + 3] = vm[p].w;
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int e = tid + p * kThreads, row = e >> 4, a = 4 * (e & 15);
+      s_o[row][a] = vo[p].x;
+      s_o[row][a + 1] = vo[p].y;
+      s_o[row][a + 2] = vo[p].z;
+      s_o[row][a + 3] = vo[p].w;
+    }
+    __syncthreads();
+    if (a0 + kFoldRC < r) fetch(a0 + kFoldRC);
+#pragma unroll 8
+    for (int k = 0; k < kFoldRC; k += 2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(s_m[k + g][32 * w + c], s_o[c][k + g], acc, 0, 0, 0);
+  }
+  __syncthreads();
+  // acc[i]: W'^T[column 32 w + 8(i/4) + 4g + i%4 of the group][feature c]; s_m is the transpose buffer
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s_m[crow(i, g)][32 * w + c] = scale * acc[i];
+  __syncthreads();
+  const int dt = grp * 4 + w;
+  if (dt >= DT) return;
+  // fragment (fb, kd = 2 dt + h): lane (c, g) holds feature c, columns 16 h + 8g + e
+  constexpr int NM = 2;
+  const int KD = d_h / 16;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = s_m[16 * h + 8 * g + e][32 * w + c];
+      hi[e] = bf16_hi(x);
+      lo[e] = x - hi[e];
+    }
+    const long f = ((long)hm * FB + fb) * KD + 2 * dt + h;
+    typename FragOf<T>::type fr;
+    make_frag(fr, hi);
+    st8(ofrag + ((f * NM) * 64 + lane) * 8, fr);
+    make_frag(fr, lo);
+    st8(ofrag + ((f * NM + 1) * 64 + lane) * 8, fr);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Token shifts for the folded path: log2(e) |M'_h x|^2 / 2 + log2(m) / 2 of
+// every query row (qshift[bh][t]) and every key row as seen by query head h
+// (kshift[bh][t] = minus that, or -inf for a masked key).  They replace the
+// projections in the key-side kernel (once per feature slice) and in the query
+// side.  Workgroup: 4 waves x 2 blocks of 32 rows (64 query and 64 key rows
+// per wave); M' goes through LDS one 32-row slice at a time, shared by all.
+// ---------------------------------------------------------------------------
+constexpr int kShiftTile = 2 * kTile;
+template <typename T, int DH, int R16>
+__global__ __launch_bounds__(kThreads) void shift_kernel(FwdArgs a, const T* __restrict__ mfrag,
+                                                          float* __restrict__ qshift, float* __restrict__ kshift) {
+  typedef typename FragOf<T>::type F;
+  constexpr int KD = DH / 16;
+  constexpr int NM = kParts<T>;
+  constexpr int R32 = (R16 + 1) / 2;
+  constexpr int SL = KD * NM;   // fragments of one 32-row slice of M'
+  __shared__ __attribute__((aligned(16))) T s_m[SL * 64 * 8];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
+  const int ntile = (a.L + kShiftTile - 1) / kShiftTile;
+  const int tile = blockIdx.x % ntile;
+  const int bh = blockIdx.x / ntile;
+  const int b = bh / a.H, h = bh % a.H;
+  const int hk = (h * a.H_kv) / a.H;
+  const T* qbase = reinterpret_cast<const T*>(a.q) + b * a.qs[0] + h * a.qs[1];
+  const T* kbase = reinterpret_cast<const T*>(a.k) + b * a.ks[0] + hk * a.ks[1];
+  const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * R32 * KD * NM * 64 * 8;
+  // rows: [0] query block 2w, [1] query block 2w+1, [2] key block 2w, [3] key block 2w+1
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < R32; ++rb) {
+    __syncthreads();   // the previous slice is no longer read
+    constexpr int PS = (SL * 64 + kThreads - 1) / kThreads;
+    F stage[PS];   // all loads of the slice in flight before the stores
+#pragma unroll
+    for (int p = 0; p < PS; ++p) stage[p] = ld8(mf + ((long)rb * SL * 64 + min(tid + p * kThreads, SL * 64 - 1)) * 8);
+#pragma unroll
+    for (int p = 0; p < PS; ++p)
+      if (tid + p * kThreads < SL * 64) st8(s_m + (tid + p * kThreads) * 8, stage[p]);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = tile * kShiftTile + 32 * (2 * w + (q & 1)) + c;
+      const T* row = (q < 2 ? qbase + (long)t * a.qs[2] : kbase + (long)t * a.ks[2]);
+      F xf[KD];
+      load_rows<T, DH>(xf, row, t < a.L, g);
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd)
+#pragma unroll
+        for (int part = 0; part < NM; ++part) acc = mma(ld8(s_m + ((kd * NM + part) * 64 + lane) * 8), xf[kd], acc);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss[q] += acc[i] * acc[i];
+    }
+  }
+  const float half_log2m = 0.5f * log2f((float)a.m);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float sum = ss[q] + __shfl_xor(ss[q], 32);
+    const float sh = 0.5f * kLog2e * sum + half_log2m;
+    const int t = tile * kShiftTile + 32 * (2 * w + (q & 1)) + c;
+    if (g == 0 && t < a.L) {
+      if (q < 2) {
+        qshift[(long)bh * a.L + t] = sh;
+      } else {
+        const bool valid = a.mask == nullptr || a.mask[(long)b * a.L + t] != 0;
+        kshift[(long)bh * a.L + t] = valid ? -sh : -INFINITY;
+      }
+    }
   }
 }
 
 // Stage rows t0 .. t0 + TT - 1 of V into LDS transposed, s_vt[d][t] (rows past
 // t_end are zero).
 template <typename T, int DH, int TT, int VST>
-__device__ __forceinline__ void stage_vt(T* s_vt, const T* vb, int64_t vstride, int t0, int t_end, int tid) {
-  typedef typename FragOf<T>::type F;
-  for (int e = tid; e < TT * (DH / 8); e += kThreads) {
-    const int tl = e % TT, d8 = (e / TT) * 8;   // consecutive lanes: consecutive tokens
-    const int t = t0 + tl;
-    const F x = (t < t_end) ? ld8(vb + (long)t * vstride + d8) : zero_frag<F>();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s_vt[(d8 + i) * VST + tl] = x[i];
-  }
-}
+__device__ __forceinline__ void stage_vt(T* s_vt, const T* vb, int64_t vstride, int t0, int t_end, int tid);
 
 // The same staging in two halves: global loads into registers (issued a tile
 // ahead of their use) and the transposed LDS stores.
@@ -308,9 +619,11 @@ __device__ __forceinline__ void load_v(typename FragOf<T>::type* vr, const T* vb
 #pragma unroll
   for (int p = 0; p < vloads_per_thread<DH, TT>(); ++p) {
     const int e = tid + p * kThreads;
-    const int tl = e % TT, d8 = (e / TT) * 8;   // consecutive lanes: consecutive tokens
+    const int tl = e % TT, d8 = ((e / TT) * 8) % DH;   // consecutive lanes: consecutive tokens
     const int t = t0 + tl;
-    vr[p] = (e < TT * (DH / 8) && t < t_end) ? ld8(vb + (long)t * vstride + d8) : zero_frag<F>();
+    // clamped (always valid) address, so that all loads are in flight at once
+    const F x = ld8(vb + (long)min(t, t_end - 1) * vstride + d8);
+    vr[p] = (e < TT * (DH / 8) && t < t_end) ? x : zero_frag<F>();
   }
 }
 template <typename T, int DH, int TT, int VST>
@@ -323,6 +636,15 @@ __device__ __forceinline__ void store_vt(T* s_vt, const typename FragOf<T>::type
 #pragma unroll
     for (int i = 0; i < 8; ++i) s_vt[(d8 + i) * VST + tl] = vr[p][i];
   }
+}
+
+// Stage rows t0 .. t0 + TT - 1 of V into LDS transposed, s_vt[d][t] (rows past
+// t_end are zero): all global loads first, then the transposed stores.
+template <typename T, int DH, int TT, int VST>
+__device__ __forceinline__ void stage_vt(T* s_vt, const T* vb, int64_t vstride, int t0, int t_end, int tid) {
+  typename FragOf<T>::type vr[vloads_per_thread<DH, TT>()];
+  load_v<T, DH, TT>(vr, vb, vstride, t0, t_end, tid);
+  store_vt<T, DH, TT, VST>(s_vt, vr, tid);
 }
 
 // [V, 1] operand fragment: column d = 32 db + c (d < d_h: V, d = d_h: ones,
@@ -364,12 +686,16 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
   constexpr int TT = kTile;
   constexpr int VST = TT + 4;   // 4 x odd: 8-byte rows of V^T fall in distinct LDS banks
 
+  constexpr bool FOLD = fold_exponent(sizeof(T), DH, R16);
+  constexpr int UK = FOLD ? KD : R16;              // K-steps of the exponent
+  constexpr int UP = FOLD ? 1 : NM;                // parts of its token operand
   constexpr int MFR = ((R16 + 1) / 2) * KD * NM;   // fragments of M' (one head)
+  constexpr bool M_LDS = MFR * 64 * 8 * sizeof(T) <= 32 * 1024;   // M' staged in LDS
   constexpr int VPT = vloads_per_thread<DH, TT>();
-  __shared__ __attribute__((aligned(16))) T s_u[kWaves][NM][R16][64 * 8];
+  __shared__ __attribute__((aligned(16))) T s_u[kWaves][UP][UK][64 * 8];
   __shared__ __attribute__((aligned(16))) float s_init[TT];
   __shared__ __attribute__((aligned(16))) T s_vt[DH * VST];
-  __shared__ __attribute__((aligned(16))) T s_m[MFR * 64 * 8];
+  __shared__ __attribute__((aligned(16))) T s_m[M_LDS ? MFR * 64 * 8 : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
@@ -382,6 +708,8 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
   const T* vbase = reinterpret_cast<const T*>(a.v) + b * a.vs[0] + hk * a.vs[1];
   const uint8_t* mrow = a.mask ? a.mask + (long)b * a.L : nullptr;
   const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * ((R16 + 1) / 2) * KD * NM * 64 * 8;
+  // omega' (shared), or W' of this head's geometry when folded
+  const T* of = ofrag + (FOLD ? (long)(a.m_per_head ? h : 0) * pl.FB * UK * NM * 64 * 8 : 0);
   const float half_log2m = 0.5f * log2f((float)a.m);
   const int t_begin = unit * pl.span1;
   const int t_end = min(a.L, t_begin + pl.span1);
@@ -392,50 +720,79 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
   for (int f = 0; f < FBW; ++f)
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[f][db] = zero16();
-  // omega' fragments of this wave's features stay in registers when they are few
-  constexpr bool kHoist = FBW * R16 * NM <= 8;
-  F ohr[kHoist ? FBW : 1][R16], olr[kHoist ? FBW : 1][R16];
+  // omega' (W') fragments of this wave's features stay in registers when they are few
+  constexpr bool kHoist = FBW * UK * NM <= (FOLD ? 32 : 8);
+  F ohr[kHoist ? FBW : 1][UK], olr[kHoist ? FBW : 1][UK];
   if constexpr (kHoist) {
 #pragma unroll
     for (int f = 0; f < FBW; ++f) {
       const int fb = min(fb0 + f, pl.FB - 1);
 #pragma unroll
-      for (int k = 0; k < R16; ++k) {
-        ohr[f][k] = ld8(ofrag + (((long)(fb * R16 + k) * NM) * 64 + lane) * 8);
-        olr[f][k] = ld8(ofrag + (((long)(fb * R16 + k) * NM + NM - 1) * 64 + lane) * 8);
+      for (int k = 0; k < UK; ++k) {
+        ohr[f][k] = ld8(of + (((long)(fb * UK + k) * NM) * 64 + lane) * 8);
+        olr[f][k] = ld8(of + (((long)(fb * UK + k) * NM + NM - 1) * 64 + lane) * 8);
       }
     }
   }
 
-  // M' of this head in LDS: every token block of every tile reads it
-  for (int i = tid; i < MFR * 64; i += kThreads) st8(s_m + i * 8, ld8(mf + (long)i * 8));
+  // M' of this head in LDS when it is small: every token block of every tile reads it
+  if constexpr (M_LDS) {   // all loads in flight, then the stores
+    constexpr int PM = (MFR * 64 + kThreads - 1) / kThreads;
+    F mreg[PM];
+#pragma unroll
+    for (int p = 0; p < PM; ++p) mreg[p] = ld8(mf + (long)min(tid + p * kThreads, MFR * 64 - 1) * 8);
+#pragma unroll
+    for (int p = 0; p < PM; ++p)
+      if (tid + p * kThreads < MFR * 64) st8(s_m + (tid + p * kThreads) * 8, mreg[p]);
+  }
+  const T* msrc = M_LDS ? s_m : mf;
   // K rows of block w and the V rows of a tile are loaded one tile ahead of their use
+  // (d_h = 256: no register prefetch, the registers go to the accumulators)
+  constexpr bool PREF = KD + VPT <= 16;
   F xpre[KD], vpre[VPT];
   auto prefetch = [&](int tt) {
     const int t = tt + 32 * w + c;
     load_rows<T, DH>(xpre, kbase + (long)t * a.ks[2], t < t_end, g);
     load_v<T, DH, TT>(vpre, vbase, a.vs[2], tt, t_end, tid);
   };
-  prefetch(t_begin);
+  if constexpr (PREF) prefetch(t_begin);
   __syncthreads();
 
   for (int t0 = t_begin; t0 < t_end; t0 += TT) {
+    // The omega' (W') and M' fragments are the same for every tile; hiding the
+    // pointers from the optimiser keeps their loads in the loop instead of
+    // hoisting all of them into registers (and spilling) before it.
+    const T* of_t = of;
+    const T* msrc_t = msrc;
+    if constexpr (!kHoist) asm volatile("" : "+s"(of_t));
+    if constexpr (!M_LDS) asm volatile("" : "+s"(msrc_t));
+    if constexpr (!PREF) prefetch(t0);
     {  // projection of token block w
       const int t = t0 + 32 * w + c;
       const bool ok = t < t_end;
-      F uhi[R16], ulo[R16];
-      const float shift = project_block<T, DH, R16>(uhi, ulo, xpre, s_m, lane, half_log2m);
+      float shift = 0.f;
+      if constexpr (FOLD) {   // the exponent reads the token rows themselves
+        if (!pl.kshift) shift = project_shift<T, DH, R16>(xpre, msrc_t, lane, half_log2m);
 #pragma unroll
-      for (int k = 0; k < R16; ++k) {
-        st8(&s_u[w][0][k][lane * 8], uhi[k]);
-        if constexpr (NM == 2) st8(&s_u[w][NM - 1][k][lane * 8], ulo[k]);
+        for (int k = 0; k < UK; ++k) st8(&s_u[w][0][k][lane * 8], xpre[k]);
+      } else {
+        F uhi[R16], ulo[R16];
+        shift = project_block<T, DH, R16>(uhi, ulo, xpre, msrc_t, lane, half_log2m);
+#pragma unroll
+        for (int k = 0; k < R16; ++k) {
+          st8(&s_u[w][0][k][lane * 8], uhi[k]);
+          if constexpr (NM == 2) st8(&s_u[w][NM - 1][k][lane * 8], ulo[k]);
+        }
       }
       const bool valid = ok && (mrow == nullptr || mrow[t] != 0);
-      if (g == 0) s_init[32 * w + c] = valid ? -shift : -INFINITY;
+      if (g == 0)
+        s_init[32 * w + c] = (FOLD && pl.kshift) ? (ok ? a.kshift[(long)bh * a.L + t] : -INFINITY)
+                                                  : (valid ? -shift : -INFINITY);
     }
     store_vt<T, DH, TT, VST>(s_vt, vpre, tid);
     __syncthreads();
-    if (t0 + TT < t_end) prefetch(t0 + TT);
+    if constexpr (PREF)
+      if (t0 + TT < t_end) prefetch(t0 + TT);
 
 #pragma unroll
     for (int tb = 0; tb < kWaves; ++tb) {
@@ -448,45 +805,40 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
         ini[4 * jj + 2] = x.z;
         ini[4 * jj + 3] = x.w;
       }
-      F uhi[R16], ulo[R16];
+      auto uload = [&](int k, int part) -> F { return ld8(&s_u[tb][part ? UP - 1 : 0][k][lane * 8]); };
+      // [V, 1] fragments of the block: held across the feature blocks when
+      // few, else read from LDS at each use
+      constexpr bool VHOLD = DB <= 4;
+      F vf[VHOLD ? DB : 1][2];
+      if constexpr (VHOLD) {
 #pragma unroll
-      for (int k = 0; k < R16; ++k) {
-        uhi[k] = ld8(&s_u[tb][0][k][lane * 8]);
-        ulo[k] = ld8(&s_u[tb][NM - 1][k][lane * 8]);
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) vf[db][k] = v_frag<T, DH, VST>(s_vt, db, 32 * tb, k, c, g);
       }
-      F vf[DB][2];
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int k = 0; k < 2; ++k) vf[db][k] = v_frag<T, DH, VST>(s_vt, db, 32 * tb, k, c, g);
 #pragma unroll
       for (int f = 0; f < FBW; ++f) {
         // a block past the last one (last slice only) runs on clamped operands
         // and is never stored: no branch in the loop
         const int fb = fb0 + f;
         const int fbc = min(fb, pl.FB - 1);
-        F ohi[R16], olo[R16];
-#pragma unroll
-        for (int k = 0; k < R16; ++k) {
-          if constexpr (kHoist) {
-            ohi[k] = ohr[f][k];
-            olo[k] = olr[f][k];
-          } else {
-            ohi[k] = ld8(ofrag + (((long)(fbc * R16 + k) * NM) * 64 + lane) * 8);
-            olo[k] = ld8(ofrag + (((long)(fbc * R16 + k) * NM + NM - 1) * 64 + lane) * 8);
-          }
-        }
+        auto oload = [&](int k, int part) -> F {
+          if constexpr (kHoist) return part ? olr[f][k] : ohr[f][k];
+          else return ld8(of_t + (((long)(fbc * UK + k) * NM + (part ? NM - 1 : 0)) * 64 + lane) * 8);
+        };
         f32x16 e = ini;
         if constexpr (PAD)   // m is not a multiple of 32: features past m give 0
           if (fb * 32 + c >= a.m) e = splat16(-INFINITY);
-        e = exponent<T, R16, true>(uhi, ulo, ohi, olo, e);
+        e = exponent_stream<T, UK, true, !FOLD>(uload, oload, e);
 #pragma unroll
         for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
         const F p0 = acc_frag<F>(e, 0), p1 = acc_frag<F>(e, 1);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          acc[f][db] = mma(p0, vf[db][0], acc[f][db]);
-          acc[f][db] = mma(p1, vf[db][1], acc[f][db]);
+          const F v0 = VHOLD ? vf[VHOLD ? db : 0][0] : v_frag<T, DH, VST>(s_vt, db, 32 * tb, 0, c, g);
+          const F v1 = VHOLD ? vf[VHOLD ? db : 0][1] : v_frag<T, DH, VST>(s_vt, db, 32 * tb, 1, c, g);
+          acc[f][db] = mma(p0, v0, acc[f][db]);
+          acc[f][db] = mma(p1, v1, acc[f][db]);
         }
       }
     }
@@ -723,7 +1075,10 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   constexpr int NB = kWaves * NQB;         // 32-token blocks per tile
   constexpr int TT = 32 * NB;              // tokens per tile
   constexpr int VST = TT + 4;
-  constexpr int NOF = R16 * NM;            // omega' fragments per feature step
+  constexpr bool FOLD = fold_exponent(sizeof(T), DH, R16);
+  constexpr int UK = FOLD ? KD : R16;      // K-steps of the exponent
+  constexpr int UP = FOLD ? 1 : NM;        // parts of its token operand
+  constexpr int NOF = UK * NM;             // omega' (W') fragments per feature step
   constexpr int NSTEP = NOF + 2 * DB;      // plus state fragments
   constexpr int PERW = (NSTEP + kWaves - 1) / kWaves;
   constexpr int VT_ELEMS = CAUSAL ? DH * VST : 8;
@@ -754,29 +1109,49 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   T* obase = reinterpret_cast<T*>(a.out) + b * a.os[0] + h * a.os[1];
   const uint8_t* mrow = a.mask ? a.mask + (long)b * a.L : nullptr;
   const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * ((R16 + 1) / 2) * KD * NM * 64 * 8;
+  const T* of = ofrag + (FOLD ? (long)(a.m_per_head ? h : 0) * pl.FB * UK * NM * 64 * 8 : 0);
   const float half_log2m = 0.5f * log2f((float)a.m);
   const int t0 = tile * TT;
   const long FK = 2L * pl.FB;
   const long unit_s = (long)bh * (CAUSAL ? pl.NU : 1) + (CAUSAL ? tile : 0);
   const T* sf = sfrag + unit_s * DB * FK * 64 * 8;
 
-  // ---- projections of this wave's query (and key) blocks ----
-  F uqh[NQB][R16], uql[NQB][R16];
+  // ---- exponent operands of this wave's query (and key) blocks: u = M' x as
+  // hi/lo fragments, or (folded) the token rows x themselves ----
+  F uqh[NQB][UK], uql[NQB][FOLD ? 1 : UK];
   float shq[NQB];
-  F ukh[CAUSAL ? NQB : 1][R16], ukl[CAUSAL ? NQB : 1][R16];
+  F ukh[CAUSAL ? NQB : 1][UK], ukl[CAUSAL ? NQB : 1][FOLD ? 1 : UK];
   float initk[CAUSAL ? NQB : 1];
+  auto operands = [&](F* uh, F* ul, const T* row, bool ok) -> float {
+    if constexpr (FOLD) {
+      load_rows<T, DH>(*reinterpret_cast<F(*)[KD]>(uh), row, ok, g);
+      return project_shift<T, DH, R16>(*reinterpret_cast<F(*)[KD]>(uh), mf, lane, half_log2m);
+    } else {
+      F xf[KD];
+      load_rows<T, DH>(xf, row, ok, g);
+      return project_block<T, DH, R16>(*reinterpret_cast<F(*)[R16]>(uh), *reinterpret_cast<F(*)[R16]>(ul), xf,
+                                       mf, lane, half_log2m);
+    }
+  };
 #pragma unroll
   for (int j = 0; j < NQB; ++j) {
     const int t = t0 + 32 * (w * NQB + j) + c;
     const bool ok = t < a.L;
-    F xf[KD];
-    load_rows<T, DH>(xf, qbase + (long)t * a.qs[2], ok, g);
-    shq[j] = project_block<T, DH, R16>(uqh[j], uql[j], xf, mf, lane, half_log2m);
+    if (FOLD && pl.kshift) {   // shifts precomputed: only the rows are needed
+      load_rows<T, DH>(*reinterpret_cast<F(*)[KD]>(uqh[j]), qbase + (long)t * a.qs[2], ok, g);
+      shq[j] = ok ? a.qshift[(long)bh * a.L + t] : 0.f;
+    } else {
+      shq[j] = operands(uqh[j], uql[j], qbase + (long)t * a.qs[2], ok);
+    }
     if constexpr (CAUSAL) {
-      load_rows<T, DH>(xf, kbase + (long)t * a.ks[2], ok, g);
-      const float sh = project_block<T, DH, R16>(ukh[j], ukl[j], xf, mf, lane, half_log2m);
-      const bool valid = ok && (mrow == nullptr || mrow[t] != 0);
-      initk[j] = valid ? -sh : -INFINITY;
+      if (FOLD && pl.kshift) {   // shifts precomputed: only the rows are needed
+        load_rows<T, DH>(*reinterpret_cast<F(*)[KD]>(ukh[j]), kbase + (long)t * a.ks[2], ok, g);
+        initk[j] = ok ? a.kshift[(long)bh * a.L + t] : -INFINITY;
+      } else {
+        const float sh = operands(ukh[j], ukl[j], kbase + (long)t * a.ks[2], ok);
+        const bool valid = ok && (mrow == nullptr || mrow[t] != 0);
+        initk[j] = valid ? -sh : -INFINITY;
+      }
     }
   }
   if constexpr (CAUSAL) stage_vt<T, DH, TT, VST>(s_vt, vbase, a.vs[2], t0, a.L, tid);
@@ -798,7 +1173,7 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   // fragments) are the same for the four waves: each wave fetches a quarter of
   // them from L2 one step ahead, and all read them from LDS.
   auto gsrc = [&](int fb, int f) -> const T* {
-    if (f < NOF) return ofrag + (((long)(fb * R16 + f / NM) * NM + f % NM) * 64 + lane) * 8;
+    if (f < NOF) return of + (((long)(fb * UK + f / NM) * NM + f % NM) * 64 + lane) * 8;
     f -= NOF;
     return sf + (((f >> 1) * FK + 2 * fb + (f & 1)) * 64 + lane) * 8;
   };
@@ -828,11 +1203,18 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
 
   // one 32-feature step; the operands of the next step are fetched before it runs
   auto step = [&](int fb, int buf) {
-    F ohi[R16], olo[R16];
+    auto oload = [&](int k, int part) -> F { return op(fb, buf, k * NM + (part ? NM - 1 : 0)); };
+    // Unfolded: omega' fragments of the step read once into registers and
+    // shared by the query and key blocks.  (Fetching them per use with the fp32
+    // 32x32x2 products gave a schedule whose first launch in a process
+    // returned wrong blocks now and then.)
+    F ohi[FOLD ? 1 : UK], olo[FOLD ? 1 : UK];
+    if constexpr (!FOLD) {
 #pragma unroll
-    for (int k = 0; k < R16; ++k) {
-      ohi[k] = op(fb, buf, k * NM);
-      olo[k] = op(fb, buf, k * NM + NM - 1);
+      for (int k = 0; k < UK; ++k) {
+        ohi[k] = op(fb, buf, k * NM);
+        olo[k] = op(fb, buf, k * NM + NM - 1);
+      }
     }
     const bool partial = PAD && (fb + 1) * 32 > a.m;   // the last block may hold padding features
     F pq[NQB][2];
@@ -844,21 +1226,28 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
         for (int i = 0; i < 16; ++i)
           if (fb * 32 + crow(i, g) >= a.m) e[i] = -INFINITY;
       }
-      e = exponent<T, R16, false>(uqh[j], uql[j], ohi, olo, e);
+      if constexpr (FOLD)
+        e = exponent_stream<T, UK, false, false>([&](int k, int) -> F { return uqh[j][k]; }, oload, e);
+      else
+        e = exponent<T, UK, false, true>(uqh[j], uql[j], ohi, olo, e);
 #pragma unroll
       for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
       pq[j][0] = acc_frag<F>(e, 0);
       pq[j][1] = acc_frag<F>(e, 1);
     }
-    // inter-chunk (or whole-sequence) state
+    // inter-chunk (or whole-sequence) state; with many column blocks the
+    // fragments are read in groups of three blocks (bounded registers)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const F sv = op(fb, buf, NOF + 2 * db + k);
 #pragma unroll
         for (int j = 0; j < NQB; ++j) acc[j][db] = mma(pq[j][k], sv, acc[j][db]);
       }
+      if constexpr (DB > 4)
+        if (db % 3 == 2) __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (CAUSAL) {
       T* kbuf = s_kf + (KBUF == 2 ? (fb & 1) : 0) * NB * 2 * 64 * 8;
 #pragma unroll
@@ -869,7 +1258,10 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
           for (int i = 0; i < 16; ++i)
             if (fb * 32 + crow(i, g) >= a.m) e[i] = -INFINITY;
         }
-        e = exponent<T, R16, false>(ukh[j], ukl[j], ohi, olo, e);
+        if constexpr (FOLD)
+          e = exponent_stream<T, UK, false, false>([&](int k, int) -> F { return ukh[j][k]; }, oload, e);
+        else
+          e = exponent<T, UK, false, true>(ukh[j], ukl[j], ohi, olo, e);
 #pragma unroll
         for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
 #pragma unroll
@@ -889,16 +1281,21 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
       if constexpr (KBUF == 1) __syncthreads();   // the buffer is rewritten by the next step
     }
   };
+  // Many operands per step (d_h = 256): no register prefetch across the step,
+  // the registers go to the accumulators; the copy runs between steps.
+  constexpr bool EARLY = PERW <= 8;
   load_step(0);
   store_step(0);
   __syncthreads();
   for (int fb = 0; fb < pl.FB; ++fb) {
     const int buf = OPB == 2 ? (fb & 1) : 0;
-    if (fb + 1 < pl.FB) load_step(fb + 1);
+    if constexpr (EARLY)
+      if (fb + 1 < pl.FB) load_step(fb + 1);
     step(fb, buf);
     if constexpr (STAGE) {
       if (fb + 1 < pl.FB) {
         if constexpr (OPB == 1) __syncthreads();   // one buffer: everyone is done reading it
+        if constexpr (!EARLY) load_step(fb + 1);
         store_step(OPB == 2 ? ((fb + 1) & 1) : 0);
       }
       __syncthreads();
@@ -954,11 +1351,15 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
 // Host launch of one forward call for (T, DH, R16).
 // ---------------------------------------------------------------------------
 constexpr size_t kMaxLds = 160 * 1024;
-// LDS of the tiled key-side kernel: u fragments of four blocks, shifts, the V^T tile
+// LDS of the tiled key-side kernel: exponent operands of four blocks, shifts,
+// the V^T tile and (when small) M'
 template <typename T, int DH, int R16> constexpr size_t kstate_tile_lds_bytes() {
-  return (size_t)(kWaves * kParts<T> * R16 * 64 * 8 + DH * (kTile + 8) + ((R16 + 1) / 2) * (DH / 16) * kParts<T> * 64 * 8) *
-             sizeof(T) +
-         kTile * sizeof(float);
+  constexpr bool FOLD = fold_exponent(sizeof(T), DH, R16);
+  constexpr int UK = FOLD ? DH / 16 : R16;
+  constexpr int UP = FOLD ? 1 : kParts<T>;
+  constexpr size_t mbytes = (size_t)((R16 + 1) / 2) * (DH / 16) * kParts<T> * 64 * 8 * sizeof(T);
+  return (size_t)(kWaves * UP * UK * 64 * 8 + DH * (kTile + 4)) * sizeof(T) + kTile * sizeof(float) +
+         (mbytes <= 32 * 1024 ? mbytes : 16);
 }
 // Least LDS of the causal query-side kernel: the V^T tile and one key-feature
 // buffer (the operand staging buffers are added only where they fit).
@@ -967,24 +1368,48 @@ template <typename T, int DH, int R16, int NQB> constexpr size_t causal_lds_byte
 }
 
 template <typename T, int DH, int R16, int FBW, bool PAD>
-dark_status launch_fwd_pad(const FwdArgs& a, const Plan& pl, void* ws, void* stream) {
+dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* base = reinterpret_cast<char*>(ws);
+  FwdArgs a = a_in;
+  a.kshift = pl.kshift ? reinterpret_cast<float*>(base + pl.off_kshift) : nullptr;
+  a.qshift = pl.kshift ? a.kshift + (long)pl.BH * a.L : nullptr;
   T* mfrag = reinterpret_cast<T*>(base + pl.off_mfrag);
   T* ofrag = reinterpret_cast<T*>(base + pl.off_ofrag);
   T* sdelta = reinterpret_cast<T*>(base + pl.off_sdelta);
   T* sfrag = reinterpret_cast<T*>(base + pl.off_sfrag);
   constexpr int NM = kParts<T>;
   {
-    const long n = (long)pl.HM * ((R16 + 1) / 2) * (DH / 16) * NM * 64 + (long)pl.FB * R16 * NM * 64;
-    const int blocks = (int)((n + 255) / 256);
+    // Folded with d_h >= 32: W' by matrix products and M' in one launch;
+    // otherwise M' and omega' (or a d_h = 16 W') elementwise.
+    const int fmode = !pl.fold ? 0 : (DH >= 32 ? 2 : 1);
+    const float s = powf((float)DH, -0.25f);
+    const long nM = (long)pl.HM * ((R16 + 1) / 2) * (DH / 16) * NM * 64;
     KernelTimer tm(kPrep, stream);
-    hipLaunchKernelGGL(prep_kernel<T>, dim3(blocks), dim3(256), 0, st, a.M, a.omega, mfrag, ofrag, pl.HM, a.r, DH,
-                       a.m, R16, pl.FB, powf((float)DH, -0.25f));
+    if (fmode == 2) {
+      if constexpr (sizeof(T) == 2 && DH >= 32) {
+        const int nW = pl.HM * pl.FB * ((DH / 32 + 3) / 4);
+        hipLaunchKernelGGL(fold_kernel<T>, dim3(nW + (int)((nM + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
+                           a.M, a.omega, ofrag, mfrag, pl.HM, R16, a.r, DH, a.m, pl.FB, s, kLog2e * s);
+      }
+    } else {
+      const long n = nM + (fmode ? (long)pl.HM * pl.FB * (DH / 16) * 64 : (long)pl.FB * R16 * NM * 64);
+      const int blocks = (int)((n + 255) / 256);
+      hipLaunchKernelGGL(prep_kernel<T>, dim3(blocks), dim3(256), 0, st, a.M, a.omega, mfrag, ofrag, pl.HM, a.r, DH,
+                         a.m, R16, pl.FB, s, fmode);
+    }
+  }
+  if (pl.kshift) {
+    const int ntile = (a.L + kShiftTile - 1) / kShiftTile;
+    KernelTimer tm(kPrep, stream);
+    hipLaunchKernelGGL((shift_kernel<T, DH, R16>), dim3(pl.BH * ntile), dim3(kThreads), 0, st, a, mfrag, a.qshift,
+                       a.kshift);
   }
   {
     KernelTimer tm(kKState, stream);
     const dim3 grid1(pl.BH * pl.NU * pl.NF);
+    static_assert(!fold_exponent(sizeof(T), DH, R16) || kstate_tile_lds_bytes<T, DH, R16>() <= kMaxLds,
+                  "the folded key side runs on the tiled kernel");
     if constexpr (kstate_tile_lds_bytes<T, DH, R16>() <= kMaxLds)
       hipLaunchKernelGGL((kstate_kernel<T, DH, R16, FBW, PAD>), grid1, dim3(kThreads), 0, st, a, pl, mfrag, ofrag,
                          sdelta);
