@@ -102,6 +102,9 @@ static void make_plan(const dark_prf_desc& d, Plan& p) {
     p.span1 = p.tile2;
     p.NU = cdiv(L, p.span1);
     p.NT2 = p.NU;
+    // fewer tiles than two per compute unit: eight waves per tile (two groups
+    // taking alternate feature steps) instead of four
+    p.split = 1;   // (two wave groups measured slower at L = 2048; kept for reference)
   } else {
     p.NQB = d.d_h <= 64 ? 2 : 1;
     p.tile2 = 128 * p.NQB;

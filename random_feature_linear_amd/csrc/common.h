@@ -47,6 +47,7 @@ struct Plan {
   int NF;      // feature slices per unit (each slice = 4 waves * FBW blocks)
   // query-side output kernel
   int NQB;     // 32-token query blocks per wave
+  int split;   // causal query side: wave groups per tile that split the feature steps (1 or 2)
   int tile2;   // queries per workgroup (4 waves * 32 * NQB); equals span1 when causal
   int NT2;     // query tiles per (b, h)
   // workspace (bytes from the base pointer)

@@ -154,6 +154,15 @@ __device__ __forceinline__ f32x8 ld4x2(const float* p0, const float* p1) {
   f32x8 f = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   return f;
 }
+// One 16-byte element per lane from global memory straight into LDS (the
+// global_load_lds path, no registers): lane l writes bytes [16 l, 16 l + 16) of
+// the 1 KB at lds_dst, which must be the same for the whole wave.  Counted by
+// vmcnt.  (The host pass of the compiler only sees an empty body.)
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+#endif
+}
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ void store_out(bf16* p, float x) { *p = (bf16)x; }
@@ -1009,6 +1018,22 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
     T* dst = sfrag + (bh * nout * per_unit + rem) * 8;
     float run[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int u = 0;
+    constexpr int UB = 16;                 // units whose loads are in flight together
+    for (; u + UB <= pl.NU; u += UB) {
+      F x[UB];
+#pragma unroll
+      for (int q = 0; q < UB; ++q) x[q] = ld8(src + (long)(u + q) * per_unit * 8);
+#pragma unroll
+      for (int q = 0; q < UB; ++q) {
+        if (a.causal) {
+          F o;
+          make_frag(o, run);
+          st8(dst + (long)(u + q) * per_unit * 8, o);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) run[e] += to_f32(x[q][e]);
+      }
+    }
     for (; u + 4 <= pl.NU; u += 4) {       // four loads in flight
       F x[4];
 #pragma unroll
@@ -1065,9 +1090,36 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
 // the keys at the same positions are mapped by the same wave and shared with
 // the other waves through LDS, one 32-feature step at a time.
 // ---------------------------------------------------------------------------
-template <typename T, int DH, int R16, int NQB, bool CAUSAL, bool PAD>
-__global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
-                                                         const T* __restrict__ ofrag, const T* __restrict__ sfrag) {
+// Whether the causal query side (one query block per wave) can run as two
+// wave groups: both groups' double-buffered operand steps and key-feature
+// buffers fit in LDS beside the V^T tile, and the operand buffers can hold the
+// partial [N, D] of four waves for the final sum.
+template <typename T, int DH, int R16> constexpr bool qout_split_fits() {
+  constexpr int UK = fold_exponent(sizeof(T), DH, R16) ? DH / 16 : R16;
+  constexpr size_t nstep = (size_t)UK * kParts<T> + 2 * vblocks<DH>();
+  constexpr size_t vt = (size_t)DH * (128 + 4) * sizeof(T);
+  constexpr size_t op = 2 * 2 * nstep * 64 * 8 * sizeof(T);     // two groups, two buffers
+  constexpr size_t kf = 2 * 2 * 4 * 2 * 64 * 8 * sizeof(T);     // two groups, two buffers
+  constexpr size_t red = (size_t)kWaves * vblocks<DH>() * 16 * 64 * 4;
+  return vt + op + kf <= 160 * 1024 && op >= red;
+}
+
+// Whether the causal query side can stage the operands of all ALLFB feature
+// steps in LDS at once (bf16): V^T tile, all steps, double key-feature buffers.
+constexpr int kAllFB = 8;
+template <typename T, int DH, int R16, int ALLFB> constexpr bool qout_all_fits() {
+  constexpr int UK = fold_exponent(sizeof(T), DH, R16) ? DH / 16 : R16;
+  constexpr size_t nstep = (size_t)UK * kParts<T> + 2 * vblocks<DH>();
+  constexpr size_t vt = (size_t)DH * (128 + 4) * sizeof(T);
+  constexpr size_t op = (size_t)ALLFB * nstep * 64 * 8 * sizeof(T);
+  constexpr size_t kf = 2 * 4 * 2 * 64 * 8 * sizeof(T);
+  return sizeof(T) == 2 && vt + op + kf <= 160 * 1024;
+}
+
+template <typename T, int DH, int R16, int NQB, bool CAUSAL, bool PAD, int SPLIT = 1, int ALLFB = 0>
+__global__ __launch_bounds__(kThreads * SPLIT) void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
+                                                                 const T* __restrict__ ofrag,
+                                                                 const T* __restrict__ sfrag) {
   typedef typename FragOf<T>::type F;
   constexpr int KD = DH / 16;
   constexpr int NM = kParts<T>;
@@ -1083,22 +1135,36 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   constexpr int PERW = (NSTEP + kWaves - 1) / kWaves;
   constexpr int VT_ELEMS = CAUSAL ? DH * VST : 8;
   constexpr size_t kBase = (size_t)VT_ELEMS * sizeof(T);
-  constexpr size_t kOpStep = (size_t)NSTEP * 64 * 8 * sizeof(T);
-  constexpr size_t kKfStep = CAUSAL ? (size_t)NB * 2 * 64 * 8 * sizeof(T) : 0;
+  constexpr size_t kOpStep = (size_t)SPLIT * NSTEP * 64 * 8 * sizeof(T);
+  constexpr size_t kKfStep = CAUSAL ? (size_t)SPLIT * NB * 2 * 64 * 8 * sizeof(T) : 0;
   // Operands staged in LDS when one step buffer fits beside the V^T tile (else
   // each wave reads them from L2 itself); double buffers (one barrier per
   // feature step) unless LDS is short.
   constexpr bool STAGE = kBase + kOpStep + kKfStep <= 160 * 1024;
   constexpr int OPB = !STAGE ? 0 : kBase + 2 * kOpStep + 2 * kKfStep <= 160 * 1024 ? 2 : 1;
   constexpr int KBUF = kBase + OPB * kOpStep + 2 * kKfStep <= 160 * 1024 ? 2 : 1;
-  constexpr int KF_ELEMS = CAUSAL ? KBUF * NB * 2 * 64 * 8 : 8;
+  constexpr int KF_ELEMS = CAUSAL ? SPLIT * KBUF * NB * 2 * 64 * 8 : 8;
+  // ALLFB > 0 (bf16, at most ALLFB feature blocks): the operands of every step
+  // are copied global -> LDS by the DMA path at the start, overlapping the
+  // projections, and the step loop has no staging and no extra barriers.
+  constexpr bool ALL = ALLFB > 0;
+  static_assert(!ALL || (sizeof(T) == 2 && SPLIT == 1), "all-step staging: bf16, one wave group");
+  constexpr int OP_ELEMS = ALL ? ALLFB * NSTEP * 64 * 8 : STAGE ? SPLIT * OPB * NSTEP * 64 * 8 : 8;
+  // SPLIT = 2: two groups of four waves share the query tile and take every
+  // other feature step; their partial [N, D] are added through LDS at the end.
+  static_assert(SPLIT == 1 || (STAGE && (size_t)OPB * kOpStep >= (size_t)kWaves * NQB * DB * 16 * 64 * 4),
+                "the split form reduces through the operand buffers");
 
   __shared__ __attribute__((aligned(16))) T s_vt[VT_ELEMS];
   __shared__ __attribute__((aligned(16))) T s_kf[KF_ELEMS];
-  __shared__ __attribute__((aligned(16))) T s_op[STAGE ? OPB * NSTEP * 64 * 8 : 8];
+  __shared__ __attribute__((aligned(16))) T s_op[OP_ELEMS];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
+  const int lane = tid & 63, c = lane & 31, g = lane >> 5;
+  const int w = (tid >> 6) % kWaves;   // query-block wave of this group
+  const int hf = (tid >> 6) / kWaves;  // feature group (SPLIT = 2)
+  T* s_opg = s_op + (STAGE ? hf * OPB * NSTEP * 64 * 8 : 0);
+  T* s_kfg = s_kf + (CAUSAL ? hf * KBUF * NB * 2 * 64 * 8 : 0);
   const int tile = blockIdx.x % pl.NT2;
   const int bh = blockIdx.x / pl.NT2;
   const int b = bh / a.H, h = bh % a.H;
@@ -1116,45 +1182,82 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   const long unit_s = (long)bh * (CAUSAL ? pl.NU : 1) + (CAUSAL ? tile : 0);
   const T* sf = sfrag + unit_s * DB * FK * 64 * 8;
 
+  // Operands of one 32-feature step (omega' (W') hi/lo fragments, then the
+  // state fragments) are the same for the four waves of a group.
+  auto gsrc = [&](int fb, int f) -> const T* {
+    if (f < NOF) return of + (((long)(fb * UK + f / NM) * NM + f % NM) * 64 + lane) * 8;
+    f -= NOF;
+    return sf + (((f >> 1) * FK + 2 * fb + (f & 1)) * 64 + lane) * 8;
+  };
+  // All-step staging: the step operands, and M' (in the key-feature buffers,
+  // free until the first step), go to LDS by DMA before anything else is loaded.
+  constexpr int MFRG = ((R16 + 1) / 2) * KD * NM;
+  constexpr bool M_LDS = ALL && CAUSAL && MFRG * 64 * 8 <= KF_ELEMS;
+  if constexpr (ALL) {
+    for (int idx = w; idx < pl.FB * NSTEP; idx += kWaves) {
+      const int fb = idx / NSTEP, f = idx - fb * NSTEP;
+      dma16(gsrc(fb, f), s_op + idx * 64 * 8);
+    }
+    if constexpr (M_LDS)
+      for (int idx = w; idx < MFRG; idx += kWaves)
+        dma16(mf + ((long)idx * 64 + lane) * 8, s_kf + idx * 64 * 8);
+  }
+
   // ---- exponent operands of this wave's query (and key) blocks: u = M' x as
-  // hi/lo fragments, or (folded) the token rows x themselves ----
+  // hi/lo fragments, or (folded) the token rows x themselves.  Rows and the
+  // V tile are requested first, the projections run once they are in. ----
   F uqh[NQB][UK], uql[NQB][FOLD ? 1 : UK];
   float shq[NQB];
   F ukh[CAUSAL ? NQB : 1][UK], ukl[CAUSAL ? NQB : 1][FOLD ? 1 : UK];
   float initk[CAUSAL ? NQB : 1];
-  auto operands = [&](F* uh, F* ul, const T* row, bool ok) -> float {
-    if constexpr (FOLD) {
-      load_rows<T, DH>(*reinterpret_cast<F(*)[KD]>(uh), row, ok, g);
-      return project_shift<T, DH, R16>(*reinterpret_cast<F(*)[KD]>(uh), mf, lane, half_log2m);
-    } else {
-      F xf[KD];
-      load_rows<T, DH>(xf, row, ok, g);
-      return project_block<T, DH, R16>(*reinterpret_cast<F(*)[R16]>(uh), *reinterpret_cast<F(*)[R16]>(ul), xf,
-                                       mf, lane, half_log2m);
-    }
-  };
+  F xq[FOLD ? 1 : NQB][KD], xk[(FOLD || !CAUSAL) ? 1 : NQB][KD];
 #pragma unroll
   for (int j = 0; j < NQB; ++j) {
     const int t = t0 + 32 * (w * NQB + j) + c;
     const bool ok = t < a.L;
-    if (FOLD && pl.kshift) {   // shifts precomputed: only the rows are needed
-      load_rows<T, DH>(*reinterpret_cast<F(*)[KD]>(uqh[j]), qbase + (long)t * a.qs[2], ok, g);
+    F* xr = FOLD ? uqh[j] : xq[FOLD ? 0 : j];
+    load_rows<T, DH>(*reinterpret_cast<F(*)[KD]>(xr), qbase + (long)t * a.qs[2], ok, g);
+    if constexpr (CAUSAL) {
+      F* kr = FOLD ? ukh[j] : xk[FOLD ? 0 : j];
+      load_rows<T, DH>(*reinterpret_cast<F(*)[KD]>(kr), kbase + (long)t * a.ks[2], ok, g);
+    }
+  }
+  constexpr int VPT = vloads_per_thread<DH, TT>();
+  F vr[CAUSAL ? VPT : 1];
+  if constexpr (CAUSAL)
+    if (hf == 0) load_v<T, DH, TT>(vr, vbase, a.vs[2], t0, a.L, tid);
+  if constexpr (ALL) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed
+  if constexpr (CAUSAL)
+    if (hf == 0) store_vt<T, DH, TT, VST>(s_vt, vr, tid);
+  if constexpr (M_LDS) __syncthreads();   // M' (and every wave's copies) visible
+  const T* msrc = M_LDS ? s_kf : mf;
+#pragma unroll
+  for (int j = 0; j < NQB; ++j) {
+    const int t = t0 + 32 * (w * NQB + j) + c;
+    const bool ok = t < a.L;
+    if (FOLD && pl.kshift) {   // shifts precomputed
       shq[j] = ok ? a.qshift[(long)bh * a.L + t] : 0.f;
+    } else if constexpr (FOLD) {
+      shq[j] = project_shift<T, DH, R16>(*reinterpret_cast<F(*)[KD]>(uqh[j]), msrc, lane, half_log2m);
     } else {
-      shq[j] = operands(uqh[j], uql[j], qbase + (long)t * a.qs[2], ok);
+      shq[j] = project_block<T, DH, R16>(*reinterpret_cast<F(*)[R16]>(uqh[j]), *reinterpret_cast<F(*)[R16]>(uql[j]),
+                                         xq[FOLD ? 0 : j], msrc, lane, half_log2m);
     }
     if constexpr (CAUSAL) {
-      if (FOLD && pl.kshift) {   // shifts precomputed: only the rows are needed
-        load_rows<T, DH>(*reinterpret_cast<F(*)[KD]>(ukh[j]), kbase + (long)t * a.ks[2], ok, g);
+      float sh = 0.f;
+      if (FOLD && pl.kshift) {
         initk[j] = ok ? a.kshift[(long)bh * a.L + t] : -INFINITY;
       } else {
-        const float sh = operands(ukh[j], ukl[j], kbase + (long)t * a.ks[2], ok);
+        if constexpr (FOLD)
+          sh = project_shift<T, DH, R16>(*reinterpret_cast<F(*)[KD]>(ukh[j]), msrc, lane, half_log2m);
+        else
+          sh = project_block<T, DH, R16>(*reinterpret_cast<F(*)[R16]>(ukh[j]), *reinterpret_cast<F(*)[R16]>(ukl[j]),
+                                         xk[FOLD ? 0 : j], msrc, lane, half_log2m);
         const bool valid = ok && (mrow == nullptr || mrow[t] != 0);
         initk[j] = valid ? -sh : -INFINITY;
       }
     }
   }
-  if constexpr (CAUSAL) stage_vt<T, DH, TT, VST>(s_vt, vbase, a.vs[2], t0, a.L, tid);
 
   f32x16 acc[NQB][DB];
 #pragma unroll
@@ -1169,17 +1272,11 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
       for (int kb2 = 0; kb2 < NB; ++kb2) at[j][kb2] = zero16();
   }
 
-  // Operands of one 32-feature step (omega' hi/lo fragments, then the state
-  // fragments) are the same for the four waves: each wave fetches a quarter of
-  // them from L2 one step ahead, and all read them from LDS.
-  auto gsrc = [&](int fb, int f) -> const T* {
-    if (f < NOF) return of + (((long)(fb * UK + f / NM) * NM + f % NM) * 64 + lane) * 8;
-    f -= NOF;
-    return sf + (((f >> 1) * FK + 2 * fb + (f & 1)) * 64 + lane) * 8;
-  };
-  F pre[STAGE ? PERW : 1];
+  // Ring staging: each wave fetches a quarter of a step's operands from L2
+  // one step ahead, and all read them from LDS.
+  F pre[STAGE && !ALL ? PERW : 1];
   auto load_step = [&](int fb) {
-    if constexpr (STAGE) {
+    if constexpr (STAGE && !ALL) {
 #pragma unroll
       for (int q = 0; q < PERW; ++q) {
         const int f = w + kWaves * q;
@@ -1188,16 +1285,17 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
     }
   };
   auto store_step = [&](int buf) {
-    if constexpr (STAGE) {
+    if constexpr (STAGE && !ALL) {
 #pragma unroll
       for (int q = 0; q < PERW; ++q) {
         const int f = w + kWaves * q;
-        if (f < NSTEP) st8(s_op + ((buf * NSTEP + f) * 64 + lane) * 8, pre[q]);
+        if (f < NSTEP) st8(s_opg + ((buf * NSTEP + f) * 64 + lane) * 8, pre[q]);
       }
     }
   };
   auto op = [&](int fb, int buf, int f) {
-    if constexpr (STAGE) return ld8(s_op + ((buf * NSTEP + f) * 64 + lane) * 8);
+    if constexpr (ALL) return ld8(s_op + ((fb * NSTEP + f) * 64 + lane) * 8);
+    else if constexpr (STAGE) return ld8(s_opg + ((buf * NSTEP + f) * 64 + lane) * 8);
     else return ld8(gsrc(fb, f));
   };
 
@@ -1249,7 +1347,7 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
         if (db % 3 == 2) __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (CAUSAL) {
-      T* kbuf = s_kf + (KBUF == 2 ? (fb & 1) : 0) * NB * 2 * 64 * 8;
+      T* kbuf = s_kfg + (KBUF == 2 ? ((fb / SPLIT) & 1) : 0) * NB * 2 * 64 * 8;
 #pragma unroll
       for (int j = 0; j < NQB; ++j) {
         f32x16 e = splat16(initk[j]);
@@ -1284,22 +1382,41 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   // Many operands per step (d_h = 256): no register prefetch across the step,
   // the registers go to the accumulators; the copy runs between steps.
   constexpr bool EARLY = PERW <= 8;
-  load_step(0);
-  store_step(0);
+  // Step i of group hf is feature block SPLIT i + hf; a group whose block is
+  // past the last one idles through the step (the barriers are shared).
+  const int nsteps = (pl.FB + SPLIT - 1) / SPLIT;
+  if constexpr (ALL) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed
+    __syncthreads();                      // and everyone else's
+    for (int fb = 0; fb < pl.FB; ++fb) step(fb, 0);
+  } else {
+  if (hf < pl.FB) {
+    load_step(hf);
+    store_step(0);
+  }
   __syncthreads();
-  for (int fb = 0; fb < pl.FB; ++fb) {
-    const int buf = OPB == 2 ? (fb & 1) : 0;
+  for (int i = 0; i < nsteps; ++i) {
+    const int fb = i * SPLIT + hf, fbn = fb + SPLIT;
+    const int buf = OPB == 2 ? (i & 1) : 0;
     if constexpr (EARLY)
-      if (fb + 1 < pl.FB) load_step(fb + 1);
-    step(fb, buf);
+      if (fbn < pl.FB) load_step(fbn);
+    if (SPLIT == 1 || fb < pl.FB) {
+      step(fb, buf);
+    } else if constexpr (CAUSAL) {
+      __syncthreads();   // the barrier inside a step
+      if constexpr (KBUF == 1) __syncthreads();
+    }
     if constexpr (STAGE) {
-      if (fb + 1 < pl.FB) {
+      if (i + 1 < nsteps) {
         if constexpr (OPB == 1) __syncthreads();   // one buffer: everyone is done reading it
-        if constexpr (!EARLY) load_step(fb + 1);
-        store_step(OPB == 2 ? ((fb + 1) & 1) : 0);
+        if constexpr (!EARLY)
+          if (fbn < pl.FB) load_step(fbn);
+        if (fbn < pl.FB) store_step(OPB == 2 ? ((i + 1) & 1) : 0);
       }
       __syncthreads();
     }
+  }
+
   }
 
   if constexpr (CAUSAL) {
@@ -1324,6 +1441,26 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
         }
       }
     }
+  }
+
+  if constexpr (SPLIT == 2) {   // group 1 hands its partial [N, D] to group 0 through LDS
+    float* red = reinterpret_cast<float*>(s_op);
+    if (hf == 1) {
+#pragma unroll
+      for (int j = 0; j < NQB; ++j)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) red[(((w * NQB + j) * DB + db) * 16 + i) * 64 + lane] = acc[j][db][i];
+    }
+    __syncthreads();
+    if (hf == 1) return;
+#pragma unroll
+    for (int j = 0; j < NQB; ++j)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[j][db][i] += red[(((w * NQB + j) * DB + db) * 16 + i) * 64 + lane];
   }
 
   // ---- out = N / D; D is column d_h of [N, D], held by lane d_h % 32 of each half ----
@@ -1428,6 +1565,20 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
   if (a.causal) {
     if constexpr (causal_lds_bytes<T, DH, R16, 1>() <= kMaxLds) {
       if (pl.NQB != 1) return DARK_ERR_UNSUPPORTED;
+      if constexpr (qout_all_fits<T, DH, R16, kAllFB>()) {   // few feature blocks: all steps staged at once
+        if (pl.FB <= kAllFB) {
+          hipLaunchKernelGGL((qout_kernel<T, DH, R16, 1, true, PAD, 1, kAllFB>), grid, dim3(kThreads), 0, st, a, pl,
+                             mfrag, ofrag, sfrag);
+          return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
+        }
+      }
+      if constexpr (DH <= 64 && qout_split_fits<T, DH, R16>()) {   // few tiles: two wave groups per tile
+        if (pl.split == 2) {
+          hipLaunchKernelGGL((qout_kernel<T, DH, R16, 1, true, PAD, 2>), grid, dim3(2 * kThreads), 0, st, a, pl,
+                             mfrag, ofrag, sfrag);
+          return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
+        }
+      }
       hipLaunchKernelGGL((qout_kernel<T, DH, R16, 1, true, PAD>), grid, dim3(kThreads), 0, st, a, pl, mfrag, ofrag,
                          sfrag);
     } else {
