@@ -547,10 +547,12 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict_
 // every query row (qshift[bh][t]) and every key row as seen by query head h
 // (kshift[bh][t] = minus that, or -inf for a masked key).  They replace the
 // projections in the key-side kernel (once per feature slice) and in the query
-// side.  Workgroup: 4 waves x 2 blocks of 32 rows (64 query and 64 key rows
-// per wave); M' goes through LDS one 32-row slice at a time, shared by all.
+// side.  Workgroup: 4 waves over 128 rows of q (first half of the grid) or of
+// k (second half); wave w keeps its 32 rows in registers while M' streams
+// through LDS one 32-row slice at a time (double-buffered, the next slice
+// fetched during the products).
 // ---------------------------------------------------------------------------
-constexpr int kShiftTile = 2 * kTile;
+constexpr int kShiftTile = kTile;
 template <typename T, int DH, int R16>
 __global__ __launch_bounds__(kThreads) void shift_kernel(FwdArgs a, const T* __restrict__ mfrag,
                                                           float* __restrict__ qshift, float* __restrict__ kshift) {
@@ -558,57 +560,64 @@ __global__ __launch_bounds__(kThreads) void shift_kernel(FwdArgs a, const T* __r
   constexpr int KD = DH / 16;
   constexpr int NM = kParts<T>;
   constexpr int R32 = (R16 + 1) / 2;
-  constexpr int SL = KD * NM;   // fragments of one 32-row slice of M'
-  __shared__ __attribute__((aligned(16))) T s_m[SL * 64 * 8];
+  constexpr int SL = KD * NM;                         // fragments of one 32-row slice of M'
+  constexpr int PS = (SL * 64 + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) T s_m[2][SL * 64 * 8];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
   const int ntile = (a.L + kShiftTile - 1) / kShiftTile;
-  const int tile = blockIdx.x % ntile;
-  const int bh = blockIdx.x / ntile;
+  const int half = (int)(blockIdx.x / (gridDim.x / 2));   // 0: queries, 1: keys
+  const int blk = blockIdx.x % (gridDim.x / 2);
+  const int tile = blk % ntile;
+  const int bh = blk / ntile;
   const int b = bh / a.H, h = bh % a.H;
   const int hk = (h * a.H_kv) / a.H;
-  const T* qbase = reinterpret_cast<const T*>(a.q) + b * a.qs[0] + h * a.qs[1];
-  const T* kbase = reinterpret_cast<const T*>(a.k) + b * a.ks[0] + hk * a.ks[1];
-  const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * R32 * KD * NM * 64 * 8;
-  // rows: [0] query block 2w, [1] query block 2w+1, [2] key block 2w, [3] key block 2w+1
-  float ss[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int rb = 0; rb < R32; ++rb) {
-    __syncthreads();   // the previous slice is no longer read
-    constexpr int PS = (SL * 64 + kThreads - 1) / kThreads;
-    F stage[PS];   // all loads of the slice in flight before the stores
-#pragma unroll
-    for (int p = 0; p < PS; ++p) stage[p] = ld8(mf + ((long)rb * SL * 64 + min(tid + p * kThreads, SL * 64 - 1)) * 8);
+  const T* base = half == 0 ? reinterpret_cast<const T*>(a.q) + b * a.qs[0] + h * a.qs[1]
+                            : reinterpret_cast<const T*>(a.k) + b * a.ks[0] + hk * a.ks[1];
+  const int64_t stride = half == 0 ? a.qs[2] : a.ks[2];
+  const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * R32 * SL * 64 * 8;
+  const int t = tile * kShiftTile + 32 * w + c;
+  const bool ok = t < a.L;
+  F stage[PS];
+  auto fetch = [&](int rb) {
 #pragma unroll
     for (int p = 0; p < PS; ++p)
-      if (tid + p * kThreads < SL * 64) st8(s_m + (tid + p * kThreads) * 8, stage[p]);
-    __syncthreads();
+      stage[p] = ld8(mf + ((long)rb * SL * 64 + min(tid + p * kThreads, SL * 64 - 1)) * 8);
+  };
+  auto put = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int t = tile * kShiftTile + 32 * (2 * w + (q & 1)) + c;
-      const T* row = (q < 2 ? qbase + (long)t * a.qs[2] : kbase + (long)t * a.ks[2]);
-      F xf[KD];
-      load_rows<T, DH>(xf, row, t < a.L, g);
-      f32x16 acc = zero16();
+    for (int p = 0; p < PS; ++p)
+      if (tid + p * kThreads < SL * 64) st8(&s_m[buf][(tid + p * kThreads) * 8], stage[p]);
+  };
+  fetch(0);
+  F xf[KD];
+  load_rows<T, DH>(xf, base + (long)t * stride, ok, g);
+  put(0);
+  __syncthreads();
+  float ss = 0.f;
+  for (int rb = 0; rb < R32; ++rb) {
+    if (rb + 1 < R32) fetch(rb + 1);
+    const T* sm = s_m[rb & 1];
+    f32x16 u = zero16();
 #pragma unroll
-      for (int kd = 0; kd < KD; ++kd)
+    for (int kd = 0; kd < KD; ++kd) {
 #pragma unroll
-        for (int part = 0; part < NM; ++part) acc = mma(ld8(s_m + ((kd * NM + part) * 64 + lane) * 8), xf[kd], acc);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ss[q] += acc[i] * acc[i];
+      for (int part = 0; part < NM; ++part) u = mma(ld8(sm + ((kd * NM + part) * 64 + lane) * 8), xf[kd], u);
+      if constexpr (SL > 8)   // bound the slice fragments in flight
+        if (kd % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
-  }
-  const float half_log2m = 0.5f * log2f((float)a.m);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float sum = ss[q] + __shfl_xor(ss[q], 32);
-    const float sh = 0.5f * kLog2e * sum + half_log2m;
-    const int t = tile * kShiftTile + 32 * (2 * w + (q & 1)) + c;
-    if (g == 0 && t < a.L) {
-      if (q < 2) {
-        qshift[(long)bh * a.L + t] = sh;
-      } else {
-        const bool valid = a.mask == nullptr || a.mask[(long)b * a.L + t] != 0;
-        kshift[(long)bh * a.L + t] = valid ? -sh : -INFINITY;
-      }
+    for (int i = 0; i < 16; ++i) ss += u[i] * u[i];
+    if (rb + 1 < R32) put((rb + 1) & 1);
+    __syncthreads();
+  }
+  ss += __shfl_xor(ss, 32);
+  const float sh = 0.5f * kLog2e * ss + 0.5f * log2f((float)a.m);
+  if (g == 0 && ok) {
+    if (half == 0) {
+      qshift[(long)bh * a.L + t] = sh;
+    } else {
+      const bool valid = a.mask == nullptr || a.mask[(long)b * a.L + t] != 0;
+      kshift[(long)bh * a.L + t] = valid ? -sh : -INFINITY;
     }
   }
 }
@@ -1539,8 +1548,8 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
   if (pl.kshift) {
     const int ntile = (a.L + kShiftTile - 1) / kShiftTile;
     KernelTimer tm(kPrep, stream);
-    hipLaunchKernelGGL((shift_kernel<T, DH, R16>), dim3(pl.BH * ntile), dim3(kThreads), 0, st, a, mfrag, a.qshift,
-                       a.kshift);
+    hipLaunchKernelGGL((shift_kernel<T, DH, R16>), dim3(2 * pl.BH * ntile), dim3(kThreads), 0, st, a, mfrag,
+                       a.qshift, a.kshift);
   }
   {
     KernelTimer tm(kKState, stream);

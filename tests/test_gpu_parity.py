@@ -67,6 +67,8 @@ SMALL = [
     ("bf16_d16_c_m16", "bf16", 2, 2, 2,   130, 16,  16,  16,  True,  True,  True,  "random"),
     ("bf16_d64_c_m48", "bf16", 1, 2, 2,   150, 64,  48,  64,  True,  True,  True,  "tail"),
     ("f32_d128_nc",    "f32",  1, 2, 2,   90,  128, 64,  32,  False, True,  True,  "tail"),
+    # many heads and chunks, masked tail, two feature slices
+    ("bf16_d64_c_many", "bf16", 16, 8, 8,  1300, 64,  512, 64,  True,  True,  True,  "tail"),
     # folded exponent with two feature slices: key shifts computed once up front
     ("bf16_d64_nc_m512", "bf16", 1, 2, 1,  300, 64,  512, 64,  False, True,  True,  "random"),
     ("f32_d256_c",     "f32",  1, 1, 1,   70,  256, 32,  64,  True,  True,  True,  "none"),
