@@ -710,9 +710,13 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
   constexpr int MFR = ((R16 + 1) / 2) * KD * NM;   // fragments of M' (one head)
   constexpr bool M_LDS = MFR * 64 * 8 * sizeof(T) <= 32 * 1024;   // M' staged in LDS
   constexpr int VPT = vloads_per_thread<DH, TT>();
-  __shared__ __attribute__((aligned(16))) T s_u[kWaves][UP][UK][64 * 8];
-  __shared__ __attribute__((aligned(16))) float s_init[TT];
-  __shared__ __attribute__((aligned(16))) T s_vt[DH * VST];
+  // Double-buffered tile state (one barrier per tile; the next tile is
+  // projected right behind the current tile's products) when it fits.
+  constexpr size_t kTileState = (size_t)(kWaves * UP * UK * 64 * 8 + DH * VST) * sizeof(T) + TT * sizeof(float);
+  constexpr int NBUF = 2 * kTileState + (M_LDS ? MFR * 64 * 8 * sizeof(T) : 0) <= 160 * 1024 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) T s_u[NBUF][kWaves][UP][UK][64 * 8];
+  __shared__ __attribute__((aligned(16))) float s_init[NBUF][TT];
+  __shared__ __attribute__((aligned(16))) T s_vt[NBUF][DH * VST];
   __shared__ __attribute__((aligned(16))) T s_m[M_LDS ? MFR * 64 * 8 : 8];
 
   const int tid = threadIdx.x;
@@ -773,57 +777,44 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
     load_rows<T, DH>(xpre, kbase + (long)t * a.ks[2], t < t_end, g);
     load_v<T, DH, TT>(vpre, vbase, a.vs[2], tt, t_end, tid);
   };
-  if constexpr (PREF) prefetch(t_begin);
-  __syncthreads();
-
-  for (int t0 = t_begin; t0 < t_end; t0 += TT) {
-    // The omega' (W') and M' fragments are the same for every tile; hiding the
-    // pointers from the optimiser keeps their loads in the loop instead of
-    // hoisting all of them into registers (and spilling) before it.
-    const T* of_t = of;
-    const T* msrc_t = msrc;
-    if constexpr (!kHoist) asm volatile("" : "+s"(of_t));
-    if constexpr (!M_LDS) asm volatile("" : "+s"(msrc_t));
-    if constexpr (!PREF) prefetch(t0);
-    {  // projection of token block w
-      const int t = t0 + 32 * w + c;
-      const bool ok = t < t_end;
-      float shift = 0.f;
-      if constexpr (FOLD) {   // the exponent reads the token rows themselves
-        if (!pl.kshift) shift = project_shift<T, DH, R16>(xpre, msrc_t, lane, half_log2m);
+  // projection of token block w of the tile at tt into buffer buf (rows from xpre)
+  auto project_tile = [&](int tt, int buf, const T* msrc_t) {
+    const int t = tt + 32 * w + c;
+    const bool ok = t < t_end;
+    float shift = 0.f;
+    if constexpr (FOLD) {   // the exponent reads the token rows themselves
+      if (!pl.kshift) shift = project_shift<T, DH, R16>(xpre, msrc_t, lane, half_log2m);
 #pragma unroll
-        for (int k = 0; k < UK; ++k) st8(&s_u[w][0][k][lane * 8], xpre[k]);
-      } else {
-        F uhi[R16], ulo[R16];
-        shift = project_block<T, DH, R16>(uhi, ulo, xpre, msrc_t, lane, half_log2m);
+      for (int k = 0; k < UK; ++k) st8(&s_u[buf][w][0][k][lane * 8], xpre[k]);
+    } else {
+      F uhi[R16], ulo[R16];
+      shift = project_block<T, DH, R16>(uhi, ulo, xpre, msrc_t, lane, half_log2m);
 #pragma unroll
-        for (int k = 0; k < R16; ++k) {
-          st8(&s_u[w][0][k][lane * 8], uhi[k]);
-          if constexpr (NM == 2) st8(&s_u[w][NM - 1][k][lane * 8], ulo[k]);
-        }
+      for (int k = 0; k < R16; ++k) {
+        st8(&s_u[buf][w][0][k][lane * 8], uhi[k]);
+        if constexpr (NM == 2) st8(&s_u[buf][w][NM - 1][k][lane * 8], ulo[k]);
       }
-      const bool valid = ok && (mrow == nullptr || mrow[t] != 0);
-      if (g == 0)
-        s_init[32 * w + c] = (FOLD && pl.kshift) ? (ok ? a.kshift[(long)bh * a.L + t] : -INFINITY)
-                                                  : (valid ? -shift : -INFINITY);
     }
-    store_vt<T, DH, TT, VST>(s_vt, vpre, tid);
-    __syncthreads();
-    if constexpr (PREF)
-      if (t0 + TT < t_end) prefetch(t0 + TT);
-
+    const bool valid = ok && (mrow == nullptr || mrow[t] != 0);
+    if (g == 0)
+      s_init[buf][32 * w + c] = (FOLD && pl.kshift) ? (ok ? a.kshift[(long)bh * a.L + t] : -INFINITY)
+                                                     : (valid ? -shift : -INFINITY);
+    store_vt<T, DH, TT, VST>(s_vt[buf], vpre, tid);
+  };
+  // the products of one tile from buffer buf
+  auto compute_tile = [&](int buf, const T* of_t) {
 #pragma unroll
     for (int tb = 0; tb < kWaves; ++tb) {
       f32x16 ini;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {   // rows 8 jj + 4g .. 8 jj + 4g + 3 are contiguous
-        const float4 x = *reinterpret_cast<const float4*>(&s_init[32 * tb + 8 * jj + 4 * g]);
+        const float4 x = *reinterpret_cast<const float4*>(&s_init[buf][32 * tb + 8 * jj + 4 * g]);
         ini[4 * jj] = x.x;
         ini[4 * jj + 1] = x.y;
         ini[4 * jj + 2] = x.z;
         ini[4 * jj + 3] = x.w;
       }
-      auto uload = [&](int k, int part) -> F { return ld8(&s_u[tb][part ? UP - 1 : 0][k][lane * 8]); };
+      auto uload = [&](int k, int part) -> F { return ld8(&s_u[buf][tb][part ? UP - 1 : 0][k][lane * 8]); };
       // [V, 1] fragments of the block: held across the feature blocks when
       // few, else read from LDS at each use
       constexpr bool VHOLD = DB <= 4;
@@ -832,7 +823,7 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int k = 0; k < 2; ++k) vf[db][k] = v_frag<T, DH, VST>(s_vt, db, 32 * tb, k, c, g);
+          for (int k = 0; k < 2; ++k) vf[db][k] = v_frag<T, DH, VST>(s_vt[buf], db, 32 * tb, k, c, g);
       }
 #pragma unroll
       for (int f = 0; f < FBW; ++f) {
@@ -853,14 +844,50 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
         const F p0 = acc_frag<F>(e, 0), p1 = acc_frag<F>(e, 1);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const F v0 = VHOLD ? vf[VHOLD ? db : 0][0] : v_frag<T, DH, VST>(s_vt, db, 32 * tb, 0, c, g);
-          const F v1 = VHOLD ? vf[VHOLD ? db : 0][1] : v_frag<T, DH, VST>(s_vt, db, 32 * tb, 1, c, g);
+          const F v0 = VHOLD ? vf[VHOLD ? db : 0][0] : v_frag<T, DH, VST>(s_vt[buf], db, 32 * tb, 0, c, g);
+          const F v1 = VHOLD ? vf[VHOLD ? db : 0][1] : v_frag<T, DH, VST>(s_vt[buf], db, 32 * tb, 1, c, g);
           acc[f][db] = mma(p0, v0, acc[f][db]);
           acc[f][db] = mma(p1, v1, acc[f][db]);
         }
       }
     }
+  };
+  // The omega' (W') and M' fragments are the same for every tile; hiding the
+  // pointers from the optimiser keeps their loads in the loop instead of
+  // hoisting all of them into registers (and spilling) before it.
+  auto opaque = [&](const T* p, bool hide) {
+    if (hide) asm volatile("" : "+s"(p));
+    return p;
+  };
+  if constexpr (NBUF == 2) {
+    prefetch(t_begin);
+    __syncthreads();   // M' in LDS
+    project_tile(t_begin, 0, msrc);
     __syncthreads();
+    int it = 0;
+    for (int t0 = t_begin; t0 < t_end; t0 += TT, ++it) {
+      const T* of_t = opaque(of, !kHoist);
+      const T* msrc_t = opaque(msrc, !M_LDS);
+      const bool more = t0 + TT < t_end;
+      if (more) prefetch(t0 + TT);
+      compute_tile(it & 1, of_t);
+      if (more) project_tile(t0 + TT, (it + 1) & 1, msrc_t);
+      __syncthreads();
+    }
+  } else {
+    if constexpr (PREF) prefetch(t_begin);
+    __syncthreads();
+    for (int t0 = t_begin; t0 < t_end; t0 += TT) {
+      const T* of_t = opaque(of, !kHoist);
+      const T* msrc_t = opaque(msrc, !M_LDS);
+      if constexpr (!PREF) prefetch(t0);
+      project_tile(t0, 0, msrc_t);
+      __syncthreads();
+      if constexpr (PREF)
+        if (t0 + TT < t_end) prefetch(t0 + TT);
+      compute_tile(0, of_t);
+      __syncthreads();
+    }
   }
 
   // ---- write this wave's part of the unit state ----
