@@ -102,9 +102,6 @@ static void make_plan(const dark_prf_desc& d, Plan& p) {
     p.span1 = p.tile2;
     p.NU = cdiv(L, p.span1);
     p.NT2 = p.NU;
-    // fewer tiles than two per compute unit: eight waves per tile (two groups
-    // taking alternate feature steps) instead of four
-    p.split = 1;   // (two wave groups measured slower at L = 2048; kept for reference)
   } else {
     p.NQB = d.d_h <= 64 ? 2 : 1;
     p.tile2 = 128 * p.NQB;
@@ -119,9 +116,9 @@ static void make_plan(const dark_prf_desc& d, Plan& p) {
   // operand copies of M' and omega' (bf16: hi and lo parts; see prf_kernels.cuh)
   const int NM = d.dtype == DARK_BF16 ? 2 : 1;
   const int R32 = (p.R16 + 1) / 2;
-  const int DB = (d.d_h + 1 + 31) / 32;  // 32-column blocks of [V, 1]
+  const int DB = (d.d_h + 31) / 32;      // 32-column blocks of V
   const size_t frag = 64 * 8;            // elements per operand fragment
-  const size_t state_frags = (size_t)DB * 2 * p.FB;   // fragments of one unit state [S, z]
+  const size_t state_frags = (size_t)DB * 2 * p.FB;   // fragments of one unit state S
   const int nout = d.causal ? p.NU : 1;
   size_t off = 0;
   p.off_mfrag = off;
@@ -135,6 +132,11 @@ static void make_plan(const dark_prf_desc& d, Plan& p) {
   off = align256(off + (size_t)p.BH * p.NU * state_frags * frag * p.elem);
   p.off_sfrag = off;
   off = align256(off + (size_t)p.BH * nout * state_frags * frag * p.elem);
+  // normaliser states z (fp32, 32 FB per unit): per unit, then combined
+  p.off_zdelta = off;
+  off = align256(off + (size_t)p.BH * p.NU * p.FB * 32 * sizeof(float));
+  p.off_zsum = off;
+  off = align256(off + (size_t)p.BH * nout * p.FB * 32 * sizeof(float));
   // keys and queries are projected once up front (for |u|^2) when several
   // feature slices, or the causal query side, would otherwise repeat it
   p.kshift = p.fold && (p.NF > 1 || (d.causal && d.d_h >= 128));

@@ -47,11 +47,10 @@ struct Plan {
   int NF;      // feature slices per unit (each slice = 4 waves * FBW blocks)
   // query-side output kernel
   int NQB;     // 32-token query blocks per wave
-  int split;   // causal query side: wave groups per tile that split the feature steps (1 or 2)
   int tile2;   // queries per workgroup (4 waves * 32 * NQB); equals span1 when causal
   int NT2;     // query tiles per (b, h)
   // workspace (bytes from the base pointer)
-  size_t off_mfrag, off_ofrag, off_sdelta, off_sfrag, off_kshift, total;
+  size_t off_mfrag, off_ofrag, off_sdelta, off_sfrag, off_zdelta, off_zsum, off_kshift, total;
   int elem;    // bytes per element of q/k/v (2 or 4)
 };
 

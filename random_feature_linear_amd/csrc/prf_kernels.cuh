@@ -665,14 +665,14 @@ __device__ __forceinline__ void stage_vt(T* s_vt, const T* vb, int64_t vstride, 
   store_vt<T, DH, TT, VST>(s_vt, vr, tid);
 }
 
-// [V, 1] operand fragment: column d = 32 db + c (d < d_h: V, d = d_h: ones,
-// past that: zero), tokens tb0 + 16k + 8 (e / 4) + 4g + e % 4
-template <typename T, int DH, int VST>
+// V operand fragment: column d = 32 db + c (with ONES, column d_h is all
+// ones; zero past that), tokens tb0 + 16k + 8 (e / 4) + 4g + e % 4
+template <typename T, int DH, int VST, bool ONES = false>
 __device__ __forceinline__ typename FragOf<T>::type v_frag(const T* s_vt, int db, int tb0, int k, int c, int g) {
   typedef typename FragOf<T>::type F;
   const int d = db * 32 + c;
-  if (d >= DH) {
-    const float o = d == DH ? 1.0f : 0.0f;
+  if ((ONES || DH % 32 != 0) && d >= DH) {
+    const float o = ONES && d == DH ? 1.0f : 0.0f;
     float v[8] = {o, o, o, o, o, o, o, o};
     F f;
     make_frag(f, v);
@@ -681,22 +681,46 @@ __device__ __forceinline__ typename FragOf<T>::type v_frag(const T* s_vt, int db
   const T* base = s_vt + d * VST + tb0 + 16 * k + 4 * g;
   return ld4x2(base, base + 8);
 }
-// 32-column blocks of [V, 1]
-template <int DH> constexpr int vblocks() { return (DH + 1 + 31) / 32; }
+// 32-column blocks of V (of the state S).  The normaliser z (the sums of the
+// features) is kept apart in fp32: the key side takes it from a column of
+// ones beside V on the matrix cores, or sums the rounded features on the
+// vector ALUs; the query side always forms D on the vector ALUs.
+template <int DH> constexpr int vblocks() { return (DH + 31) / 32; }
+template <int DH> constexpr int vblocks_ones() { return (DH + 1 + 31) / 32; }
+// s + the sum of the 8 elements of an operand fragment, in fp32 (bf16: pairwise
+// dot products with (1, 1), so the sum sees the rounded values the products use)
+__device__ __forceinline__ float frag_sum(const bf16x8& f, float s) {
+  typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 0, 1), one, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 2, 3), one, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 4, 5), one, s, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 6, 7), one, s, false);
+}
+__device__ __forceinline__ float frag_sum(const f32x8& f, float s) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += f[i];
+  return s;
+}
 
 // ---------------------------------------------------------------------------
 // Key side.  Per unit (a chunk when causal, an L-split otherwise) and feature
-// slice:  S[j][d] = sum_t phi(k_t)_j v_t[d]  and  z[j] = sum_t phi(k_t)_j,
-// written as bf16 operand fragments of the query side
-//   sdelta[bh][unit][db][fk][lane][8]: column d = 32 db + c of [S, z] (column
-//                                      d_h is z), feature 16 fk + 8 (e / 4) + 4g + e % 4.
+// slice:  S[j][d] = sum_t phi(k_t)_j v_t[d]  and  z[j] = sum_t phi(k_t)_j.
+// S is written as operand fragments of the query side (bf16 for bf16 inputs)
+//   sdelta[bh][unit][db][fk][lane][8]: column d = 32 db + c of S,
+//                                      feature 16 fk + 8 (e / 4) + 4g + e % 4,
+// z in fp32, zdelta[bh][unit][j] (32 FB features).  Unfolded (or d_h not a
+// multiple of 32): z is the column of ones beside V in the products; folded:
+// the rounded features summed on the vector ALUs (the products are fewer, the
+// registers tighter).
 // Workgroup: 4 waves; a tile is 128 tokens; wave w projects token block w and
 // publishes its rank-index fragments and shifts in LDS; then every wave maps
 // its own FBW x 32 features over the whole tile.
 // ---------------------------------------------------------------------------
 template <typename T, int DH, int R16, int FBW, bool PAD>
 __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
-                                                           const T* __restrict__ ofrag, T* __restrict__ sdelta) {
+                                                           const T* __restrict__ ofrag, T* __restrict__ sdelta,
+                                                           float* __restrict__ zdelta) {
   typedef typename FragOf<T>::type F;
   constexpr int KD = DH / 16;
   constexpr int NM = kParts<T>;
@@ -707,6 +731,8 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
   constexpr bool FOLD = fold_exponent(sizeof(T), DH, R16);
   constexpr int UK = FOLD ? KD : R16;              // K-steps of the exponent
   constexpr int UP = FOLD ? 1 : NM;                // parts of its token operand
+  constexpr bool ZMMA = !FOLD || DH % 32 != 0;     // z from a column of ones in the products
+  constexpr int DBK = ZMMA ? vblocks_ones<DH>() : DB;   // accumulator column blocks
   constexpr int MFR = ((R16 + 1) / 2) * KD * NM;   // fragments of M' (one head)
   constexpr bool M_LDS = MFR * 64 * 8 * sizeof(T) <= 32 * 1024;   // M' staged in LDS
   constexpr int VPT = vloads_per_thread<DH, TT>();
@@ -737,11 +763,14 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
   const int t_end = min(a.L, t_begin + pl.span1);
   const int fb0 = (fslice * kWaves + w) * FBW;     // first 32-feature block of this wave
 
-  f32x16 acc[FBW][DB];
+  f32x16 acc[FBW][DBK];
 #pragma unroll
   for (int f = 0; f < FBW; ++f)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[f][db] = zero16();
+    for (int db = 0; db < DBK; ++db) acc[f][db] = zero16();
+  float zacc[FBW];   // (!ZMMA) this lane's part of z for feature 32 fb + c
+#pragma unroll
+  for (int f = 0; f < FBW; ++f) zacc[f] = 0.f;
   // omega' (W') fragments of this wave's features stay in registers when they are few
   constexpr bool kHoist = FBW * UK * NM <= (FOLD ? 32 : 8);
   F ohr[kHoist ? FBW : 1][UK], olr[kHoist ? FBW : 1][UK];
@@ -815,15 +844,15 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
         ini[4 * jj + 3] = x.w;
       }
       auto uload = [&](int k, int part) -> F { return ld8(&s_u[buf][tb][part ? UP - 1 : 0][k][lane * 8]); };
-      // [V, 1] fragments of the block: held across the feature blocks when
-      // few, else read from LDS at each use
-      constexpr bool VHOLD = DB <= 4;
-      F vf[VHOLD ? DB : 1][2];
+      // V (and ones) fragments of the block: held across the feature blocks
+      // when few, else read from LDS at each use
+      constexpr bool VHOLD = DBK <= 4;
+      F vf[VHOLD ? DBK : 1][2];
       if constexpr (VHOLD) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DBK; ++db)
 #pragma unroll
-          for (int k = 0; k < 2; ++k) vf[db][k] = v_frag<T, DH, VST>(s_vt[buf], db, 32 * tb, k, c, g);
+          for (int k = 0; k < 2; ++k) vf[db][k] = v_frag<T, DH, VST, ZMMA>(s_vt[buf], db, 32 * tb, k, c, g);
       }
 #pragma unroll
       for (int f = 0; f < FBW; ++f) {
@@ -842,10 +871,11 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
 #pragma unroll
         for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
         const F p0 = acc_frag<F>(e, 0), p1 = acc_frag<F>(e, 1);
+        if constexpr (!ZMMA) zacc[f] = frag_sum(p1, frag_sum(p0, zacc[f]));
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const F v0 = VHOLD ? vf[VHOLD ? db : 0][0] : v_frag<T, DH, VST>(s_vt[buf], db, 32 * tb, 0, c, g);
-          const F v1 = VHOLD ? vf[VHOLD ? db : 0][1] : v_frag<T, DH, VST>(s_vt[buf], db, 32 * tb, 1, c, g);
+        for (int db = 0; db < DBK; ++db) {
+          const F v0 = VHOLD ? vf[VHOLD ? db : 0][0] : v_frag<T, DH, VST, ZMMA>(s_vt[buf], db, 32 * tb, 0, c, g);
+          const F v1 = VHOLD ? vf[VHOLD ? db : 0][1] : v_frag<T, DH, VST, ZMMA>(s_vt[buf], db, 32 * tb, 1, c, g);
           acc[f][db] = mma(p0, v0, acc[f][db]);
           acc[f][db] = mma(p1, v1, acc[f][db]);
         }
@@ -893,6 +923,7 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
   // ---- write this wave's part of the unit state ----
   const long FK = 2L * pl.FB;     // 16-feature fragments per d-block
   T* sd = sdelta + ((long)bh * pl.NU + unit) * DB * FK * 64 * 8;
+  float* zd = zdelta + ((long)bh * pl.NU + unit) * pl.FB * 32;
 #pragma unroll
   for (int f = 0; f < FBW; ++f) {
     const int fb = fb0 + f;
@@ -901,6 +932,15 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int k = 0; k < 2; ++k) st8(sd + ((db * FK + 2 * fb + k) * 64 + lane) * 8, acc_frag<F>(acc[f][db], k));
+    if constexpr (ZMMA) {   // column d_h: lane d_h % 32 of each half holds rows crow(i, g)
+      if (c == DH % 32) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) zd[fb * 32 + crow(i, g)] = acc[f][DBK - 1][i];
+      }
+    } else {
+      const float z = zacc[f] + __shfl_xor(zacc[f], 32);   // the two token halves
+      if (g == 0) zd[fb * 32 + c] = z;
+    }
   }
 }
 
@@ -913,11 +953,12 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
 template <typename T, int DH, int R16, int FBW, bool PAD>
 __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
                                                                const T* __restrict__ ofrag,
-                                                               T* __restrict__ sdelta) {
+                                                               T* __restrict__ sdelta, float* __restrict__ zdelta) {
   typedef typename FragOf<T>::type F;
   constexpr int KD = DH / 16;
   constexpr int NM = kParts<T>;
   constexpr int DB = vblocks<DH>();
+  constexpr int DBK = vblocks_ones<DH>();   // V and the column of ones (z)
   constexpr int R32 = (R16 + 1) / 2;
   constexpr int VST = 32 + 4;
 
@@ -941,11 +982,11 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
   const int t_end = min(a.L, t_begin + pl.span1);
   const int fb0 = (fslice * kWaves + w) * FBW;
 
-  f32x16 acc[FBW][DB];
+  f32x16 acc[FBW][DBK];
 #pragma unroll
   for (int f = 0; f < FBW; ++f)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[f][db] = zero16();
+    for (int db = 0; db < DBK; ++db) acc[f][db] = zero16();
 
   for (int t0 = t_begin; t0 < t_end; t0 += 32) {
     {  // projection slices rb = w, w + 4, ... of this block
@@ -1011,9 +1052,9 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
       for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
       const F p0 = acc_frag<F>(e, 0), p1 = acc_frag<F>(e, 1);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        acc[f][db] = mma(p0, v_frag<T, DH, VST>(s_vt, db, 0, 0, c, g), acc[f][db]);
-        acc[f][db] = mma(p1, v_frag<T, DH, VST>(s_vt, db, 0, 1, c, g), acc[f][db]);
+      for (int db = 0; db < DBK; ++db) {
+        acc[f][db] = mma(p0, v_frag<T, DH, VST, true>(s_vt, db, 0, 0, c, g), acc[f][db]);
+        acc[f][db] = mma(p1, v_frag<T, DH, VST, true>(s_vt, db, 0, 1, c, g), acc[f][db]);
       }
     }
     __syncthreads();
@@ -1021,6 +1062,7 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
 
   const long FK = 2L * pl.FB;
   T* sd = sdelta + ((long)bh * pl.NU + unit) * DB * FK * 64 * 8;
+  float* zd = zdelta + ((long)bh * pl.NU + unit) * pl.FB * 32;
 #pragma unroll
   for (int f = 0; f < FBW; ++f) {
     const int fb = fb0 + f;
@@ -1029,6 +1071,10 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int k = 0; k < 2; ++k) st8(sd + ((db * FK + 2 * fb + k) * 64 + lane) * 8, acc_frag<F>(acc[f][db], k));
+    if (c == DH % 32) {   // column d_h: lane d_h % 32 of each half holds rows crow(i, g)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) zd[fb * 32 + crow(i, g)] = acc[f][DBK - 1][i];
+    }
   }
 }
 
@@ -1036,25 +1082,51 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
 // State combination.  Non-causal: the sum over the L-splits.  Causal: the
 // exclusive prefix over chunks (the state before each chunk) and, if asked, the
 // state after the last token as S[b][h][j][d], z[b][h][j] (fp32).  Sums run in
-// fp32; the per-unit states the query side reads are written in the operand
-// order of the key side's output.  One thread per fragment lane (8 elements).
+// fp32; the per-unit S the query side reads is written in the operand order of
+// the key side's output, z stays fp32.  One thread per fragment lane of S (8
+// elements) or per feature of z.
 // ---------------------------------------------------------------------------
 template <typename T, int DH>
-__global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T* __restrict__ sfrag) {
+__global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T* __restrict__ sfrag,
+                            const float* __restrict__ zdelta, float* __restrict__ zsum) {
   typedef typename FragOf<T>::type F;
   constexpr int DB = vblocks<DH>();
   const long FK = 2L * pl.FB;
   const long per_unit = DB * FK * 64;          // fragment lanes per unit
   const long nS = (long)pl.BH * per_unit;
+  const long z_unit = 32L * pl.FB;             // z values per unit
+  const long nZ = (long)pl.BH * z_unit;
   const int nout = a.causal ? pl.NU : 1;
-  for (long idx = blockIdx.x * (long)blockDim.x + threadIdx.x; idx < nS; idx += (long)gridDim.x * blockDim.x) {
+  constexpr int UB = 16;                       // units whose loads are in flight together
+  for (long idx = blockIdx.x * (long)blockDim.x + threadIdx.x; idx < nS + nZ; idx += (long)gridDim.x * blockDim.x) {
+    if (idx >= nS) {   // z: one feature per thread
+      const long zi = idx - nS;
+      const long bh = zi / z_unit, j = zi % z_unit;
+      const float* src = zdelta + bh * pl.NU * z_unit + j;
+      float* dst = zsum + bh * nout * z_unit + j;
+      float run = 0.f;
+      for (int u = 0; u < pl.NU; u += UB) {
+        const int nb = min(UB, pl.NU - u);
+        float x[UB];
+#pragma unroll
+        for (int q = 0; q < UB; ++q) x[q] = src[(long)(u + min(q, nb - 1)) * z_unit];
+#pragma unroll
+        for (int q = 0; q < UB; ++q) {
+          if (q >= nb) break;
+          if (a.causal) dst[(long)(u + q) * z_unit] = run;
+          run += x[q];
+        }
+      }
+      if (!a.causal) dst[0] = run;
+      else if (a.z_out && j < a.m) a.z_out[bh * a.m + j] = run;
+      continue;
+    }
     const long bh = idx / per_unit;
     const long rem = idx % per_unit;
     const T* src = sdelta + (bh * pl.NU * per_unit + rem) * 8;
     T* dst = sfrag + (bh * nout * per_unit + rem) * 8;
     float run[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int u = 0;
-    constexpr int UB = 16;                 // units whose loads are in flight together
     for (; u + UB <= pl.NU; u += UB) {
       F x[UB];
 #pragma unroll
@@ -1105,13 +1177,11 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
       const int fk = (int)(frag % FK), db = (int)(frag / FK);
       const int c = lane & 31, g = lane >> 5;
       const int d = db * 32 + c;
-      if (d <= DH) {
+      if (d < DH) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = 16 * fk + 8 * (e >> 2) + 4 * g + (e & 3);
-          if (j >= a.m) continue;
-          if (d < DH) a.S_out[(bh * a.m + j) * DH + d] = run[e];
-          else a.z_out[bh * a.m + j] = run[e];
+          if (j < a.m) a.S_out[(bh * a.m + j) * DH + d] = run[e];
         }
       }
     }
@@ -1120,42 +1190,34 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
 
 // ---------------------------------------------------------------------------
 // Query side.  Per (b, h) and tile of 128 NQB queries (a chunk when causal):
-//   [N, D] = Phi(Q) [S, z] (+ tril(Phi(Q) Phi(K_chunk)^T) [V, 1] when causal),
-//   out = N / D (0 if D == 0).
+//   N = Phi(Q) S (+ tril(Phi(Q) Phi(K_chunk)^T) V when causal) on the matrix
+//   cores, D = Phi(Q) z (fp32 features and z; + the row sums of the masked
+//   scores as rounded for the products) on the vector ALUs, out = N / D
+//   (0 if D == 0).
 // Wave w owns query blocks w NQB .. w NQB + NQB - 1 of the tile; when causal,
 // the keys at the same positions are mapped by the same wave and shared with
 // the other waves through LDS, one 32-feature step at a time.
 // ---------------------------------------------------------------------------
-// Whether the causal query side (one query block per wave) can run as two
-// wave groups: both groups' double-buffered operand steps and key-feature
-// buffers fit in LDS beside the V^T tile, and the operand buffers can hold the
-// partial [N, D] of four waves for the final sum.
-template <typename T, int DH, int R16> constexpr bool qout_split_fits() {
+// Operand slots of one 32-feature step: omega' (W') hi/lo fragments, the state
+// fragments, and one slot whose first 128 bytes hold the step's 32 z values.
+template <typename T, int DH, int R16> constexpr int qout_nstep() {
   constexpr int UK = fold_exponent(sizeof(T), DH, R16) ? DH / 16 : R16;
-  constexpr size_t nstep = (size_t)UK * kParts<T> + 2 * vblocks<DH>();
-  constexpr size_t vt = (size_t)DH * (128 + 4) * sizeof(T);
-  constexpr size_t op = 2 * 2 * nstep * 64 * 8 * sizeof(T);     // two groups, two buffers
-  constexpr size_t kf = 2 * 2 * 4 * 2 * 64 * 8 * sizeof(T);     // two groups, two buffers
-  constexpr size_t red = (size_t)kWaves * vblocks<DH>() * 16 * 64 * 4;
-  return vt + op + kf <= 160 * 1024 && op >= red;
+  return UK * kParts<T> + 2 * vblocks<DH>() + 1;
 }
-
 // Whether the causal query side can stage the operands of all ALLFB feature
 // steps in LDS at once (bf16): V^T tile, all steps, double key-feature buffers.
 constexpr int kAllFB = 8;
 template <typename T, int DH, int R16, int ALLFB> constexpr bool qout_all_fits() {
-  constexpr int UK = fold_exponent(sizeof(T), DH, R16) ? DH / 16 : R16;
-  constexpr size_t nstep = (size_t)UK * kParts<T> + 2 * vblocks<DH>();
   constexpr size_t vt = (size_t)DH * (128 + 4) * sizeof(T);
-  constexpr size_t op = (size_t)ALLFB * nstep * 64 * 8 * sizeof(T);
+  constexpr size_t op = (size_t)ALLFB * qout_nstep<T, DH, R16>() * 64 * 8 * sizeof(T);
   constexpr size_t kf = 2 * 4 * 2 * 64 * 8 * sizeof(T);
   return sizeof(T) == 2 && vt + op + kf <= 160 * 1024;
 }
 
-template <typename T, int DH, int R16, int NQB, bool CAUSAL, bool PAD, int SPLIT = 1, int ALLFB = 0>
-__global__ __launch_bounds__(kThreads * SPLIT) void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
-                                                                 const T* __restrict__ ofrag,
-                                                                 const T* __restrict__ sfrag) {
+template <typename T, int DH, int R16, int NQB, bool CAUSAL, bool PAD, int ALLFB = 0>
+__global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
+                                                        const T* __restrict__ ofrag, const T* __restrict__ sfrag,
+                                                        const float* __restrict__ zsum) {
   typedef typename FragOf<T>::type F;
   constexpr int KD = DH / 16;
   constexpr int NM = kParts<T>;
@@ -1165,31 +1227,29 @@ __global__ __launch_bounds__(kThreads * SPLIT) void qout_kernel(FwdArgs a, Plan 
   constexpr int VST = TT + 4;
   constexpr bool FOLD = fold_exponent(sizeof(T), DH, R16);
   constexpr int UK = FOLD ? KD : R16;      // K-steps of the exponent
-  constexpr int UP = FOLD ? 1 : NM;        // parts of its token operand
   constexpr int NOF = UK * NM;             // omega' (W') fragments per feature step
-  constexpr int NSTEP = NOF + 2 * DB;      // plus state fragments
+  constexpr int NSTEP = qout_nstep<T, DH, R16>();
+  constexpr int ZS = NSTEP - 1;            // the z slot
+  constexpr int ZW = 8 * (int)sizeof(T) / 4;   // z values per lane of a slot copy
+  static_assert(NSTEP == NOF + 2 * DB + 1, "step layout");
   constexpr int PERW = (NSTEP + kWaves - 1) / kWaves;
   constexpr int VT_ELEMS = CAUSAL ? DH * VST : 8;
   constexpr size_t kBase = (size_t)VT_ELEMS * sizeof(T);
-  constexpr size_t kOpStep = (size_t)SPLIT * NSTEP * 64 * 8 * sizeof(T);
-  constexpr size_t kKfStep = CAUSAL ? (size_t)SPLIT * NB * 2 * 64 * 8 * sizeof(T) : 0;
+  constexpr size_t kOpStep = (size_t)NSTEP * 64 * 8 * sizeof(T);
+  constexpr size_t kKfStep = CAUSAL ? (size_t)NB * 2 * 64 * 8 * sizeof(T) : 0;
   // Operands staged in LDS when one step buffer fits beside the V^T tile (else
   // each wave reads them from L2 itself); double buffers (one barrier per
   // feature step) unless LDS is short.
   constexpr bool STAGE = kBase + kOpStep + kKfStep <= 160 * 1024;
   constexpr int OPB = !STAGE ? 0 : kBase + 2 * kOpStep + 2 * kKfStep <= 160 * 1024 ? 2 : 1;
   constexpr int KBUF = kBase + OPB * kOpStep + 2 * kKfStep <= 160 * 1024 ? 2 : 1;
-  constexpr int KF_ELEMS = CAUSAL ? SPLIT * KBUF * NB * 2 * 64 * 8 : 8;
+  constexpr int KF_ELEMS = CAUSAL ? KBUF * NB * 2 * 64 * 8 : 8;
   // ALLFB > 0 (bf16, at most ALLFB feature blocks): the operands of every step
   // are copied global -> LDS by the DMA path at the start, overlapping the
   // projections, and the step loop has no staging and no extra barriers.
   constexpr bool ALL = ALLFB > 0;
-  static_assert(!ALL || (sizeof(T) == 2 && SPLIT == 1), "all-step staging: bf16, one wave group");
-  constexpr int OP_ELEMS = ALL ? ALLFB * NSTEP * 64 * 8 : STAGE ? SPLIT * OPB * NSTEP * 64 * 8 : 8;
-  // SPLIT = 2: two groups of four waves share the query tile and take every
-  // other feature step; their partial [N, D] are added through LDS at the end.
-  static_assert(SPLIT == 1 || (STAGE && (size_t)OPB * kOpStep >= (size_t)kWaves * NQB * DB * 16 * 64 * 4),
-                "the split form reduces through the operand buffers");
+  static_assert(!ALL || sizeof(T) == 2, "all-step staging: bf16");
+  constexpr int OP_ELEMS = ALL ? ALLFB * NSTEP * 64 * 8 : STAGE ? OPB * NSTEP * 64 * 8 : 8;
 
   __shared__ __attribute__((aligned(16))) T s_vt[VT_ELEMS];
   __shared__ __attribute__((aligned(16))) T s_kf[KF_ELEMS];
@@ -1197,10 +1257,7 @@ __global__ __launch_bounds__(kThreads * SPLIT) void qout_kernel(FwdArgs a, Plan 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, c = lane & 31, g = lane >> 5;
-  const int w = (tid >> 6) % kWaves;   // query-block wave of this group
-  const int hf = (tid >> 6) / kWaves;  // feature group (SPLIT = 2)
-  T* s_opg = s_op + (STAGE ? hf * OPB * NSTEP * 64 * 8 : 0);
-  T* s_kfg = s_kf + (CAUSAL ? hf * KBUF * NB * 2 * 64 * 8 : 0);
+  const int w = tid >> 6;
   const int tile = blockIdx.x % pl.NT2;
   const int bh = blockIdx.x / pl.NT2;
   const int b = bh / a.H, h = bh % a.H;
@@ -1217,11 +1274,14 @@ __global__ __launch_bounds__(kThreads * SPLIT) void qout_kernel(FwdArgs a, Plan 
   const long FK = 2L * pl.FB;
   const long unit_s = (long)bh * (CAUSAL ? pl.NU : 1) + (CAUSAL ? tile : 0);
   const T* sf = sfrag + unit_s * DB * FK * 64 * 8;
+  const float* zs = zsum + unit_s * pl.FB * 32;
 
-  // Operands of one 32-feature step (omega' (W') hi/lo fragments, then the
-  // state fragments) are the same for the four waves of a group.
+  // Operands of one 32-feature step are the same for the four waves.  The z
+  // slot: lanes 0 .. 32 / ZW - 1 copy the 32 values (the others repeat the last
+  // part, inside the slot).
   auto gsrc = [&](int fb, int f) -> const T* {
     if (f < NOF) return of + (((long)(fb * UK + f / NM) * NM + f % NM) * 64 + lane) * 8;
+    if (f == ZS) return reinterpret_cast<const T*>(zs + fb * 32 + min(lane, 32 / ZW - 1) * ZW);
     f -= NOF;
     return sf + (((f >> 1) * FK + 2 * fb + (f & 1)) * 64 + lane) * 8;
   };
@@ -1260,11 +1320,9 @@ __global__ __launch_bounds__(kThreads * SPLIT) void qout_kernel(FwdArgs a, Plan 
   }
   constexpr int VPT = vloads_per_thread<DH, TT>();
   F vr[CAUSAL ? VPT : 1];
-  if constexpr (CAUSAL)
-    if (hf == 0) load_v<T, DH, TT>(vr, vbase, a.vs[2], t0, a.L, tid);
+  if constexpr (CAUSAL) load_v<T, DH, TT>(vr, vbase, a.vs[2], t0, a.L, tid);
   if constexpr (ALL) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed
-  if constexpr (CAUSAL)
-    if (hf == 0) store_vt<T, DH, TT, VST>(s_vt, vr, tid);
+  if constexpr (CAUSAL) store_vt<T, DH, TT, VST>(s_vt, vr, tid);
   if constexpr (M_LDS) __syncthreads();   // M' (and every wave's copies) visible
   const T* msrc = M_LDS ? s_kf : mf;
 #pragma unroll
@@ -1296,10 +1354,13 @@ __global__ __launch_bounds__(kThreads * SPLIT) void qout_kernel(FwdArgs a, Plan 
   }
 
   f32x16 acc[NQB][DB];
+  float den[NQB];   // this lane's part of D for query c of block j
 #pragma unroll
-  for (int j = 0; j < NQB; ++j)
+  for (int j = 0; j < NQB; ++j) {
+    den[j] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[j][db] = zero16();
+  }
   f32x16 at[CAUSAL ? NQB : 1][CAUSAL ? NB : 1];   // A^T[key block][query block of the wave]
   if constexpr (CAUSAL) {
 #pragma unroll
@@ -1325,14 +1386,22 @@ __global__ __launch_bounds__(kThreads * SPLIT) void qout_kernel(FwdArgs a, Plan 
 #pragma unroll
       for (int q = 0; q < PERW; ++q) {
         const int f = w + kWaves * q;
-        if (f < NSTEP) st8(s_opg + ((buf * NSTEP + f) * 64 + lane) * 8, pre[q]);
+        if (f < NSTEP) st8(s_op + ((buf * NSTEP + f) * 64 + lane) * 8, pre[q]);
       }
     }
   };
   auto op = [&](int fb, int buf, int f) {
     if constexpr (ALL) return ld8(s_op + ((fb * NSTEP + f) * 64 + lane) * 8);
-    else if constexpr (STAGE) return ld8(s_opg + ((buf * NSTEP + f) * 64 + lane) * 8);
+    else if constexpr (STAGE) return ld8(s_op + ((buf * NSTEP + f) * 64 + lane) * 8);
     else return ld8(gsrc(fb, f));
+  };
+  // z of features 32 fb + 8 jj + 4 g .. + 3 (the rows this lane holds)
+  auto zrow4 = [&](int fb, int buf, int jj) -> float4 {
+    const float* zb;
+    if constexpr (ALL) zb = reinterpret_cast<const float*>(s_op + (fb * NSTEP + ZS) * 64 * 8);
+    else if constexpr (STAGE) zb = reinterpret_cast<const float*>(s_op + (buf * NSTEP + ZS) * 64 * 8);
+    else zb = zs + fb * 32;
+    return *reinterpret_cast<const float4*>(zb + 8 * jj + 4 * g);
   };
 
   // one 32-feature step; the operands of the next step are fetched before it runs
@@ -1366,6 +1435,11 @@ __global__ __launch_bounds__(kThreads * SPLIT) void qout_kernel(FwdArgs a, Plan 
         e = exponent<T, UK, false, true>(uqh[j], uql[j], ohi, olo, e);
 #pragma unroll
       for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {   // D += phi(q) . z
+        const float4 z = zrow4(fb, buf, jj);
+        den[j] += e[4 * jj] * z.x + e[4 * jj + 1] * z.y + e[4 * jj + 2] * z.z + e[4 * jj + 3] * z.w;
+      }
       pq[j][0] = acc_frag<F>(e, 0);
       pq[j][1] = acc_frag<F>(e, 1);
     }
@@ -1383,7 +1457,7 @@ __global__ __launch_bounds__(kThreads * SPLIT) void qout_kernel(FwdArgs a, Plan 
         if (db % 3 == 2) __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (CAUSAL) {
-      T* kbuf = s_kfg + (KBUF == 2 ? ((fb / SPLIT) & 1) : 0) * NB * 2 * 64 * 8;
+      T* kbuf = s_kf + (KBUF == 2 ? (fb & 1) : 0) * NB * 2 * 64 * 8;
 #pragma unroll
       for (int j = 0; j < NQB; ++j) {
         f32x16 e = splat16(initk[j]);
@@ -1418,41 +1492,28 @@ __global__ __launch_bounds__(kThreads * SPLIT) void qout_kernel(FwdArgs a, Plan 
   // Many operands per step (d_h = 256): no register prefetch across the step,
   // the registers go to the accumulators; the copy runs between steps.
   constexpr bool EARLY = PERW <= 8;
-  // Step i of group hf is feature block SPLIT i + hf; a group whose block is
-  // past the last one idles through the step (the barriers are shared).
-  const int nsteps = (pl.FB + SPLIT - 1) / SPLIT;
   if constexpr (ALL) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed
     __syncthreads();                      // and everyone else's
     for (int fb = 0; fb < pl.FB; ++fb) step(fb, 0);
   } else {
-  if (hf < pl.FB) {
-    load_step(hf);
+    load_step(0);
     store_step(0);
-  }
-  __syncthreads();
-  for (int i = 0; i < nsteps; ++i) {
-    const int fb = i * SPLIT + hf, fbn = fb + SPLIT;
-    const int buf = OPB == 2 ? (i & 1) : 0;
-    if constexpr (EARLY)
-      if (fbn < pl.FB) load_step(fbn);
-    if (SPLIT == 1 || fb < pl.FB) {
+    __syncthreads();
+    for (int fb = 0; fb < pl.FB; ++fb) {
+      const int buf = OPB == 2 ? (fb & 1) : 0;
+      if constexpr (EARLY)
+        if (fb + 1 < pl.FB) load_step(fb + 1);
       step(fb, buf);
-    } else if constexpr (CAUSAL) {
-      __syncthreads();   // the barrier inside a step
-      if constexpr (KBUF == 1) __syncthreads();
-    }
-    if constexpr (STAGE) {
-      if (i + 1 < nsteps) {
-        if constexpr (OPB == 1) __syncthreads();   // one buffer: everyone is done reading it
-        if constexpr (!EARLY)
-          if (fbn < pl.FB) load_step(fbn);
-        if (fbn < pl.FB) store_step(OPB == 2 ? ((i + 1) & 1) : 0);
+      if constexpr (STAGE) {
+        if (fb + 1 < pl.FB) {
+          if constexpr (OPB == 1) __syncthreads();   // one buffer: everyone is done reading it
+          if constexpr (!EARLY) load_step(fb + 1);
+          store_step(OPB == 2 ? ((fb + 1) & 1) : 0);
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
-  }
-
   }
 
   if constexpr (CAUSAL) {
@@ -1471,6 +1532,7 @@ __global__ __launch_bounds__(kThreads * SPLIT) void qout_kernel(FwdArgs a, Plan 
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const F pf = acc_frag<F>(at[j][kb2], k);
+          den[j] = frag_sum(pf, den[j]);   // the rounded scores the products use
 #pragma unroll
           for (int db = 0; db < DB; ++db)
             acc[j][db] = mma(pf, v_frag<T, DH, VST>(s_vt, db, 32 * kb2, k, c, g), acc[j][db]);
@@ -1479,34 +1541,14 @@ __global__ __launch_bounds__(kThreads * SPLIT) void qout_kernel(FwdArgs a, Plan 
     }
   }
 
-  if constexpr (SPLIT == 2) {   // group 1 hands its partial [N, D] to group 0 through LDS
-    float* red = reinterpret_cast<float*>(s_op);
-    if (hf == 1) {
-#pragma unroll
-      for (int j = 0; j < NQB; ++j)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) red[(((w * NQB + j) * DB + db) * 16 + i) * 64 + lane] = acc[j][db][i];
-    }
-    __syncthreads();
-    if (hf == 1) return;
-#pragma unroll
-    for (int j = 0; j < NQB; ++j)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[j][db][i] += red[(((w * NQB + j) * DB + db) * 16 + i) * 64 + lane];
-  }
-
-  // ---- out = N / D; D is column d_h of [N, D], held by lane d_h % 32 of each half ----
-  constexpr int DBLK = DH / 32, DCOL = DH % 32;
+  // ---- out = N / D; lanes c and c + 32 hold the two halves of D for query c ----
 #pragma unroll
   for (int j = 0; j < NQB; ++j) {
     const int blk = w * NQB + j;
+    const float dq = den[j] + __shfl_xor(den[j], 32);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float dd = __shfl(acc[j][DBLK][i], (lane & 32) | DCOL);
+      const float dd = __shfl(dq, crow(i, g));
       const int t = t0 + 32 * blk + crow(i, g);
       const float inv = dd > 0.f ? __builtin_amdgcn_rcpf(dd) : 0.f;
       if (t < a.L) {
@@ -1551,6 +1593,8 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
   T* ofrag = reinterpret_cast<T*>(base + pl.off_ofrag);
   T* sdelta = reinterpret_cast<T*>(base + pl.off_sdelta);
   T* sfrag = reinterpret_cast<T*>(base + pl.off_sfrag);
+  float* zdelta = reinterpret_cast<float*>(base + pl.off_zdelta);
+  float* zsum = reinterpret_cast<float*>(base + pl.off_zsum);
   constexpr int NM = kParts<T>;
   {
     // Folded with d_h >= 32: W' by matrix products and M' in one launch;
@@ -1585,16 +1629,16 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
                   "the folded key side runs on the tiled kernel");
     if constexpr (kstate_tile_lds_bytes<T, DH, R16>() <= kMaxLds)
       hipLaunchKernelGGL((kstate_kernel<T, DH, R16, FBW, PAD>), grid1, dim3(kThreads), 0, st, a, pl, mfrag, ofrag,
-                         sdelta);
+                         sdelta, zdelta);
     else
       hipLaunchKernelGGL((kstate_seq_kernel<T, DH, R16, FBW, PAD>), grid1, dim3(kThreads), 0, st, a, pl, mfrag,
-                         ofrag, sdelta);
+                         ofrag, sdelta, zdelta);
   }
   {
-    const long n = (long)pl.BH * vblocks<DH>() * 2 * pl.FB * 64;
+    const long n = (long)pl.BH * vblocks<DH>() * 2 * pl.FB * 64 + (long)pl.BH * pl.FB * 32;   // S lanes, z values
     const int blocks = (int)((n + 255) / 256);
     KernelTimer tm(kScan, stream);
-    hipLaunchKernelGGL((scan_kernel<T, DH>), dim3(blocks), dim3(256), 0, st, a, pl, sdelta, sfrag);
+    hipLaunchKernelGGL((scan_kernel<T, DH>), dim3(blocks), dim3(256), 0, st, a, pl, sdelta, sfrag, zdelta, zsum);
   }
   const dim3 grid(pl.BH * pl.NT2);
   KernelTimer tm(kQOut, stream);
@@ -1603,30 +1647,23 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
       if (pl.NQB != 1) return DARK_ERR_UNSUPPORTED;
       if constexpr (qout_all_fits<T, DH, R16, kAllFB>()) {   // few feature blocks: all steps staged at once
         if (pl.FB <= kAllFB) {
-          hipLaunchKernelGGL((qout_kernel<T, DH, R16, 1, true, PAD, 1, kAllFB>), grid, dim3(kThreads), 0, st, a, pl,
-                             mfrag, ofrag, sfrag);
-          return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
-        }
-      }
-      if constexpr (DH <= 64 && qout_split_fits<T, DH, R16>()) {   // few tiles: two wave groups per tile
-        if (pl.split == 2) {
-          hipLaunchKernelGGL((qout_kernel<T, DH, R16, 1, true, PAD, 2>), grid, dim3(2 * kThreads), 0, st, a, pl,
-                             mfrag, ofrag, sfrag);
+          hipLaunchKernelGGL((qout_kernel<T, DH, R16, 1, true, PAD, kAllFB>), grid, dim3(kThreads), 0, st, a, pl,
+                             mfrag, ofrag, sfrag, zsum);
           return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
         }
       }
       hipLaunchKernelGGL((qout_kernel<T, DH, R16, 1, true, PAD>), grid, dim3(kThreads), 0, st, a, pl, mfrag, ofrag,
-                         sfrag);
+                         sfrag, zsum);
     } else {
       return DARK_ERR_UNSUPPORTED;
     }
   } else {
     switch (pl.NQB) {
-      case 1: hipLaunchKernelGGL((qout_kernel<T, DH, R16, 1, false, PAD>), grid, dim3(kThreads), 0, st, a, pl, mfrag, ofrag, sfrag); break;
+      case 1: hipLaunchKernelGGL((qout_kernel<T, DH, R16, 1, false, PAD>), grid, dim3(kThreads), 0, st, a, pl, mfrag, ofrag, sfrag, zsum); break;
       case 2:
         if constexpr (DH <= 128) {   // the planner takes two query blocks per wave only for d_h <= 64
           hipLaunchKernelGGL((qout_kernel<T, DH, R16, 2, false, PAD>), grid, dim3(kThreads), 0, st, a, pl, mfrag,
-                             ofrag, sfrag);
+                             ofrag, sfrag, zsum);
           break;
         } else {
           return DARK_ERR_UNSUPPORTED;
