@@ -248,6 +248,14 @@ def test_c5_decode_sampled():
     assert err_o <= TOL["bf16"] and err_s <= TOL["bf16"] and err_z <= TOL["bf16"]
 
 
+# ---- many causal chunks ---------------------------------------------------------
+def test_causal_many_chunks():
+    """33 chunks of 128 keys with a masked tail: the chunk-state prefix over many units."""
+    w = Workload(name="chunks33", B=1, H=2, H_kv=1, L=4200, d_h=64, m=128, r=64, dtype="bf16", causal=True,
+                 seed=99, m_kind="eye_noise", m_noise=0.3, mask_kind="tail", max_pad=300)
+    _check(w)
+
+
 # ---- invariants on the device --------------------------------------------------
 def test_deterministic_and_row0():
     import torch
