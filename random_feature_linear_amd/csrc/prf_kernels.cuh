@@ -141,19 +141,6 @@ __device__ __forceinline__ void st8(float* p, const f32x8& f) {
   *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
 }
-// elements p0[0..3] and p1[0..3] as one fragment
-__device__ __forceinline__ bf16x8 ld4x2(const bf16* p0, const bf16* p1) {
-  uint2 a = *reinterpret_cast<const uint2*>(p0);
-  uint2 b = *reinterpret_cast<const uint2*>(p1);
-  uint4 u = make_uint4(a.x, a.y, b.x, b.y);
-  return __builtin_bit_cast(bf16x8, u);
-}
-__device__ __forceinline__ f32x8 ld4x2(const float* p0, const float* p1) {
-  float4 a = *reinterpret_cast<const float4*>(p0);
-  float4 b = *reinterpret_cast<const float4*>(p1);
-  f32x8 f = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  return f;
-}
 // One 16-byte element per lane from global memory straight into LDS (the
 // global_load_lds path, no registers): lane l writes bytes [16 l, 16 l + 16) of
 // the 1 KB at lds_dst, which must be the same for the whole wave.  Counted by
@@ -644,6 +631,10 @@ __device__ __forceinline__ void load_v(typename FragOf<T>::type* vr, const T* vb
     vr[p] = (e < TT * (DH / 8) && t < t_end) ? x : zero_frag<F>();
   }
 }
+// Position of token t in a row of the V^T tile: bits 2 and 3 swapped, so that
+// the 8 tokens one lane of a V operand fragment holds (16k + 8(e / 4) + 4g + e % 4,
+// the operand order of the feature products) are 8 consecutive elements.
+__device__ __forceinline__ int vt_pos(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
 template <typename T, int DH, int TT, int VST>
 __device__ __forceinline__ void store_vt(T* s_vt, const typename FragOf<T>::type* vr, int tid) {
 #pragma unroll
@@ -652,7 +643,7 @@ __device__ __forceinline__ void store_vt(T* s_vt, const typename FragOf<T>::type
     if (e >= TT * (DH / 8)) break;
     const int tl = e % TT, d8 = (e / TT) * 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s_vt[(d8 + i) * VST + tl] = vr[p][i];
+    for (int i = 0; i < 8; ++i) s_vt[(d8 + i) * VST + vt_pos(tl)] = vr[p][i];
   }
 }
 
@@ -678,8 +669,7 @@ __device__ __forceinline__ typename FragOf<T>::type v_frag(const T* s_vt, int db
     make_frag(f, v);
     return f;
   }
-  const T* base = s_vt + d * VST + tb0 + 16 * k + 4 * g;
-  return ld4x2(base, base + 8);
+  return ld8(s_vt + d * VST + tb0 + 16 * k + 8 * g);   // tokens in vt_pos order
 }
 // 32-column blocks of V (of the state S).  The normaliser z (the sums of the
 // features) is kept apart in fp32: the key side takes it from a column of
@@ -726,7 +716,7 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
   constexpr int NM = kParts<T>;
   constexpr int DB = vblocks<DH>();
   constexpr int TT = kTile;
-  constexpr int VST = TT + 4;   // 4 x odd: 8-byte rows of V^T fall in distinct LDS banks
+  constexpr int VST = TT + 8;   // 16-byte aligned rows, an odd number of 16-byte units apart
 
   constexpr bool FOLD = fold_exponent(sizeof(T), DH, R16);
   constexpr int UK = FOLD ? KD : R16;              // K-steps of the exponent
@@ -960,7 +950,7 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
   constexpr int DB = vblocks<DH>();
   constexpr int DBK = vblocks_ones<DH>();   // V and the column of ones (z)
   constexpr int R32 = (R16 + 1) / 2;
-  constexpr int VST = 32 + 4;
+  constexpr int VST = 32 + 8;
 
   __shared__ __attribute__((aligned(16))) T s_u[NM][R16][64 * 8];
   __shared__ __attribute__((aligned(16))) float s_ss[kWaves][32];
@@ -1208,7 +1198,7 @@ template <typename T, int DH, int R16> constexpr int qout_nstep() {
 // steps in LDS at once (bf16): V^T tile, all steps, double key-feature buffers.
 constexpr int kAllFB = 8;
 template <typename T, int DH, int R16, int ALLFB> constexpr bool qout_all_fits() {
-  constexpr size_t vt = (size_t)DH * (128 + 4) * sizeof(T);
+  constexpr size_t vt = (size_t)DH * (128 + 8) * sizeof(T);
   constexpr size_t op = (size_t)ALLFB * qout_nstep<T, DH, R16>() * 64 * 8 * sizeof(T);
   constexpr size_t kf = 2 * 4 * 2 * 64 * 8 * sizeof(T);
   return sizeof(T) == 2 && vt + op + kf <= 160 * 1024;
@@ -1224,7 +1214,7 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   constexpr int DB = vblocks<DH>();
   constexpr int NB = kWaves * NQB;         // 32-token blocks per tile
   constexpr int TT = 32 * NB;              // tokens per tile
-  constexpr int VST = TT + 4;
+  constexpr int VST = TT + 8;
   constexpr bool FOLD = fold_exponent(sizeof(T), DH, R16);
   constexpr int UK = FOLD ? KD : R16;      // K-steps of the exponent
   constexpr int NOF = UK * NM;             // omega' (W') fragments per feature step
@@ -1573,13 +1563,13 @@ template <typename T, int DH, int R16> constexpr size_t kstate_tile_lds_bytes() 
   constexpr int UK = FOLD ? DH / 16 : R16;
   constexpr int UP = FOLD ? 1 : kParts<T>;
   constexpr size_t mbytes = (size_t)((R16 + 1) / 2) * (DH / 16) * kParts<T> * 64 * 8 * sizeof(T);
-  return (size_t)(kWaves * UP * UK * 64 * 8 + DH * (kTile + 4)) * sizeof(T) + kTile * sizeof(float) +
+  return (size_t)(kWaves * UP * UK * 64 * 8 + DH * (kTile + 8)) * sizeof(T) + kTile * sizeof(float) +
          (mbytes <= 32 * 1024 ? mbytes : 16);
 }
 // Least LDS of the causal query-side kernel: the V^T tile and one key-feature
 // buffer (the operand staging buffers are added only where they fit).
 template <typename T, int DH, int R16, int NQB> constexpr size_t causal_lds_bytes() {
-  return (size_t)(DH * (128 * NQB + 4) + 4 * NQB * 2 * 64 * 8) * sizeof(T);
+  return (size_t)(DH * (128 * NQB + 8) + 4 * NQB * 2 * 64 * 8) * sizeof(T);
 }
 
 template <typename T, int DH, int R16, int FBW, bool PAD>
