@@ -150,6 +150,17 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 #endif
 }
+// Workgroups are dispatched to the 8 XCDs in turn (block b runs on XCD b % 8),
+// and each XCD has its own L2.  The logical index returned here gives each XCD
+// a contiguous range of logical work items, so that items next to each other
+// (the feature slices of one key tile, the tiles of one head) share an L2.
+__device__ __forceinline__ int xcd_block() {
+  constexpr int NX = 8;
+  const int n = gridDim.x, b = blockIdx.x;
+  const int per = n / NX, rem = n % NX;   // XCD x runs per + (x < rem) blocks
+  const int x = b % NX;
+  return x * per + min(x, rem) + b / NX;
+}
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ void store_out(bf16* p, float x) { *p = (bf16)x; }
@@ -552,10 +563,12 @@ __global__ __launch_bounds__(kThreads) void shift_kernel(FwdArgs a, const T* __r
   __shared__ __attribute__((aligned(16))) T s_m[2][SL * 64 * 8];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
   const int ntile = (a.L + kShiftTile - 1) / kShiftTile;
-  const int half = (int)(blockIdx.x / (gridDim.x / 2));   // 0: queries, 1: keys
-  const int blk = blockIdx.x % (gridDim.x / 2);
-  const int tile = blk % ntile;
-  const int bh = blk / ntile;
+  const int lb = xcd_block();
+  const int half = lb / (int)(gridDim.x / 2);   // 0: queries, 1: keys
+  const int blk = lb % (int)(gridDim.x / 2);
+  // keys: the heads that share a K/V head take consecutive blocks (one L2)
+  const int tile = half == 0 ? blk % ntile : (blk / a.H) % ntile;
+  const int bh = half == 0 ? blk / ntile : (blk / (a.H * ntile)) * a.H + blk % a.H;
   const int b = bh / a.H, h = bh % a.H;
   const int hk = (h * a.H_kv) / a.H;
   const T* base = half == 0 ? reinterpret_cast<const T*>(a.q) + b * a.qs[0] + h * a.qs[1]
@@ -737,9 +750,10 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
-  const int fslice = blockIdx.x % pl.NF;
-  const int unit = (blockIdx.x / pl.NF) % pl.NU;
-  const int bh = blockIdx.x / (pl.NF * pl.NU);
+  const int lb = xcd_block();
+  const int fslice = lb % pl.NF;
+  const int unit = (lb / pl.NF) % pl.NU;
+  const int bh = lb / (pl.NF * pl.NU);
   const int b = bh / a.H, h = bh % a.H;
   const int hk = (h * a.H_kv) / a.H;
   const T* kbase = reinterpret_cast<const T*>(a.k) + b * a.ks[0] + hk * a.ks[1];
@@ -958,9 +972,10 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
-  const int fslice = blockIdx.x % pl.NF;
-  const int unit = (blockIdx.x / pl.NF) % pl.NU;
-  const int bh = blockIdx.x / (pl.NF * pl.NU);
+  const int lb = xcd_block();
+  const int fslice = lb % pl.NF;
+  const int unit = (lb / pl.NF) % pl.NU;
+  const int bh = lb / (pl.NF * pl.NU);
   const int b = bh / a.H, h = bh % a.H;
   const int hk = (h * a.H_kv) / a.H;
   const T* kbase = reinterpret_cast<const T*>(a.k) + b * a.ks[0] + hk * a.ks[1];
@@ -1248,8 +1263,9 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   const int tid = threadIdx.x;
   const int lane = tid & 63, c = lane & 31, g = lane >> 5;
   const int w = tid >> 6;
-  const int tile = blockIdx.x % pl.NT2;
-  const int bh = blockIdx.x / pl.NT2;
+  const int lb = xcd_block();
+  const int tile = lb % pl.NT2;
+  const int bh = lb / pl.NT2;
   const int b = bh / a.H, h = bh % a.H;
   const int hk = (h * a.H_kv) / a.H;
   const T* qbase = reinterpret_cast<const T*>(a.q) + b * a.qs[0] + h * a.qs[1];
