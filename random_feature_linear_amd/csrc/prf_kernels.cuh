@@ -32,9 +32,12 @@
 // pair of bf16 values hi + lo (about 16 significant bits): u = M'_hi x + M'_lo x
 // and E = u_hi omega'_hi + u_lo omega'_hi + u_hi omega'_lo.
 //
-// The ones column of [V, 1] rides through the same MFMA as V (column d_h of
-// the combined operand), so numerator and denominator see identical rounded
-// feature values and the vector ALU is left to the exp.
+// The normaliser z = Phi(K)^T 1 is kept apart from the state S in fp32, so S
+// holds only V's column blocks.  The key side forms z as a column of ones
+// beside V in its products (unfolded form, or d_h = 16 where that column is
+// free) or sums the rounded bf16 features on the vector ALUs (folded form); the
+// query side forms D = Phi(Q) z on the vector ALUs, and the causal part adds
+// the row sums of the masked scores as rounded for the products.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <math.h>
