@@ -151,6 +151,9 @@ __device__ __forceinline__ void st8(float* p, const f32x8& f) {
 __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+#else
+  (void)src;
+  (void)lds_dst;
 #endif
 }
 // Workgroups are dispatched to the 8 XCDs in turn (block b runs on XCD b % 8),
