@@ -167,9 +167,10 @@ const char* dark_prf_status_str(dark_status status);
  *     and stop recording.  Returns DARK_ERR_INVALID_ARG for NULL arrays and
  *     DARK_ERR_HIP if an event failed.
  * Kernel kinds: 0 operand preparation of M and omega, 1 key-side feature
- * state, 2 state sum / prefix scan, 3 query-side output, 4 decode step.
+ * state, 2 state sum / prefix scan, 3 query-side output, 4 decode step,
+ * 5 exponent shift pass (the per-token maxima of the folded exponent).
  */
-#define DARK_KERNEL_KINDS 5
+#define DARK_KERNEL_KINDS 6
 dark_status dark_prf_timing_begin(void);
 dark_status dark_prf_timing_end(double* ms, int32_t* launches);
 

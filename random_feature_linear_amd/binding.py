@@ -123,7 +123,7 @@ def dark_prf_decode_step(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, omeg
                                       ctypes.c_uint64(state_tag), out or None, stream or None)
 
 
-KERNEL_KINDS = ("prep", "kstate", "scan", "qout", "decode")
+KERNEL_KINDS = ("prep", "kstate", "scan", "qout", "decode", "shift")
 
 
 def dark_prf_timing_begin() -> None:

@@ -56,7 +56,7 @@ struct Plan {
 
 // Optional per-kernel timing (dark_prf_timing_begin / _end): records a HIP
 // event pair on `stream` around one launch while timing is on.
-enum KernelKind { kPrep = 0, kKState = 1, kScan = 2, kQOut = 3, kDecode = 4 };
+enum KernelKind { kPrep = 0, kKState = 1, kScan = 2, kQOut = 3, kDecode = 4, kShift = 5 };
 struct KernelTimer {
   KernelTimer(int kind, void* stream);
   ~KernelTimer();

@@ -1630,7 +1630,7 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
   }
   if (pl.kshift) {
     const int ntile = (a.L + kShiftTile - 1) / kShiftTile;
-    KernelTimer tm(kPrep, stream);
+    KernelTimer tm(kShift, stream);
     hipLaunchKernelGGL((shift_kernel<T, DH, R16>), dim3(2 * pl.BH * ntile), dim3(kThreads), 0, st, a, mfrag,
                        a.qshift, a.kshift);
   }
