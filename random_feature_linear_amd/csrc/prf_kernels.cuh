@@ -551,19 +551,24 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict_
 // every query row (qshift[bh][t]) and every key row as seen by query head h
 // (kshift[bh][t] = minus that, or -inf for a masked key).  They replace the
 // projections in the key-side kernel (once per feature slice) and in the query
-// side.  Workgroup: 4 waves over 128 rows of q (first half of the grid) or of
-// k (second half); wave w keeps its 32 rows in registers while M' streams
-// through LDS one 32-row slice at a time (double-buffered, the next slice
-// fetched during the products).
+// side.  Workgroup: 4 waves over 256 rows (fp32: 128) of q (first half of the
+// grid) or of k (second half); wave w keeps its two 32-row blocks (fp32: one)
+// in registers while M' streams through LDS one 32-row slice at a time
+// (double-buffered, the next slice fetched during the products), so that every
+// slice fragment read from LDS feeds two products.
 // ---------------------------------------------------------------------------
-constexpr int kShiftTile = kTile;
+// 32-row blocks per wave (fp32: one, for registers) and rows per workgroup
+template <typename T> constexpr int shift_rb() { return sizeof(T) == 2 ? 2 : 1; }
+template <typename T> constexpr int shift_tile() { return shift_rb<T>() * kTile; }
 template <typename T, int DH, int R16>
-__global__ __launch_bounds__(kThreads) void shift_kernel(FwdArgs a, const T* __restrict__ mfrag,
+__global__ __launch_bounds__(kThreads, 2) void shift_kernel(FwdArgs a, const T* __restrict__ mfrag,
                                                           float* __restrict__ qshift, float* __restrict__ kshift) {
   typedef typename FragOf<T>::type F;
   constexpr int KD = DH / 16;
   constexpr int NM = kParts<T>;
   constexpr int R32 = (R16 + 1) / 2;
+  constexpr int RB = shift_rb<T>();
+  constexpr int kShiftTile = shift_tile<T>();
   constexpr int SL = KD * NM;                         // fragments of one 32-row slice of M'
   constexpr int PS = (SL * 64 + kThreads - 1) / kThreads;
   __shared__ __attribute__((aligned(16))) T s_m[2][SL * 64 * 8];
@@ -581,8 +586,7 @@ __global__ __launch_bounds__(kThreads) void shift_kernel(FwdArgs a, const T* __r
                             : reinterpret_cast<const T*>(a.k) + b * a.ks[0] + hk * a.ks[1];
   const int64_t stride = half == 0 ? a.qs[2] : a.ks[2];
   const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * R32 * SL * 64 * 8;
-  const int t = tile * kShiftTile + 32 * w + c;
-  const bool ok = t < a.L;
+  const int t0 = tile * kShiftTile + RB * 32 * w + c;   // row of block 0 of this lane
   F stage[PS];
   auto fetch = [&](int rb) {
 #pragma unroll
@@ -595,35 +599,52 @@ __global__ __launch_bounds__(kThreads) void shift_kernel(FwdArgs a, const T* __r
       if (tid + p * kThreads < SL * 64) st8(&s_m[buf][(tid + p * kThreads) * 8], stage[p]);
   };
   fetch(0);
-  F xf[KD];
-  load_rows<T, DH>(xf, base + (long)t * stride, ok, g);
+  F xf[RB][KD];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) load_rows<T, DH>(xf[j], base + (long)(t0 + 32 * j) * stride, t0 + 32 * j < a.L, g);
   put(0);
   __syncthreads();
-  float ss = 0.f;
+  float ss[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) ss[j] = 0.f;
+#pragma unroll 1   // one slice in registers at a time
   for (int rb = 0; rb < R32; ++rb) {
     if (rb + 1 < R32) fetch(rb + 1);
     const T* sm = s_m[rb & 1];
-    f32x16 u = zero16();
+    f32x16 u[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) u[j] = zero16();
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd) {
 #pragma unroll
-      for (int part = 0; part < NM; ++part) u = mma(ld8(sm + ((kd * NM + part) * 64 + lane) * 8), xf[kd], u);
+      for (int part = 0; part < NM; ++part) {
+        const F mfr = ld8(sm + ((kd * NM + part) * 64 + lane) * 8);
+#pragma unroll
+        for (int j = 0; j < RB; ++j) u[j] = mma(mfr, xf[j][kd], u[j]);
+      }
       if constexpr (SL > 8)   // bound the slice fragments in flight
         if (kd % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ss += u[i] * u[i];
+    for (int j = 0; j < RB; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss[j] += u[j][i] * u[j][i];
     if (rb + 1 < R32) put((rb + 1) & 1);
     __syncthreads();
   }
-  ss += __shfl_xor(ss, 32);
-  const float sh = 0.5f * kLog2e * ss + 0.5f * log2f((float)a.m);
-  if (g == 0 && ok) {
-    if (half == 0) {
-      qshift[(long)bh * a.L + t] = sh;
-    } else {
-      const bool valid = a.mask == nullptr || a.mask[(long)b * a.L + t] != 0;
-      kshift[(long)bh * a.L + t] = valid ? -sh : -INFINITY;
+  const float hl = 0.5f * log2f((float)a.m);
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    const float sq = ss[j] + __shfl_xor(ss[j], 32);
+    const float sh = 0.5f * kLog2e * sq + hl;
+    const int t = t0 + 32 * j;
+    if (g == 0 && t < a.L) {
+      if (half == 0) {
+        qshift[(long)bh * a.L + t] = sh;
+      } else {
+        const bool valid = a.mask == nullptr || a.mask[(long)b * a.L + t] != 0;
+        kshift[(long)bh * a.L + t] = valid ? -sh : -INFINITY;
+      }
     }
   }
 }
@@ -1629,7 +1650,7 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
     }
   }
   if (pl.kshift) {
-    const int ntile = (a.L + kShiftTile - 1) / kShiftTile;
+    const int ntile = (a.L + shift_tile<T>() - 1) / shift_tile<T>();
     KernelTimer tm(kShift, stream);
     hipLaunchKernelGGL((shift_kernel<T, DH, R16>), dim3(2 * pl.BH * ntile), dim3(kThreads), 0, st, a, mfrag,
                        a.qshift, a.kshift);
