@@ -8,6 +8,8 @@ from .prf_oracle import (  # noqa: F401
     attend_causal_blockwise,
     attend_noncausal,
     attention,
+    context_state,
+    cross_attention,
     decode_step,
     exact_kernel_attention,
     head_geometry,

@@ -24,6 +24,9 @@ geometry, Sigma = M^T M; Omega (m x r) holds the feature directions omega_j.
 * Recurrent decoding keeps the running statistics S = sum phi(k) v^T and
   z = sum phi(k) and updates them per appended token (section "Encoder-decoder
   model and generation").
+* Cross-attention (section "Cross-attention"): queries of one sequence attend
+  to a context of another length; query and context masks are separate and
+  there is no causal option; the context is summarised once as (S, z).
 
 Readings where the README is silent (each is listed with its support in the
 design notes): q and k are scaled inside (callers pass unscaled tensors); one
@@ -31,7 +34,8 @@ Omega is shared by all heads; M is [H][r][d_h] per head or [r][d_h] shared;
 query head h reads key/value head floor(h * H_kv / H); the mask masks keys
 only; a query with no visible key gets output 0 (the denominator is positive
 otherwise since every feature is positive); the decode output uses the state
-after the new token has been added.
+after the new token has been added; in cross-attention the context mask masks
+context keys and a masked query row gets output 0.
 """
 from __future__ import annotations
 
@@ -184,6 +188,53 @@ def decode_step(S, z, q, k, v, M, omega):
         den = np.einsum("nm,nm->n", pq, z[:, h])
         o[:, h] = _ratio(num, den)
     return o, S, z
+
+
+def context_state(k, v, M, omega, H: int, context_mask: Optional[np.ndarray] = None):
+    """Summary of an encoded source for cross-attention (section "Cross-attention";
+    section "Encoder-decoder model and generation": decoder cross-attention
+    projects and summarises the source once per layer).
+
+    k and v [B][H_kv][L_k][d_h], context_mask [B][L_k] (nonzero = valid) or None.
+    For every batch row b and query head h (geometry M_h, K/V head g(h)):
+    S = Phi(K)^T V and z = Phi(K)^T 1 over the valid context keys.
+    Returns S [B][H][m][d_h] and z [B][H][m].
+    """
+    k, v = f64(k), f64(v)
+    B, H_kv, L_k, d = k.shape
+    m = np.asarray(omega).shape[0]
+    S = np.zeros((B, H, m, d))
+    z = np.zeros((B, H, m))
+    for b in range(B):
+        for h in range(H):
+            g = kv_head(h, H, H_kv)
+            PK = prf_features(k[b, g], head_geometry(M, h), omega)
+            if context_mask is not None:
+                PK = PK * (np.asarray(context_mask[b]) != 0)[:, None]
+            S[b, h] = PK.T @ v[b, g]
+            z[b, h] = PK.T @ np.ones(L_k)
+    return S, z
+
+
+def cross_attention(q, S, z, M, omega, query_mask: Optional[np.ndarray] = None):
+    """Queries against a context summary (section "Cross-attention"): query and
+    context masks stay separate; there is no causal option.
+
+    q [B][H][L_q][d_h], S [B][H][m][d_h], z [B][H][m] (from context_state),
+    query_mask [B][L_q] (nonzero = valid) or None.
+    O_t = Phi(q_t) S / Phi(q_t) z; a masked query row, or one whose denominator
+    is not positive (no valid context key), gives 0.
+    """
+    q, S, z = f64(q), f64(S), f64(z)
+    B, H, L_q, d = q.shape
+    O = np.zeros((B, H, L_q, d))
+    for b in range(B):
+        for h in range(H):
+            PQ = prf_features(q[b, h], head_geometry(M, h), omega)
+            O[b, h] = _ratio(PQ @ S[b, h], PQ @ z[b, h])
+            if query_mask is not None:
+                O[b, h][np.asarray(query_mask[b]) == 0] = 0.0
+    return O
 
 
 def exact_kernel_attention(q, k, v, M, mask: Optional[np.ndarray] = None, causal: bool = False):

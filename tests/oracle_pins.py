@@ -366,6 +366,53 @@ def check_decode_vs_causal(seed=61, P=37, T=11):
     _close(z, z_full, 1e-12, "decode final z")
 
 
+# ----------------------------------------------------------------------------
+# cross-attention (section "Cross-attention"): the context summary written out
+# key by key, and the output against the explicit quadratic form
+# ----------------------------------------------------------------------------
+def check_context_state_explicit(seed=71):
+    """S = sum_j phi(k_j) v_j^T and z = sum_j phi(k_j) over valid context keys,
+    with phi written out here from the section "Kernel" feature map."""
+    rng = np.random.default_rng(seed)
+    B, H, H_kv, Lk, d, m, r = 2, 4, 2, 23, 8, 16, 8
+    _, k, v, M, om = _random_case(rng, B=B, H=H, H_kv=H_kv, Lq=1, Lk=Lk, d=d, m=m, r=r)
+    cmask = (rng.random((B, Lk)) < 0.7).astype(np.uint8)
+    S, z = po.context_state(k, v, M, om, H, context_mask=cmask)
+    for b in range(B):
+        for h in range(H):
+            g = (h * H_kv) // H
+            S_ref = np.zeros((m, d))
+            z_ref = np.zeros(m)
+            for j in range(Lk):
+                if not cmask[b, j]:
+                    continue
+                u = _u(k[b, g, j][None, :], M[h], d)[0]
+                phi = np.exp(om @ u - 0.5 * float(u @ u)) / math.sqrt(m)
+                S_ref += np.outer(phi, v[b, g, j])
+                z_ref += phi
+            _close(S[b, h], S_ref, 1e-12, f"context S b={b} h={h}")
+            _close(z[b, h], z_ref, 1e-12, f"context z b={b} h={h}")
+
+
+def check_cross_vs_explicit(seed=72):
+    """Queries of length L_q against a context of length L_k, GQA, both masks:
+    the explicit quadratic form, with masked query rows set to 0."""
+    rng = np.random.default_rng(seed)
+    B, H, H_kv = 3, 4, 2
+    for Lq, Lk in ((1, 9), (13, 40), (29, 5)):
+        q, k, v, M, om = _random_case(rng, B=B, H=H, H_kv=H_kv, Lq=Lq, Lk=Lk)
+        cmask = (rng.random((B, Lk)) < 0.6).astype(np.uint8)
+        cmask[0, 0] = 1
+        cmask[2, :] = 0                               # a context with no valid key
+        qmask = (rng.random((B, Lq)) < 0.7).astype(np.uint8)
+        ref = explicit_attention(q, k, v, M, om, mask=cmask)
+        ref = ref * (qmask != 0)[:, None, :, None]
+        S, z = po.context_state(k, v, M, om, H, context_mask=cmask)
+        O = po.cross_attention(q, S, z, M, om, query_mask=qmask)
+        _close(O, ref, 1e-12, f"cross Lq={Lq} Lk={Lk}")
+        assert np.all(O[2] == 0.0)
+
+
 ALL_CHECKS = [
     check_closed_form_features,
     check_closed_form_attention,
@@ -376,4 +423,6 @@ ALL_CHECKS = [
     check_scaling_rule,
     check_decode_vs_causal,
     check_exact_vs_sdpa,
+    check_context_state_explicit,
+    check_cross_vs_explicit,
 ]

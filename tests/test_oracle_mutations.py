@@ -72,6 +72,18 @@ def _decode_before_update(S, z, q, k, v, M, omega):
     return o, S, z
 
 
+def _context_mask_ignored(orig):
+    def context_state(k, v, M, omega, H, context_mask=None):
+        return orig(k, v, M, omega, H, context_mask=None)
+    return context_state
+
+
+def _query_mask_ignored(orig):
+    def cross_attention(q, S, z, M, omega, query_mask=None):
+        return orig(q, S, z, M, omega, query_mask=None)
+    return cross_attention
+
+
 MUTATIONS = {
     "scale_d^-1/2": ("prf_features", _feat(scale=lambda d: d ** -0.5)),
     "no_scale": ("prf_features", _feat(scale=lambda d: 1.0)),
@@ -86,6 +98,8 @@ MUTATIONS = {
     "gqa_modulo": ("kv_head", lambda h, H, H_kv: h % H_kv),
     "decode_pre_update": ("decode_step", _decode_before_update),
     "eps_denominator": ("_ratio", lambda N, D: N / (D + 1e-8)[:, None]),
+    "context_mask_ignored": ("context_state", None),
+    "query_mask_ignored": ("cross_attention", None),
 }
 
 QUICK = pins.ALL_CHECKS + [pins.check_mc_kernel]
@@ -96,6 +110,10 @@ def test_pins_catch_mutation(name, monkeypatch):
     attr, repl = MUTATIONS[name]
     if name == "mask_ignored":
         repl = _ignore_mask(po.attention)
+    elif name == "context_mask_ignored":
+        repl = _context_mask_ignored(po.context_state)
+    elif name == "query_mask_ignored":
+        repl = _query_mask_ignored(po.cross_attention)
     monkeypatch.setattr(po, attr, repl)
     caught = []
     for check in QUICK:

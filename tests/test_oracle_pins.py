@@ -44,3 +44,11 @@ def test_scaling_rule():
 
 def test_decode_recurrence_vs_causal():
     pins.check_decode_vs_causal()
+
+
+def test_context_state_explicit():
+    pins.check_context_state_explicit()
+
+
+def test_cross_vs_explicit():
+    pins.check_cross_vs_explicit()
