@@ -152,6 +152,55 @@ dark_status dark_prf_decode_step(const dark_prf_desc* desc, const void* q, const
                                  float* S, float* z, uint64_t state_tag, void* out,
                                  void* stream);
 
+/*
+ * Cross-attention (README section "Cross-attention": queries attend to a
+ * context of another length; query and context masks are separate; there is
+ * no causal option.  Section "Encoder-decoder model and generation": decoder
+ * cross-attention projects and summarises the encoded source once per layer,
+ * and every decoder step reuses that summary).  Two calls: the summary of a
+ * context, then any number of query batches against it.  Query head h uses
+ * geometry M_h and reads context K/V head h*H_kv/H, as in dark_prf_fwd.
+ *
+ * dark_prf_context_state - the summary of a context.  desc->L = context
+ * length L_k, desc->causal = 0; q_str and o_str are not used.
+ *   k, v  [B][H_kv][L_k][d_h]  (strides k_str, v_str), dtype
+ *   M, omega as for dark_prf_fwd
+ *   context_mask uint8 [B][L_k] contiguous, nonzero = valid context token, or
+ *     NULL (all valid); masked tokens are removed as keys
+ *   S_out fp32 [B][H][m][d_h], z_out fp32 [B][H][m], contiguous (both
+ *     required): S = sum_j phi(k_j) v_j^T and z = sum_j phi(k_j) over the
+ *     valid context tokens (all zero when L_k = 0); tagged, like any exported
+ *     state, with desc->proj_tag
+ *   workspace, ws_bytes: at least dark_prf_workspace_bytes(desc)
+ * Returns DARK_ERR_INVALID_ARG for causal != 0 or a missing S_out / z_out.
+ */
+dark_status dark_prf_context_state(const dark_prf_desc* desc, const void* k, const void* v,
+                                   const float* M, const float* omega,
+                                   const uint8_t* context_mask, float* S_out, float* z_out,
+                                   void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dark_prf_cross_fwd - queries against a context summary.  desc->L = query
+ * length L_q, desc->causal = 0; desc->H, H_kv, d_h, m, r, m_per_head and dtype
+ * as for the dark_prf_context_state call that made the summary; k_str and
+ * v_str are not used.
+ *   q   [B][H][L_q][d_h] (strides q_str), dtype
+ *   M, omega as for dark_prf_fwd (the same as for the summary)
+ *   S fp32 [B][H][m][d_h], z fp32 [B][H][m], contiguous: the summary (read
+ *     only; S is rounded to the input dtype for the products, z stays fp32)
+ *   state_tag: the proj_tag the summary was made with; it must equal
+ *     desc->proj_tag, else DARK_ERR_STALE_STATE and nothing is queued
+ *   query_mask uint8 [B][L_q] contiguous, nonzero = valid query, or NULL;
+ *     a masked query row is written as 0
+ *   out [B][H][L_q][d_h] (strides o_str), dtype: out_t = phi(q_t)^T S /
+ *     phi(q_t)^T z (0 when the denominator is 0)
+ *   workspace, ws_bytes: at least dark_prf_workspace_bytes(desc)
+ */
+dark_status dark_prf_cross_fwd(const dark_prf_desc* desc, const void* q, const float* M,
+                               const float* omega, const float* S, const float* z,
+                               uint64_t state_tag, const uint8_t* query_mask, void* out,
+                               void* workspace, size_t ws_bytes, void* stream);
+
 /* dark_prf_status_str - a static, human-readable name of a status. */
 const char* dark_prf_status_str(dark_status status);
 

@@ -72,6 +72,12 @@ def lib() -> ctypes.CDLL:
         L.dark_prf_decode_step.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P,
                                            ctypes.c_uint64, P, P]
         L.dark_prf_decode_step.restype = ctypes.c_int
+        L.dark_prf_context_state.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P, P,
+                                             ctypes.c_size_t, P]
+        L.dark_prf_context_state.restype = ctypes.c_int
+        L.dark_prf_cross_fwd.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, ctypes.c_uint64,
+                                         P, P, P, ctypes.c_size_t, P]
+        L.dark_prf_cross_fwd.restype = ctypes.c_int
         L.dark_prf_status_str.argtypes = [ctypes.c_int]
         L.dark_prf_status_str.restype = ctypes.c_char_p
         L.dark_prf_timing_begin.argtypes = []
@@ -114,6 +120,21 @@ def dark_prf_fwd(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, omega: int, 
     return lib().dark_prf_fwd(ctypes.byref(desc), q or None, k or None, v or None, M or None,
                               omega or None, mask or None, out or None, S_out or None,
                               z_out or None, workspace or None, ws_bytes, stream or None)
+
+
+def dark_prf_context_state(desc: DarkPrfDesc, k: int, v: int, M: int, omega: int, context_mask: int,
+                           S_out: int, z_out: int, workspace: int, ws_bytes: int, stream: int) -> int:
+    return lib().dark_prf_context_state(ctypes.byref(desc), k or None, v or None, M or None,
+                                        omega or None, context_mask or None, S_out or None,
+                                        z_out or None, workspace or None, ws_bytes, stream or None)
+
+
+def dark_prf_cross_fwd(desc: DarkPrfDesc, q: int, M: int, omega: int, S: int, z: int, state_tag: int,
+                       query_mask: int, out: int, workspace: int, ws_bytes: int, stream: int) -> int:
+    return lib().dark_prf_cross_fwd(ctypes.byref(desc), q or None, M or None, omega or None,
+                                    S or None, z or None, ctypes.c_uint64(state_tag),
+                                    query_mask or None, out or None, workspace or None, ws_bytes,
+                                    stream or None)
 
 
 def dark_prf_decode_step(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, omega: int, S: int,
@@ -222,4 +243,76 @@ def decode_step(q, k, v, M, omega, S, z, state_tag: int, proj_tag: int, out=None
                               out.data_ptr(), stream)
     if st != DARK_OK:
         raise DarkPrfError(st, "dark_prf_decode_step")
+    return out
+
+
+def _mask_ptr(mask, what: str) -> int:
+    import torch
+    if mask is None:
+        return 0
+    if mask.dtype != torch.uint8 or not mask.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous uint8 [B][L] tensor")
+    return mask.data_ptr()
+
+
+def context_state(k, v, M, omega, H: int, context_mask=None, proj_tag: int = 0, workspace=None):
+    """dark_prf_context_state: k/v [B][H_kv][L_k][d_h] -> S [B][H][m][d_h], z [B][H][m] (fp32)."""
+    import torch
+    B, H_kv, L_k, d_h = k.shape
+    d = DarkPrfDesc()
+    d.B, d.H, d.H_kv, d.L, d.d_h = B, H, H_kv, L_k, d_h
+    d.m, d.r = omega.shape[0], omega.shape[1]
+    d.dtype = _dtype_code(k)
+    d.causal = 0
+    d.m_per_head = int(M.dim() == 3)
+    for name, t in (("k_str", k), ("v_str", v)):
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name}: the last dimension must be contiguous")
+        getattr(d, name)[:] = list(t.stride()[:3])
+    d.q_str[:] = list(k.stride()[:3])   # not used by this call
+    d.o_str[:] = list(k.stride()[:3])
+    d.proj_tag = proj_tag
+    nbytes = dark_prf_workspace_bytes(d)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
+    S = torch.empty((B, H, d.m, d_h), dtype=torch.float32, device=k.device)
+    z = torch.empty((B, H, d.m), dtype=torch.float32, device=k.device)
+    stream = torch.cuda.current_stream(k.device).cuda_stream
+    st = dark_prf_context_state(d, k.data_ptr(), v.data_ptr(), M.data_ptr(), omega.data_ptr(),
+                                _mask_ptr(context_mask, "context_mask"), S.data_ptr(), z.data_ptr(),
+                                workspace.data_ptr(), workspace.numel(), stream)
+    if st != DARK_OK:
+        raise DarkPrfError(st, "dark_prf_context_state")
+    return S, z
+
+
+def cross_attention(q, M, omega, S, z, state_tag: int, proj_tag: int, query_mask=None, H_kv: int = 1,
+                    out=None, workspace=None):
+    """dark_prf_cross_fwd: q [B][H][L_q][d_h] against a summary (S, z) -> out [B][H][L_q][d_h]."""
+    import torch
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    B, H, L_q, d_h = q.shape
+    d = DarkPrfDesc()
+    d.B, d.H, d.H_kv, d.L, d.d_h = B, H, H_kv, L_q, d_h
+    d.m, d.r = omega.shape[0], omega.shape[1]
+    d.dtype = _dtype_code(q)
+    d.causal = 0
+    d.m_per_head = int(M.dim() == 3)
+    for name, t in (("q_str", q), ("o_str", out)):
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name}: the last dimension must be contiguous")
+        getattr(d, name)[:] = list(t.stride()[:3])
+    d.k_str[:] = list(q.stride()[:3])   # not used by this call
+    d.v_str[:] = list(q.stride()[:3])
+    d.proj_tag = proj_tag
+    nbytes = dark_prf_workspace_bytes(d)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = dark_prf_cross_fwd(d, q.data_ptr(), M.data_ptr(), omega.data_ptr(), S.data_ptr(), z.data_ptr(),
+                            state_tag, _mask_ptr(query_mask, "query_mask"), out.data_ptr(),
+                            workspace.data_ptr(), workspace.numel(), stream)
+    if st != DARK_OK:
+        raise DarkPrfError(st, "dark_prf_cross_fwd")
     return out

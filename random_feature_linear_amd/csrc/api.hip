@@ -81,7 +81,7 @@ static int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 // 32-feature blocks per wave in the key-side kernel (must match the instantiation units).
 static int feature_blocks_per_wave(int d_h) { return d_h <= 64 ? 2 : 1; }
 
-static void make_plan(const dark_prf_desc& d, Plan& p) {
+static void make_plan(const dark_prf_desc& d, Plan& p, int mode = kPlanForward) {
   memset(&p, 0, sizeof(p));
   p.DH = d.d_h;
   p.R16 = rank_blocks(d.r);
@@ -139,7 +139,9 @@ static void make_plan(const dark_prf_desc& d, Plan& p) {
   off = align256(off + (size_t)p.BH * nout * p.FB * 32 * sizeof(float));
   // keys and queries are projected once up front (for |u|^2) when several
   // feature slices, or the causal query side, would otherwise repeat it
-  p.kshift = p.fold && (p.NF > 1 || (d.causal && d.d_h >= 128));
+  // (the cross-attention calls have one side each: each side projects its own shifts)
+  p.mode = mode;
+  p.kshift = mode == kPlanForward && p.fold && (p.NF > 1 || (d.causal && d.d_h >= 128));
   p.off_kshift = off;
   if (p.kshift) off = align256(off + 2 * (size_t)p.BH * L * sizeof(float));   // key, then query shifts
   p.total = off;
@@ -147,8 +149,9 @@ static void make_plan(const dark_prf_desc& d, Plan& p) {
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Shape and stride checks shared by the forward and decode entry points.
-static dark_status check_desc(const dark_prf_desc* d, bool decode) {
+// Shape and stride checks shared by every entry point; `tensors` selects the
+// stride sets that the call uses (bit 0 q, 1 k, 2 v, 3 out).
+static dark_status check_desc(const dark_prf_desc* d, bool decode, int tensors = 15) {
   if (!d) return DARK_ERR_INVALID_ARG;
   if (d->B < 0 || d->L < 0 || d->H < 1 || d->H_kv < 1 || d->H % d->H_kv != 0) return DARK_ERR_INVALID_ARG;
   if (dh_index(d->d_h) < 0) return DARK_ERR_INVALID_ARG;
@@ -160,14 +163,13 @@ static dark_status check_desc(const dark_prf_desc* d, bool decode) {
   if (decode && (d->L != 1 || d->causal != 1)) return DARK_ERR_INVALID_ARG;
   const int64_t elem = d->dtype == DARK_BF16 ? 2 : 4;
   const int64_t* strides[4] = {d->q_str, d->k_str, d->v_str, d->o_str};
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 4; ++t) {
+    if (!(tensors >> t & 1)) continue;
     for (int i = 0; i < 3; ++i) {
       if (decode && i == 2) continue;
       if (strides[t][i] < 0 || (strides[t][i] * elem) % 16 != 0) return DARK_ERR_INVALID_ARG;
     }
-  if (!decode) {
-    for (int t = 0; t < 4; ++t)
-      if (d->L > 1 && strides[t][2] < d->d_h) return DARK_ERR_INVALID_ARG;
+    if (!decode && d->L > 1 && strides[t][2] < d->d_h) return DARK_ERR_INVALID_ARG;
   }
   // element offsets are formed in 64-bit; the grid is formed in 32-bit
   if ((int64_t)d->B * d->H * ((int64_t)d->L + 255) > (int64_t)1 << 31) return DARK_ERR_UNSUPPORTED;
@@ -386,6 +388,9 @@ dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k
   a.z_out = z_out;
   a.kshift = nullptr;   // set by the launcher from the workspace
   a.qshift = nullptr;
+  a.qmask = nullptr;
+  a.S_in = nullptr;
+  a.z_in = nullptr;
   a.B = d.B;
   a.H = d.H;
   a.H_kv = d.H_kv;
@@ -394,6 +399,96 @@ dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k
   a.r = d.r;
   a.causal = d.causal;
   a.m_per_head = d.m_per_head;
+  return fn(a, p, workspace, stream);
+}
+
+// Arguments common to the forward-chain calls (pointers the call does not use stay null).
+static FwdArgs fwd_args(const dark_prf_desc& d) {
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = d.q_str[i];
+    a.ks[i] = d.k_str[i];
+    a.vs[i] = d.v_str[i];
+    a.os[i] = d.o_str[i];
+  }
+  a.B = d.B;
+  a.H = d.H;
+  a.H_kv = d.H_kv;
+  a.L = d.L;
+  a.m = d.m;
+  a.r = d.r;
+  a.causal = d.causal;
+  a.m_per_head = d.m_per_head;
+  return a;
+}
+
+static dark_status zero_state(const dark_prf_desc& d, float* S, float* z, void* stream) {
+  (void)hipGetLastError();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const long nS = (long)d.B * d.H * d.m * d.d_h, nz = (long)d.B * d.H * d.m;
+  hipLaunchKernelGGL(dk_fill_zero, dim3(256), dim3(256), 0, s, S, nS);
+  hipLaunchKernelGGL(dk_fill_zero, dim3(64), dim3(256), 0, s, z, nz);
+  return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
+}
+
+dark_status dark_prf_context_state(const dark_prf_desc* desc, const void* k, const void* v, const float* M,
+                                   const float* omega, const uint8_t* context_mask, float* S_out, float* z_out,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  dark_status st = check_desc(desc, false, 2 | 4);
+  if (st != DARK_OK) return st;
+  const dark_prf_desc& d = *desc;
+  if (d.causal != 0) return DARK_ERR_INVALID_ARG;
+  if (!S_out || !z_out || !aligned16(S_out) || !aligned16(z_out)) return DARK_ERR_INVALID_ARG;
+  if (d.B == 0) return DARK_OK;
+  if (d.L == 0) return zero_state(d, S_out, z_out, stream);
+  if (!k || !v || !M || !omega) return DARK_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(M) || !aligned16(omega)) return DARK_ERR_INVALID_ARG;
+  Plan p;
+  make_plan(d, p, kPlanContext);
+  if (workspace == nullptr || ws_bytes < p.total) return DARK_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DARK_ERR_INVALID_ARG;
+  fwd_launcher fn = find_fwd_launcher(d.dtype, d.d_h, p.R16);
+  if (!fn) return DARK_ERR_UNSUPPORTED;
+  (void)hipGetLastError();   // launch errors below are ours, not an earlier caller's
+  FwdArgs a = fwd_args(d);
+  a.k = k;
+  a.v = v;
+  a.mask = context_mask;
+  a.M = M;
+  a.omega = omega;
+  a.S_out = S_out;
+  a.z_out = z_out;
+  return fn(a, p, workspace, stream);
+}
+
+dark_status dark_prf_cross_fwd(const dark_prf_desc* desc, const void* q, const float* M, const float* omega,
+                               const float* S, const float* z, uint64_t state_tag, const uint8_t* query_mask,
+                               void* out, void* workspace, size_t ws_bytes, void* stream) {
+  dark_status st = check_desc(desc, false, 1 | 8);
+  if (st != DARK_OK) return st;
+  const dark_prf_desc& d = *desc;
+  if (d.causal != 0) return DARK_ERR_INVALID_ARG;
+  if (state_tag != d.proj_tag) return DARK_ERR_STALE_STATE;
+  if (d.B == 0 || d.L == 0) return DARK_OK;
+  if (!q || !M || !omega || !S || !z || !out) return DARK_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(M) || !aligned16(omega)) return DARK_ERR_INVALID_ARG;
+  if (!aligned16(S) || !aligned16(z)) return DARK_ERR_INVALID_ARG;
+  Plan p;
+  make_plan(d, p, kPlanCross);
+  if (workspace == nullptr || ws_bytes < p.total) return DARK_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DARK_ERR_INVALID_ARG;
+  fwd_launcher fn = find_fwd_launcher(d.dtype, d.d_h, p.R16);
+  if (!fn) return DARK_ERR_UNSUPPORTED;
+  (void)hipGetLastError();   // launch errors below are ours, not an earlier caller's
+  FwdArgs a = fwd_args(d);
+  a.q = q;
+  a.out = out;
+  a.qmask = query_mask;
+  a.M = M;
+  a.omega = omega;
+  a.S_in = S;
+  a.z_in = z;
   return fn(a, p, workspace, stream);
 }
 

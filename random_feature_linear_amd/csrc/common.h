@@ -21,6 +21,9 @@ struct FwdArgs {
   float* z_out;
   float* kshift;   // per-key shifts in the workspace (folded path), or null
   float* qshift;   // per-query shifts, likewise
+  const uint8_t* qmask;   // cross-attention query mask [B][L] (nonzero = valid), or null
+  const float* S_in;      // cross-attention context summary S [B][H][m][d_h], z [B][H][m]
+  const float* z_in;
   int B, H, H_kv, L, m, r, causal, m_per_head;
 };
 
@@ -31,6 +34,11 @@ struct FwdArgs {
 // for |u|^2) against 4 r d_h + 6 r m, so it is taken when d_h < 1.5 r.
 constexpr bool fold_exponent(int elem_bytes, int d_h, int r16) { return elem_bytes == 2 && 2 * d_h < 3 * 16 * r16; }
 
+// What one call runs: the whole forward; the key side and its sum only, with the
+// summary exported (a cross-attention context); or the query side against a
+// summary the caller passes in.
+enum PlanMode { kPlanForward = 0, kPlanContext = 1, kPlanCross = 2 };
+
 // How one call is cut into kernels; all sizes derived on the host.
 struct Plan {
   int DH;      // head dimension (template value)
@@ -39,6 +47,7 @@ struct Plan {
   int HM;      // number of geometry matrices (H or 1)
   int fold;    // exponent from W' x (see fold_exponent)
   int kshift;  // folded path with per-key shifts precomputed once (kshift_kernel)
+  int mode;    // kPlanForward, kPlanContext (key side and sum only) or kPlanCross (query side on a given state)
   int BH;      // B * H
   // key-side state kernel
   int span1;   // tokens per unit (a chunk when causal, an L-split otherwise)

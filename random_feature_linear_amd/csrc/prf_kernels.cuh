@@ -1150,7 +1150,7 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
         }
       }
       if (!a.causal) dst[0] = run;
-      else if (a.z_out && j < a.m) a.z_out[bh * a.m + j] = run;
+      if (a.z_out && j < a.m) a.z_out[bh * a.m + j] = run;
       continue;
     }
     const long bh = idx / per_unit;
@@ -1203,7 +1203,8 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
       F o;
       make_frag(o, run);
       st8(dst, o);
-    } else if (a.S_out) {
+    }
+    if (a.S_out) {
       const int lane = (int)(rem & 63);
       const long frag = rem >> 6;
       const int fk = (int)(frag % FK), db = (int)(frag / FK);
@@ -1217,6 +1218,47 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cross-attention: a context summary S [B][H][m][d_h], z [B][H][m] (fp32, from
+// the caller) laid out as the query side's operands, in the order the sum over
+// units writes them: fragment (d-block db, 16-feature half-block fk), lane
+// (c, g), element e holds S[16 fk + 8 (e / 4) + 4 g + e % 4][32 db + c] (0 past
+// m or d_h); z is padded with zeros to whole 32-feature blocks.
+// ---------------------------------------------------------------------------
+template <typename T, int DH>
+__global__ void state_frag_kernel(FwdArgs a, Plan pl, T* __restrict__ sfrag, float* __restrict__ zsum) {
+  typedef typename FragOf<T>::type F;
+  constexpr int DB = vblocks<DH>();
+  const long FK = 2L * pl.FB;
+  const long per_unit = DB * FK * 64;
+  const long nS = (long)pl.BH * per_unit;
+  const long z_unit = 32L * pl.FB;
+  const long nZ = (long)pl.BH * z_unit;
+  for (long idx = blockIdx.x * (long)blockDim.x + threadIdx.x; idx < nS + nZ; idx += (long)gridDim.x * blockDim.x) {
+    if (idx >= nS) {
+      const long zi = idx - nS;
+      const long bh = zi / z_unit, j = zi % z_unit;
+      zsum[zi] = j < a.m ? a.z_in[bh * a.m + j] : 0.f;
+      continue;
+    }
+    const long bh = idx / per_unit, rem = idx % per_unit;
+    const int lane = (int)(rem & 63);
+    const long frag = rem >> 6;
+    const int fk = (int)(frag % FK), db = (int)(frag / FK);
+    const int c = lane & 31, g = lane >> 5;
+    const int d = db * 32 + c;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 16 * fk + 8 * (e >> 2) + 4 * g + (e & 3);
+      x[e] = (d < DH && j < a.m) ? a.S_in[(bh * a.m + j) * DH + d] : 0.f;
+    }
+    F o;
+    make_frag(o, x);
+    st8(sfrag + idx * 8, o);
   }
 }
 
@@ -1583,7 +1625,9 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
     for (int i = 0; i < 16; ++i) {
       const float dd = __shfl(dq, crow(i, g));
       const int t = t0 + 32 * blk + crow(i, g);
-      const float inv = dd > 0.f ? __builtin_amdgcn_rcpf(dd) : 0.f;
+      // a masked query row (cross-attention) gives 0
+      const bool qvalid = a.qmask == nullptr || (t < a.L && a.qmask[(long)b * a.L + t] != 0);
+      const float inv = (dd > 0.f && qvalid) ? __builtin_amdgcn_rcpf(dd) : 0.f;
       if (t < a.L) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -1649,13 +1693,18 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
                          a.m, R16, pl.FB, s, fmode);
     }
   }
+  if (pl.mode == kPlanCross) {   // the caller's summary as the query side's operands
+    const long n = (long)pl.BH * vblocks<DH>() * 2 * pl.FB * 64 + (long)pl.BH * pl.FB * 32;
+    KernelTimer tm(kScan, stream);
+    hipLaunchKernelGGL((state_frag_kernel<T, DH>), dim3((int)((n + 255) / 256)), dim3(256), 0, st, a, pl, sfrag, zsum);
+  }
   if (pl.kshift) {
     const int ntile = (a.L + shift_tile<T>() - 1) / shift_tile<T>();
     KernelTimer tm(kShift, stream);
     hipLaunchKernelGGL((shift_kernel<T, DH, R16>), dim3(2 * pl.BH * ntile), dim3(kThreads), 0, st, a, mfrag,
                        a.qshift, a.kshift);
   }
-  {
+  if (pl.mode != kPlanCross) {
     KernelTimer tm(kKState, stream);
     const dim3 grid1(pl.BH * pl.NU * pl.NF);
     static_assert(!fold_exponent(sizeof(T), DH, R16) || kstate_tile_lds_bytes<T, DH, R16>() <= kMaxLds,
@@ -1667,12 +1716,13 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
       hipLaunchKernelGGL((kstate_seq_kernel<T, DH, R16, FBW, PAD>), grid1, dim3(kThreads), 0, st, a, pl, mfrag,
                          ofrag, sdelta, zdelta);
   }
-  {
+  if (pl.mode != kPlanCross) {
     const long n = (long)pl.BH * vblocks<DH>() * 2 * pl.FB * 64 + (long)pl.BH * pl.FB * 32;   // S lanes, z values
     const int blocks = (int)((n + 255) / 256);
     KernelTimer tm(kScan, stream);
     hipLaunchKernelGGL((scan_kernel<T, DH>), dim3(blocks), dim3(256), 0, st, a, pl, sdelta, sfrag, zdelta, zsum);
   }
+  if (pl.mode == kPlanContext) return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
   const dim3 grid(pl.BH * pl.NT2);
   KernelTimer tm(kQOut, stream);
   if (a.causal) {

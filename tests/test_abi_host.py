@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     L = bd.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -108,6 +108,43 @@ def test_decode_argument_checks():
     assert bd.dark_prf_decode_step(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0) == bd.DARK_ERR_INVALID_ARG
     d = _dec_desc()
     assert bd.dark_prf_decode_step(d, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0, FAKE, 0) == bd.DARK_ERR_INVALID_ARG
+
+
+def _ctx(d, S=FAKE, z=FAKE, ws=FAKE, nb=None):
+    nb = bd.dark_prf_workspace_bytes(d) if nb is None else nb
+    return bd.dark_prf_context_state(d, FAKE, FAKE, FAKE, FAKE, 0, S, z, ws, nb, 0)
+
+
+def _cross(d, tag=None, q=FAKE, S=FAKE, ws=FAKE, nb=None):
+    nb = bd.dark_prf_workspace_bytes(d) if nb is None else nb
+    tag = d.proj_tag if tag is None else tag
+    return bd.dark_prf_cross_fwd(d, q, FAKE, FAKE, S, FAKE, tag, 0, FAKE, ws, nb, 0)
+
+
+def test_context_state_argument_checks():
+    assert _ctx(_desc(causal=1)) == bd.DARK_ERR_INVALID_ARG           # no causal cross-attention
+    assert _ctx(_desc(causal=0), S=0) == bd.DARK_ERR_INVALID_ARG      # the summary is the output
+    assert _ctx(_desc(causal=0), z=FAKE + 4) == bd.DARK_ERR_INVALID_ARG
+    assert _ctx(_desc(causal=0), nb=0) == bd.DARK_ERR_WORKSPACE
+    assert _ctx(_desc(causal=0, B=0), ws=0, nb=0) == bd.DARK_OK
+    # the query and output strides are not used by this call
+    assert _ctx(_desc(causal=0, q_str=[0, 0, 0], o_str=[0, 0, 0]), nb=0) == bd.DARK_ERR_WORKSPACE
+    assert _ctx(_desc(causal=0, k_str=[0, 0, 0])) == bd.DARK_ERR_INVALID_ARG
+
+
+def test_cross_fwd_argument_checks():
+    d = _desc(causal=0, L=100)
+    d.proj_tag = bd.dark_prf_proj_tag(7, 256, 64, True)
+    other = bd.dark_prf_proj_tag(8, 256, 64, True)
+    assert _cross(d, tag=other) == bd.DARK_ERR_STALE_STATE
+    assert _cross(_desc(causal=1)) == bd.DARK_ERR_INVALID_ARG
+    assert _cross(d, q=0) == bd.DARK_ERR_INVALID_ARG
+    assert _cross(d, S=FAKE + 8) == bd.DARK_ERR_INVALID_ARG
+    assert _cross(d, nb=0) == bd.DARK_ERR_WORKSPACE
+    assert _cross(_desc(causal=0, L=0), ws=0, nb=0) == bd.DARK_OK
+    # the key and value strides are not used by this call
+    e = _desc(causal=0, L=100, k_str=[0, 0, 0], v_str=[0, 0, 0])
+    assert _cross(e, nb=0) == bd.DARK_ERR_WORKSPACE
 
 
 def test_status_strings():
