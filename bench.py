@@ -315,6 +315,99 @@ def decode_line(steps: int) -> dict:
                          "bytes_per_launch": state_bytes, "avg_launch_us": round(avg_us, 3)}}
 
 
+def cross_line(steps: int, eager: bool = False) -> dict:
+    """Cross-attention at the pages' example shape: queries B=2 x L_q=256 against
+    a context of L_k=1024 (8 heads of 64, m=256), with a padded context.  One
+    step = the context summary (dark_prf_context_state) and the queries against
+    it (dark_prf_cross_fwd); both run in one HIP graph of `steps` steps."""
+    import torch
+
+    from random_feature_linear_amd import binding as bd
+    from random_feature_linear_amd.workloads import Workload, make_inputs
+    Lq, Lk = 256, 1024
+    wk = Workload(name="cross_example", B=2, H=8, L=Lk, d_h=64, m=256, r=64, dtype="bf16", causal=False,
+                  seed=1010, mask_kind="tail", max_pad=256)
+    wq = wk.with_(L=Lq, mask_kind="none")
+    ctx, qry = make_inputs(wk), make_inputs(wq)
+    dt = torch.bfloat16
+    dev = lambda a, t=None: torch.from_numpy(a).to(t).to("cuda:0") if t else torch.from_numpy(a).to("cuda:0")
+    k, v, q = dev(ctx["k"], dt), dev(ctx["v"], dt), dev(qry["q"], dt)
+    cmask = dev(ctx["mask"])
+    M = dev(ctx["M"])
+    om = torch.from_numpy(bd.dark_prf_omega(wk.seed, wk.m, wk.r, wk.orthogonal)).to("cuda:0")
+    tag = bd.dark_prf_proj_tag(wk.seed, wk.m, wk.r, wk.orthogonal)
+    S = torch.empty((wk.B, wk.H, wk.m, wk.d_h), dtype=torch.float32, device="cuda:0")
+    z = torch.empty((wk.B, wk.H, wk.m), dtype=torch.float32, device="cuda:0")
+    out = torch.empty_like(q)
+    dk = bd.make_desc(k, k, v, k, M, om, False, tag)
+    dk.H = wk.H
+    dq = bd.make_desc(q, q, q, out, M, om, False, tag)
+    dq.H_kv = wk.H
+    nb = max(bd.dark_prf_workspace_bytes(dk), bd.dark_prf_workspace_bytes(dq))
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        st = torch.cuda.current_stream().cuda_stream
+        r1 = bd.dark_prf_context_state(dk, k.data_ptr(), v.data_ptr(), M.data_ptr(), om.data_ptr(),
+                                       cmask.data_ptr(), S.data_ptr(), z.data_ptr(), ws.data_ptr(), nb, st)
+        r2 = bd.dark_prf_cross_fwd(dq, q.data_ptr(), M.data_ptr(), om.data_ptr(), S.data_ptr(), z.data_ptr(),
+                                   tag, 0, out.data_ptr(), ws.data_ptr(), nb, st)
+        if r1 != bd.DARK_OK or r2 != bd.DARK_OK:
+            raise bd.DarkPrfError(r1 or r2, "cross-attention")
+
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    if eager:   # plain launches (for profilers that follow kernel dispatches)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            step()
+        t1.record()
+        torch.cuda.synchronize()
+        return {"workload": "cross_example", "ms_per_step": t0.elapsed_time(t1) / steps, "steps": steps,
+                "launch": "eager"}
+    sm = torch.cuda.Stream()
+    sm.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(sm):
+        with torch.cuda.graph(g, stream=sm):
+            for _ in range(steps):
+                step()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del g
+    bd.dark_prf_timing_begin()
+    for _ in range(steps):
+        step()
+    per = bd.dark_prf_timing_end()
+    torch.cuda.synchronize()
+    kern = {kk: 1e3 * vv[0] / vv[1] for kk, vv in per.items() if vv[1] > 0}
+    # key side: projection, exponent and state per context token and head; query
+    # side: projection, exponent and output per query token and head
+    per_tok = 2 * wk.r * wk.d_h + 2 * wk.r * wk.m + 2 * wk.m * (wk.d_h + 1)
+    flops = {"kstate": wk.B * wk.H * Lk * per_tok, "qout": wk.B * wk.H * Lq * per_tok}
+    dom = max(("kstate", "qout"), key=lambda kk: kern.get(kk, 0.0))
+    ach = flops[dom] / (kern[dom] * 1e-6) / 1e12
+    return {"value": round(wk.B * Lq / (ms * 1e-3), 1), "unit": "query tokens/s", "ms_per_step": round(ms, 6),
+            "config": {"workload": "cross_example", "B": wk.B, "H": wk.H, "L_q": Lq, "L_k": Lk, "d_h": wk.d_h,
+                       "m": wk.m, "r": wk.r, "context_mask": "tail", "query_mask": "none",
+                       "step": "dark_prf_context_state + dark_prf_cross_fwd",
+                       "launch": "one hipGraph of %d steps" % steps},
+            "kernels_us": {kk: round(vv, 3) for kk, vv in kern.items()},
+            "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic_from_profiles(dom, "cross_example"),
+                         "flops_per_launch": flops[dom], "avg_launch_us": round(kern[dom], 3)}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -322,7 +415,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2_causal_L2048")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--no-secondary", action="store_true", help="skip the L=64K measurement")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the L=64K and the cross-attention measurements")
+    ap.add_argument("--no-cross", action="store_true", help="skip the cross-attention measurement")
     ap.add_argument("--eager", action="store_true",
                     help="plain launches instead of a HIP graph, no per-kernel timing (for profilers)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -350,6 +445,14 @@ def main() -> int:
                     "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"})
         print(json.dumps(rec), flush=True)
         return 0
+    if args.workload == "cross_example":
+        rec = cross_line(min(args.steps, 400), eager=args.eager)
+        if not args.eager:
+            rec.update({"metric": "cross-attention query tokens/sec (context summary + queries)", "n_gpus": 1,
+                        "steps": min(args.steps, 400), "warmup": 10, "higher_is_better": True,
+                        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"})
+        print(json.dumps(rec), flush=True)
+        return 0
     w = CONFIGS[args.workload]
     if args.eager:
         res = measure(w, args.steps, args.warmup, eager=True)
@@ -375,6 +478,8 @@ def main() -> int:
             sec["cpu_baseline"] = cpu_baseline(w3, max_heads=1)
         sec["steps"] = res3["n_fwd"]
         rec["secondary"] = sec
+    if args.workload == "c2_causal_L2048" and not args.no_secondary and not args.no_cross:
+        rec["cross"] = cross_line(max(20, args.steps // 4))
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -103,7 +103,9 @@ static void make_plan(const dark_prf_desc& d, Plan& p, int mode = kPlanForward) 
     p.NU = cdiv(L, p.span1);
     p.NT2 = p.NU;
   } else {
-    p.NQB = d.d_h <= 64 ? 2 : 1;
+    // two query blocks per wave (d_h <= 64) when that still leaves at least
+    // two workgroups per compute unit
+    p.NQB = (d.d_h <= 64 && (long)p.BH * cdiv(L, 256) >= 512) ? 2 : 1;
     p.tile2 = 128 * p.NQB;
     p.NT2 = cdiv(L, p.tile2);
     int splits = cdiv(512, (long)p.BH * p.NF);
