@@ -408,6 +408,55 @@ def cross_line(steps: int, eager: bool = False) -> dict:
                          "flops_per_launch": flops[dom], "avg_launch_us": round(kern[dom], 3)}}
 
 
+def cross_step_line(steps: int) -> dict:
+    """Cross-attention in generation: 256 sequences x 8 heads, each with a context
+    summary of 1024 tokens (made once, untimed); every step is one query token per
+    sequence against its summary (dark_prf_cross_fwd with L_q = 1)."""
+    import torch
+
+    from random_feature_linear_amd import binding as bd
+    from random_feature_linear_amd.workloads import Workload, make_inputs
+    wk = Workload(name="cross_step", B=256, H=8, L=1024, d_h=64, m=256, r=64, dtype="bf16", causal=False,
+                  seed=1011, mask_kind="tail", max_pad=256)
+    ctx = make_inputs(wk)
+    dt = torch.bfloat16
+    k = torch.from_numpy(ctx["k"]).to(dt).to("cuda:0")
+    v = torch.from_numpy(ctx["v"]).to(dt).to("cuda:0")
+    cmask = torch.from_numpy(ctx["mask"]).to("cuda:0")
+    M = torch.from_numpy(ctx["M"]).to("cuda:0")
+    om = torch.from_numpy(bd.dark_prf_omega(wk.seed, wk.m, wk.r, wk.orthogonal)).to("cuda:0")
+    tag = bd.dark_prf_proj_tag(wk.seed, wk.m, wk.r, wk.orthogonal)
+    S, z = bd.context_state(k, v, M, om, wk.H, context_mask=cmask, proj_tag=tag)
+    del k, v
+    g = torch.Generator(device="cuda:0").manual_seed(wk.seed)
+    tq = torch.randn((steps, wk.B, wk.H, 1, wk.d_h), generator=g, device="cuda:0").to(dt)
+    out = torch.empty_like(tq[0])
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda:0")
+    for t in range(4):
+        bd.cross_attention(tq[t], M, om, S, z, tag, tag, H_kv=wk.H, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for t in range(steps):
+        bd.cross_attention(tq[t], M, om, S, z, tag, tag, H_kv=wk.H, out=out, workspace=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    bd.dark_prf_timing_begin()
+    for t in range(min(steps, 64)):
+        bd.cross_attention(tq[t], M, om, S, z, tag, tag, H_kv=wk.H, out=out, workspace=ws)
+    per = bd.dark_prf_timing_end()
+    avg_us = 1e3 * per["decode"][0] / per["decode"][1]
+    state_bytes = wk.B * wk.H * wk.m * (wk.d_h + 1) * 4   # the summary, read once
+    ach = state_bytes / (avg_us * 1e-6) / 1e9
+    return {"value": round(wk.B / (ms * 1e-3), 1), "ms_per_step": round(ms, 6), "unit": "query tokens/s",
+            "config": {"workload": "cross_step", "N": wk.B, "H": wk.H, "L_q": 1, "L_k": wk.L, "d_h": wk.d_h,
+                       "m": wk.m, "r": wk.r, "steps": steps, "launch": "eager, one launch per step"},
+            "roofline": {"bound": "hbm", "kernel": "decode_kernel (read-only form)", "achieved": round(ach, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                         "traffic": None, "bytes_per_launch": state_bytes, "avg_launch_us": round(avg_us, 3)}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -441,6 +490,13 @@ def main() -> int:
     if args.workload == "c5_decode":
         rec = decode_line(min(args.steps, 512))
         rec.update({"metric": "decode tokens/sec (256 sequences x 8 heads, one token each)",
+                    "n_gpus": 1, "steps": min(args.steps, 512), "warmup": 4, "higher_is_better": True,
+                    "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"})
+        print(json.dumps(rec), flush=True)
+        return 0
+    if args.workload == "cross_step":
+        rec = cross_step_line(min(args.steps, 512))
+        rec.update({"metric": "cross-attention decoder-step query tokens/sec (one token per sequence)",
                     "n_gpus": 1, "steps": min(args.steps, 512), "warmup": 4, "higher_is_better": True,
                     "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"})
         print(json.dumps(rec), flush=True)
@@ -480,6 +536,7 @@ def main() -> int:
         rec["secondary"] = sec
     if args.workload == "c2_causal_L2048" and not args.no_secondary and not args.no_cross:
         rec["cross"] = cross_line(max(20, args.steps // 4))
+        rec["cross_step"] = cross_step_line(256)
     print(json.dumps(rec), flush=True)
     return 0
 

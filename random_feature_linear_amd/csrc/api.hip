@@ -20,7 +20,8 @@ namespace dk {
   dark_status fwd_##dt##_d##dh##_r8(const FwdArgs&, const Plan&, void*, void*);                       \
   dark_status fwd_##dt##_d##dh##_r16(const FwdArgs&, const Plan&, void*, void*);                      \
   dark_status dec_##dt##_d##dh(const dark_prf_desc&, const void*, const void*, const void*,            \
-                               const float*, const float*, float*, float*, void*, void*);
+                               const float*, const float*, float*, float*, void*, const uint8_t*, int,  \
+                               void*);
 DK_DECL(bf16, 16)
 DK_DECL(bf16, 32)
 DK_DECL(bf16, 64)
@@ -476,6 +477,13 @@ dark_status dark_prf_cross_fwd(const dark_prf_desc* desc, const void* q, const f
   if (!q || !M || !omega || !S || !z || !out) return DARK_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(out) || !aligned16(M) || !aligned16(omega)) return DARK_ERR_INVALID_ARG;
   if (!aligned16(S) || !aligned16(z)) return DARK_ERR_INVALID_ARG;
+  if (d.L == 1) {   // one query per sequence (a decoder step): one pass over the fp32 summary
+    decode_launcher fn = find_decode_launcher(d.dtype, d.d_h);
+    if (!fn) return DARK_ERR_UNSUPPORTED;
+    (void)hipGetLastError();
+    return fn(d, q, nullptr, nullptr, M, omega, const_cast<float*>(S), const_cast<float*>(z), out, query_mask, 0,
+              stream);
+  }
   Plan p;
   make_plan(d, p, kPlanCross);
   if (workspace == nullptr || ws_bytes < p.total) return DARK_ERR_WORKSPACE;
@@ -507,7 +515,7 @@ dark_status dark_prf_decode_step(const dark_prf_desc* desc, const void* q, const
   decode_launcher fn = find_decode_launcher(d.dtype, d.d_h);
   if (!fn) return DARK_ERR_UNSUPPORTED;
   (void)hipGetLastError();   // launch errors below are ours, not an earlier caller's
-  return fn(d, q, k, v, M, omega, S, z, out, stream);
+  return fn(d, q, k, v, M, omega, S, z, out, nullptr, 1, stream);
 }
 
 dark_status dark_prf_timing_begin(void) {

@@ -80,9 +80,12 @@ struct KernelTimer {
 typedef dark_status (*fwd_launcher)(const FwdArgs&, const Plan&, void* ws, void* stream);
 fwd_launcher find_fwd_launcher(int dtype, int d_h, int r16);
 
+// update = 1: one decode step (S and z updated in place); update = 0: the
+// read-only cross-attention step (k, v unused; qmask [N] or null).
 typedef dark_status (*decode_launcher)(const dark_prf_desc&, const void* q, const void* k,
                                        const void* v, const float* M, const float* omega,
-                                       float* S, float* z, void* out, void* stream);
+                                       float* S, float* z, void* out, const uint8_t* qmask,
+                                       int update, void* stream);
 decode_launcher find_decode_launcher(int dtype, int d_h);
 
 }  // namespace dk

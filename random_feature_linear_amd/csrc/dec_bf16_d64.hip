@@ -4,7 +4,7 @@
 
 namespace dk {
 dark_status dec_bf16_d64(const dark_prf_desc& d, const void* q, const void* k, const void* v, const float* M,
-                         const float* om, float* S, float* z, void* out, void* s) {
-  return launch_decode_impl<bf16, 64>(d, q, k, v, M, om, S, z, out, s);
+                         const float* om, float* S, float* z, void* out, const uint8_t* qm, int upd, void* s) {
+  return launch_decode_impl<bf16, 64>(d, q, k, v, M, om, S, z, out, qm, upd, s);
 }
 }  // namespace dk

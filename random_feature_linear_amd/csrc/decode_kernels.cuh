@@ -29,6 +29,7 @@ struct DecodeArgs {
   const float* omega;
   float* S;
   float* z;
+  const uint8_t* qmask;   // read-only pass: query mask [N] (nonzero = valid), or null
   int N, H, H_kv, m, r, m_per_head, NS;
 };
 
@@ -49,7 +50,11 @@ __device__ __forceinline__ void st_elem(float* p, int i, float x) { p[i] = x; }
 // Dynamic LDS (dec_lds_bytes): x[3][NS][DH] (q, k, v), u[2 NS][r], nrm[2 NS],
 // ph[2 NS][m], red[NS][256][4], dred[NS][4].
 constexpr int kDecThreads = 256;
-constexpr int kDecVec = 16;   // float4 per thread per sequence and slice
+// float4 per thread per sequence and slice: the update streams the state in
+// one slice of 16 (m = 256, d_h = 64); the read-only form in slices of 8, which
+// leaves fewer registers per wave (measured 28.4 against 33.8 us per step for
+// 256 sequences x 8 heads; 16 is 2% faster for the update)
+template <bool UPD> constexpr int dec_vec() { return UPD ? 16 : 8; }
 
 // LDS carve-up in floats, each array starting on a 16-byte boundary
 __host__ __device__ constexpr int dec_align4(int n) { return (n + 3) & ~3; }
@@ -65,8 +70,13 @@ template <int DH> __device__ __forceinline__ void dec_rows(int tid, int i, int& 
   d0 = (tid % Q4) * 4;
 }
 
-template <typename T, int DH, int NS>
+// UPD = false is the read-only form for cross-attention against a context
+// summary (README section "Cross-attention"): no key or value, S and z are only
+// read, and out = phi(q)^T S / phi(q)^T z (0 for a masked query).
+template <typename T, int DH, int NS, bool UPD>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
+  constexpr int NV = UPD ? 2 : 1;   // feature vectors per sequence: q (and k)
+  constexpr int kDecVec = dec_vec<UPD>();
   extern __shared__ float smem[];
   constexpr int Q4 = DH / 4;
   constexpr int RPS = kDecThreads / Q4;   // rows per slice step
@@ -106,7 +116,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   };
 
   // ---- token rows to LDS (fp32) ----
-  for (int e = tid; e < 3 * NS * DH; e += kDecThreads) {
+  for (int e = tid; e < (UPD ? 3 : 1) * NS * DH; e += kDecThreads) {
     const int which = e / (NS * DH), sq = (e / DH) % NS, d = e % DH;
     float x = 0.f;
     if (sq < ns) {
@@ -119,10 +129,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // ---- u = s M x for q and k of every sequence (vector vi: 2 sq + {0: q, 1: k}) ----
-  for (int p = tid; p < 2 * NS * a.r; p += kDecThreads) {
+  // ---- u = s M x for q and k of every sequence (vector vi: NV sq + {0: q, 1: k}) ----
+  for (int p = tid; p < NV * NS * a.r; p += kDecThreads) {
     const int row = p % a.r, vi = p / a.r;
-    const float* xr = xs + ((vi & 1) * NS + (vi >> 1)) * DH;
+    const float* xr = xs + ((vi % NV) * NS + (vi / NV)) * DH;
     const float* mr = Mh + (long)row * DH;
     float acc = 0.f;
 #pragma unroll 4
@@ -134,7 +144,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
   // |u|^2 / 2 of each vector: one wave per vector, lanes over the rank index
-  for (int vi = wv; vi < 2 * NS; vi += kDecThreads / 64) {
+  for (int vi = wv; vi < NV * NS; vi += kDecThreads / 64) {
     float acc = 0.f;
     for (int i = lane; i < a.r; i += 64) acc += us[vi * a.r + i] * us[vi * a.r + i];
 #pragma unroll
@@ -149,14 +159,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   const float half_log2m = 0.5f * log2f((float)a.m);
   for (int j = tid; j < a.m; j += kDecThreads) {
     const float* om = a.omega + (long)j * a.r;
-    float e[2 * NS];
+    float e[NV * NS];
 #pragma unroll
-    for (int vi = 0; vi < 2 * NS; ++vi) e[vi] = 0.f;
+    for (int vi = 0; vi < NV * NS; ++vi) e[vi] = 0.f;
     if (a.r % 4 == 0) {   // rows of omega are 16-byte aligned
       for (int i = 0; i < a.r; i += 4) {
         const float4 w = *reinterpret_cast<const float4*>(om + i);
 #pragma unroll
-        for (int vi = 0; vi < 2 * NS; ++vi) {
+        for (int vi = 0; vi < NV * NS; ++vi) {
           const float* u = us + vi * a.r + i;
           e[vi] += w.x * u[0] + w.y * u[1] + w.z * u[2] + w.w * u[3];
         }
@@ -165,11 +175,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
       for (int i = 0; i < a.r; ++i) {
         const float w = om[i];
 #pragma unroll
-        for (int vi = 0; vi < 2 * NS; ++vi) e[vi] += w * us[vi * a.r + i];
+        for (int vi = 0; vi < NV * NS; ++vi) e[vi] += w * us[vi * a.r + i];
       }
     }
 #pragma unroll
-    for (int vi = 0; vi < 2 * NS; ++vi)
+    for (int vi = 0; vi < NV * NS; ++vi)
       ph[vi * a.m + j] = exp2f(kLog2eDec * (e[vi] - nrm[vi]) - half_log2m);
   }
   __syncthreads();
@@ -181,11 +191,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     dp[sq] = 0.f;
     if (sq >= ns) continue;
     const long st = (long)(n0 + sq) * a.H + h;
-    const float* pq = ph + (2 * sq) * a.m;
-    const float* pk = ph + (2 * sq + 1) * a.m;
+    const float* pq = ph + (NV * sq) * a.m;
     for (int j = tid; j < a.m; j += kDecThreads) {
-      const float zj = a.z[st * a.m + j] + pk[j];
-      a.z[st * a.m + j] = zj;
+      float zj = a.z[st * a.m + j];
+      if constexpr (UPD) {
+        zj += ph[(NV * sq + 1) * a.m + j];
+        a.z[st * a.m + j] = zj;
+      }
       dp[sq] += pq[j] * zj;
     }
   }
@@ -202,23 +214,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     for (int sq = 0; sq < NS; ++sq) {
       if (sq >= ns) continue;
       float* Sb = a.S + ((long)(n0 + sq) * a.H + h) * (long)a.m * DH;
-      const float* pq = ph + (2 * sq) * a.m;
-      const float* pk = ph + (2 * sq + 1) * a.m;
+      const float* pq = ph + (NV * sq) * a.m;
+      const float* pk = ph + (NV * sq + (UPD ? 1 : 0)) * a.m;
       const float* vv = xs + (2 * NS + sq) * DH;
       int j0, d0;
       dec_rows<DH>(tid, 0, j0, d0);
-      const float4 v4 = *reinterpret_cast<const float4*>(vv + d0);
+      const float4 v4 = UPD ? *reinterpret_cast<const float4*>(vv + d0) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int i = 0; i < kDecVec; ++i) {
         const int j = j0 + i * RPS + sl * nrows_slice;
         if (j >= a.m) break;
-        const float kj = pk[j], qj = pq[j];
+        const float qj = pq[j];
         float4 s4 = sreg[sq][i];
-        s4.x += kj * v4.x;
-        s4.y += kj * v4.y;
-        s4.z += kj * v4.z;
-        s4.w += kj * v4.w;
-        *reinterpret_cast<float4*>(Sb + (long)j * DH + d0) = s4;
+        if constexpr (UPD) {
+          const float kj = pk[j];
+          s4.x += kj * v4.x;
+          s4.y += kj * v4.y;
+          s4.z += kj * v4.z;
+          s4.w += kj * v4.w;
+          *reinterpret_cast<float4*>(Sb + (long)j * DH + d0) = s4;
+        }
         np[sq][0] += qj * s4.x;
         np[sq][1] += qj * s4.y;
         np[sq][2] += qj * s4.z;
@@ -250,7 +265,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
       acc.w += x.w;
     }
     const float dd = dred[sq * 4] + dred[sq * 4 + 1] + dred[sq * 4 + 2] + dred[sq * 4 + 3];
-    const float inv = dd > 0.f ? 1.0f / dd : 0.f;
+    const bool qvalid = a.qmask == nullptr || a.qmask[n0 + sq] != 0;
+    const float inv = (dd > 0.f && qvalid) ? 1.0f / dd : 0.f;
     T* o = reinterpret_cast<T*>(a.out) + (n0 + sq) * a.os[0] + h * a.os[1];
     st_elem(o, 4 * cg, acc.x * inv);
     st_elem(o, 4 * cg + 1, acc.y * inv);
@@ -262,7 +278,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
 template <typename T, int DH>
 dark_status launch_decode_impl(const dark_prf_desc& d, const void* q, const void* k, const void* v,
                                const float* M, const float* omega, float* S, float* z, void* out,
-                               void* stream) {
+                               const uint8_t* qmask, int update, void* stream) {
   DecodeArgs a;
   a.q = q;
   a.k = k;
@@ -276,6 +292,7 @@ dark_status launch_decode_impl(const dark_prf_desc& d, const void* q, const void
   a.omega = omega;
   a.S = S;
   a.z = z;
+  a.qmask = qmask;
   a.N = d.B;
   a.H = d.H;
   a.H_kv = d.H_kv;
@@ -291,10 +308,14 @@ dark_status launch_decode_impl(const dark_prf_desc& d, const void* q, const void
   const int groups = (d.B + NS - 1) / NS;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   KernelTimer tm(kDecode, stream);
-  if (NS == 2)
-    hipLaunchKernelGGL((decode_kernel<T, DH, 2>), dim3(groups * d.H), dim3(kDecThreads), lds(NS), st, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<T, DH, 1>), dim3(groups * d.H), dim3(kDecThreads), lds(NS), st, a);
+  const dim3 grid(groups * d.H), block(kDecThreads);
+  if (update) {
+    if (NS == 2) hipLaunchKernelGGL((decode_kernel<T, DH, 2, true>), grid, block, lds(NS), st, a);
+    else hipLaunchKernelGGL((decode_kernel<T, DH, 1, true>), grid, block, lds(NS), st, a);
+  } else {
+    if (NS == 2) hipLaunchKernelGGL((decode_kernel<T, DH, 2, false>), grid, block, lds(NS), st, a);
+    else hipLaunchKernelGGL((decode_kernel<T, DH, 1, false>), grid, block, lds(NS), st, a);
+  }
   return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
 }
 

@@ -30,6 +30,10 @@ CASES = [
     ("cross_bf16_step",    "bf16", 3, 4, 2,   1,   200,  64,  256, 64,  True,  True,  "tail",   "none"),
     ("cross_bf16_d256",    "bf16", 1, 2, 1,   100, 150,  256, 64,  200, True,  True,  "random", "random"),
     ("cross_bf16_d128_shared", "bf16", 1, 2, 2, 200, 333, 128, 160, 16, False, False, "none",   "tail"),
+    # one query per sequence (a decoder step): the single pass over the fp32 summary,
+    # two sequences per workgroup from 64 sequences on
+    ("cross_step_B80",     "bf16", 80, 4, 2,  1,   300,  64,  256, 64,  True,  True,  "tail",   "random"),
+    ("cross_step_f32_d128", "f32", 66, 2, 1,  1,   90,   128, 96,  100, True,  True,  "random", "random"),
 ]
 
 
