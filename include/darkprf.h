@@ -201,6 +201,31 @@ dark_status dark_prf_cross_fwd(const dark_prf_desc* desc, const void* q, const f
                                uint64_t state_tag, const uint8_t* query_mask, void* out,
                                void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Exact learned-kernel attention (README section "Attention modes": the exact
+ * mode evaluates the learned kernel with exact softmax attention, applying the
+ * geometry to queries and keys before scaled dot-product attention; "auto"
+ * uses it up to a caller-chosen sequence length and the linear mode beyond).
+ * With u = d_h^(-1/4) M_h x for every query and key row:
+ *   out_t = sum_j w_tj v_j / sum_j w_tj,  w_tj = exp(u_t . u_j),
+ * over the keys j that are valid under `mask` and, when desc->causal, j <= t;
+ * a row with no such key is 0.  This is the m -> infinity limit of
+ * dark_prf_fwd on the same inputs.  Computed with a row-maximum shift and
+ * fp32 accumulation; the weights are rounded to the input dtype for the
+ * products with V.  omega and desc->m are not used (m must still be valid).
+ *
+ * dark_prf_exact_workspace_bytes - device workspace dark_prf_exact_fwd needs
+ * (M' and the projected rows of q and k); 0 for an invalid descriptor.
+ *
+ * dark_prf_exact_fwd - arguments as for dark_prf_fwd (q, k, v, M, mask, out,
+ * strides and GQA head map); workspace of at least
+ * dark_prf_exact_workspace_bytes(desc).
+ */
+size_t dark_prf_exact_workspace_bytes(const dark_prf_desc* desc);
+dark_status dark_prf_exact_fwd(const dark_prf_desc* desc, const void* q, const void* k,
+                               const void* v, const float* M, const uint8_t* mask, void* out,
+                               void* workspace, size_t ws_bytes, void* stream);
+
 /* dark_prf_status_str - a static, human-readable name of a status. */
 const char* dark_prf_status_str(dark_status status);
 

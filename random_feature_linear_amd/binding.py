@@ -78,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.dark_prf_cross_fwd.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, ctypes.c_uint64,
                                          P, P, P, ctypes.c_size_t, P]
         L.dark_prf_cross_fwd.restype = ctypes.c_int
+        L.dark_prf_exact_workspace_bytes.argtypes = [ctypes.POINTER(DarkPrfDesc)]
+        L.dark_prf_exact_workspace_bytes.restype = ctypes.c_size_t
+        L.dark_prf_exact_fwd.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.dark_prf_exact_fwd.restype = ctypes.c_int
         L.dark_prf_status_str.argtypes = [ctypes.c_int]
         L.dark_prf_status_str.restype = ctypes.c_char_p
         L.dark_prf_timing_begin.argtypes = []
@@ -135,6 +139,16 @@ def dark_prf_cross_fwd(desc: DarkPrfDesc, q: int, M: int, omega: int, S: int, z:
                                     S or None, z or None, ctypes.c_uint64(state_tag),
                                     query_mask or None, out or None, workspace or None, ws_bytes,
                                     stream or None)
+
+
+def dark_prf_exact_workspace_bytes(desc: DarkPrfDesc) -> int:
+    return int(lib().dark_prf_exact_workspace_bytes(ctypes.byref(desc)))
+
+
+def dark_prf_exact_fwd(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, mask: int, out: int,
+                       workspace: int, ws_bytes: int, stream: int) -> int:
+    return lib().dark_prf_exact_fwd(ctypes.byref(desc), q or None, k or None, v or None, M or None,
+                                    mask or None, out or None, workspace or None, ws_bytes, stream or None)
 
 
 def dark_prf_decode_step(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, omega: int, S: int,
@@ -315,4 +329,32 @@ def cross_attention(q, M, omega, S, z, state_tag: int, proj_tag: int, query_mask
                             workspace.data_ptr(), workspace.numel(), stream)
     if st != DARK_OK:
         raise DarkPrfError(st, "dark_prf_cross_fwd")
+    return out
+
+
+def exact_attention(q, k, v, M, mask=None, causal: bool = False, out=None, workspace=None):
+    """dark_prf_exact_fwd: softmax attention on u = d_h^(-1/4) M_h x for q and k."""
+    import torch
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    B, H, L, d_h = q.shape
+    d = DarkPrfDesc()
+    d.B, d.H, d.H_kv, d.L, d.d_h = B, H, k.shape[1], L, d_h
+    d.m, d.r = 16, M.shape[-2]          # m is not used by the exact path
+    d.dtype = _dtype_code(q)
+    d.causal = int(bool(causal))
+    d.m_per_head = int(M.dim() == 3)
+    for name, t in (("q_str", q), ("k_str", k), ("v_str", v), ("o_str", out)):
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name}: the last dimension must be contiguous")
+        getattr(d, name)[:] = list(t.stride()[:3])
+    nbytes = dark_prf_exact_workspace_bytes(d)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = dark_prf_exact_fwd(d, q.data_ptr(), k.data_ptr(), v.data_ptr(), M.data_ptr(),
+                            _mask_ptr(mask, "mask"), out.data_ptr(), workspace.data_ptr(),
+                            workspace.numel(), stream)
+    if st != DARK_OK:
+        raise DarkPrfError(st, "dark_prf_exact_fwd")
     return out

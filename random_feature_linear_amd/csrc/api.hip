@@ -19,6 +19,11 @@ namespace dk {
   dark_status fwd_##dt##_d##dh##_r4(const FwdArgs&, const Plan&, void*, void*);                       \
   dark_status fwd_##dt##_d##dh##_r8(const FwdArgs&, const Plan&, void*, void*);                       \
   dark_status fwd_##dt##_d##dh##_r16(const FwdArgs&, const Plan&, void*, void*);                      \
+  dark_status exact_##dt##_d##dh##_r1(const FwdArgs&, void*, void*);                                  \
+  dark_status exact_##dt##_d##dh##_r2(const FwdArgs&, void*, void*);                                  \
+  dark_status exact_##dt##_d##dh##_r4(const FwdArgs&, void*, void*);                                  \
+  dark_status exact_##dt##_d##dh##_r8(const FwdArgs&, void*, void*);                                  \
+  dark_status exact_##dt##_d##dh##_r16(const FwdArgs&, void*, void*);                                 \
   dark_status dec_##dt##_d##dh(const dark_prf_desc&, const void*, const void*, const void*,            \
                                const float*, const float*, float*, float*, void*, const uint8_t*, int,  \
                                void*);
@@ -60,6 +65,17 @@ static const fwd_launcher kFwd[2][5][5] = {
     {DK_ROW(f32, 16), DK_ROW(f32, 32), DK_ROW(f32, 64), DK_ROW(f32, 128), DK_ROW(f32, 256)},
     {DK_ROW(bf16, 16), DK_ROW(bf16, 32), DK_ROW(bf16, 64), DK_ROW(bf16, 128), DK_ROW(bf16, 256)}};
 #undef DK_ROW
+typedef dark_status (*exact_launcher)(const FwdArgs&, void* ws, void* stream);
+#define DK_XROW(dt, dh) {exact_##dt##_d##dh##_r1, exact_##dt##_d##dh##_r2, exact_##dt##_d##dh##_r4, exact_##dt##_d##dh##_r8, exact_##dt##_d##dh##_r16}
+static const exact_launcher kExact[2][5][5] = {
+    {DK_XROW(f32, 16), DK_XROW(f32, 32), DK_XROW(f32, 64), DK_XROW(f32, 128), DK_XROW(f32, 256)},
+    {DK_XROW(bf16, 16), DK_XROW(bf16, 32), DK_XROW(bf16, 64), DK_XROW(bf16, 128), DK_XROW(bf16, 256)}};
+#undef DK_XROW
+static exact_launcher find_exact_launcher(int dtype, int d_h, int r16) {
+  const int i = dh_index(d_h), j = r16_index(r16);
+  if (dtype < 0 || dtype > 1 || i < 0 || j < 0) return nullptr;
+  return kExact[dtype][i][j];
+}
 static const decode_launcher kDec[2][5] = {
     {dec_f32_d16, dec_f32_d32, dec_f32_d64, dec_f32_d128, dec_f32_d256},
     {dec_bf16_d16, dec_bf16_d32, dec_bf16_d64, dec_bf16_d128, dec_bf16_d256}};
@@ -500,6 +516,37 @@ dark_status dark_prf_cross_fwd(const dark_prf_desc* desc, const void* q, const f
   a.S_in = S;
   a.z_in = z;
   return fn(a, p, workspace, stream);
+}
+
+size_t dark_prf_exact_workspace_bytes(const dark_prf_desc* desc) {
+  if (check_desc(desc, false, 1 | 2 | 4 | 8) != DARK_OK) return 0;
+  const dark_prf_desc& d = *desc;
+  return exact_layout(d.B, d.H, d.L > 0 ? d.L : 1, d.d_h, rank_blocks(d.r), d.m_per_head ? d.H : 1,
+                      d.dtype == DARK_BF16 ? 2 : 4).total;
+}
+
+dark_status dark_prf_exact_fwd(const dark_prf_desc* desc, const void* q, const void* k, const void* v,
+                               const float* M, const uint8_t* mask, void* out, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  dark_status st = check_desc(desc, false, 1 | 2 | 4 | 8);
+  if (st != DARK_OK) return st;
+  const dark_prf_desc& d = *desc;
+  if (d.B == 0 || d.L == 0) return DARK_OK;
+  if (!q || !k || !v || !M || !out) return DARK_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(M)) return DARK_ERR_INVALID_ARG;
+  if (workspace == nullptr || ws_bytes < dark_prf_exact_workspace_bytes(desc)) return DARK_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DARK_ERR_INVALID_ARG;
+  exact_launcher fn = find_exact_launcher(d.dtype, d.d_h, rank_blocks(d.r));
+  if (!fn) return DARK_ERR_UNSUPPORTED;
+  (void)hipGetLastError();   // launch errors below are ours, not an earlier caller's
+  FwdArgs a = fwd_args(d);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.mask = mask;
+  a.M = M;
+  return fn(a, workspace, stream);
 }
 
 dark_status dark_prf_decode_step(const dark_prf_desc* desc, const void* q, const void* k, const void* v,

@@ -63,6 +63,26 @@ struct Plan {
   int elem;    // bytes per element of q/k/v (2 or 4)
 };
 
+// Workspace of the exact-attention path: the M' fragments, then the projected
+// rows of q and k (hi/lo operand fragments, 32-token blocks).
+struct ExactLayout {
+  size_t off_mfrag, off_ufrag, total;
+  int NBLK;   // 32-token blocks per sequence
+};
+inline ExactLayout exact_layout(int B, int H, int L, int d_h, int R16, int HM, int elem) {
+  ExactLayout e;
+  const int NM = elem == 2 ? 2 : 1;
+  const size_t frag = 64 * 8;
+  e.NBLK = (L + 31) / 32;
+  e.off_mfrag = 0;
+  size_t off = (size_t)HM * ((R16 + 1) / 2) * (d_h / 16) * NM * frag * elem;
+  off = (off + 255) & ~(size_t)255;
+  e.off_ufrag = off;
+  off += (size_t)2 * B * H * e.NBLK * R16 * NM * frag * elem;
+  e.total = (off + 255) & ~(size_t)255;
+  return e;
+}
+
 // Optional per-kernel timing (dark_prf_timing_begin / _end): records a HIP
 // event pair on `stream` around one launch while timing is on.
 enum KernelKind { kPrep = 0, kKState = 1, kScan = 2, kQOut = 3, kDecode = 4, kShift = 5 };

@@ -5,4 +5,7 @@ namespace dk {
 dark_status fwd_bf16_d256_r16(const FwdArgs& a, const Plan& p, void* ws, void* s) {
   return launch_fwd_impl<bf16, 256, 16, 1>(a, p, ws, s);
 }
+dark_status exact_bf16_d256_r16(const FwdArgs& a, void* ws, void* s) {
+  return launch_exact_impl<bf16, 256, 16>(a, ws, s);
+}
 }  // namespace dk

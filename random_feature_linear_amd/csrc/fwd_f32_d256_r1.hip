@@ -5,4 +5,7 @@ namespace dk {
 dark_status fwd_f32_d256_r1(const FwdArgs& a, const Plan& p, void* ws, void* s) {
   return launch_fwd_impl<float, 256, 1, 1>(a, p, ws, s);
 }
+dark_status exact_f32_d256_r1(const FwdArgs& a, void* ws, void* s) {
+  return launch_exact_impl<float, 256, 1>(a, ws, s);
+}
 }  // namespace dk

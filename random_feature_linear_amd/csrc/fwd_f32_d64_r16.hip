@@ -5,4 +5,7 @@ namespace dk {
 dark_status fwd_f32_d64_r16(const FwdArgs& a, const Plan& p, void* ws, void* s) {
   return launch_fwd_impl<float, 64, 16, 2>(a, p, ws, s);
 }
+dark_status exact_f32_d64_r16(const FwdArgs& a, void* ws, void* s) {
+  return launch_exact_impl<float, 64, 16>(a, ws, s);
+}
 }  // namespace dk

@@ -1765,4 +1765,234 @@ dark_status launch_fwd_impl(const FwdArgs& a, const Plan& pl, void* ws, void* st
                          : launch_fwd_pad<T, DH, R16, FBW, false>(a, pl, ws, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Exact learned-kernel attention (README section "Attention modes": the exact
+// path applies the learned geometry to q and k and then runs softmax
+// attention):  out_t = sum_j softmax_j(u_t . u_j) v_j over the visible valid
+// keys j, with u = d_h^(-1/4) M_h x for queries and keys alike.
+//
+// Workspace: the M' fragments, then ufrag[tensor][b h][32-token block][R16]
+// [part][lane][8]: the hi/lo operand fragments of u for q (tensor 0) and for k
+// as seen by query head h (tensor 1), in the order project_block leaves them
+// (the same for both, so the score sum runs over the same rank permutation).
+// ---------------------------------------------------------------------------
+// M' = d_h^(-1/4) M in fragment order (the projection operand).
+template <typename T>
+__global__ void mfrag_kernel(const float* __restrict__ M, T* __restrict__ mfrag, long n, int r, int d_h, int R16,
+                             float s) {
+  for (long idx = blockIdx.x * (long)blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x)
+    mfrag_lane<T>(idx, M, mfrag, r, d_h, R16, s);
+}
+
+// u of every 32-token block of q and of k (one wave per block).
+template <typename T, int DH, int R16>
+__global__ __launch_bounds__(kThreads) void exact_proj_kernel(FwdArgs a, const T* __restrict__ mfrag,
+                                                               T* __restrict__ ufrag, int NBLK) {
+  typedef typename FragOf<T>::type F;
+  constexpr int KD = DH / 16;
+  constexpr int NM = kParts<T>;
+  constexpr int R32 = (R16 + 1) / 2;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, g = lane >> 5;
+  const int BH = a.B * a.H;
+  const int per = (NBLK + kWaves - 1) / kWaves;
+  const int tensor = blockIdx.x / (BH * per);   // 0: queries, 1: keys
+  const int rem = blockIdx.x % (BH * per);
+  const int bh = rem / per, blk = (rem % per) * kWaves + w;
+  if (blk >= NBLK) return;
+  const int b = bh / a.H, h = bh % a.H, hk = (h * a.H_kv) / a.H;
+  const T* base = tensor == 0 ? reinterpret_cast<const T*>(a.q) + b * a.qs[0] + h * a.qs[1]
+                              : reinterpret_cast<const T*>(a.k) + b * a.ks[0] + hk * a.ks[1];
+  const int64_t stride = tensor == 0 ? a.qs[2] : a.ks[2];
+  const int t = blk * 32 + c;
+  F xf[KD];
+  load_rows<T, DH>(xf, base + (long)t * stride, t < a.L, g);
+  const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * R32 * KD * NM * 64 * 8;
+  F uhi[R16], ulo[R16];
+  (void)project_block<T, DH, R16>(uhi, ulo, xf, mf, lane, 0.f);
+  T* dst = ufrag + (((long)tensor * BH + bh) * NBLK + blk) * R16 * NM * 64 * 8;
+#pragma unroll
+  for (int kr = 0; kr < R16; ++kr) {
+    st8(dst + ((kr * NM) * 64 + lane) * 8, uhi[kr]);
+    if constexpr (NM == 2) st8(dst + ((kr * NM + 1) * 64 + lane) * 8, ulo[kr]);
+  }
+}
+
+// Softmax attention on the projected rows.  Workgroup: 128 queries of one (b,
+// h), wave w owning the 32-query block 4 tile + w; the keys go by in tiles of
+// 128 (V staged transposed in LDS, with an additive 0 / -inf key bias from the
+// mask and the sequence end).  Pass 1 finds each query's score maximum over
+// its visible keys; pass 2 forms p = exp(s - max) rounded to the operand type,
+// the row sums of the rounded weights and the products p V.  Scores are
+// computed in transposed form (rows = keys, columns = queries), so a lane holds
+// one query and its maximum and sum need no cross-lane reduction but one
+// exchange between the two lane halves.
+template <typename T, int DH, int R16, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __restrict__ ufrag, int NBLK) {
+  typedef typename FragOf<T>::type F;
+  constexpr int NM = kParts<T>;
+  constexpr int DB = vblocks<DH>();
+  constexpr int TT = kTile;
+  constexpr int VST = TT + 8;
+  constexpr int VPT = vloads_per_thread<DH, TT>();
+  constexpr int UFR = R16 * NM * 64 * 8;   // elements of one block's u fragments
+  __shared__ __attribute__((aligned(16))) T s_vt[DH * VST];
+  __shared__ __attribute__((aligned(16))) float s_bias[TT];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
+  const int NT = (a.L + TT - 1) / TT;
+  const int lb = xcd_block();
+  const int tile = CAUSAL ? NT - 1 - lb % NT : lb % NT;   // causal: the longest tiles first
+  const int bh = lb / NT;
+  const int b = bh / a.H, h = bh % a.H, hk = (h * a.H_kv) / a.H;
+  const int BH = a.B * a.H;
+  const int qb = tile * kWaves + w;                     // this wave's query block
+  const T* uq = ufrag + ((long)bh * NBLK + min(qb, NBLK - 1)) * UFR;
+  const T* uk0 = ufrag + ((long)BH + bh) * NBLK * UFR;
+  const uint8_t* mrow = a.mask ? a.mask + (long)b * a.L : nullptr;
+  const T* vbase = reinterpret_cast<const T*>(a.v) + b * a.vs[0] + hk * a.vs[1];
+  // ranks up to 64: the query block's u fragments stay in registers; above,
+  // both operands of the score products stream from memory (L1)
+  constexpr bool QREG = R16 <= 4;
+  F qh[QREG ? R16 : 1], ql[QREG ? R16 : 1];
+  if constexpr (QREG) {
+#pragma unroll
+    for (int kr = 0; kr < R16; ++kr) {
+      qh[kr] = ld8(uq + ((kr * NM) * 64 + lane) * 8);
+      ql[kr] = ld8(uq + ((kr * NM + NM - 1) * 64 + lane) * 8);
+    }
+  }
+  const int tiles = CAUSAL ? tile + 1 : NT;             // key tiles the workgroup visits
+  // last key block this wave uses (a block past the sequence end holds no query
+  // that is stored; it still reads only blocks of this sequence)
+  const int kb_last = min(CAUSAL ? qb : NBLK - 1, NBLK - 1);
+  // scores of key block kb (rows = keys, columns = queries), biased and masked
+  auto scores = [&](int kb, int kbl) -> f32x16 {
+    const T* uk = uk0 + (long)kb * UFR;
+    f32x16 s;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {   // rows 8 jj + 4g .. 8 jj + 4g + 3 are contiguous
+      const float4 x = *reinterpret_cast<const float4*>(&s_bias[32 * kbl + 8 * jj + 4 * g]);
+      s[4 * jj] = x.x;
+      s[4 * jj + 1] = x.y;
+      s[4 * jj + 2] = x.z;
+      s[4 * jj + 3] = x.w;
+    }
+    auto kload = [&](int k, int part) -> F { return ld8(uk + ((k * NM + (part ? NM - 1 : 0)) * 64 + lane) * 8); };
+    if constexpr (QREG) {
+      F kh[R16], kl[R16];
+#pragma unroll
+      for (int kr = 0; kr < R16; ++kr) {
+        kh[kr] = kload(kr, 0);
+        kl[kr] = kload(kr, 1);
+      }
+      s = exponent<T, R16, true, true>(kh, kl, qh, ql, s);
+    } else {
+      auto qload = [&](int k, int part) -> F { return ld8(uq + ((k * NM + (part ? NM - 1 : 0)) * 64 + lane) * 8); };
+      s = exponent_stream<T, R16, true, true>(kload, qload, s);
+    }
+    if (CAUSAL && kb == qb) {   // the diagonal block: key crow(i, g) visible to query c iff crow <= c
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (crow(i, g) > c) s[i] = -INFINITY;
+    }
+    return s;
+  };
+  auto put_bias = [&](int t0) {
+    if (tid < TT) {
+      const int j = t0 + tid;
+      s_bias[tid] = (j < a.L && (mrow == nullptr || mrow[j] != 0)) ? 0.f : -INFINITY;
+    }
+  };
+  // ---- pass 1: the score maximum of each query ----
+  float mx = -INFINITY;
+  for (int kt = 0; kt < tiles; ++kt) {
+    put_bias(kt * TT);
+    __syncthreads();
+#pragma unroll 1
+    for (int kbl = 0; kbl < kWaves; ++kbl) {
+      const int kb = kt * kWaves + kbl;
+      if (kb > kb_last) break;
+      const f32x16 s = scores(kb, kbl);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    }
+    __syncthreads();
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mL = mx == -INFINITY ? 0.f : mx * kLog2e;   // no visible key: every weight is 0
+  // ---- pass 2: weights, their sums and the products with V ----
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = zero16();
+  float den = 0.f;
+  F vr[VPT];
+  load_v<T, DH, TT>(vr, vbase, a.vs[2], 0, a.L, tid);
+  for (int kt = 0; kt < tiles; ++kt) {
+    store_vt<T, DH, TT, VST>(s_vt, vr, tid);
+    put_bias(kt * TT);
+    __syncthreads();
+    if (kt + 1 < tiles) load_v<T, DH, TT>(vr, vbase, a.vs[2], (kt + 1) * TT, a.L, tid);
+#pragma unroll 1
+    for (int kbl = 0; kbl < kWaves; ++kbl) {
+      const int kb = kt * kWaves + kbl;
+      if (kb > kb_last) break;
+      f32x16 s = scores(kb, kbl);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = fast_exp2(s[i] * kLog2e - mL);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const F pf = acc_frag<F>(s, k);
+        den = frag_sum(pf, den);   // the rounded weights the products use
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = mma(pf, v_frag<T, DH, VST>(s_vt, db, 32 * kbl, k, c, g), acc[db]);
+      }
+    }
+    __syncthreads();
+  }
+  // ---- out = (p V) / sum p; lanes c and c + 32 hold the two halves of the sum ----
+  T* obase = reinterpret_cast<T*>(a.out) + b * a.os[0] + h * a.os[1];
+  const float dq = den + __shfl_xor(den, 32);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float dd = __shfl(dq, crow(i, g));
+    const int t = qb * 32 + crow(i, g);
+    const float inv = dd > 0.f ? __builtin_amdgcn_rcpf(dd) : 0.f;
+    if (t < a.L) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = db * 32 + c;
+        if (d < DH) store_out(obase + (long)t * a.os[2] + d, acc[db][i] * inv);
+      }
+    }
+  }
+}
+
+template <typename T, int DH, int R16>
+dark_status launch_exact_impl(const FwdArgs& a, void* ws, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int HM = a.m_per_head ? a.H : 1;
+  const ExactLayout lay = exact_layout(a.B, a.H, a.L, DH, R16, HM, (int)sizeof(T));
+  char* base = reinterpret_cast<char*>(ws);
+  T* mfrag = reinterpret_cast<T*>(base + lay.off_mfrag);
+  T* ufrag = reinterpret_cast<T*>(base + lay.off_ufrag);
+  const long nM = (long)HM * ((R16 + 1) / 2) * (DH / 16) * kParts<T> * 64;
+  {
+    KernelTimer tm(kPrep, stream);
+    hipLaunchKernelGGL(mfrag_kernel<T>, dim3((int)((nM + 255) / 256)), dim3(256), 0, st, a.M, mfrag, nM, a.r, DH,
+                       R16, powf((float)DH, -0.25f));
+  }
+  {
+    KernelTimer tm(kShift, stream);
+    const int per = (lay.NBLK + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL((exact_proj_kernel<T, DH, R16>), dim3(2 * a.B * a.H * per), dim3(kThreads), 0, st, a, mfrag,
+                       ufrag, lay.NBLK);
+  }
+  KernelTimer tm(kQOut, stream);
+  const dim3 grid(a.B * a.H * ((a.L + kTile - 1) / kTile));
+  if (a.causal)
+    hipLaunchKernelGGL((exact_kernel<T, DH, R16, true>), grid, dim3(kThreads), 0, st, a, ufrag, lay.NBLK);
+  else
+    hipLaunchKernelGGL((exact_kernel<T, DH, R16, false>), grid, dim3(kThreads), 0, st, a, ufrag, lay.NBLK);
+  return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
+}
+
 }  // namespace dk

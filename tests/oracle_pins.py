@@ -282,6 +282,16 @@ def check_exact_vs_sdpa(seed=31):
             torch.from_numpy(uq), torch.from_numpy(uk), torch.from_numpy(v),
             attn_mask=torch.from_numpy(vis), scale=1.0).numpy()
         _close(O, ref, 1e-12, f"exact vs SDPA causal={causal}")
+    # grouped K/V heads: query head h reads K/V head h * H_kv / H
+    q, k, v, M, _ = _random_case(rng, B=1, H=4, H_kv=2, Lq=L, d=d, r=r)
+    O = po.exact_kernel_attention(q, k, v, M, causal=True)
+    for h in range(4):
+        g = h // 2
+        uq, uk = _u(q[0, h], M[h], d), _u(k[0, g], M[h], d)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(uq)[None], torch.from_numpy(uk)[None], torch.from_numpy(v[0, g])[None],
+            is_causal=True, scale=1.0).numpy()[0]
+        _close(O[0, h], ref, 1e-12, f"exact vs SDPA, GQA head {h}")
 
 
 # ----------------------------------------------------------------------------

@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     L = bd.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -145,6 +145,21 @@ def test_cross_fwd_argument_checks():
     # the key and value strides are not used by this call
     e = _desc(causal=0, L=100, k_str=[0, 0, 0], v_str=[0, 0, 0])
     assert _cross(e, nb=0) == bd.DARK_ERR_WORKSPACE
+
+
+def test_exact_argument_checks():
+    d = _desc(causal=1)
+    nb = bd.dark_prf_exact_workspace_bytes(d)
+    assert nb > 0
+    call = lambda q=FAKE, ws=FAKE, n=nb, dd=d: bd.dark_prf_exact_fwd(dd, q, FAKE, FAKE, FAKE, 0, FAKE, ws, n, 0)
+    assert call(q=0) == bd.DARK_ERR_INVALID_ARG
+    assert call(q=FAKE + 2) == bd.DARK_ERR_INVALID_ARG
+    assert call(n=nb - 1) == bd.DARK_ERR_WORKSPACE
+    assert call(ws=0) == bd.DARK_ERR_WORKSPACE
+    assert call(dd=_desc(B=0), ws=0, n=0) == bd.DARK_OK
+    assert bd.dark_prf_exact_workspace_bytes(_desc(d_h=48)) == 0
+    # more tokens never need less workspace
+    assert bd.dark_prf_exact_workspace_bytes(_desc(L=4096)) >= nb
 
 
 def test_status_strings():
