@@ -457,6 +457,77 @@ def cross_step_line(steps: int) -> dict:
                          "traffic": None, "bytes_per_launch": state_bytes, "avg_launch_us": round(avg_us, 3)}}
 
 
+def exact_line(w, steps: int) -> dict:
+    """The exact learned-kernel path (dark_prf_exact_fwd) on a workload's inputs,
+    timed like the linear forward (one HIP graph over rotating input copies).
+    Algorithmic flops: 2 r (score) + 2 d_h (weighted sum) per visible
+    (query, key) pair; the projections 2 r d_h per row of q and k."""
+    import torch
+
+    from random_feature_linear_amd import binding as bd
+    from random_feature_linear_amd.workloads import make_inputs
+    inp = make_inputs(w)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+    copies = max(2, min(32, -(-(MALL_BYTES + (64 << 20)) // io_bytes(w))))
+    base = {n: torch.from_numpy(inp[n]).to(dt).to("cuda:0") for n in ("q", "k", "v")}
+    M = torch.from_numpy(inp["M"]).to("cuda:0")
+    mask = torch.from_numpy(inp["mask"]).to("cuda:0") if inp["mask"] is not None else None
+    sets = [{n: base[n].clone() for n in base} for _ in range(copies)]
+    outs = [torch.empty_like(base["q"]) for _ in range(copies)]
+    c0 = sets[0]
+    d = bd.make_desc(c0["q"], c0["k"], c0["v"], outs[0], M, torch.empty((16, w.r)), w.causal, 0)
+    nb = bd.dark_prf_exact_workspace_bytes(d)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    mptr = mask.data_ptr() if mask is not None else 0
+
+    def step(i):
+        c, o = sets[i % copies], outs[i % copies]
+        st = bd.dark_prf_exact_fwd(d, c["q"].data_ptr(), c["k"].data_ptr(), c["v"].data_ptr(), M.data_ptr(), mptr,
+                                   o.data_ptr(), ws.data_ptr(), nb, torch.cuda.current_stream().cuda_stream)
+        if st != bd.DARK_OK:
+            raise bd.DarkPrfError(st, "dark_prf_exact_fwd")
+
+    for i in range(10):
+        step(i)
+    torch.cuda.synchronize()
+    sm = torch.cuda.Stream()
+    sm.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(sm):
+        with torch.cuda.graph(g, stream=sm):
+            for i in range(steps):
+                step(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del g
+    bd.dark_prf_timing_begin()
+    for i in range(steps):
+        step(i)
+    per = bd.dark_prf_timing_end()
+    torch.cuda.synchronize()
+    kern = {{"prep": "mfrag", "shift": "project", "qout": "attention"}.get(kk, kk): 1e3 * vv[0] / vv[1]
+            for kk, vv in per.items() if vv[1] > 0}
+    pairs = w.L * (w.L + 1) // 2 if w.causal else w.L * w.L
+    flops = w.B * w.H * pairs * 2 * (w.r + w.d_h)
+    ach = flops / (kern["attention"] * 1e-6) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    return {"value": round(w.B * w.L / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 6),
+            "config": {"workload": w.name, "path": "exact (dark_prf_exact_fwd)", "B": w.B, "H": w.H,
+                       "H_kv": w.hkv, "L": w.L, "d_h": w.d_h, "r": w.r, "causal": w.causal,
+                       "launch": "one hipGraph of %d forwards over %d rotating input copies" % (steps, copies)},
+            "kernels_us": {kk: round(vv, 3) for kk, vv in kern.items()},
+            "roofline": {"bound": "mfma", "kernel": "attention", "achieved": round(ach, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                         "flops_per_launch": flops, "avg_launch_us": round(kern["attention"], 3)}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -509,6 +580,14 @@ def main() -> int:
                         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"})
         print(json.dumps(rec), flush=True)
         return 0
+    if args.workload.startswith("exact:"):   # the exact path on one of the workloads' inputs
+        we = CONFIGS[args.workload.split(":", 1)[1]]
+        rec = exact_line(we, min(args.steps, 200))
+        rec.update({"metric": "exact-path fwd tokens/sec", "n_gpus": 1, "steps": min(args.steps, 200),
+                    "warmup": 10, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                    "dtype": we.dtype, "data": "synthetic"})
+        print(json.dumps(rec), flush=True)
+        return 0
     w = CONFIGS[args.workload]
     if args.eager:
         res = measure(w, args.steps, args.warmup, eager=True)
@@ -537,6 +616,7 @@ def main() -> int:
     if args.workload == "c2_causal_L2048" and not args.no_secondary and not args.no_cross:
         rec["cross"] = cross_line(max(20, args.steps // 4))
         rec["cross_step"] = cross_step_line(256)
+        rec["exact"] = exact_line(w, max(20, args.steps // 4))
     print(json.dumps(rec), flush=True)
     return 0
 

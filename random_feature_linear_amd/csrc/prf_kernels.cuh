@@ -1835,8 +1835,14 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
   constexpr int VST = TT + 8;
   constexpr int VPT = vloads_per_thread<DH, TT>();
   constexpr int UFR = R16 * NM * 64 * 8;   // elements of one block's u fragments
+  // ranks up to 64: a key tile's u fragments are staged in LDS beside V^T (the
+  // next tile's fetched into registers during the current one); above, every
+  // wave reads them from L2
+  constexpr bool KLDS = R16 <= 4 && (size_t)(DH * VST + kWaves * UFR) * sizeof(T) + TT * 4 <= 160 * 1024;
+  constexpr int KCH = KLDS ? kWaves * UFR / 8 / kThreads : 1;   // 16-byte pieces per thread and tile
   __shared__ __attribute__((aligned(16))) T s_vt[DH * VST];
   __shared__ __attribute__((aligned(16))) float s_bias[TT];
+  __shared__ __attribute__((aligned(16))) T s_uk[KLDS ? kWaves * UFR : 8];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
   const int NT = (a.L + TT - 1) / TT;
   const int lb = xcd_block();
@@ -1864,9 +1870,29 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
   // last key block this wave uses (a block past the sequence end holds no query
   // that is stored; it still reads only blocks of this sequence)
   const int kb_last = min(CAUSAL ? qb : NBLK - 1, NBLK - 1);
+  // the u fragments of key tile kt: registers, then LDS (blocks past the
+  // sequence end are read clamped and never used)
+  F kreg[KCH];
+  auto fetch_k = [&](int kt) {
+    if constexpr (KLDS) {
+#pragma unroll
+      for (int p = 0; p < KCH; ++p) {
+        const int e = tid + p * kThreads;                 // 16-byte piece of the tile
+        const int kbl = e / (UFR / 8), within = e % (UFR / 8);
+        const int kb = min(kt * kWaves + kbl, NBLK - 1);
+        kreg[p] = ld8(uk0 + (long)kb * UFR + within * 8);
+      }
+    }
+  };
+  auto put_k = [&]() {
+    if constexpr (KLDS) {
+#pragma unroll
+      for (int p = 0; p < KCH; ++p) st8(s_uk + (tid + p * kThreads) * 8, kreg[p]);
+    }
+  };
   // scores of key block kb (rows = keys, columns = queries), biased and masked
   auto scores = [&](int kb, int kbl) -> f32x16 {
-    const T* uk = uk0 + (long)kb * UFR;
+    const T* uk = KLDS ? s_uk + kbl * UFR : uk0 + (long)kb * UFR;
     f32x16 s;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {   // rows 8 jj + 4g .. 8 jj + 4g + 3 are contiguous
@@ -1904,9 +1930,12 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
   };
   // ---- pass 1: the score maximum of each query ----
   float mx = -INFINITY;
+  fetch_k(0);
   for (int kt = 0; kt < tiles; ++kt) {
     put_bias(kt * TT);
+    put_k();
     __syncthreads();
+    fetch_k(kt + 1 < tiles ? kt + 1 : 0);   // pass 2 starts again at tile 0
 #pragma unroll 1
     for (int kbl = 0; kbl < kWaves; ++kbl) {
       const int kb = kt * kWaves + kbl;
@@ -1929,8 +1958,12 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
   for (int kt = 0; kt < tiles; ++kt) {
     store_vt<T, DH, TT, VST>(s_vt, vr, tid);
     put_bias(kt * TT);
+    put_k();
     __syncthreads();
-    if (kt + 1 < tiles) load_v<T, DH, TT>(vr, vbase, a.vs[2], (kt + 1) * TT, a.L, tid);
+    if (kt + 1 < tiles) {
+      load_v<T, DH, TT>(vr, vbase, a.vs[2], (kt + 1) * TT, a.L, tid);
+      fetch_k(kt + 1);
+    }
 #pragma unroll 1
     for (int kbl = 0; kbl < kWaves; ++kbl) {
       const int kb = kt * kWaves + kbl;
