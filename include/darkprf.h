@@ -94,6 +94,25 @@ dark_status dark_prf_omega(uint64_t seed, int32_t m, int32_t r, int32_t orthogon
                            float* omega_host);
 
 /*
+ * dark_prf_omega_device - the same projection as dark_prf_omega, generated on
+ * the device into omega [m][r] (fp32, row-major, device memory) on `stream`
+ * (README section "Projection lifecycle": a redraw replaces the projection;
+ * with this call it stays on the device).  The same stream and construction
+ * as dark_prf_omega; the fp64 arithmetic runs in a different order, so results
+ * agree with the host's to within an ulp of fp32 or two, not bit for bit.
+ * Orthogonal blocks use one workgroup each (fp64 Householder QR in the
+ * workspace).  1 <= r <= 256.
+ *   dark_prf_omega_device_workspace_bytes: device workspace needed (0 for
+ *     i.i.d. entries, and for invalid m or r).
+ * Returns DARK_ERR_INVALID_ARG for m < 1, r outside 1..256 or omega == NULL,
+ * DARK_ERR_WORKSPACE for a missing or short workspace (it must be 8-byte
+ * aligned).
+ */
+size_t dark_prf_omega_device_workspace_bytes(int32_t m, int32_t r, int32_t orthogonal);
+dark_status dark_prf_omega_device(uint64_t seed, int32_t m, int32_t r, int32_t orthogonal,
+                                  float* omega, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * dark_prf_proj_tag - a 64-bit tag naming the projection (seed, m, r,
  * orthogonal).  Store it in desc->proj_tag; states exported by dark_prf_fwd
  * are valid only for calls that carry the same tag.

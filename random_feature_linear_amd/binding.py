@@ -62,6 +62,11 @@ def lib() -> ctypes.CDLL:
         P = ctypes.c_void_p
         L.dark_prf_omega.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
         L.dark_prf_omega.restype = ctypes.c_int
+        L.dark_prf_omega_device_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+        L.dark_prf_omega_device_workspace_bytes.restype = ctypes.c_size_t
+        L.dark_prf_omega_device.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P,
+                                            ctypes.c_size_t, P]
+        L.dark_prf_omega_device.restype = ctypes.c_int
         L.dark_prf_proj_tag.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         L.dark_prf_proj_tag.restype = ctypes.c_uint64
         L.dark_prf_workspace_bytes.argtypes = [ctypes.POINTER(DarkPrfDesc)]
@@ -106,6 +111,29 @@ def dark_prf_omega(seed: int, m: int, r: int, orthogonal: bool) -> np.ndarray:
                               out.ctypes.data_as(ctypes.c_void_p))
     if st != DARK_OK:
         raise DarkPrfError(st, "dark_prf_omega")
+    return out
+
+
+def dark_prf_omega_device_workspace_bytes(m: int, r: int, orthogonal: bool) -> int:
+    return int(lib().dark_prf_omega_device_workspace_bytes(m, r, int(bool(orthogonal))))
+
+
+def dark_prf_omega_device(seed: int, m: int, r: int, orthogonal: bool, omega: int, workspace: int,
+                          ws_bytes: int, stream: int) -> int:
+    return lib().dark_prf_omega_device(ctypes.c_uint64(seed), m, r, int(bool(orthogonal)), omega or None,
+                                       workspace or None, ws_bytes, stream or None)
+
+
+def omega_on_device(seed: int, m: int, r: int, orthogonal: bool, device="cuda:0"):
+    """dark_prf_omega_device into a new fp32 [m][r] device tensor."""
+    import torch
+    out = torch.empty((m, r), dtype=torch.float32, device=device)
+    nb = dark_prf_omega_device_workspace_bytes(m, r, orthogonal)
+    ws = torch.empty(max(nb, 8), dtype=torch.uint8, device=device)
+    st = dark_prf_omega_device(seed, m, r, orthogonal, out.data_ptr(), ws.data_ptr(), nb,
+                               torch.cuda.current_stream(out.device).cuda_stream)
+    if st != DARK_OK:
+        raise DarkPrfError(st, "dark_prf_omega_device")
     return out
 
 

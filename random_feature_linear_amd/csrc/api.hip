@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "common.h"
+#include "omega_stream.h"
 
 namespace dk {
 
@@ -195,24 +196,7 @@ static dark_status check_desc(const dark_prf_desc* d, bool decode, int tensors =
   return DARK_OK;
 }
 
-// ---- Omega: SplitMix64 + Box-Muller; Householder QR with the sign of R ----
-static inline uint64_t mix64(uint64_t z) {
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
-  return z ^ (z >> 31);
-}
-static inline double uniform_at(uint64_t seed, uint64_t i) {
-  const uint64_t x = mix64(seed + (i + 1) * 0x9E3779B97F4A7C15ULL);
-  return ((double)(x >> 11) + 1.0) * 0x1.0p-53;
-}
-static double normal_at(uint64_t seed, uint64_t k) {
-  const uint64_t p = k >> 1;
-  const double u1 = uniform_at(seed, 2 * p);
-  const double u2 = uniform_at(seed, 2 * p + 1);
-  const double rad = sqrt(-2.0 * log(u1));
-  const double ang = 2.0 * M_PI * u2;
-  return (k & 1) ? rad * sin(ang) : rad * cos(ang);
-}
+// ---- Omega: the Gaussian stream (omega_stream.h); Householder QR with the sign of R ----
 
 // Q of G = Q R (n x n, row-major, overwritten) by Householder reflections,
 // with column j of Q multiplied by the sign of R[j][j] so that Q is Haar.
@@ -345,6 +329,21 @@ dark_status dark_prf_omega(uint64_t seed, int32_t m, int32_t r, int32_t orthogon
     }
   }
   return DARK_OK;
+}
+
+size_t dark_prf_omega_device_workspace_bytes(int32_t m, int32_t r, int32_t orthogonal) {
+  if (m < 1 || r < 1 || r > 256) return 0;
+  return omega_device_ws_bytes(m, r, orthogonal != 0);
+}
+
+dark_status dark_prf_omega_device(uint64_t seed, int32_t m, int32_t r, int32_t orthogonal, float* omega,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  if (m < 1 || r < 1 || r > 256 || omega == nullptr) return DARK_ERR_INVALID_ARG;
+  const size_t need = omega_device_ws_bytes(m, r, orthogonal != 0);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need)) return DARK_ERR_WORKSPACE;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 7) != 0) return DARK_ERR_INVALID_ARG;
+  (void)hipGetLastError();   // launch errors below are ours, not an earlier caller's
+  return launch_omega_device(seed, m, r, orthogonal != 0, omega, workspace, stream);
 }
 
 size_t dark_prf_workspace_bytes(const dark_prf_desc* desc) {

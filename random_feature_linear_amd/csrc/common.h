@@ -100,6 +100,10 @@ struct KernelTimer {
 typedef dark_status (*fwd_launcher)(const FwdArgs&, const Plan&, void* ws, void* stream);
 fwd_launcher find_fwd_launcher(int dtype, int d_h, int r16);
 
+// The random projection on the device (omega_device.hip).
+size_t omega_device_ws_bytes(int m, int r, int orthogonal);
+dark_status launch_omega_device(uint64_t seed, int m, int r, int orthogonal, float* omega, void* ws, void* stream);
+
 // update = 1: one decode step (S and z updated in place); update = 0: the
 // read-only cross-attention step (k, v unused; qmask [N] or null).
 typedef dark_status (*decode_launcher)(const dark_prf_desc&, const void* q, const void* k,

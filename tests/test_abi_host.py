@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     L = bd.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -160,6 +160,20 @@ def test_exact_argument_checks():
     assert bd.dark_prf_exact_workspace_bytes(_desc(d_h=48)) == 0
     # more tokens never need less workspace
     assert bd.dark_prf_exact_workspace_bytes(_desc(L=4096)) >= nb
+
+
+def test_omega_device_argument_checks():
+    assert bd.dark_prf_omega_device_workspace_bytes(256, 64, False) == 0
+    nb = bd.dark_prf_omega_device_workspace_bytes(100, 64, True)
+    assert nb == 2 * 3 * 64 * 64 * 8                  # two blocks of G, V and Q in fp64
+    assert bd.dark_prf_omega_device_workspace_bytes(16, 257, True) == 0
+    call = lambda m=100, r=64, orth=True, om=FAKE, ws=FAKE, n=nb: bd.dark_prf_omega_device(1, m, r, orth, om, ws, n, 0)
+    assert call(m=0) == bd.DARK_ERR_INVALID_ARG
+    assert call(r=300) == bd.DARK_ERR_INVALID_ARG
+    assert call(om=0) == bd.DARK_ERR_INVALID_ARG
+    assert call(n=nb - 1) == bd.DARK_ERR_WORKSPACE
+    assert call(ws=0) == bd.DARK_ERR_WORKSPACE
+    assert call(ws=FAKE + 4) == bd.DARK_ERR_INVALID_ARG
 
 
 def test_status_strings():
