@@ -245,6 +245,49 @@ dark_status dark_prf_exact_fwd(const dark_prf_desc* desc, const void* q, const v
                                const void* v, const float* M, const uint8_t* mask, void* out,
                                void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Projection lifecycle (README section "Projection lifecycle"): a projection
+ * stays unchanged unless a redraw is requested; a positive redraw interval
+ * redraws after that many training forwards, and evaluation forwards do not
+ * advance the schedule; a fixed projection ignores ordinary manual and
+ * scheduled redraws, and a forced redraw applies once while fixed; a seed
+ * makes the initial projection reproducible; "deterministic" fixes the
+ * projection at construction.  Host-side state only: after a redraw the
+ * caller regenerates omega from `seed` (dark_prf_omega or
+ * dark_prf_omega_device) and uses the new `tag`, so recurrent states and
+ * cross-attention summaries made with the old projection are rejected.
+ * Draw k uses seed mix(base_seed, k) (SplitMix64's finaliser over base_seed +
+ * k * golden ratio; draw 0 uses base_seed itself).  Not thread-safe: one
+ * object per module.
+ */
+typedef struct {
+  uint64_t base_seed;  /* the projection seed of draw 0 */
+  uint64_t seed;       /* seed of the current draw */
+  uint64_t tag;        /* dark_prf_proj_tag(seed, m, r, orthogonal) */
+  int64_t draw;        /* index of the current draw (0 = initial) */
+  int64_t forwards;    /* training forwards since the current draw */
+  int32_t m, r, orthogonal;
+  int32_t interval;    /* redraw after this many training forwards; <= 0: never */
+  int32_t fixed;       /* 1: ordinary redraws are ignored */
+} dark_prf_projection;
+
+/* dark_prf_projection_init - draw 0 from `seed`; DARK_ERR_INVALID_ARG for
+ * p == NULL, m < 1 or r < 1. */
+dark_status dark_prf_projection_init(dark_prf_projection* p, uint64_t seed, int32_t m, int32_t r,
+                                     int32_t orthogonal, int32_t redraw_interval,
+                                     int32_t deterministic);
+/* dark_prf_projection_forward - call once before each forward.  Training
+ * forwards (training != 0) count toward the interval: when the count has
+ * reached it and the projection is not fixed, the projection is redrawn first
+ * and the count restarts.  Returns 1 if a redraw happened (the caller must
+ * regenerate omega), 0 if not, -1 for p == NULL. */
+int32_t dark_prf_projection_forward(dark_prf_projection* p, int32_t training);
+/* dark_prf_projection_redraw - a manual redraw; ignored while fixed unless
+ * force != 0.  Returns 1 if a redraw happened, 0 if not, -1 for p == NULL. */
+int32_t dark_prf_projection_redraw(dark_prf_projection* p, int32_t force);
+/* dark_prf_projection_fix - fixed != 0 fixes the projection, 0 unfixes it. */
+dark_status dark_prf_projection_fix(dark_prf_projection* p, int32_t fixed);
+
 /* dark_prf_status_str - a static, human-readable name of a status. */
 const char* dark_prf_status_str(dark_status status);
 

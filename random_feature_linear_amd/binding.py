@@ -37,6 +37,15 @@ class DarkPrfDesc(ctypes.Structure):
     ]
 
 
+class DarkPrfProjection(ctypes.Structure):
+    _fields_ = [
+        ("base_seed", ctypes.c_uint64), ("seed", ctypes.c_uint64), ("tag", ctypes.c_uint64),
+        ("draw", ctypes.c_int64), ("forwards", ctypes.c_int64),
+        ("m", ctypes.c_int32), ("r", ctypes.c_int32), ("orthogonal", ctypes.c_int32),
+        ("interval", ctypes.c_int32), ("fixed", ctypes.c_int32),
+    ]
+
+
 class DarkPrfError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {status_str(status)} ({status})")
@@ -87,6 +96,16 @@ def lib() -> ctypes.CDLL:
         L.dark_prf_exact_workspace_bytes.restype = ctypes.c_size_t
         L.dark_prf_exact_fwd.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.dark_prf_exact_fwd.restype = ctypes.c_int
+        PP = ctypes.POINTER(DarkPrfProjection)
+        L.dark_prf_projection_init.argtypes = [PP, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int32]
+        L.dark_prf_projection_init.restype = ctypes.c_int
+        L.dark_prf_projection_forward.argtypes = [PP, ctypes.c_int32]
+        L.dark_prf_projection_forward.restype = ctypes.c_int32
+        L.dark_prf_projection_redraw.argtypes = [PP, ctypes.c_int32]
+        L.dark_prf_projection_redraw.restype = ctypes.c_int32
+        L.dark_prf_projection_fix.argtypes = [PP, ctypes.c_int32]
+        L.dark_prf_projection_fix.restype = ctypes.c_int
         L.dark_prf_status_str.argtypes = [ctypes.c_int]
         L.dark_prf_status_str.restype = ctypes.c_char_p
         L.dark_prf_timing_begin.argtypes = []
@@ -135,6 +154,28 @@ def omega_on_device(seed: int, m: int, r: int, orthogonal: bool, device="cuda:0"
     if st != DARK_OK:
         raise DarkPrfError(st, "dark_prf_omega_device")
     return out
+
+
+def dark_prf_projection_init(seed: int, m: int, r: int, orthogonal: bool, redraw_interval: int = 0,
+                             deterministic: bool = False) -> DarkPrfProjection:
+    p = DarkPrfProjection()
+    st = lib().dark_prf_projection_init(ctypes.byref(p), ctypes.c_uint64(seed), m, r, int(bool(orthogonal)),
+                                        redraw_interval, int(bool(deterministic)))
+    if st != DARK_OK:
+        raise DarkPrfError(st, "dark_prf_projection_init")
+    return p
+
+
+def dark_prf_projection_forward(p: DarkPrfProjection, training: bool) -> int:
+    return int(lib().dark_prf_projection_forward(ctypes.byref(p), int(bool(training))))
+
+
+def dark_prf_projection_redraw(p: DarkPrfProjection, force: bool = False) -> int:
+    return int(lib().dark_prf_projection_redraw(ctypes.byref(p), int(bool(force))))
+
+
+def dark_prf_projection_fix(p: DarkPrfProjection, fixed: bool) -> int:
+    return int(lib().dark_prf_projection_fix(ctypes.byref(p), int(bool(fixed))))
 
 
 def dark_prf_proj_tag(seed: int, m: int, r: int, orthogonal: bool) -> int:

@@ -331,6 +331,55 @@ dark_status dark_prf_omega(uint64_t seed, int32_t m, int32_t r, int32_t orthogon
   return DARK_OK;
 }
 
+static uint64_t draw_seed(uint64_t base, int64_t draw) {
+  return draw == 0 ? base : mix64(base + (uint64_t)draw * 0x9E3779B97F4A7C15ULL);
+}
+static void set_draw(dark_prf_projection* p, int64_t draw) {
+  p->draw = draw;
+  p->seed = draw_seed(p->base_seed, draw);
+  p->tag = dark_prf_proj_tag(p->seed, p->m, p->r, p->orthogonal);
+  p->forwards = 0;
+}
+
+dark_status dark_prf_projection_init(dark_prf_projection* p, uint64_t seed, int32_t m, int32_t r,
+                                     int32_t orthogonal, int32_t redraw_interval, int32_t deterministic) {
+  if (!p || m < 1 || r < 1) return DARK_ERR_INVALID_ARG;
+  memset(p, 0, sizeof(*p));
+  p->base_seed = seed;
+  p->m = m;
+  p->r = r;
+  p->orthogonal = orthogonal != 0;
+  p->interval = redraw_interval;
+  p->fixed = deterministic != 0;
+  set_draw(p, 0);
+  return DARK_OK;
+}
+
+int32_t dark_prf_projection_forward(dark_prf_projection* p, int32_t training) {
+  if (!p) return -1;
+  if (!training) return 0;
+  int32_t redrawn = 0;
+  if (!p->fixed && p->interval > 0 && p->forwards >= p->interval) {
+    set_draw(p, p->draw + 1);
+    redrawn = 1;
+  }
+  p->forwards += 1;
+  return redrawn;
+}
+
+int32_t dark_prf_projection_redraw(dark_prf_projection* p, int32_t force) {
+  if (!p) return -1;
+  if (p->fixed && !force) return 0;
+  set_draw(p, p->draw + 1);
+  return 1;
+}
+
+dark_status dark_prf_projection_fix(dark_prf_projection* p, int32_t fixed) {
+  if (!p) return DARK_ERR_INVALID_ARG;
+  p->fixed = fixed != 0;
+  return DARK_OK;
+}
+
 size_t dark_prf_omega_device_workspace_bytes(int32_t m, int32_t r, int32_t orthogonal) {
   if (m < 1 || r < 1 || r > 256) return 0;
   return omega_device_ws_bytes(m, r, orthogonal != 0);

@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 18, names
     L = bd.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -218,3 +218,81 @@ def test_timing_end_without_records():
     bd.dark_prf_timing_begin()
     res = bd.dark_prf_timing_end()
     assert set(res) == set(bd.KERNEL_KINDS) and all(v == (0.0, 0) for v in res.values())
+
+
+# ---- projection lifecycle (README section "Projection lifecycle") ----------------
+def test_projection_initial_draw_is_reproducible():
+    a = bd.dark_prf_projection_init(7, 256, 64, True)
+    b = bd.dark_prf_projection_init(7, 256, 64, True)
+    assert (a.seed, a.tag, a.draw) == (b.seed, b.tag, 0)
+    assert a.seed == 7 and a.tag == bd.dark_prf_proj_tag(7, 256, 64, True)
+    assert bd.dark_prf_projection_init(8, 256, 64, True).tag != a.tag
+
+
+def test_projection_stays_unchanged_without_a_schedule():
+    p = bd.dark_prf_projection_init(7, 256, 64, True, redraw_interval=0)
+    tag = p.tag
+    assert all(bd.dark_prf_projection_forward(p, True) == 0 for _ in range(50))
+    assert p.tag == tag and p.draw == 0
+
+
+def test_scheduled_redraw_after_interval_training_forwards():
+    p = bd.dark_prf_projection_init(7, 256, 64, True, redraw_interval=3)
+    tags, flags = [], []
+    for _ in range(10):
+        flags.append(bd.dark_prf_projection_forward(p, True))
+        tags.append(p.tag)
+    # three forwards per draw: the 4th, 7th and 10th forwards start with a redraw
+    assert flags == [0, 0, 0, 1, 0, 0, 1, 0, 0, 1]
+    assert len(set(tags)) == 4 and p.draw == 3
+    assert p.tag == bd.dark_prf_proj_tag(p.seed, 256, 64, True)
+
+
+def test_evaluation_forwards_do_not_advance_the_schedule():
+    p = bd.dark_prf_projection_init(7, 256, 64, True, redraw_interval=2)
+    assert bd.dark_prf_projection_forward(p, True) == 0
+    for _ in range(20):
+        assert bd.dark_prf_projection_forward(p, False) == 0
+    assert p.forwards == 1 and p.draw == 0
+    assert bd.dark_prf_projection_forward(p, True) == 0
+    assert bd.dark_prf_projection_forward(p, True) == 1
+
+
+def test_fixed_projection_ignores_ordinary_redraws_but_not_forced():
+    p = bd.dark_prf_projection_init(7, 256, 64, True, redraw_interval=1)
+    bd.dark_prf_projection_fix(p, True)
+    tag = p.tag
+    assert all(bd.dark_prf_projection_forward(p, True) == 0 for _ in range(5))
+    assert bd.dark_prf_projection_redraw(p) == 0 and p.tag == tag
+    assert bd.dark_prf_projection_redraw(p, force=True) == 1 and p.tag != tag and p.fixed == 1
+    bd.dark_prf_projection_fix(p, False)
+    assert bd.dark_prf_projection_redraw(p) == 1
+
+
+def test_deterministic_fixes_at_construction():
+    p = bd.dark_prf_projection_init(7, 256, 64, True, redraw_interval=1, deterministic=True)
+    assert p.fixed == 1
+    assert all(bd.dark_prf_projection_forward(p, True) == 0 for _ in range(5))
+
+
+def test_redraw_seeds_are_reproducible_and_distinct():
+    a = bd.dark_prf_projection_init(11, 64, 16, False)
+    b = bd.dark_prf_projection_init(11, 64, 16, False)
+    seeds = set()
+    for _ in range(5):
+        bd.dark_prf_projection_redraw(a)
+        bd.dark_prf_projection_redraw(b)
+        assert a.seed == b.seed
+        seeds.add(a.seed)
+    assert len(seeds) == 5 and 11 not in seeds
+
+
+def test_projection_argument_checks():
+    import ctypes
+    L = bd.lib()
+    assert L.dark_prf_projection_init(None, 1, 16, 16, 0, 0, 0) == bd.DARK_ERR_INVALID_ARG
+    p = bd.DarkPrfProjection()
+    assert L.dark_prf_projection_init(ctypes.byref(p), 1, 0, 16, 0, 0, 0) == bd.DARK_ERR_INVALID_ARG
+    assert L.dark_prf_projection_forward(None, 1) == -1
+    assert L.dark_prf_projection_redraw(None, 1) == -1
+    assert L.dark_prf_projection_fix(None, 1) == bd.DARK_ERR_INVALID_ARG
