@@ -570,7 +570,7 @@ size_t dark_prf_exact_workspace_bytes(const dark_prf_desc* desc) {
   if (check_desc(desc, false, 1 | 2 | 4 | 8) != DARK_OK) return 0;
   const dark_prf_desc& d = *desc;
   return exact_layout(d.B, d.H, d.L > 0 ? d.L : 1, d.d_h, rank_blocks(d.r), d.m_per_head ? d.H : 1,
-                      d.dtype == DARK_BF16 ? 2 : 4).total;
+                      d.dtype == DARK_BF16 ? 2 : 4, d.causal).total;
 }
 
 dark_status dark_prf_exact_fwd(const dark_prf_desc* desc, const void* q, const void* k, const void* v,

@@ -1826,8 +1826,14 @@ __global__ __launch_bounds__(kThreads) void exact_proj_kernel(FwdArgs a, const T
 // computed in transposed form (rows = keys, columns = queries), so a lane holds
 // one query and its maximum and sum need no cross-lane reduction but one
 // exchange between the two lane halves.
+// With KS > 0 the keys of a query tile are split into runs of KS key tiles,
+// one workgroup each: the workgroup writes its partial maximum m_s, weight sum
+// l_s and unnormalised product O_s per query to `part` (exact_combine_kernel
+// then forms the softmax over all runs); with KS == 0 one workgroup takes all
+// of a tile's keys and writes out directly.
 template <typename T, int DH, int R16, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __restrict__ ufrag, int NBLK) {
+__global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __restrict__ ufrag, int NBLK, int KS,
+                                                          float* __restrict__ part) {
   typedef typename FragOf<T>::type F;
   constexpr int NM = kParts<T>;
   constexpr int DB = vblocks<DH>();
@@ -1846,8 +1852,29 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
   const int NT = (a.L + TT - 1) / TT;
   const int lb = xcd_block();
-  const int tile = CAUSAL ? NT - 1 - lb % NT : lb % NT;   // causal: the longest tiles first
-  const int bh = lb / NT;
+  int tile, bh, split = 0, kt0 = 0, kt1;
+  long pidx = 0;   // (b h, tile, split) index of this workgroup's partial
+  if (KS == 0) {
+    tile = CAUSAL ? NT - 1 - lb % NT : lb % NT;   // causal: the longest tiles first
+    bh = lb / NT;
+    kt1 = CAUSAL ? tile + 1 : NT;
+  } else {   // runs of KS key tiles: tile t has ceil(n_t / KS) of them, n_t = t + 1 (causal) or NT
+    const int nsplit_nc = (NT + KS - 1) / KS;
+    int per_head = 0;
+    for (int t = 0; t < NT; ++t) per_head += CAUSAL ? t / KS + 1 : nsplit_nc;
+    bh = lb / per_head;
+    int r0 = lb % per_head;
+    tile = 0;
+    for (;; ++tile) {
+      const int ns = CAUSAL ? tile / KS + 1 : nsplit_nc;
+      if (r0 < ns) break;
+      r0 -= ns;
+    }
+    split = r0;
+    pidx = (long)lb;
+    kt0 = split * KS;
+    kt1 = min(kt0 + KS, CAUSAL ? tile + 1 : NT);
+  }
   const int b = bh / a.H, h = bh % a.H, hk = (h * a.H_kv) / a.H;
   const int BH = a.B * a.H;
   const int qb = tile * kWaves + w;                     // this wave's query block
@@ -1866,7 +1893,7 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
       ql[kr] = ld8(uq + ((kr * NM + NM - 1) * 64 + lane) * 8);
     }
   }
-  const int tiles = CAUSAL ? tile + 1 : NT;             // key tiles the workgroup visits
+  const int tiles = kt1;                                // key tiles kt0 .. kt1 - 1
   // last key block this wave uses (a block past the sequence end holds no query
   // that is stored; it still reads only blocks of this sequence)
   const int kb_last = min(CAUSAL ? qb : NBLK - 1, NBLK - 1);
@@ -1930,12 +1957,12 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
   };
   // ---- pass 1: the score maximum of each query ----
   float mx = -INFINITY;
-  fetch_k(0);
-  for (int kt = 0; kt < tiles; ++kt) {
+  fetch_k(kt0);
+  for (int kt = kt0; kt < tiles; ++kt) {
     put_bias(kt * TT);
     put_k();
     __syncthreads();
-    fetch_k(kt + 1 < tiles ? kt + 1 : 0);   // pass 2 starts again at tile 0
+    fetch_k(kt + 1 < tiles ? kt + 1 : kt0);   // pass 2 starts again at the first tile
 #pragma unroll 1
     for (int kbl = 0; kbl < kWaves; ++kbl) {
       const int kb = kt * kWaves + kbl;
@@ -1954,8 +1981,8 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
   for (int db = 0; db < DB; ++db) acc[db] = zero16();
   float den = 0.f;
   F vr[VPT];
-  load_v<T, DH, TT>(vr, vbase, a.vs[2], 0, a.L, tid);
-  for (int kt = 0; kt < tiles; ++kt) {
+  load_v<T, DH, TT>(vr, vbase, a.vs[2], kt0 * TT, a.L, tid);
+  for (int kt = kt0; kt < tiles; ++kt) {
     store_vt<T, DH, TT, VST>(s_vt, vr, tid);
     put_bias(kt * TT);
     put_k();
@@ -1984,6 +2011,22 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
   // ---- out = (p V) / sum p; lanes c and c + 32 hold the two halves of the sum ----
   T* obase = reinterpret_cast<T*>(a.out) + b * a.os[0] + h * a.os[1];
   const float dq = den + __shfl_xor(den, 32);
+  if (KS > 0) {   // partial: O_s [128][d_h], then m_s and l_s [128] per workgroup
+    float* po = part + pidx * (long)(TT * DH + 2 * TT);
+    float* pm = po + TT * DH;
+    if (g == 0) {
+      pm[32 * w + c] = mx;
+      pm[TT + 32 * w + c] = dq;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = db * 32 + c;
+        if (d < DH) po[(32 * w + crow(i, g)) * DH + d] = acc[db][i];
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float dd = __shfl(dq, crow(i, g));
@@ -1999,11 +2042,57 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
   }
 }
 
+// Softmax over the runs: out = sum_s O_s e^(m_s - m) / sum_s l_s e^(m_s - m),
+// m = max_s m_s (0 when no run saw a visible key).  One thread per query and
+// 4 columns.
+template <typename T, int DH, bool CAUSAL>
+__global__ void exact_combine_kernel(FwdArgs a, const float* __restrict__ part, int KS) {
+  constexpr int TT = kTile;
+  const int NT = (a.L + TT - 1) / TT;
+  const int nsplit_nc = (NT + KS - 1) / KS;
+  const long n = (long)a.B * a.H * a.L * (DH / 4);
+  for (long idx = blockIdx.x * (long)blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x) {
+    const int d4 = (int)(idx % (DH / 4));
+    const long row = idx / (DH / 4);
+    const int t = (int)(row % a.L);
+    const int bh = (int)(row / a.L);
+    const int tile = t / TT, q = t % TT;
+    // first partial of (bh, tile): the same order as the workgroups
+    int per_head = 0, before = 0;
+    for (int u = 0; u < NT; ++u) {
+      const int ns = CAUSAL ? u / KS + 1 : nsplit_nc;
+      if (u < tile) before += ns;
+      per_head += ns;
+    }
+    const int ns = CAUSAL ? tile / KS + 1 : nsplit_nc;
+    const float* p0 = part + ((long)bh * per_head + before) * (long)(TT * DH + 2 * TT);
+    float m = -INFINITY;
+    for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, p0[sp * (long)(TT * DH + 2 * TT) + TT * DH + q]);
+    float num[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
+    if (m != -INFINITY) {
+      for (int sp = 0; sp < ns; ++sp) {
+        const float* ps = p0 + sp * (long)(TT * DH + 2 * TT);
+        const float ms = ps[TT * DH + q];
+        if (ms == -INFINITY) continue;
+        const float wgt = exp2f((ms - m) * kLog2e);
+        den += ps[TT * DH + TT + q] * wgt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) num[e] += ps[q * DH + 4 * d4 + e] * wgt;
+      }
+    }
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    const int b = bh / a.H, h = bh % a.H;
+    T* o = reinterpret_cast<T*>(a.out) + b * a.os[0] + h * a.os[1] + (long)t * a.os[2] + 4 * d4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out(o + e, num[e] * inv);
+  }
+}
+
 template <typename T, int DH, int R16>
 dark_status launch_exact_impl(const FwdArgs& a, void* ws, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int HM = a.m_per_head ? a.H : 1;
-  const ExactLayout lay = exact_layout(a.B, a.H, a.L, DH, R16, HM, (int)sizeof(T));
+  const ExactLayout lay = exact_layout(a.B, a.H, a.L, DH, R16, HM, (int)sizeof(T), a.causal);
   char* base = reinterpret_cast<char*>(ws);
   T* mfrag = reinterpret_cast<T*>(base + lay.off_mfrag);
   T* ufrag = reinterpret_cast<T*>(base + lay.off_ufrag);
@@ -2019,12 +2108,27 @@ dark_status launch_exact_impl(const FwdArgs& a, void* ws, void* stream) {
     hipLaunchKernelGGL((exact_proj_kernel<T, DH, R16>), dim3(2 * a.B * a.H * per), dim3(kThreads), 0, st, a, mfrag,
                        ufrag, lay.NBLK);
   }
-  KernelTimer tm(kQOut, stream);
-  const dim3 grid(a.B * a.H * ((a.L + kTile - 1) / kTile));
-  if (a.causal)
-    hipLaunchKernelGGL((exact_kernel<T, DH, R16, true>), grid, dim3(kThreads), 0, st, a, ufrag, lay.NBLK);
-  else
-    hipLaunchKernelGGL((exact_kernel<T, DH, R16, false>), grid, dim3(kThreads), 0, st, a, ufrag, lay.NBLK);
+  float* part = reinterpret_cast<float*>(base + lay.off_part);
+  const int NT = (a.L + kTile - 1) / kTile;
+  const int KS = lay.KS;
+  {
+    KernelTimer tm(kQOut, stream);
+    const dim3 grid(KS == 0 ? a.B * a.H * NT : a.B * a.H * lay.splits_per_head);
+    if (a.causal)
+      hipLaunchKernelGGL((exact_kernel<T, DH, R16, true>), grid, dim3(kThreads), 0, st, a, ufrag, lay.NBLK, KS, part);
+    else
+      hipLaunchKernelGGL((exact_kernel<T, DH, R16, false>), grid, dim3(kThreads), 0, st, a, ufrag, lay.NBLK, KS,
+                         part);
+  }
+  if (KS > 0) {
+    KernelTimer tm(kScan, stream);
+    const long n = (long)a.B * a.H * a.L * (DH / 4);
+    const int blocks = (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
+    if (a.causal)
+      hipLaunchKernelGGL((exact_combine_kernel<T, DH, true>), dim3(blocks), dim3(256), 0, st, a, part, KS);
+    else
+      hipLaunchKernelGGL((exact_combine_kernel<T, DH, false>), dim3(blocks), dim3(256), 0, st, a, part, KS);
+  }
   return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
 }
 

@@ -31,6 +31,11 @@ CASES = [
     ("exact_bf16_d128_nc", "bf16", 1, 2, 2,  260, 128, 128, False, False, "random"),
     ("exact_bf16_d256_c", "bf16", 1, 2, 1,   150, 256, 200, True,  True,  "random"),
     ("exact_bf16_d16_c",  "bf16", 2, 2, 2,   130, 16,  16,  True,  True,  "tail"),
+    # few (b, h) x query tiles: the keys of a tile split into runs of 2 key tiles
+    # and combined (9 key tiles: runs of 2, 2, 2, 2, 1)
+    ("exact_split_nc",    "bf16", 1, 2, 1,   1100, 64, 64,  False, True,  "random"),
+    ("exact_split_c",     "bf16", 1, 4, 2,   1500, 64, 48,  True,  True,  "tail"),
+    ("exact_split_f32_c", "f32",  1, 1, 1,   700,  32, 16,  True,  False, "random"),
 ]
 
 
