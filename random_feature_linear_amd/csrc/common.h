@@ -68,6 +68,9 @@ struct Plan {
 // a query tile are split into runs of KS key tiles, the partial results of
 // every run (O_s [128][d_h], m_s and l_s [128], fp32).  The keys are split when
 // one workgroup per query tile would leave most compute units idle.
+// key tiles per run when the keys are split (measured at L = 2048, 16 heads:
+// 79 us per forward against 82 with runs of 4, 86 with 8 and 102 unsplit)
+constexpr int kExactKS = 2;
 struct ExactLayout {
   size_t off_mfrag, off_ufrag, off_part, total;
   int NBLK;             // 32-token blocks per sequence
@@ -86,9 +89,7 @@ inline ExactLayout exact_layout(int B, int H, int L, int d_h, int R16, int HM, i
   off += (size_t)2 * B * H * e.NBLK * R16 * NM * frag * elem;
   off = (off + 255) & ~(size_t)255;
   const int NT = (L + 127) / 128;
-  // runs of 2 key tiles (measured at L = 2048, 16 heads: 79 us per forward
-  // against 82 with runs of 4, 86 with 8 and 102 unsplit)
-  e.KS = ((long)B * H * NT < 512 && NT > 4) ? 2 : 0;
+  e.KS = ((long)B * H * NT < 512 && NT > 4) ? kExactKS : 0;
   e.splits_per_head = 0;
   if (e.KS > 0)
     for (int t = 0; t < NT; ++t) e.splits_per_head += causal ? t / e.KS + 1 : (NT + e.KS - 1) / e.KS;

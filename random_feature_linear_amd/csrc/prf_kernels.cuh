@@ -1858,22 +1858,23 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
     tile = CAUSAL ? NT - 1 - lb % NT : lb % NT;   // causal: the longest tiles first
     bh = lb / NT;
     kt1 = CAUSAL ? tile + 1 : NT;
-  } else {   // runs of KS key tiles: tile t has ceil(n_t / KS) of them, n_t = t + 1 (causal) or NT
-    const int nsplit_nc = (NT + KS - 1) / KS;
+  } else {   // runs of KS = kExactKS key tiles: tile t has ceil(n_t / KS), n_t = t + 1 (causal) or NT
+    constexpr int KSC = kExactKS;
+    const int nsplit_nc = (NT + KSC - 1) / KSC;
     int per_head = 0;
-    for (int t = 0; t < NT; ++t) per_head += CAUSAL ? t / KS + 1 : nsplit_nc;
+    for (int t = 0; t < NT; ++t) per_head += CAUSAL ? t / KSC + 1 : nsplit_nc;
     bh = lb / per_head;
     int r0 = lb % per_head;
     tile = 0;
     for (;; ++tile) {
-      const int ns = CAUSAL ? tile / KS + 1 : nsplit_nc;
+      const int ns = CAUSAL ? tile / KSC + 1 : nsplit_nc;
       if (r0 < ns) break;
       r0 -= ns;
     }
     split = r0;
     pidx = (long)lb;
-    kt0 = split * KS;
-    kt1 = min(kt0 + KS, CAUSAL ? tile + 1 : NT);
+    kt0 = split * KSC;
+    kt1 = min(kt0 + KSC, CAUSAL ? tile + 1 : NT);
   }
   const int b = bh / a.H, h = bh % a.H, hk = (h * a.H_kv) / a.H;
   const int BH = a.B * a.H;
@@ -2046,8 +2047,9 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
 // m = max_s m_s (0 when no run saw a visible key).  One thread per query and
 // 4 columns.
 template <typename T, int DH, bool CAUSAL>
-__global__ void exact_combine_kernel(FwdArgs a, const float* __restrict__ part, int KS) {
+__global__ void exact_combine_kernel(FwdArgs a, const float* __restrict__ part) {
   constexpr int TT = kTile;
+  constexpr int KS = kExactKS;
   const int NT = (a.L + TT - 1) / TT;
   const int nsplit_nc = (NT + KS - 1) / KS;
   const long n = (long)a.B * a.H * a.L * (DH / 4);
@@ -2125,9 +2127,9 @@ dark_status launch_exact_impl(const FwdArgs& a, void* ws, void* stream) {
     const long n = (long)a.B * a.H * a.L * (DH / 4);
     const int blocks = (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
     if (a.causal)
-      hipLaunchKernelGGL((exact_combine_kernel<T, DH, true>), dim3(blocks), dim3(256), 0, st, a, part, KS);
+      hipLaunchKernelGGL((exact_combine_kernel<T, DH, true>), dim3(blocks), dim3(256), 0, st, a, part);
     else
-      hipLaunchKernelGGL((exact_combine_kernel<T, DH, false>), dim3(blocks), dim3(256), 0, st, a, part, KS);
+      hipLaunchKernelGGL((exact_combine_kernel<T, DH, false>), dim3(blocks), dim3(256), 0, st, a, part);
   }
   return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
 }
