@@ -131,6 +131,31 @@ __device__ __forceinline__ bf16x8 ld8(const bf16* p) {
   uint4 u = *reinterpret_cast<const uint4*>(p);
   return __builtin_bit_cast(bf16x8, u);
 }
+// 16-byte loads and stores of data that is touched once (the per-unit states
+// between the key side and the sum): non-temporal, so they do not displace
+// data that is read again.  Measured for the L=8192 GQA workload: sum 212 ->
+// 182 us, key side 413 -> 405 us.  (Non-temporal stores of the sum's output,
+// which the query side reads, made the sum slower again: 197 us.)
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 ld8_stream(const bf16* p) {
+  const u32x4v u = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ f32x8 ld8_stream(const float* p) {
+  const f32x4v a = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+  const f32x4v b = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p + 4));
+  f32x8 f = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  return f;
+}
+__device__ __forceinline__ void st8_stream(bf16* p, const bf16x8& f) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4v, f), reinterpret_cast<u32x4v*>(p));
+}
+__device__ __forceinline__ void st8_stream(float* p, const f32x8& f) {
+  const f32x4v a = {f[0], f[1], f[2], f[3]}, b = {f[4], f[5], f[6], f[7]};
+  __builtin_nontemporal_store(a, reinterpret_cast<f32x4v*>(p));
+  __builtin_nontemporal_store(b, reinterpret_cast<f32x4v*>(p + 4));
+}
 __device__ __forceinline__ f32x8 ld8(const float* p) {
   float4 a = *reinterpret_cast<const float4*>(p);
   float4 b = *reinterpret_cast<const float4*>(p + 4);
@@ -962,7 +987,7 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int k = 0; k < 2; ++k) st8(sd + ((db * FK + 2 * fb + k) * 64 + lane) * 8, acc_frag<F>(acc[f][db], k));
+      for (int k = 0; k < 2; ++k) st8_stream(sd + ((db * FK + 2 * fb + k) * 64 + lane) * 8, acc_frag<F>(acc[f][db], k));
     if constexpr (ZMMA) {   // column d_h: lane d_h % 32 of each half holds rows crow(i, g)
       if (c == DH % 32) {
 #pragma unroll
@@ -1102,7 +1127,7 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int k = 0; k < 2; ++k) st8(sd + ((db * FK + 2 * fb + k) * 64 + lane) * 8, acc_frag<F>(acc[f][db], k));
+      for (int k = 0; k < 2; ++k) st8_stream(sd + ((db * FK + 2 * fb + k) * 64 + lane) * 8, acc_frag<F>(acc[f][db], k));
     if (c == DH % 32) {   // column d_h: lane d_h % 32 of each half holds rows crow(i, g)
 #pragma unroll
       for (int i = 0; i < 16; ++i) zd[fb * 32 + crow(i, g)] = acc[f][DBK - 1][i];
@@ -1162,7 +1187,7 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
     for (; u + UB <= pl.NU; u += UB) {
       F x[UB];
 #pragma unroll
-      for (int q = 0; q < UB; ++q) x[q] = ld8(src + (long)(u + q) * per_unit * 8);
+      for (int q = 0; q < UB; ++q) x[q] = ld8_stream(src + (long)(u + q) * per_unit * 8);
 #pragma unroll
       for (int q = 0; q < UB; ++q) {
         if (a.causal) {
@@ -1177,7 +1202,7 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
     for (; u + 4 <= pl.NU; u += 4) {       // four loads in flight
       F x[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] = ld8(src + (long)(u + q) * per_unit * 8);
+      for (int q = 0; q < 4; ++q) x[q] = ld8_stream(src + (long)(u + q) * per_unit * 8);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (a.causal) {
@@ -1190,7 +1215,7 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
       }
     }
     for (; u < pl.NU; ++u) {
-      const F x = ld8(src + (long)u * per_unit * 8);
+      const F x = ld8_stream(src + (long)u * per_unit * 8);
       if (a.causal) {
         F o;
         make_frag(o, run);
