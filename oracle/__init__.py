@@ -8,6 +8,7 @@ from .prf_oracle import (  # noqa: F401
     attend_causal_blockwise,
     attend_noncausal,
     attention,
+    attention_backward,
     context_state,
     cross_attention,
     decode_step,

@@ -268,3 +268,69 @@ def exact_kernel_attention(q, k, v, M, mask: Optional[np.ndarray] = None, causal
             den = w.sum(axis=1)
             O[b, h] = _ratio(w @ v[b, g], den)
     return O
+
+
+def attention_backward(q, k, v, M, omega, dout, mask: Optional[np.ndarray] = None, causal: bool = False):
+    """Gradients of the linear-mode attention core with respect to q, k, v and M.
+
+    The package README (section "Kernel") has M learned, and the DARKFormer
+    abstract pages finetune the q-k-v projections together with the
+    projection covariance (Figure 4), so the core needs gradients for q, k,
+    v and M.  Omega is a fixed random draw and gets none.  The pages give no
+    backward formulas: this is the chain rule applied to the forward as
+    defined above, written with the quadratic weight matrix
+    W[t, j] = phi(q_t) . phi(k_j) * visible(t, j), so O = (W V) / (W 1):
+
+      D_t = sum_j W[t, j], O_t = N_t / D_t with N = W V;
+      dN_t = dO_t / D_t,  dD_t = -(dO_t . O_t) / D_t  (both 0 where D_t = 0);
+      dW[t, j] = visible(t, j) * (dN_t . v_j + dD_t);   dV = W^T dN;
+      dPhi(Q) = dW Phi(K),  dPhi(K) = dW^T Phi(Q);
+      phi_j(u) = exp(omega_j . u - |u|^2 / 2) / sqrt(m), so
+      dU = (dPhi * Phi) Omega - U * rowsum(dPhi * Phi);
+      u = s M x with s = d_h^(-1/4):  dX = s dU M,  dM += s dU^T X.
+
+    With H_kv < H, dk and dv of a key/value head sum over the query heads that
+    read it; a shared M ([r][d_h]) sums dM over heads.  Returns fp64
+    (dq, dk, dv, dM) shaped like q, k, v and M.
+    """
+    q, k, v, dout = f64(q), f64(k), f64(v), f64(dout)
+    B, H, L, d = q.shape
+    H_kv = k.shape[1]
+    omega = f64(omega)
+    s = qk_scale(d)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dM = np.zeros_like(f64(M))
+    vis = np.tril(np.ones((L, L))) if causal else np.ones((L, L))
+    for b in range(B):
+        visb = vis if mask is None else vis * (np.asarray(mask[b]) != 0)[None, :]
+        for h in range(H):
+            g = kv_head(h, H, H_kv)
+            M_h = head_geometry(M, h)
+            UQ, UK = project(q[b, h], M_h), project(k[b, g], M_h)
+            PQ = prf_features(q[b, h], M_h, omega)
+            PK = prf_features(k[b, g], M_h, omega)
+            W = (PQ @ PK.T) * visb
+            D = W.sum(axis=1)
+            O = _ratio(W @ v[b, g], D)
+            ok = D > 0
+            dN = np.zeros((L, d))
+            dD = np.zeros(L)
+            dN[ok] = dout[b, h][ok] / D[ok, None]
+            dD[ok] = -np.sum(dout[b, h][ok] * O[ok], axis=1) / D[ok]
+            dW = visb * (dN @ v[b, g].T + dD[:, None])
+            dv[b, g] += W.T @ dN
+            grads = []
+            for P, U, dP in ((PQ, UQ, dW @ PK), (PK, UK, dW.T @ PQ)):
+                dE = dP * P
+                grads.append(dE @ omega - U * dE.sum(axis=1, keepdims=True))
+            dUQ, dUK = grads
+            dq[b, h] += s * (dUQ @ M_h)
+            dk[b, g] += s * (dUK @ M_h)
+            dM_h = s * (dUQ.T @ q[b, h] + dUK.T @ k[b, g])
+            if dM.ndim == 3:
+                dM[h] += dM_h
+            else:
+                dM += dM_h
+    return dq, dk, dv, dM

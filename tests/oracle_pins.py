@@ -423,7 +423,59 @@ def check_cross_vs_explicit(seed=72):
         assert np.all(O[2] == 0.0)
 
 
+# ----------------------------------------------------------------------------
+# backward: the oracle's chain-rule gradients against central finite
+# differences of the oracle's forward (pinned above)
+# ----------------------------------------------------------------------------
+def _fd_case(rng, causal, per_head, H_kv, masked):
+    B, H, L, d, m, r = 2, 2, 11, 4, 8, 3
+    q, k, v, M, om = _random_case(rng, B=B, H=H, H_kv=H_kv, Lq=L, d=d, m=m, r=r, per_head=per_head)
+    q, k = 0.7 * q, 0.7 * k
+    mask = None
+    if masked:
+        mask = np.ones((B, L), np.uint8)
+        mask[0, [0, 4, 9]] = 0          # causal: query row 0 of batch 0 sees no key
+        mask[1, :] = 0
+        mask[1, [3, 7]] = 1
+    dout = rng.standard_normal((B, H, L, d))
+    return q, k, v, M, om, mask, dout
+
+
+def check_backward_finite_differences(seed=81, eps=1e-5, n_dir=3):
+    rng = np.random.default_rng(seed)
+    for causal in (False, True):
+        for per_head, H_kv, masked in ((True, 2, False), (True, 1, True), (False, 1, True), (False, 2, False)):
+            q, k, v, M, om, mask, dout = _fd_case(rng, causal, per_head, H_kv, masked)
+            grads = dict(zip("qkvM", po.attention_backward(q, k, v, M, om, dout, mask=mask, causal=causal)))
+            base = dict(q=q, k=k, v=v, M=M)
+
+            def f(**over):
+                a = dict(base, **over)
+                O = po.attention(a["q"], a["k"], a["v"], a["M"], om, mask=mask, causal=causal)
+                return float(np.sum(dout * O))
+
+            for name, x in base.items():
+                assert grads[name].shape == x.shape, name
+                for _ in range(n_dir):
+                    dirn = rng.standard_normal(x.shape)
+                    fd = (f(**{name: x + eps * dirn}) - f(**{name: x - eps * dirn})) / (2 * eps)
+                    an = float(np.sum(grads[name] * dirn))
+                    tol = 1e-6 * max(1.0, abs(fd))
+                    assert abs(an - fd) <= tol, (
+                        f"d{name} (causal={causal}, per_head={per_head}, H_kv={H_kv}, masked={masked}): "
+                        f"analytic {an:.9e} vs finite difference {fd:.9e}")
+            if mask is not None:
+                # a masked key has no weight anywhere: its k and v rows get no gradient
+                for b in range(q.shape[0]):
+                    off = np.asarray(mask[b]) == 0
+                    assert np.all(grads["k"][b][:, off] == 0) and np.all(grads["v"][b][:, off] == 0)
+                if causal:
+                    # batch 0, row 0: no visible key, output fixed at 0, so no dq
+                    assert np.all(grads["q"][0, :, 0] == 0)
+
+
 ALL_CHECKS = [
+    check_backward_finite_differences,
     check_closed_form_features,
     check_closed_form_attention,
     check_associative_vs_explicit,

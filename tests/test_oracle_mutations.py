@@ -84,6 +84,52 @@ def _query_mask_ignored(orig):
     return cross_attention
 
 
+def _bwd(drop_norm=False, dD_sign=-1.0, dpk_untransposed=False, dM_scale=True, gqa_overwrite=False):
+    """A copy of the oracle's backward with one planted mistake."""
+    def attention_backward(q, k, v, M, omega, dout, mask=None, causal=False):
+        q, k, v, dout, omega = (np.asarray(a, np.float64) for a in (q, k, v, dout, omega))
+        B, H, L, d = q.shape
+        H_kv = k.shape[1]
+        s = d ** -0.25
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        dM = np.zeros_like(np.asarray(M, np.float64))
+        vis = np.tril(np.ones((L, L))) if causal else np.ones((L, L))
+        for b in range(B):
+            visb = vis if mask is None else vis * (np.asarray(mask[b]) != 0)[None, :]
+            for h in range(H):
+                g = (h * H_kv) // H
+                M_h = np.asarray(M[h] if np.asarray(M).ndim == 3 else M, np.float64)
+                UQ, UK = s * q[b, h] @ M_h.T, s * k[b, g] @ M_h.T
+                PQ, PK = po.prf_features(q[b, h], M_h, omega), po.prf_features(k[b, g], M_h, omega)
+                W = (PQ @ PK.T) * visb
+                D = W.sum(1)
+                ok = D > 0
+                O = np.zeros((L, d))
+                O[ok] = (W @ v[b, g])[ok] / D[ok, None]
+                dN, dD = np.zeros((L, d)), np.zeros(L)
+                dN[ok] = dout[b, h][ok] / D[ok, None]
+                dD[ok] = dD_sign * np.sum(dout[b, h][ok] * O[ok], 1) / D[ok]
+                dW = visb * (dN @ v[b, g].T + dD[:, None])
+                dv[b, g] += W.T @ dN
+                dPK = (dW if dpk_untransposed else dW.T) @ PQ
+                out = []
+                for P, U, dP in ((PQ, UQ, dW @ PK), (PK, UK, dPK)):
+                    dE = dP * P
+                    out.append(dE @ omega - (0 if drop_norm else U * dE.sum(1, keepdims=True)))
+                dq[b, h] += s * out[0] @ M_h
+                if gqa_overwrite:
+                    dk[b, g] = s * out[1] @ M_h
+                else:
+                    dk[b, g] += s * out[1] @ M_h
+                dM_h = (s if dM_scale else 1.0) * (out[0].T @ q[b, h] + out[1].T @ k[b, g])
+                if dM.ndim == 3:
+                    dM[h] += dM_h
+                else:
+                    dM += dM_h
+        return dq, dk, dv, dM
+    return attention_backward
+
+
 MUTATIONS = {
     "scale_d^-1/2": ("prf_features", _feat(scale=lambda d: d ** -0.5)),
     "no_scale": ("prf_features", _feat(scale=lambda d: 1.0)),
@@ -100,6 +146,11 @@ MUTATIONS = {
     "eps_denominator": ("_ratio", lambda N, D: N / (D + 1e-8)[:, None]),
     "context_mask_ignored": ("context_state", None),
     "query_mask_ignored": ("cross_attention", None),
+    "bwd_no_norm_term": ("attention_backward", _bwd(drop_norm=True)),
+    "bwd_dD_sign": ("attention_backward", _bwd(dD_sign=1.0)),
+    "bwd_dPK_untransposed": ("attention_backward", _bwd(dpk_untransposed=True)),
+    "bwd_dM_unscaled": ("attention_backward", _bwd(dM_scale=False)),
+    "bwd_gqa_overwrite": ("attention_backward", _bwd(gqa_overwrite=True)),
 }
 
 QUICK = pins.ALL_CHECKS + [pins.check_mc_kernel]

@@ -52,3 +52,7 @@ def test_context_state_explicit():
 
 def test_cross_vs_explicit():
     pins.check_cross_vs_explicit()
+
+
+def test_backward_finite_differences():
+    pins.check_backward_finite_differences()
