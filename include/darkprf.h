@@ -288,6 +288,40 @@ int32_t dark_prf_projection_redraw(dark_prf_projection* p, int32_t force);
 /* dark_prf_projection_fix - fixed != 0 fixes the projection, 0 unfixes it. */
 dark_status dark_prf_projection_fix(dark_prf_projection* p, int32_t fixed);
 
+/*
+ * Backward pass of dark_prf_fwd: gradients of a scalar loss with respect to
+ * q, k, v and the geometry M, given dout = d loss / d out.  README section
+ * "Kernel" has M learned (and the DARKFormer abstract pages finetune the q-k-v
+ * projections with the projection covariance, Figure 4); omega is a fixed
+ * draw and gets no gradient.  The pages give no backward formulas: these are
+ * the chain rule through out = N / D, N = W V, D = W 1 with
+ * W[t][j] = phi(q_t) . phi(k_j) over the visible keys (mask, causal), the
+ * feature map phi and u = d_h^(-1/4) M_h x.  A query row with no visible key
+ * (out fixed at 0) gets no gradient; a masked key gets dk = dv = 0.
+ *
+ * dark_prf_bwd_workspace_bytes - device workspace dark_prf_bwd needs for
+ * desc; 0 for an invalid descriptor.  It holds the fp32 features, the
+ * per-chunk states and the intermediate gradients: about
+ * 4*B*H*Lp*(4*m + 4*r + 6*d_h + 135) + 8*B*H*(Lp/64)*m*(d_h+1) bytes, with Lp
+ * the sequence length rounded up to a multiple of 64.
+ *
+ * dark_prf_bwd - arguments as for dark_prf_fwd, plus:
+ *   dout  [B][H][L][d_h] (strides o_str), dtype
+ *   dq    [B][H][L][d_h] (strides q_str), dtype, overwritten
+ *   dk, dv [B][H_kv][L][d_h] (strides k_str, v_str), dtype, overwritten; with
+ *         H_kv < H they sum over the query heads that share the key/value head
+ *   dM    fp32, shaped like M ([H][r][d_h] or [r][d_h], contiguous),
+ *         overwritten; a shared M sums over heads; summed over the batch
+ *   workspace, ws_bytes: at least dark_prf_bwd_workspace_bytes(desc)
+ * Computed in fp32 throughout (fp32 matrix cores); dq, dk and dv are rounded
+ * to the input dtype once at the end.  Error codes as for dark_prf_fwd.
+ */
+size_t dark_prf_bwd_workspace_bytes(const dark_prf_desc* desc);
+dark_status dark_prf_bwd(const dark_prf_desc* desc, const void* q, const void* k, const void* v,
+                         const float* M, const float* omega, const uint8_t* mask, const void* dout,
+                         void* dq, void* dk, void* dv, float* dM, void* workspace, size_t ws_bytes,
+                         void* stream);
+
 /* dark_prf_status_str - a static, human-readable name of a status. */
 const char* dark_prf_status_str(dark_status status);
 
@@ -304,9 +338,10 @@ const char* dark_prf_status_str(dark_status status);
  *     DARK_ERR_HIP if an event failed.
  * Kernel kinds: 0 operand preparation of M and omega, 1 key-side feature
  * state, 2 state sum / prefix scan, 3 query-side output, 4 decode step,
- * 5 exponent shift pass (the per-token maxima of the folded exponent).
+ * 5 exponent shift pass (the per-token maxima of the folded exponent),
+ * 6 backward matrix products, 7 backward element-wise passes and chunk scans.
  */
-#define DARK_KERNEL_KINDS 6
+#define DARK_KERNEL_KINDS 8
 dark_status dark_prf_timing_begin(void);
 dark_status dark_prf_timing_end(double* ms, int32_t* launches);
 

@@ -96,6 +96,11 @@ def lib() -> ctypes.CDLL:
         L.dark_prf_exact_workspace_bytes.restype = ctypes.c_size_t
         L.dark_prf_exact_fwd.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.dark_prf_exact_fwd.restype = ctypes.c_int
+        L.dark_prf_bwd_workspace_bytes.argtypes = [ctypes.POINTER(DarkPrfDesc)]
+        L.dark_prf_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.dark_prf_bwd.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P, P, P, P, P, P,
+                                   ctypes.c_size_t, P]
+        L.dark_prf_bwd.restype = ctypes.c_int
         PP = ctypes.POINTER(DarkPrfProjection)
         L.dark_prf_projection_init.argtypes = [PP, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int32, ctypes.c_int32]
@@ -220,6 +225,17 @@ def dark_prf_exact_fwd(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, mask: 
                                     mask or None, out or None, workspace or None, ws_bytes, stream or None)
 
 
+def dark_prf_bwd_workspace_bytes(desc: DarkPrfDesc) -> int:
+    return int(lib().dark_prf_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def dark_prf_bwd(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, omega: int, mask: int, dout: int,
+                 dq: int, dk: int, dv: int, dM: int, workspace: int, ws_bytes: int, stream: int) -> int:
+    return lib().dark_prf_bwd(ctypes.byref(desc), q or None, k or None, v or None, M or None, omega or None,
+                              mask or None, dout or None, dq or None, dk or None, dv or None, dM or None,
+                              workspace or None, ws_bytes, stream or None)
+
+
 def dark_prf_decode_step(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, omega: int, S: int,
                          z: int, state_tag: int, out: int, stream: int) -> int:
     return lib().dark_prf_decode_step(ctypes.byref(desc), q or None, k or None, v or None,
@@ -227,7 +243,7 @@ def dark_prf_decode_step(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, omeg
                                       ctypes.c_uint64(state_tag), out or None, stream or None)
 
 
-KERNEL_KINDS = ("prep", "kstate", "scan", "qout", "decode", "shift")
+KERNEL_KINDS = ("prep", "kstate", "scan", "qout", "decode", "shift", "bwd_gemm", "bwd_aux")
 
 
 def dark_prf_timing_begin() -> None:
@@ -399,6 +415,32 @@ def cross_attention(q, M, omega, S, z, state_tag: int, proj_tag: int, query_mask
     if st != DARK_OK:
         raise DarkPrfError(st, "dark_prf_cross_fwd")
     return out
+
+
+def prf_attention_backward(q, k, v, M, omega, dout, mask=None, causal: bool = False, workspace=None):
+    """dark_prf_bwd on torch device tensors: returns (dq, dk, dv, dM).
+
+    dq, dk and dv take the strides of q, k and v; dout must have the strides of
+    q (the forward's output layout); dM is fp32 shaped like M.
+    """
+    import torch
+    if tuple(dout.shape) != tuple(q.shape) or dout.dtype != q.dtype:
+        raise ValueError("dout must match q in shape and dtype")
+    dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
+    dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
+    dM = torch.empty(M.shape, dtype=torch.float32, device=M.device)
+    desc = make_desc(q, k, v, dout, M, omega, causal)
+    nbytes = dark_prf_bwd_workspace_bytes(desc)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = dark_prf_bwd(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), M.data_ptr(), omega.data_ptr(),
+                      _mask_ptr(mask, "mask"), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      dM.data_ptr(), workspace.data_ptr(), workspace.numel(), stream)
+    if st != DARK_OK:
+        raise DarkPrfError(st, "dark_prf_bwd")
+    return dq, dk, dv, dM
 
 
 def exact_attention(q, k, v, M, mask=None, causal: bool = False, out=None, workspace=None):

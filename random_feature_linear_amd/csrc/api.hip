@@ -597,6 +597,43 @@ dark_status dark_prf_exact_fwd(const dark_prf_desc* desc, const void* q, const v
   return fn(a, workspace, stream);
 }
 
+size_t dark_prf_bwd_workspace_bytes(const dark_prf_desc* desc) {
+  if (check_desc(desc, false) != DARK_OK) return 0;
+  return bwd_ws_bytes(*desc);
+}
+
+dark_status dark_prf_bwd(const dark_prf_desc* desc, const void* q, const void* k, const void* v, const float* M,
+                         const float* omega, const uint8_t* mask, const void* dout, void* dq, void* dk, void* dv,
+                         float* dM, void* workspace, size_t ws_bytes, void* stream) {
+  dark_status st = check_desc(desc, false);
+  if (st != DARK_OK) return st;
+  const dark_prf_desc& d = *desc;
+  if (!M || !dM || !aligned16(M) || !aligned16(dM)) return DARK_ERR_INVALID_ARG;
+  const bool tokens = d.B > 0 && d.L > 0;
+  if (tokens) {
+    if (!q || !k || !v || !omega || !dout || !dq || !dk || !dv) return DARK_ERR_INVALID_ARG;
+    const void* ptrs[8] = {q, k, v, omega, dout, dq, dk, dv};
+    for (const void* ptr : ptrs)
+      if (!aligned16(ptr)) return DARK_ERR_INVALID_ARG;
+    if (workspace == nullptr || ws_bytes < dark_prf_bwd_workspace_bytes(desc)) return DARK_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return DARK_ERR_INVALID_ARG;
+  }
+  (void)hipGetLastError();   // launch errors below are ours, not an earlier caller's
+  BwdPtrs p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.M = M;
+  p.omega = omega;
+  p.mask = mask;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dM = dM;
+  return launch_bwd(d, p, workspace, stream, nullptr);
+}
+
 dark_status dark_prf_decode_step(const dark_prf_desc* desc, const void* q, const void* k, const void* v,
                                  const float* M, const float* omega, float* S, float* z, uint64_t state_tag,
                                  void* out, void* stream) {

@@ -1,0 +1,566 @@
+// Backward pass of the linear-mode attention core: gradients for q, k, v and
+// the learned geometry M (package README "Data-Aware Random Feature Kernels
+// for Transformers (DARKformer)", section "Kernel": M is learned; the
+// DARKFormer abstract pages finetune the q-k-v projections together with the
+// projection covariance, Figure 4).  Omega is a fixed draw and gets none.
+//
+// With u = s M_h x (s = d_h^(-1/4)), phi the feature map, the visible weights
+// W[t][j] = phi(q_t).phi(k_j) (j valid under the key mask, and j <= t when
+// causal), N = W V, D = W 1 and O = N / D, the chain rule gives
+//   Gd_t = [dN_t, dD_t] = [dO_t / D_t, -(dO_t . O_t) / D_t]   (0 when D_t = 0)
+//   dW[t][j] = visible * ([V, 1]_j . Gd_t)
+//   dPhi(Q) = dW Phi(K),  dPhi(K) = dW^T Phi(Q),  dV = W^T dN
+//   dU = (dPhi * Phi) Omega - U * rowsum(dPhi * Phi)
+//   dX = s dU M_h,  dM_h += s dU^T X.
+// The quadratic products are never formed: as in the forward, the sequence is
+// cut into chunks of C tokens and the sums over earlier (or later) chunks go
+// through m x (d_h + 1) states, with exclusive prefix sums over chunks:
+//   Sx_c = sum_{c' < c} Phi(K_c')^T [V, 1]_c'        (key side, forward scan)
+//   Gx_c = sum_{c' > c} Phi(Q_c')^T Gd_c'            (query side, reverse scan)
+//   [N, D]_c = Phi(Q_c) Sx_c + tril(Phi(Q_c) Phi(K_c)^T) [V, 1]_c
+//   dPhi(Q)_c = Gd_c Sx_c^T + tril(Gd_c [V, 1]_c^T) Phi(K_c)
+//   dPhi(K)_c = [V, 1]_c Gx_c^T + tril(Gd_c [V, 1]_c^T)^T Phi(Q_c)
+//   dV_c = Phi(K_c) Gx_c[:, :d] + tril(Phi(Q_c) Phi(K_c)^T)^T dN_c.
+// Without causality the states are the plain totals and the tril terms vanish.
+//
+// Every product runs through one batched GEMM kernel on the fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32): 64 x 64 output tiles, 32-deep K slices staged
+// through LDS, operands addressed by strides so that transposed operands need
+// no copies.  Features, states and intermediate gradients are fp32 in the
+// workspace.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+
+#include "common.h"
+
+namespace dk {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kChunk = 64;     // tokens per causal chunk
+constexpr int kMChunk = 512;   // tokens per split of the dM reduction
+
+__device__ __forceinline__ float ld_f(const float* p) { return *p; }
+__device__ __forceinline__ float ld_f(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+__device__ __forceinline__ void st_t(float* p, float x) { *p = x; }
+__device__ __forceinline__ void st_t(uint16_t* p, float x) {   // round to nearest even
+  uint32_t u = __float_as_uint(x);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  *p = (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Operand element (i, k) of batch (b, h, c) sits at
+// p + b*sb + (h / hg)*sh + c*sc + i*si + k*sk.
+struct GOp {
+  const void* p;
+  int64_t sb, sh, sc, si, sk;
+  int hg;
+};
+struct GOut {
+  float* p;
+  int64_t sb, sh, sc, si;
+};
+
+enum Epi { kEpiPlain = 0, kEpiTril = 1, kEpiFeature = 2 };
+
+struct GemmArgs {
+  GOp A, B;
+  GOut C;           // element (i, j) at p + b*sb + h*sh + c*sc + i*si + j
+  int M, N, K;      // C (M x N) = alpha * A (M x K) * B (K x N), per batch
+  int Ktot;         // > 0: batch c reduces over min(K, Ktot - c*K) terms
+  int Arows;        // rows of A at or beyond this read as 0
+  int H, NCB;       // batch = (b*H + h)*NCB + c
+  int tiles_n, tiles;
+  float alpha;
+  int accumulate;   // C += result instead of C = result
+  int epi;
+  // kEpiFeature: C = valid ? exp(acc - nrm[bh*nrm_sbh + i]) * alpha : 0, valid =
+  // i < L and (mask == null or mask[b*L + i] != 0)
+  const float* nrm;
+  int64_t nrm_sbh;
+  const uint8_t* mask;
+  int L;
+};
+
+template <typename TA, typename TB>
+__global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
+  __shared__ float As[64][33];   // [i][k]
+  __shared__ float Bs[32][65];   // [k][j]
+  const int64_t bid = blockIdx.x;
+  const int batch = (int)(bid / a.tiles);
+  const int tile = (int)(bid - (int64_t)batch * a.tiles);
+  const int tm = tile / a.tiles_n, tn = tile - tm * a.tiles_n;
+  const int bh = batch / a.NCB, c = batch - bh * a.NCB;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const TA* A = static_cast<const TA*>(a.A.p) + b * a.A.sb + (int64_t)(h / a.A.hg) * a.A.sh + c * a.A.sc;
+  const TB* Bp = static_cast<const TB*>(a.B.p) + b * a.B.sb + (int64_t)(h / a.B.hg) * a.B.sh + c * a.B.sc;
+  float* C = a.C.p + b * a.C.sb + h * a.C.sh + c * a.C.sc;
+  const int K = a.Ktot > 0 ? min(a.K, a.Ktot - c * a.K) : a.K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
+  const int i0 = tm * 64, j0 = tn * 64;
+  const bool a_krow = a.A.sk == 1;   // k contiguous in A: threads walk k
+  const bool b_jrow = a.B.sk == 1;   // j contiguous in B: threads walk j
+  f32x16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += 32) {
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) {
+      const int e = tid + 256 * e8;
+      int i, k;
+      if (a_krow) { i = e >> 5; k = e & 31; } else { i = e & 63; k = e >> 6; }
+      const int gi = i0 + i, gk = k0 + k;
+      As[i][k] = (gi < a.Arows && gk < K) ? ld_f(A + gi * a.A.si + gk * a.A.sk) : 0.f;
+      int kb, j;
+      if (b_jrow) { kb = e >> 6; j = e & 63; } else { kb = e & 31; j = e >> 5; }
+      const int gkb = k0 + kb, gj = j0 + j;
+      Bs[kb][j] = (gkb < K && gj < a.N) ? ld_f(Bp + gkb * a.B.si + gj * a.B.sk) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 32; kk += 8)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[wi + l32][kk + 4 * g + s], Bs[kk + 4 * g + s][wj + l32],
+                                                   acc, 0, 0, 0);
+    __syncthreads();
+  }
+  const int col = j0 + wj + l32;
+  if (col >= a.N) return;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = i0 + wi + 8 * (e >> 2) + 4 * g + (e & 3);
+    if (row >= a.M) continue;
+    float x = a.alpha * acc[e];
+    if (a.epi == kEpiTril) {
+      if (col > row) x = 0.f;
+    } else if (a.epi == kEpiFeature) {
+      const bool ok = row < a.L && (a.mask == nullptr || a.mask[(int64_t)b * a.L + row] != 0);
+      x = ok ? __expf(acc[e] - a.nrm[bh * a.nrm_sbh + row]) * a.alpha : 0.f;
+    }
+    float* cp = C + row * a.C.si + col;
+    if (a.accumulate) x += *cp;
+    *cp = x;
+  }
+}
+
+// [V, 1] rows of query head h (its key/value head), fp32; rows t >= L are 0.
+template <typename T>
+__global__ void vx_kernel(const T* v, int64_t sb, int64_t sh, int64_t sl, float* Vx, int H, int hg, int L, int Lp,
+                          int d, int64_t total) {
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int e = (int)(idx % (d + 1));
+    const int64_t row = idx / (d + 1);
+    const int t = (int)(row % Lp);
+    const int bh = (int)(row / Lp);
+    const int b = bh / H, h = bh - b * H;
+    float x = 0.f;
+    if (t < L) x = e < d ? ld_f(v + b * sb + (int64_t)(h / hg) * sh + t * sl + e) : 1.f;
+    Vx[idx] = x;
+  }
+}
+
+// nrm[row] = |U_row|^2 / 2
+__global__ void halfnorm_kernel(const float* U, float* nrm, int r, int64_t rows) {
+  const int64_t row = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  const float* u = U + row * r;
+  float s = 0.f;
+  for (int j = 0; j < r; ++j) s = fmaf(u[j], u[j], s);
+  nrm[row] = 0.5f * s;
+}
+
+// Gd = [dO / D, -(dO . O) / D] per row (one wave per row), 0 when D <= 0 or t >= L.
+template <typename T>
+__global__ __launch_bounds__(256) void gd_kernel(const T* dout, int64_t sb, int64_t sh, int64_t sl, const float* ND,
+                                                 float* Gd, int H, int L, int Lp, int d, int64_t rows) {
+  const int64_t row = blockIdx.x * 4LL + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int t = (int)(row % Lp);
+  const int bh = (int)(row / Lp);
+  const int b = bh / H, h = bh - b * H;
+  const float* nd = ND + row * (d + 1);
+  float* gd = Gd + row * (d + 1);
+  const float D = nd[d];
+  const bool ok = t < L && D > 0.f;
+  const float inv = ok ? 1.f / D : 0.f;
+  float dot = 0.f;
+  for (int e = lane; e < d; e += 64) {
+    const float go = ok ? ld_f(dout + b * sb + h * sh + t * sl + e) : 0.f;
+    dot = fmaf(go, nd[e] * inv, dot);
+    gd[e] = go * inv;
+  }
+  dot = wave_sum(dot);
+  if (lane == 0) gd[d] = -dot * inv;
+}
+
+// dE = dP * P in place and rs[row] = sum_j dE[row][j] (one wave per row)
+__global__ __launch_bounds__(256) void de_kernel(float* dP, const float* P, float* rs, int m, int64_t rows) {
+  const int64_t row = blockIdx.x * 4LL + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float* dp = dP + row * m;
+  const float* p = P + row * m;
+  float s = 0.f;
+  for (int j = lane; j < m; j += 64) {
+    const float x = dp[j] * p[j];
+    dp[j] = x;
+    s += x;
+  }
+  s = wave_sum(s);
+  if (lane == 0) rs[row] = s;
+}
+
+// dU -= U * rs (per row)
+__global__ void fixdu_kernel(float* dU, const float* U, const float* rs, int r, int64_t total) {
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x)
+    dU[idx] -= U[idx] * rs[idx / r];
+}
+
+// Exclusive prefix (reverse = 0) or suffix (reverse = 1) sums over the NC
+// chunk states of each (b, h), in place; X floats per state.
+__global__ void chunk_scan_kernel(float* buf, int NC, int64_t X, int64_t total, int reverse) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t bh = idx / X, x = idx - bh * X;
+  float* p = buf + bh * NC * X + x;
+  float run = 0.f;
+  for (int i = 0; i < NC; ++i) {
+    const int c = reverse ? NC - 1 - i : i;
+    const float v = p[c * X];
+    p[c * X] = run;
+    run += v;
+  }
+}
+
+// out[bh][x] = sum over the NC chunk states
+__global__ void chunk_sum_kernel(const float* buf, float* out, int NC, int64_t X, int64_t total) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t bh = idx / X, x = idx - bh * X;
+  const float* p = buf + bh * NC * X + x;
+  float s = 0.f;
+  for (int c = 0; c < NC; ++c) s += p[c * X];
+  out[idx] = s;
+}
+
+// dst[b][g][t][e] (strides) = sum over the query heads h of group g of src[b][h][t][e]
+template <typename T>
+__global__ void head_sum_kernel(const float* src, T* dst, int64_t sb, int64_t sh, int64_t sl, int H, int G, int L,
+                                int Lp, int d, int64_t total) {
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int e = (int)(idx % d);
+    const int64_t r1 = idx / d;
+    const int t = (int)(r1 % L);
+    const int64_t r2 = r1 / L;
+    const int Hg = H / G;
+    const int gidx = (int)(r2 % Hg);
+    const int b = (int)(r2 / Hg);
+    float s = 0.f;
+    for (int i = 0; i < G; ++i) s += src[(((int64_t)b * H + gidx * G + i) * Lp + t) * d + e];
+    st_t(dst + b * sb + gidx * sh + t * sl + e, s);
+  }
+}
+
+// dM = sum of the partials [B][H][NKC][r*d] over b and splits (and heads when shared)
+__global__ void dm_sum_kernel(const float* part, float* dM, int B, int H, int NKC, int64_t rd, int per_head) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t n = per_head ? (int64_t)H * rd : rd;
+  if (idx >= n) return;
+  const int h0 = per_head ? (int)(idx / rd) : 0;
+  const int64_t x = idx - (per_head ? h0 * rd : 0);
+  const int hn = per_head ? h0 + 1 : H;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int h = h0; h < hn; ++h)
+      for (int c = 0; c < NKC; ++c) s += part[(((int64_t)b * H + h) * NKC + c) * rd + x];
+  dM[idx] = s;
+}
+
+__global__ void fill_zero_kernel(float* p, int64_t n) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx < n) p[idx] = 0.f;
+}
+
+inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+  int C, NC, Lp, NKC, D1;
+  size_t Uq, Uk, dUq, dUk, nq, nk, rsq, rsk, Pq, Pk, dPq, dPk, Vx, ND, Gd, Sx, Gx, St, Gt, Wc, A2, dQh, dKh, dVh,
+      dMp;
+  size_t total;
+};
+
+BwdLayout bwd_layout(const dark_prf_desc& d) {
+  BwdLayout o;
+  o.C = kChunk;
+  const int L = d.L > 0 ? d.L : 1;
+  o.NC = (int)cdiv64(L, kChunk);
+  o.Lp = o.NC * kChunk;
+  o.NKC = (int)cdiv64(L, kMChunk);
+  o.D1 = d.d_h + 1;
+  const size_t BH = (size_t)d.B * d.H, Lp = o.Lp, m = d.m, r = d.r, dh = d.d_h, D1 = o.D1, NC = o.NC;
+  size_t off = 0;
+  auto take = [&](size_t floats) {
+    const size_t at = off;
+    off = al256(off + floats * sizeof(float));
+    return at;
+  };
+  o.Uq = take(BH * Lp * r);
+  o.Uk = take(BH * Lp * r);
+  o.dUq = take(BH * Lp * r);
+  o.dUk = take(BH * Lp * r);
+  o.nq = take(BH * Lp);
+  o.nk = take(BH * Lp);
+  o.rsq = take(BH * Lp);
+  o.rsk = take(BH * Lp);
+  o.Pq = take(BH * Lp * m);
+  o.Pk = take(BH * Lp * m);
+  o.dPq = take(BH * Lp * m);
+  o.dPk = take(BH * Lp * m);
+  o.Vx = take(BH * Lp * D1);
+  o.ND = take(BH * Lp * D1);
+  o.Gd = take(BH * Lp * D1);
+  o.Sx = take(BH * NC * m * D1);
+  o.Gx = take(BH * NC * m * D1);
+  o.St = take(d.causal ? 0 : BH * m * D1);
+  o.Gt = take(d.causal ? 0 : BH * m * D1);
+  o.Wc = take(d.causal ? BH * Lp * kChunk : 0);
+  o.A2 = take(d.causal ? BH * Lp * kChunk : 0);
+  o.dQh = take(BH * Lp * dh);
+  o.dKh = take(BH * Lp * dh);
+  o.dVh = take(BH * Lp * dh);
+  o.dMp = take(BH * o.NKC * r * dh);
+  o.total = off;
+  return o;
+}
+
+GOp op(const void* p, int64_t sb, int64_t sh, int64_t sc, int64_t si, int64_t sk, int hg = 1) {
+  GOp o;
+  o.p = p;
+  o.sb = sb;
+  o.sh = sh;
+  o.sc = sc;
+  o.si = si;
+  o.sk = sk;
+  o.hg = hg;
+  return o;
+}
+GOut out(float* p, int64_t sb, int64_t sh, int64_t sc, int64_t si) {
+  GOut o;
+  o.p = p;
+  o.sb = sb;
+  o.sh = sh;
+  o.sc = sc;
+  o.si = si;
+  return o;
+}
+
+struct Launcher {
+  hipStream_t st;
+  int H;
+  double flops = 0.0;
+  dark_status status = DARK_OK;
+
+  template <typename TA, typename TB>
+  void gemm(GOp A, GOp B, GOut C, int M, int N, int K, int batches, int NCB, float alpha = 1.f, int accumulate = 0,
+            int epi = kEpiPlain, int Ktot = 0, int Arows = -1, const float* nrm = nullptr, int64_t nrm_sbh = 0,
+            const uint8_t* mask = nullptr, int L = 0) {
+    if (status != DARK_OK || M <= 0 || N <= 0 || batches <= 0) return;
+    GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.Ktot = Ktot;
+    a.Arows = Arows < 0 ? M : Arows;
+    a.H = H;
+    a.NCB = NCB;
+    a.tiles_n = (N + 63) / 64;
+    a.tiles = ((M + 63) / 64) * a.tiles_n;
+    a.alpha = alpha;
+    a.accumulate = accumulate;
+    a.epi = epi;
+    a.nrm = nrm;
+    a.nrm_sbh = nrm_sbh;
+    a.mask = mask;
+    a.L = L;
+    const int64_t grid = (int64_t)batches * a.tiles;
+    if (grid > INT_MAX) {
+      status = DARK_ERR_UNSUPPORTED;
+      return;
+    }
+    // multiply-adds of the products as posed (K summed over the splits)
+    const int64_t kt = Ktot > 0 ? (int64_t)Ktot * (batches / NCB) : (int64_t)K * batches;
+    flops += 2.0 * M * N * (double)kt;
+    KernelTimer tm(kBwdGemm, st);
+    hipLaunchKernelGGL((bgemm_kernel<TA, TB>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    if (hipGetLastError() != hipSuccess) status = DARK_ERR_HIP;
+  }
+
+  template <typename F, typename... Args>
+  void aux(F kern, int64_t threads, int block, Args... args) {
+    if (status != DARK_OK || threads <= 0) return;
+    const int64_t grid = cdiv64(threads, block);
+    if (grid > INT_MAX) {
+      status = DARK_ERR_UNSUPPORTED;
+      return;
+    }
+    KernelTimer tm(kBwdAux, st);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(block), 0, st, args...);
+    if (hipGetLastError() != hipSuccess) status = DARK_ERR_HIP;
+  }
+};
+
+template <typename T>
+dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStream_t st, double* flops_out) {
+  const BwdLayout o = bwd_layout(d);
+  const int H = d.H, G = d.H / d.H_kv, L = d.L, Lp = o.Lp, NC = o.NC, C = o.C, D1 = o.D1;
+  const int m = d.m, r = d.r, dh = d.d_h;
+  const int64_t BH = (int64_t)d.B * H;
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  float *Uq = F(o.Uq), *Uk = F(o.Uk), *dUq = F(o.dUq), *dUk = F(o.dUk), *nq = F(o.nq), *nk = F(o.nk);
+  float *rsq = F(o.rsq), *rsk = F(o.rsk), *Pq = F(o.Pq), *Pk = F(o.Pk), *dPq = F(o.dPq), *dPk = F(o.dPk);
+  float *Vx = F(o.Vx), *ND = F(o.ND), *Gd = F(o.Gd), *Sx = F(o.Sx), *Gx = F(o.Gx), *St = F(o.St), *Gt = F(o.Gt);
+  float *Wc = F(o.Wc), *A2 = F(o.A2), *dQh = F(o.dQh), *dKh = F(o.dKh), *dVh = F(o.dVh), *dMp = F(o.dMp);
+  const float s = 1.0f / sqrtf(sqrtf((float)dh));
+  const int64_t hM = d.m_per_head ? (int64_t)r * dh : 0;   // M_h offset per head
+  Launcher ln{st, H};
+
+  // per-(b, h) row-major fp32 buffers [BH][Lp][w]: operand and output strides
+  auto rows = [&](const float* p, int w) { return op(p, (int64_t)H * Lp * w, (int64_t)Lp * w, (int64_t)C * w, w, 1); };
+  auto rowsT = [&](const float* p, int w) { return op(p, (int64_t)H * Lp * w, (int64_t)Lp * w, (int64_t)C * w, 1, w); };
+  auto orows = [&](float* p, int w) { return out(p, (int64_t)H * Lp * w, (int64_t)Lp * w, (int64_t)C * w, w); };
+  // chunk states [BH][NC][m][D1]
+  const int64_t X = (int64_t)m * D1;
+  auto states = [&](const float* p) { return op(p, (int64_t)H * NC * X, (int64_t)NC * X, X, D1, 1); };
+  auto statesT = [&](const float* p) { return op(p, (int64_t)H * NC * X, (int64_t)NC * X, X, 1, D1); };
+  auto ostates = [&](float* p) { return out(p, (int64_t)H * NC * X, (int64_t)NC * X, X, D1); };
+  // one total state per (b, h) [BH][m][D1]
+  auto tot = [&](const float* p) { return op(p, (int64_t)H * X, X, 0, D1, 1); };
+  auto totT = [&](const float* p) { return op(p, (int64_t)H * X, X, 0, 1, D1); };
+  // intra-chunk C x C blocks [BH][NC][C][C]
+  auto blk = [&](const float* p) { return op(p, (int64_t)H * Lp * C, (int64_t)Lp * C, (int64_t)C * C, C, 1); };
+  auto blkT = [&](const float* p) { return op(p, (int64_t)H * Lp * C, (int64_t)Lp * C, (int64_t)C * C, 1, C); };
+  auto oblk = [&](float* p) { return out(p, (int64_t)H * Lp * C, (int64_t)Lp * C, (int64_t)C * C, C); };
+
+  // 1. projections u = s M_h x (rows t >= L read as 0) and half norms
+  const GOp Mt = op(p.M, 0, hM, 0, 1, dh);   // (k, j) = M_h[j][k]
+  ln.gemm<T, float>(op(p.q, d.q_str[0], d.q_str[1], 0, d.q_str[2], 1), Mt, orows(Uq, r), Lp, r, dh, (int)BH, 1, s, 0,
+                    kEpiPlain, 0, L);
+  ln.gemm<T, float>(op(p.k, d.k_str[0], d.k_str[1], 0, d.k_str[2], 1, G), Mt, orows(Uk, r), Lp, r, dh, (int)BH, 1, s,
+                    0, kEpiPlain, 0, L);
+  ln.aux(halfnorm_kernel, BH * Lp, 256, (const float*)Uq, nq, r, BH * Lp);
+  ln.aux(halfnorm_kernel, BH * Lp, 256, (const float*)Uk, nk, r, BH * Lp);
+  // 2. features phi = exp(u . omega_j - |u|^2 / 2) / sqrt(m); keys masked, rows t >= L zero
+  const GOp OmT = op(p.omega, 0, 0, 0, 1, r);   // (k, j) = omega[j][k]
+  const float inv_sqrt_m = 1.0f / sqrtf((float)m);
+  ln.gemm<float, float>(rows(Uq, r), OmT, orows(Pq, m), Lp, m, r, (int)BH, 1, inv_sqrt_m, 0, kEpiFeature, 0, -1, nq,
+                        Lp, nullptr, L);
+  ln.gemm<float, float>(rows(Uk, r), OmT, orows(Pk, m), Lp, m, r, (int)BH, 1, inv_sqrt_m, 0, kEpiFeature, 0, -1, nk,
+                        Lp, p.mask, L);
+  // 3. [V, 1] per query head
+  ln.aux(vx_kernel<T>, BH * Lp * D1, 256, (const T*)p.v, d.v_str[0], d.v_str[1], d.v_str[2], Vx, H, G, L, Lp, dh,
+         BH * Lp * D1);
+  // 4. key-side chunk states Phi(K_c)^T [V, 1]_c
+  ln.gemm<float, float>(rowsT(Pk, m), rows(Vx, D1), ostates(Sx), m, D1, C, (int)(BH * NC), NC);
+  const int NB = (int)(BH * NC);
+  if (d.causal) {
+    ln.aux(chunk_scan_kernel, BH * X, 256, Sx, NC, X, BH * X, 0);
+    // 5. [N, D] = Phi(Q_c) Sx_c + tril(Phi(Q_c) Phi(K_c)^T) [V, 1]_c
+    ln.gemm<float, float>(rows(Pq, m), rowsT(Pk, m), oblk(Wc), C, C, m, NB, NC, 1.f, 0, kEpiTril);
+    ln.gemm<float, float>(rows(Pq, m), states(Sx), orows(ND, D1), C, D1, m, NB, NC);
+    ln.gemm<float, float>(blk(Wc), rows(Vx, D1), orows(ND, D1), C, D1, C, NB, NC, 1.f, 1);
+  } else {
+    ln.aux(chunk_sum_kernel, BH * X, 256, (const float*)Sx, St, NC, X, BH * X);
+    ln.gemm<float, float>(rows(Pq, m), tot(St), orows(ND, D1), Lp, D1, m, (int)BH, 1);
+  }
+  // 6. Gd = [dO / D, -(dO . O) / D]
+  ln.aux(gd_kernel<T>, BH * Lp * 64, 256, (const T*)p.dout, d.o_str[0], d.o_str[1], d.o_str[2], (const float*)ND, Gd,
+         H, L, Lp, dh, BH * Lp);
+  // 7. dPhi(Q), the query-side chunk states Phi(Q_c)^T Gd_c, dPhi(K) and dV
+  ln.gemm<float, float>(rowsT(Pq, m), rows(Gd, D1), ostates(Gx), m, D1, C, NB, NC);
+  if (d.causal) {
+    ln.aux(chunk_scan_kernel, BH * X, 256, Gx, NC, X, BH * X, 1);
+    ln.gemm<float, float>(rows(Gd, D1), rowsT(Vx, D1), oblk(A2), C, C, D1, NB, NC, 1.f, 0, kEpiTril);
+    ln.gemm<float, float>(rows(Gd, D1), statesT(Sx), orows(dPq, m), C, m, D1, NB, NC);
+    ln.gemm<float, float>(blk(A2), rows(Pk, m), orows(dPq, m), C, m, C, NB, NC, 1.f, 1);
+    ln.gemm<float, float>(rows(Vx, D1), statesT(Gx), orows(dPk, m), C, m, D1, NB, NC);
+    ln.gemm<float, float>(blkT(A2), rows(Pq, m), orows(dPk, m), C, m, C, NB, NC, 1.f, 1);
+    ln.gemm<float, float>(rows(Pk, m), states(Gx), orows(dVh, dh), C, dh, m, NB, NC);
+    ln.gemm<float, float>(blkT(Wc), rows(Gd, D1), orows(dVh, dh), C, dh, C, NB, NC, 1.f, 1);
+  } else {
+    ln.aux(chunk_sum_kernel, BH * X, 256, (const float*)Gx, Gt, NC, X, BH * X);
+    ln.gemm<float, float>(rows(Gd, D1), totT(St), orows(dPq, m), Lp, m, D1, (int)BH, 1);
+    ln.gemm<float, float>(rows(Vx, D1), totT(Gt), orows(dPk, m), Lp, m, D1, (int)BH, 1);
+    ln.gemm<float, float>(rows(Pk, m), tot(Gt), orows(dVh, dh), Lp, dh, m, (int)BH, 1);
+  }
+  // 8. through the feature map: dU = (dPhi * Phi) Omega - U * rowsum(dPhi * Phi)
+  ln.aux(de_kernel, BH * Lp * 64, 256, dPq, (const float*)Pq, rsq, m, BH * Lp);
+  ln.aux(de_kernel, BH * Lp * 64, 256, dPk, (const float*)Pk, rsk, m, BH * Lp);
+  const GOp Om = op(p.omega, 0, 0, 0, r, 1);
+  ln.gemm<float, float>(rows(dPq, m), Om, orows(dUq, r), Lp, r, m, (int)BH, 1);
+  ln.gemm<float, float>(rows(dPk, m), Om, orows(dUk, r), Lp, r, m, (int)BH, 1);
+  ln.aux(fixdu_kernel, BH * Lp * r, 256, dUq, (const float*)Uq, (const float*)rsq, r, BH * Lp * r);
+  ln.aux(fixdu_kernel, BH * Lp * r, 256, dUk, (const float*)Uk, (const float*)rsk, r, BH * Lp * r);
+  // 9. dX = s dU M_h, dM_h = s sum dU^T X
+  const GOp Mh = op(p.M, 0, hM, 0, dh, 1);
+  ln.gemm<float, float>(rows(dUq, r), Mh, orows(dQh, dh), Lp, dh, r, (int)BH, 1, s);
+  ln.gemm<float, float>(rows(dUk, r), Mh, orows(dKh, dh), Lp, dh, r, (int)BH, 1, s);
+  const int KC = kMChunk, NKC = o.NKC;
+  const int64_t RD = (int64_t)r * dh;
+  const GOut oMp = out(dMp, (int64_t)H * NKC * RD, (int64_t)NKC * RD, RD, dh);
+  const GOp dUqT = op(dUq, (int64_t)H * Lp * r, (int64_t)Lp * r, (int64_t)KC * r, 1, r);
+  const GOp dUkT = op(dUk, (int64_t)H * Lp * r, (int64_t)Lp * r, (int64_t)KC * r, 1, r);
+  ln.gemm<float, T>(dUqT, op(p.q, d.q_str[0], d.q_str[1], KC * d.q_str[2], d.q_str[2], 1), oMp, r, dh, KC,
+                    (int)(BH * NKC), NKC, s, 0, kEpiPlain, L);
+  ln.gemm<float, T>(dUkT, op(p.k, d.k_str[0], d.k_str[1], KC * d.k_str[2], d.k_str[2], 1, G), oMp, r, dh, KC,
+                    (int)(BH * NKC), NKC, s, 1, kEpiPlain, L);
+  // 10. outputs: dq per head, dk and dv summed over the heads of each group, dM
+  ln.aux(head_sum_kernel<T>, (int64_t)d.B * H * L * dh, 256, (const float*)dQh, (T*)p.dq, d.q_str[0], d.q_str[1],
+         d.q_str[2], H, 1, L, Lp, dh, (int64_t)d.B * H * L * dh);
+  ln.aux(head_sum_kernel<T>, (int64_t)d.B * d.H_kv * L * dh, 256, (const float*)dKh, (T*)p.dk, d.k_str[0],
+         d.k_str[1], d.k_str[2], H, G, L, Lp, dh, (int64_t)d.B * d.H_kv * L * dh);
+  ln.aux(head_sum_kernel<T>, (int64_t)d.B * d.H_kv * L * dh, 256, (const float*)dVh, (T*)p.dv, d.v_str[0],
+         d.v_str[1], d.v_str[2], H, G, L, Lp, dh, (int64_t)d.B * d.H_kv * L * dh);
+  const int64_t nM = (d.m_per_head ? H : 1) * RD;
+  ln.aux(dm_sum_kernel, nM, 256, (const float*)dMp, p.dM, d.B, H, NKC, RD, d.m_per_head);
+  if (flops_out) *flops_out = ln.flops;
+  return ln.status;
+}
+
+}  // namespace
+
+size_t bwd_ws_bytes(const dark_prf_desc& d) { return bwd_layout(d).total; }
+
+dark_status launch_bwd(const dark_prf_desc& d, const BwdPtrs& p, void* ws, void* stream, double* flops) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (d.L == 0 || d.B == 0) {   // no tokens: every gradient is empty except dM, which is 0
+    const int64_t nM = (d.m_per_head ? d.H : 1) * (int64_t)d.r * d.d_h;
+    if (flops) *flops = 0.0;
+    if (nM > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)cdiv64(nM, 256)), dim3(256), 0, st, p.dM, nM);
+    return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
+  }
+  char* w = static_cast<char*>(ws);
+  return d.dtype == DARK_BF16 ? run_bwd<uint16_t>(d, p, w, st, flops) : run_bwd<float>(d, p, w, st, flops);
+}
+
+}  // namespace dk

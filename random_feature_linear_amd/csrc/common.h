@@ -101,7 +101,7 @@ inline ExactLayout exact_layout(int B, int H, int L, int d_h, int R16, int HM, i
 
 // Optional per-kernel timing (dark_prf_timing_begin / _end): records a HIP
 // event pair on `stream` around one launch while timing is on.
-enum KernelKind { kPrep = 0, kKState = 1, kScan = 2, kQOut = 3, kDecode = 4, kShift = 5 };
+enum KernelKind { kPrep = 0, kKState = 1, kScan = 2, kQOut = 3, kDecode = 4, kShift = 5, kBwdGemm = 6, kBwdAux = 7 };
 struct KernelTimer {
   KernelTimer(int kind, void* stream);
   ~KernelTimer();
@@ -127,5 +127,23 @@ typedef dark_status (*decode_launcher)(const dark_prf_desc&, const void* q, cons
                                        float* S, float* z, void* out, const uint8_t* qmask,
                                        int update, void* stream);
 decode_launcher find_decode_launcher(int dtype, int d_h);
+
+// The backward pass (bwd.hip): device pointers of one call.
+struct BwdPtrs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* M;
+  const float* omega;
+  const uint8_t* mask;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dM;
+};
+size_t bwd_ws_bytes(const dark_prf_desc& d);
+// flops (optional): the multiply-adds of the matrix products queued, times 2
+dark_status launch_bwd(const dark_prf_desc& d, const BwdPtrs& p, void* ws, void* stream, double* flops);
 
 }  // namespace dk

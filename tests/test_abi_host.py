@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     L = bd.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -296,3 +296,25 @@ def test_projection_argument_checks():
     assert L.dark_prf_projection_forward(None, 1) == -1
     assert L.dark_prf_projection_redraw(None, 1) == -1
     assert L.dark_prf_projection_fix(None, 1) == bd.DARK_ERR_INVALID_ARG
+
+
+def test_bwd_argument_checks():
+    d = _desc(causal=1)
+    nb = bd.dark_prf_bwd_workspace_bytes(d)
+    # the size the header states for the causal call: per token and head
+    # 4*(4m + 4r + 6 d_h + 135) bytes, plus two fp32 m x (d_h + 1) states per 64 tokens
+    B, H, L, m, r, dh = 2, 8, 256, 256, 64, 64
+    stated = 4 * B * H * L * (4 * m + 4 * r + 6 * dh + 135) + 8 * B * H * (L // 64) * m * (dh + 1)
+    assert stated <= nb <= 1.02 * stated + 64 * 1024, (nb, stated)
+
+    def call(q=FAKE, dout=FAKE, dM=FAKE, ws=FAKE, n=nb, dd=d):
+        return bd.dark_prf_bwd(dd, q, FAKE, FAKE, FAKE, FAKE, 0, dout, FAKE, FAKE, FAKE, dM, ws, n, 0)
+    assert call(q=0) == bd.DARK_ERR_INVALID_ARG
+    assert call(q=FAKE + 2) == bd.DARK_ERR_INVALID_ARG
+    assert call(dout=0) == bd.DARK_ERR_INVALID_ARG
+    assert call(dM=0) == bd.DARK_ERR_INVALID_ARG
+    assert call(n=nb - 1) == bd.DARK_ERR_WORKSPACE
+    assert call(ws=0) == bd.DARK_ERR_WORKSPACE
+    assert call(dd=_desc(o_str=[0, 0, 3])) == bd.DARK_ERR_INVALID_ARG
+    assert bd.dark_prf_bwd_workspace_bytes(_desc(d_h=48)) == 0
+    assert bd.dark_prf_bwd_workspace_bytes(_desc(L=4096)) >= nb
