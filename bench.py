@@ -528,6 +528,96 @@ def exact_line(w, steps: int) -> dict:
                          "flops_per_launch": flops, "avg_launch_us": round(kern["attention"], 3)}}
 
 
+def bwd_flops_per_token_head(w, chunk: int = 64) -> int:
+    """Algorithmic flops of the backward's matrix products per (token, head):
+    projections of q and k (2 * 2 r d_h), their features (2 * 2 r m), the key
+    and query chunk states (2 * 2 m (d_h+1)), [N, D] from the states
+    (2 m (d_h+1)), dPhi(Q) and dPhi(K) from the states (2 * 2 m (d_h+1)), dV
+    from the state (2 m d_h), dU (2 * 2 m r), dX (2 * 2 r d_h) and dM
+    (2 * 2 r d_h); causal adds the intra-chunk blocks over C = 64 tokens:
+    Phi(Q)Phi(K)^T (2 C m), Gd [V,1]^T (2 C (d_h+1)) and their products with
+    [V,1], Phi(K), Phi(Q) and dN (2 C (d_h+1) + 2 * 2 C m + 2 C d_h)."""
+    d, m, r, C = w.d_h, w.m, w.r, chunk
+    f = 4 * r * d + 4 * r * m + 4 * m * (d + 1) + 2 * m * (d + 1) + 4 * m * (d + 1) + 2 * m * d \
+        + 4 * m * r + 4 * r * d + 4 * r * d
+    if w.causal:
+        f += 2 * C * m + 2 * C * (d + 1) + 2 * C * (d + 1) + 4 * C * m + 2 * C * d
+    return f
+
+
+def bwd_line(w, steps: int) -> dict:
+    """The backward pass (dark_prf_bwd) on a workload's inputs with a seeded
+    upstream gradient: one HIP graph of `steps` backward calls, then one eager
+    pass with per-kernel HIP-event timing for the matrix-product roofline."""
+    import numpy as np
+    import torch
+
+    from random_feature_linear_amd import binding as bd
+    from random_feature_linear_amd.workloads import make_inputs
+    inp = make_inputs(w)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+    dev = {n: torch.from_numpy(inp[n]).to(dt).to("cuda:0") for n in ("q", "k", "v")}
+    rng = np.random.default_rng(w.seed + 7)
+    dout = torch.from_numpy(rng.standard_normal(inp["q"].shape).astype(np.float32)).to(dt).to("cuda:0")
+    M = torch.from_numpy(inp["M"]).to("cuda:0")
+    om = torch.from_numpy(bd.dark_prf_omega(w.seed, w.m, w.r, w.orthogonal)).to("cuda:0")
+    mask = torch.from_numpy(inp["mask"]).to("cuda:0") if inp["mask"] is not None else None
+    grads = [torch.empty_like(dev[n]) for n in ("q", "k", "v")] + [torch.empty_like(M)]
+    d = bd.make_desc(dev["q"], dev["k"], dev["v"], dout, M, om, w.causal)
+    nb = bd.dark_prf_bwd_workspace_bytes(d)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    mptr = mask.data_ptr() if mask is not None else 0
+
+    def step():
+        st = bd.dark_prf_bwd(d, dev["q"].data_ptr(), dev["k"].data_ptr(), dev["v"].data_ptr(), M.data_ptr(),
+                             om.data_ptr(), mptr, dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                             grads[2].data_ptr(), grads[3].data_ptr(), ws.data_ptr(), nb,
+                             torch.cuda.current_stream().cuda_stream)
+        if st != bd.DARK_OK:
+            raise bd.DarkPrfError(st, "dark_prf_bwd")
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    sm = torch.cuda.Stream()
+    sm.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(sm):
+        with torch.cuda.graph(g, stream=sm):
+            for _ in range(steps):
+                step()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del g
+    bd.dark_prf_timing_begin()
+    for _ in range(steps):
+        step()
+    per = bd.dark_prf_timing_end()
+    torch.cuda.synchronize()
+    gemm_ms, gemm_n = per["bwd_gemm"]
+    aux_ms, aux_n = per["bwd_aux"]
+    flops = w.B * w.H * w.L * bwd_flops_per_token_head(w)
+    gemm_per_call_us = 1e3 * gemm_ms / steps
+    ach = flops / (gemm_per_call_us * 1e-6) / 1e12
+    return {"value": round(w.B * w.L / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 6),
+            "config": {"workload": w.name, "path": "backward (dark_prf_bwd)", "B": w.B, "H": w.H,
+                       "H_kv": w.hkv, "L": w.L, "d_h": w.d_h, "m": w.m, "r": w.r, "causal": w.causal,
+                       "launch": "one hipGraph of %d backward calls" % steps},
+            "kernels_us": {"gemm_per_call": round(gemm_per_call_us, 3), "gemm_launches_per_call": gemm_n // steps,
+                           "aux_per_call": round(1e3 * aux_ms / steps, 3), "aux_launches_per_call": aux_n // steps},
+            "roofline": {"bound": "mfma", "kernel": "bgemm (all matrix products of one call)",
+                         "achieved": round(ach, 2), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ach / PEAK_F32_TFLOPS, 4), "traffic": None, "flops_per_launch": flops,
+                         "avg_launch_us": round(gemm_per_call_us, 3)}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -580,6 +670,15 @@ def main() -> int:
                         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"})
         print(json.dumps(rec), flush=True)
         return 0
+    if args.workload.startswith("bwd:"):   # the backward pass on one of the workloads' inputs
+        wb = CONFIGS[args.workload.split(":", 1)[1]]
+        nsteps = max(2, min(args.steps, 50))
+        rec = bwd_line(wb, nsteps)
+        rec.update({"metric": "backward tokens/sec", "n_gpus": 1, "steps": nsteps, "warmup": 3,
+                    "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+                    "data": "synthetic"})
+        print(json.dumps(rec), flush=True)
+        return 0
     if args.workload.startswith("exact:"):   # the exact path on one of the workloads' inputs
         we = CONFIGS[args.workload.split(":", 1)[1]]
         rec = exact_line(we, min(args.steps, 200))
@@ -617,6 +716,7 @@ def main() -> int:
         rec["cross"] = cross_line(max(20, args.steps // 4))
         rec["cross_step"] = cross_step_line(256)
         rec["exact"] = exact_line(w, max(20, args.steps // 4))
+        rec["backward"] = bwd_line(w, 20)
     print(json.dumps(rec), flush=True)
     return 0
 
