@@ -303,7 +303,8 @@ dark_status dark_prf_projection_fix(dark_prf_projection* p, int32_t fixed);
  * desc; 0 for an invalid descriptor.  It holds the fp32 features, the
  * per-chunk states and the intermediate gradients: about
  * 4*B*H*Lp*(4*m + 4*r + 6*d_h + 135) + 8*B*H*(Lp/64)*m*(d_h+1) bytes, with Lp
- * the sequence length rounded up to a multiple of 64.
+ * the sequence length rounded up to a multiple of 64, plus at most
+ * 4*B*H*r*d_h*(Lp/64) bytes of partial sums of dM.
  *
  * dark_prf_bwd - arguments as for dark_prf_fwd, plus:
  *   dout  [B][H][L][d_h] (strides o_str), dtype

@@ -41,7 +41,7 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kChunk = 64;     // tokens per causal chunk
-constexpr int kMChunk = 512;   // tokens per split of the dM reduction
+constexpr int kMTarget = 2048; // workgroups the split dM reduction aims for
 
 __device__ __forceinline__ float ld_f(const float* p) { return *p; }
 __device__ __forceinline__ float ld_f(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
@@ -114,20 +114,35 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
   f32x16 acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-  for (int k0 = 0; k0 < K; k0 += 32) {
+  // the next K slice is fetched into registers while the current one is
+  // multiplied out of LDS
+  float ra[8], rb[8];
+  auto fetch = [&](int k0) {
 #pragma unroll
     for (int e8 = 0; e8 < 8; ++e8) {
       const int e = tid + 256 * e8;
       int i, k;
       if (a_krow) { i = e >> 5; k = e & 31; } else { i = e & 63; k = e >> 6; }
       const int gi = i0 + i, gk = k0 + k;
-      As[i][k] = (gi < a.Arows && gk < K) ? ld_f(A + gi * a.A.si + gk * a.A.sk) : 0.f;
+      ra[e8] = (gi < a.Arows && gk < K) ? ld_f(A + gi * a.A.si + gk * a.A.sk) : 0.f;
       int kb, j;
       if (b_jrow) { kb = e >> 6; j = e & 63; } else { kb = e & 31; j = e >> 5; }
       const int gkb = k0 + kb, gj = j0 + j;
-      Bs[kb][j] = (gkb < K && gj < a.N) ? ld_f(Bp + gkb * a.B.si + gj * a.B.sk) : 0.f;
+      rb[e8] = (gkb < K && gj < a.N) ? ld_f(Bp + gkb * a.B.si + gj * a.B.sk) : 0.f;
+    }
+  };
+  fetch(0);
+  for (int k0 = 0; k0 < K; k0 += 32) {
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) {
+      const int e = tid + 256 * e8;
+      if (a_krow) As[e >> 5][e & 31] = ra[e8];
+      else As[e & 63][e >> 6] = ra[e8];
+      if (b_jrow) Bs[e >> 6][e & 63] = rb[e8];
+      else Bs[e & 31][e >> 5] = rb[e8];
     }
     __syncthreads();
+    if (k0 + 32 < K) fetch(k0 + 32);
 #pragma unroll
     for (int kk = 0; kk < 32; kk += 8)
 #pragma unroll
@@ -172,14 +187,16 @@ __global__ void vx_kernel(const T* v, int64_t sb, int64_t sh, int64_t sl, float*
   }
 }
 
-// nrm[row] = |U_row|^2 / 2
-__global__ void halfnorm_kernel(const float* U, float* nrm, int r, int64_t rows) {
-  const int64_t row = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+// nrm[row] = |U_row|^2 / 2 (one wave per row)
+__global__ __launch_bounds__(256) void halfnorm_kernel(const float* U, float* nrm, int r, int64_t rows) {
+  const int64_t row = blockIdx.x * 4LL + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float* u = U + row * r;
   float s = 0.f;
-  for (int j = 0; j < r; ++j) s = fmaf(u[j], u[j], s);
-  nrm[row] = 0.5f * s;
+  for (int j = lane; j < r; j += 64) s = fmaf(u[j], u[j], s);
+  s = wave_sum(s);
+  if (lane == 0) nrm[row] = 0.5f * s;
 }
 
 // Gd = [dO / D, -(dO . O) / D] per row (one wave per row), 0 when D <= 0 or t >= L.
@@ -301,7 +318,7 @@ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  int C, NC, Lp, NKC, D1;
+  int C, NC, Lp, KC, NKC, D1;
   size_t Uq, Uk, dUq, dUk, nq, nk, rsq, rsk, Pq, Pk, dPq, dPk, Vx, ND, Gd, Sx, Gx, St, Gt, Wc, A2, dQh, dKh, dVh,
       dMp;
   size_t total;
@@ -313,7 +330,12 @@ BwdLayout bwd_layout(const dark_prf_desc& d) {
   const int L = d.L > 0 ? d.L : 1;
   o.NC = (int)cdiv64(L, kChunk);
   o.Lp = o.NC * kChunk;
-  o.NKC = (int)cdiv64(L, kMChunk);
+  // dM = s sum_t dU_t^T x_t is split over runs of KC tokens (a multiple of 64)
+  // so that the partial products fill about kMTarget workgroups
+  const int64_t mtiles = (int64_t)d.B * d.H * cdiv64(d.r, 64) * cdiv64(d.d_h, 64);
+  const int64_t nkc = std::max<int64_t>(1, cdiv64(kMTarget, mtiles));
+  o.KC = (int)std::max<int64_t>(64, cdiv64(cdiv64(L, nkc), 64) * 64);
+  o.NKC = (int)cdiv64(L, o.KC);
   o.D1 = d.d_h + 1;
   const size_t BH = (size_t)d.B * d.H, Lp = o.Lp, m = d.m, r = d.r, dh = d.d_h, D1 = o.D1, NC = o.NC;
   size_t off = 0;
@@ -468,8 +490,8 @@ dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStrea
                     kEpiPlain, 0, L);
   ln.gemm<T, float>(op(p.k, d.k_str[0], d.k_str[1], 0, d.k_str[2], 1, G), Mt, orows(Uk, r), Lp, r, dh, (int)BH, 1, s,
                     0, kEpiPlain, 0, L);
-  ln.aux(halfnorm_kernel, BH * Lp, 256, (const float*)Uq, nq, r, BH * Lp);
-  ln.aux(halfnorm_kernel, BH * Lp, 256, (const float*)Uk, nk, r, BH * Lp);
+  ln.aux(halfnorm_kernel, BH * Lp * 64, 256, (const float*)Uq, nq, r, BH * Lp);
+  ln.aux(halfnorm_kernel, BH * Lp * 64, 256, (const float*)Uk, nk, r, BH * Lp);
   // 2. features phi = exp(u . omega_j - |u|^2 / 2) / sqrt(m); keys masked, rows t >= L zero
   const GOp OmT = op(p.omega, 0, 0, 0, 1, r);   // (k, j) = omega[j][k]
   const float inv_sqrt_m = 1.0f / sqrtf((float)m);
@@ -525,7 +547,7 @@ dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStrea
   const GOp Mh = op(p.M, 0, hM, 0, dh, 1);
   ln.gemm<float, float>(rows(dUq, r), Mh, orows(dQh, dh), Lp, dh, r, (int)BH, 1, s);
   ln.gemm<float, float>(rows(dUk, r), Mh, orows(dKh, dh), Lp, dh, r, (int)BH, 1, s);
-  const int KC = kMChunk, NKC = o.NKC;
+  const int KC = o.KC, NKC = o.NKC;
   const int64_t RD = (int64_t)r * dh;
   const GOut oMp = out(dMp, (int64_t)H * NKC * RD, (int64_t)NKC * RD, RD, dh);
   const GOp dUqT = op(dUq, (int64_t)H * Lp * r, (int64_t)Lp * r, (int64_t)KC * r, 1, r);
