@@ -42,6 +42,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kChunk = 64;     // tokens per causal chunk
 constexpr int kMTarget = 2048; // workgroups the split dM reduction aims for
+constexpr int kSTarget = 4096; // workgroups the non-causal state partials aim for
 
 __device__ __forceinline__ float ld_f(const float* p) { return *p; }
 __device__ __forceinline__ float ld_f(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
@@ -64,6 +65,7 @@ struct GOp {
   const void* p;
   int64_t sb, sh, sc, si, sk;
   int hg;
+  const float* p2;   // PROD operands: element (i, k) is p[..] * p2[..] (same offsets)
 };
 struct GOut {
   float* p;
@@ -80,6 +82,10 @@ struct GemmArgs {
   int Arows;        // rows of A at or beyond this read as 0
   int H, NCB;       // batch = (b*H + h)*NCB + c
   int tiles_n, tiles;
+  // PROD with k contiguous in A: rowsum[bh*rs_sbh + i] = sum_k A(i, k), written
+  // by the workgroups of the first column tile
+  float* rowsum;
+  int64_t rs_sbh;
   float alpha;
   int accumulate;   // C += result instead of C = result
   int epi;
@@ -91,7 +97,7 @@ struct GemmArgs {
   int L;
 };
 
-template <typename TA, typename TB>
+template <typename TA, typename TB, bool PROD>
 __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
   __shared__ float As[64][33];   // [i][k]
   __shared__ float Bs[32][65];   // [k][j]
@@ -101,7 +107,9 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
   const int tm = tile / a.tiles_n, tn = tile - tm * a.tiles_n;
   const int bh = batch / a.NCB, c = batch - bh * a.NCB;
   const int b = bh / a.H, h = bh - b * a.H;
-  const TA* A = static_cast<const TA*>(a.A.p) + b * a.A.sb + (int64_t)(h / a.A.hg) * a.A.sh + c * a.A.sc;
+  const int64_t aoff = b * a.A.sb + (int64_t)(h / a.A.hg) * a.A.sh + c * a.A.sc;
+  const TA* A = static_cast<const TA*>(a.A.p) + aoff;
+  const float* A2 = PROD ? a.A.p2 + aoff : nullptr;
   const TB* Bp = static_cast<const TB*>(a.B.p) + b * a.B.sb + (int64_t)(h / a.B.hg) * a.B.sh + c * a.B.sc;
   float* C = a.C.p + b * a.C.sb + h * a.C.sh + c * a.C.sc;
   const int K = a.Ktot > 0 ? min(a.K, a.Ktot - c * a.K) : a.K;
@@ -124,18 +132,28 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
       int i, k;
       if (a_krow) { i = e >> 5; k = e & 31; } else { i = e & 63; k = e >> 6; }
       const int gi = i0 + i, gk = k0 + k;
-      ra[e8] = (gi < a.Arows && gk < K) ? ld_f(A + gi * a.A.si + gk * a.A.sk) : 0.f;
+      if (gi < a.Arows && gk < K) {
+        const int64_t o = gi * a.A.si + gk * a.A.sk;
+        ra[e8] = PROD ? ld_f(A + o) * A2[o] : ld_f(A + o);
+      } else {
+        ra[e8] = 0.f;
+      }
       int kb, j;
       if (b_jrow) { kb = e >> 6; j = e & 63; } else { kb = e & 31; j = e >> 5; }
       const int gkb = k0 + kb, gj = j0 + j;
       rb[e8] = (gkb < K && gj < a.N) ? ld_f(Bp + gkb * a.B.si + gj * a.B.sk) : 0.f;
     }
   };
+  // with k contiguous in A, thread tid holds rows tid / 32 + 8 e8 in every slice
+  float rsum[8];
+#pragma unroll
+  for (int e8 = 0; e8 < 8; ++e8) rsum[e8] = 0.f;
   fetch(0);
   for (int k0 = 0; k0 < K; k0 += 32) {
 #pragma unroll
     for (int e8 = 0; e8 < 8; ++e8) {
       const int e = tid + 256 * e8;
+      if (PROD) rsum[e8] += ra[e8];
       if (a_krow) As[e >> 5][e & 31] = ra[e8];
       else As[e & 63][e >> 6] = ra[e8];
       if (b_jrow) Bs[e >> 6][e & 63] = rb[e8];
@@ -150,6 +168,16 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[wi + l32][kk + 4 * g + s], Bs[kk + 4 * g + s][wj + l32],
                                                    acc, 0, 0, 0);
     __syncthreads();
+  }
+  if (PROD && a.rowsum != nullptr && tn == 0) {
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) {
+      float v = rsum[e8];
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+      const int row = i0 + (tid >> 5) + 8 * e8;
+      if ((tid & 31) == 0 && row < a.M) a.rowsum[bh * a.rs_sbh + row] = v;
+    }
   }
   const int col = j0 + wj + l32;
   if (col >= a.N) return;
@@ -222,23 +250,6 @@ __global__ __launch_bounds__(256) void gd_kernel(const T* dout, int64_t sb, int6
   }
   dot = wave_sum(dot);
   if (lane == 0) gd[d] = -dot * inv;
-}
-
-// dE = dP * P in place and rs[row] = sum_j dE[row][j] (one wave per row)
-__global__ __launch_bounds__(256) void de_kernel(float* dP, const float* P, float* rs, int m, int64_t rows) {
-  const int64_t row = blockIdx.x * 4LL + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  float* dp = dP + row * m;
-  const float* p = P + row * m;
-  float s = 0.f;
-  for (int j = lane; j < m; j += 64) {
-    const float x = dp[j] * p[j];
-    dp[j] = x;
-    s += x;
-  }
-  s = wave_sum(s);
-  if (lane == 0) rs[row] = s;
 }
 
 // dU -= U * rs (per row)
@@ -318,7 +329,7 @@ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  int C, NC, Lp, KC, NKC, D1;
+  int C, NC, Lp, KC, NKC, D1, CS, NCS;
   size_t Uq, Uk, dUq, dUk, nq, nk, rsq, rsk, Pq, Pk, dPq, dPk, Vx, ND, Gd, Sx, Gx, St, Gt, Wc, A2, dQh, dKh, dVh,
       dMp;
   size_t total;
@@ -337,6 +348,17 @@ BwdLayout bwd_layout(const dark_prf_desc& d) {
   o.KC = (int)std::max<int64_t>(64, cdiv64(cdiv64(L, nkc), 64) * 64);
   o.NKC = (int)cdiv64(L, o.KC);
   o.D1 = d.d_h + 1;
+  // the state partials: per 64-token chunk when causal (the prefix needs them);
+  // otherwise per run of CS tokens, sized so the partial products fill about
+  // kSTarget workgroups, and summed
+  if (d.causal) {
+    o.CS = kChunk;
+  } else {
+    const int64_t stiles = (int64_t)d.B * d.H * cdiv64(d.m, 64) * cdiv64(d.d_h + 1, 64);
+    const int64_t ncs = std::max<int64_t>(1, cdiv64(kSTarget, stiles));
+    o.CS = (int)std::max<int64_t>(64, cdiv64(cdiv64(o.Lp, ncs), 64) * 64);
+  }
+  o.NCS = (int)cdiv64(o.Lp, o.CS);
   const size_t BH = (size_t)d.B * d.H, Lp = o.Lp, m = d.m, r = d.r, dh = d.d_h, D1 = o.D1, NC = o.NC;
   size_t off = 0;
   auto take = [&](size_t floats) {
@@ -359,8 +381,8 @@ BwdLayout bwd_layout(const dark_prf_desc& d) {
   o.Vx = take(BH * Lp * D1);
   o.ND = take(BH * Lp * D1);
   o.Gd = take(BH * Lp * D1);
-  o.Sx = take(BH * NC * m * D1);
-  o.Gx = take(BH * NC * m * D1);
+  o.Sx = take(BH * o.NCS * m * D1);
+  o.Gx = take(BH * o.NCS * m * D1);
   o.St = take(d.causal ? 0 : BH * m * D1);
   o.Gt = take(d.causal ? 0 : BH * m * D1);
   o.Wc = take(d.causal ? BH * Lp * kChunk : 0);
@@ -382,6 +404,7 @@ GOp op(const void* p, int64_t sb, int64_t sh, int64_t sc, int64_t si, int64_t sk
   o.si = si;
   o.sk = sk;
   o.hg = hg;
+  o.p2 = nullptr;
   return o;
 }
 GOut out(float* p, int64_t sb, int64_t sh, int64_t sc, int64_t si) {
@@ -400,10 +423,10 @@ struct Launcher {
   double flops = 0.0;
   dark_status status = DARK_OK;
 
-  template <typename TA, typename TB>
+  template <typename TA, typename TB, bool PROD = false>
   void gemm(GOp A, GOp B, GOut C, int M, int N, int K, int batches, int NCB, float alpha = 1.f, int accumulate = 0,
             int epi = kEpiPlain, int Ktot = 0, int Arows = -1, const float* nrm = nullptr, int64_t nrm_sbh = 0,
-            const uint8_t* mask = nullptr, int L = 0) {
+            const uint8_t* mask = nullptr, int L = 0, float* rowsum = nullptr, int64_t rs_sbh = 0) {
     if (status != DARK_OK || M <= 0 || N <= 0 || batches <= 0) return;
     GemmArgs a;
     a.A = A;
@@ -418,6 +441,12 @@ struct Launcher {
     a.NCB = NCB;
     a.tiles_n = (N + 63) / 64;
     a.tiles = ((M + 63) / 64) * a.tiles_n;
+    a.rowsum = rowsum;
+    a.rs_sbh = rs_sbh;
+    if (rowsum != nullptr && (!PROD || A.sk != 1 || NCB != 1)) {
+      status = DARK_ERR_UNSUPPORTED;
+      return;
+    }
     a.alpha = alpha;
     a.accumulate = accumulate;
     a.epi = epi;
@@ -434,7 +463,7 @@ struct Launcher {
     const int64_t kt = Ktot > 0 ? (int64_t)Ktot * (batches / NCB) : (int64_t)K * batches;
     flops += 2.0 * M * N * (double)kt;
     KernelTimer tm(kBwdGemm, st);
-    hipLaunchKernelGGL((bgemm_kernel<TA, TB>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bgemm_kernel<TA, TB, PROD>), dim3((unsigned)grid), dim3(256), 0, st, a);
     if (hipGetLastError() != hipSuccess) status = DARK_ERR_HIP;
   }
 
@@ -471,11 +500,14 @@ dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStrea
   auto rows = [&](const float* p, int w) { return op(p, (int64_t)H * Lp * w, (int64_t)Lp * w, (int64_t)C * w, w, 1); };
   auto rowsT = [&](const float* p, int w) { return op(p, (int64_t)H * Lp * w, (int64_t)Lp * w, (int64_t)C * w, 1, w); };
   auto orows = [&](float* p, int w) { return out(p, (int64_t)H * Lp * w, (int64_t)Lp * w, (int64_t)C * w, w); };
-  // chunk states [BH][NC][m][D1]
+  // state partials [BH][NCS][m][D1], one per run of CS tokens (CS = C when causal)
+  const int CS = o.CS, NCS = o.NCS;
   const int64_t X = (int64_t)m * D1;
-  auto states = [&](const float* p) { return op(p, (int64_t)H * NC * X, (int64_t)NC * X, X, D1, 1); };
-  auto statesT = [&](const float* p) { return op(p, (int64_t)H * NC * X, (int64_t)NC * X, X, 1, D1); };
-  auto ostates = [&](float* p) { return out(p, (int64_t)H * NC * X, (int64_t)NC * X, X, D1); };
+  auto states = [&](const float* p) { return op(p, (int64_t)H * NCS * X, (int64_t)NCS * X, X, D1, 1); };
+  auto statesT = [&](const float* p) { return op(p, (int64_t)H * NCS * X, (int64_t)NCS * X, X, 1, D1); };
+  auto ostates = [&](float* p) { return out(p, (int64_t)H * NCS * X, (int64_t)NCS * X, X, D1); };
+  auto run = [&](const float* p, int w) { return op(p, (int64_t)H * Lp * w, (int64_t)Lp * w, (int64_t)CS * w, w, 1); };
+  auto runT = [&](const float* p, int w) { return op(p, (int64_t)H * Lp * w, (int64_t)Lp * w, (int64_t)CS * w, 1, w); };
   // one total state per (b, h) [BH][m][D1]
   auto tot = [&](const float* p) { return op(p, (int64_t)H * X, X, 0, D1, 1); };
   auto totT = [&](const float* p) { return op(p, (int64_t)H * X, X, 0, 1, D1); };
@@ -502,8 +534,9 @@ dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStrea
   // 3. [V, 1] per query head
   ln.aux(vx_kernel<T>, BH * Lp * D1, 256, (const T*)p.v, d.v_str[0], d.v_str[1], d.v_str[2], Vx, H, G, L, Lp, dh,
          BH * Lp * D1);
-  // 4. key-side chunk states Phi(K_c)^T [V, 1]_c
-  ln.gemm<float, float>(rowsT(Pk, m), rows(Vx, D1), ostates(Sx), m, D1, C, (int)(BH * NC), NC);
+  // 4. key-side state partials Phi(K_c)^T [V, 1]_c
+  ln.gemm<float, float>(runT(Pk, m), run(Vx, D1), ostates(Sx), m, D1, CS, (int)(BH * NCS), NCS, 1.f, 0, kEpiPlain,
+                        Lp);
   const int NB = (int)(BH * NC);
   if (d.causal) {
     ln.aux(chunk_scan_kernel, BH * X, 256, Sx, NC, X, BH * X, 0);
@@ -512,14 +545,15 @@ dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStrea
     ln.gemm<float, float>(rows(Pq, m), states(Sx), orows(ND, D1), C, D1, m, NB, NC);
     ln.gemm<float, float>(blk(Wc), rows(Vx, D1), orows(ND, D1), C, D1, C, NB, NC, 1.f, 1);
   } else {
-    ln.aux(chunk_sum_kernel, BH * X, 256, (const float*)Sx, St, NC, X, BH * X);
+    ln.aux(chunk_sum_kernel, BH * X, 256, (const float*)Sx, St, NCS, X, BH * X);
     ln.gemm<float, float>(rows(Pq, m), tot(St), orows(ND, D1), Lp, D1, m, (int)BH, 1);
   }
   // 6. Gd = [dO / D, -(dO . O) / D]
   ln.aux(gd_kernel<T>, BH * Lp * 64, 256, (const T*)p.dout, d.o_str[0], d.o_str[1], d.o_str[2], (const float*)ND, Gd,
          H, L, Lp, dh, BH * Lp);
-  // 7. dPhi(Q), the query-side chunk states Phi(Q_c)^T Gd_c, dPhi(K) and dV
-  ln.gemm<float, float>(rowsT(Pq, m), rows(Gd, D1), ostates(Gx), m, D1, C, NB, NC);
+  // 7. dPhi(Q), the query-side state partials Phi(Q_c)^T Gd_c, dPhi(K) and dV
+  ln.gemm<float, float>(runT(Pq, m), run(Gd, D1), ostates(Gx), m, D1, CS, (int)(BH * NCS), NCS, 1.f, 0, kEpiPlain,
+                        Lp);
   if (d.causal) {
     ln.aux(chunk_scan_kernel, BH * X, 256, Gx, NC, X, BH * X, 1);
     ln.gemm<float, float>(rows(Gd, D1), rowsT(Vx, D1), oblk(A2), C, C, D1, NB, NC, 1.f, 0, kEpiTril);
@@ -530,17 +564,21 @@ dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStrea
     ln.gemm<float, float>(rows(Pk, m), states(Gx), orows(dVh, dh), C, dh, m, NB, NC);
     ln.gemm<float, float>(blkT(Wc), rows(Gd, D1), orows(dVh, dh), C, dh, C, NB, NC, 1.f, 1);
   } else {
-    ln.aux(chunk_sum_kernel, BH * X, 256, (const float*)Gx, Gt, NC, X, BH * X);
+    ln.aux(chunk_sum_kernel, BH * X, 256, (const float*)Gx, Gt, NCS, X, BH * X);
     ln.gemm<float, float>(rows(Gd, D1), totT(St), orows(dPq, m), Lp, m, D1, (int)BH, 1);
     ln.gemm<float, float>(rows(Vx, D1), totT(Gt), orows(dPk, m), Lp, m, D1, (int)BH, 1);
     ln.gemm<float, float>(rows(Pk, m), tot(Gt), orows(dVh, dh), Lp, dh, m, (int)BH, 1);
   }
   // 8. through the feature map: dU = (dPhi * Phi) Omega - U * rowsum(dPhi * Phi)
-  ln.aux(de_kernel, BH * Lp * 64, 256, dPq, (const float*)Pq, rsq, m, BH * Lp);
-  ln.aux(de_kernel, BH * Lp * 64, 256, dPk, (const float*)Pk, rsk, m, BH * Lp);
-  const GOp Om = op(p.omega, 0, 0, 0, r, 1);
-  ln.gemm<float, float>(rows(dPq, m), Om, orows(dUq, r), Lp, r, m, (int)BH, 1);
-  ln.gemm<float, float>(rows(dPk, m), Om, orows(dUk, r), Lp, r, m, (int)BH, 1);
+  // (the A operand dPhi * Phi is formed in the loads, which also sum its rows)
+  const GOp Om = op(p.omega, 0, 0, 0, r, 1);   // (k, j) = omega[k][j]
+  GOp dEq = rows(dPq, m), dEk = rows(dPk, m);
+  dEq.p2 = Pq;
+  dEk.p2 = Pk;
+  ln.gemm<float, float, true>(dEq, Om, orows(dUq, r), Lp, r, m, (int)BH, 1, 1.f, 0, kEpiPlain, 0, -1, nullptr, 0,
+                              nullptr, 0, rsq, Lp);
+  ln.gemm<float, float, true>(dEk, Om, orows(dUk, r), Lp, r, m, (int)BH, 1, 1.f, 0, kEpiPlain, 0, -1, nullptr, 0,
+                              nullptr, 0, rsk, Lp);
   ln.aux(fixdu_kernel, BH * Lp * r, 256, dUq, (const float*)Uq, (const float*)rsq, r, BH * Lp * r);
   ln.aux(fixdu_kernel, BH * Lp * r, 256, dUk, (const float*)Uk, (const float*)rsk, r, BH * Lp * r);
   // 9. dX = s dU M_h, dM_h = s sum dU^T X
