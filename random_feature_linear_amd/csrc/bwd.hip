@@ -40,7 +40,10 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kChunk = 64;     // tokens per causal chunk
+// Tokens per chunk.  The causal prefix needs a state per chunk; longer chunks
+// write fewer m x (d_h + 1) states but do more intra-chunk work: 128 tokens pay
+// off once the state is wide (d_h >= 128), 64 below.
+inline int bwd_chunk(const dark_prf_desc& d) { return d.causal && d.d_h >= 128 ? 128 : 64; }
 constexpr int kMTarget = 2048; // workgroups the split dM reduction aims for
 constexpr int kSTarget = 4096; // workgroups the non-causal state partials aim for
 
@@ -337,10 +340,10 @@ struct BwdLayout {
 
 BwdLayout bwd_layout(const dark_prf_desc& d) {
   BwdLayout o;
-  o.C = kChunk;
+  o.C = bwd_chunk(d);
   const int L = d.L > 0 ? d.L : 1;
-  o.NC = (int)cdiv64(L, kChunk);
-  o.Lp = o.NC * kChunk;
+  o.NC = (int)cdiv64(L, o.C);
+  o.Lp = o.NC * o.C;
   // dM = s sum_t dU_t^T x_t is split over runs of KC tokens (a multiple of 64)
   // so that the partial products fill about kMTarget workgroups
   const int64_t mtiles = (int64_t)d.B * d.H * cdiv64(d.r, 64) * cdiv64(d.d_h, 64);
@@ -352,7 +355,7 @@ BwdLayout bwd_layout(const dark_prf_desc& d) {
   // otherwise per run of CS tokens, sized so the partial products fill about
   // kSTarget workgroups, and summed
   if (d.causal) {
-    o.CS = kChunk;
+    o.CS = o.C;
   } else {
     const int64_t stiles = (int64_t)d.B * d.H * cdiv64(d.m, 64) * cdiv64(d.d_h + 1, 64);
     const int64_t ncs = std::max<int64_t>(1, cdiv64(kSTarget, stiles));
@@ -385,8 +388,8 @@ BwdLayout bwd_layout(const dark_prf_desc& d) {
   o.Gx = take(BH * o.NCS * m * D1);
   o.St = take(d.causal ? 0 : BH * m * D1);
   o.Gt = take(d.causal ? 0 : BH * m * D1);
-  o.Wc = take(d.causal ? BH * Lp * kChunk : 0);
-  o.A2 = take(d.causal ? BH * Lp * kChunk : 0);
+  o.Wc = take(d.causal ? BH * Lp * o.C : 0);
+  o.A2 = take(d.causal ? BH * Lp * o.C : 0);
   o.dQh = take(BH * Lp * dh);
   o.dKh = take(BH * Lp * dh);
   o.dVh = take(BH * Lp * dh);
