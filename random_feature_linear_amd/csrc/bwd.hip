@@ -100,10 +100,13 @@ struct GemmArgs {
   int L;
 };
 
+constexpr int kKT = 32;   // K depth of one LDS slice
+
 template <typename TA, typename TB, bool PROD>
 __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
-  __shared__ float As[64][33];   // [i][k]
-  __shared__ float Bs[32][65];   // [k][j]
+  constexpr int KT = kKT, NE = 64 * KT / 256;   // elements of each operand per thread and slice
+  __shared__ float As[64][KT + 1];   // [i][k]
+  __shared__ float Bs[KT][65];       // [k][j]
   const int64_t bid = blockIdx.x;
   const int batch = (int)(bid / a.tiles);
   const int tile = (int)(bid - (int64_t)batch * a.tiles);
@@ -122,64 +125,66 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
   const int i0 = tm * 64, j0 = tn * 64;
   const bool a_krow = a.A.sk == 1;   // k contiguous in A: threads walk k
   const bool b_jrow = a.B.sk == 1;   // j contiguous in B: threads walk j
+  // offsets inside one batch fit in 32 bits (checked on the host)
+  const int asi = (int)a.A.si, ask = (int)a.A.sk, bsi = (int)a.B.si, bsk = (int)a.B.sk;
   f32x16 acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
   // the next K slice is fetched into registers while the current one is
   // multiplied out of LDS
-  float ra[8], rb[8];
+  float ra[NE], rb[NE];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) {
+    for (int e8 = 0; e8 < NE; ++e8) {
       const int e = tid + 256 * e8;
       int i, k;
-      if (a_krow) { i = e >> 5; k = e & 31; } else { i = e & 63; k = e >> 6; }
+      if (a_krow) { i = e / KT; k = e % KT; } else { i = e & 63; k = e >> 6; }
       const int gi = i0 + i, gk = k0 + k;
       if (gi < a.Arows && gk < K) {
-        const int64_t o = gi * a.A.si + gk * a.A.sk;
+        const int o = gi * asi + gk * ask;
         ra[e8] = PROD ? ld_f(A + o) * A2[o] : ld_f(A + o);
       } else {
         ra[e8] = 0.f;
       }
       int kb, j;
-      if (b_jrow) { kb = e >> 6; j = e & 63; } else { kb = e & 31; j = e >> 5; }
+      if (b_jrow) { kb = e >> 6; j = e & 63; } else { kb = e % KT; j = e / KT; }
       const int gkb = k0 + kb, gj = j0 + j;
-      rb[e8] = (gkb < K && gj < a.N) ? ld_f(Bp + gkb * a.B.si + gj * a.B.sk) : 0.f;
+      rb[e8] = (gkb < K && gj < a.N) ? ld_f(Bp + (gkb * bsi + gj * bsk)) : 0.f;
     }
   };
-  // with k contiguous in A, thread tid holds rows tid / 32 + 8 e8 in every slice
-  float rsum[8];
+  // with k contiguous in A, thread tid holds rows tid / KT + (256 / KT) e8 in every slice
+  float rsum[NE];
 #pragma unroll
-  for (int e8 = 0; e8 < 8; ++e8) rsum[e8] = 0.f;
+  for (int e8 = 0; e8 < NE; ++e8) rsum[e8] = 0.f;
   fetch(0);
-  for (int k0 = 0; k0 < K; k0 += 32) {
+  for (int k0 = 0; k0 < K; k0 += KT) {
 #pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) {
+    for (int e8 = 0; e8 < NE; ++e8) {
       const int e = tid + 256 * e8;
       if (PROD) rsum[e8] += ra[e8];
-      if (a_krow) As[e >> 5][e & 31] = ra[e8];
+      if (a_krow) As[e / KT][e % KT] = ra[e8];
       else As[e & 63][e >> 6] = ra[e8];
       if (b_jrow) Bs[e >> 6][e & 63] = rb[e8];
-      else Bs[e & 31][e >> 5] = rb[e8];
+      else Bs[e % KT][e / KT] = rb[e8];
     }
     __syncthreads();
-    if (k0 + 32 < K) fetch(k0 + 32);
+    if (k0 + KT < K) fetch(k0 + KT);
 #pragma unroll
-    for (int kk = 0; kk < 32; kk += 8)
+    for (int kk = 0; kk < KT; kk += 8)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[wi + l32][kk + 4 * g + s], Bs[kk + 4 * g + s][wj + l32],
                                                    acc, 0, 0, 0);
     __syncthreads();
   }
-  if (PROD && a.rowsum != nullptr && tn == 0) {
+  if (PROD && a.rowsum != nullptr && tn == 0) {   // KT lanes share a row
 #pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) {
+    for (int e8 = 0; e8 < NE; ++e8) {
       float v = rsum[e8];
 #pragma unroll
-      for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-      const int row = i0 + (tid >> 5) + 8 * e8;
-      if ((tid & 31) == 0 && row < a.M) a.rowsum[bh * a.rs_sbh + row] = v;
+      for (int o = KT / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+      const int row = i0 + tid / KT + (256 / KT) * e8;
+      if ((tid % KT) == 0 && row < a.M) a.rowsum[bh * a.rs_sbh + row] = v;
     }
   }
   const int col = j0 + wj + l32;
@@ -458,7 +463,9 @@ struct Launcher {
     a.mask = mask;
     a.L = L;
     const int64_t grid = (int64_t)batches * a.tiles;
-    if (grid > INT_MAX) {
+    const int64_t amax = (int64_t)(a.Arows - 1) * A.si + (int64_t)(K - 1) * A.sk;
+    const int64_t bmax = (int64_t)(K - 1) * B.si + (int64_t)(N - 1) * B.sk;
+    if (grid > INT_MAX || amax > INT_MAX || bmax > INT_MAX) {
       status = DARK_ERR_UNSUPPORTED;
       return;
     }
