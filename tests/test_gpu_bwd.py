@@ -30,6 +30,7 @@ CASES = [
     ("bwd_bf16_d256_nc",  "bf16", 1, 4, 1,   100, 256, 64,  200, False, True,  True,  "random"),
     ("bwd_bf16_L700_c",   "bf16", 1, 2, 1,   700, 64,  64,  32,  True,  False, True,  "tail"),
     ("bwd_f32_m512_nc",   "f32",  1, 1, 1,   260, 64,  512, 64,  False, True,  True,  "none"),
+    ("bwd_f32_d16_gqa4",  "f32",  1, 8, 2,   90,  16,  32,  8,   True,  False, True,  "random"),
 ]
 
 
@@ -139,3 +140,25 @@ def test_bwd_single_token():
     assert np.max(np.abs(dv - dout.sum(axis=1, keepdims=True))) <= 1e-6 * np.max(np.abs(dout))
     for g in (dq, dk, dM):
         assert np.max(np.abs(g)) <= 1e-4 * np.max(np.abs(dout)), np.max(np.abs(g))
+
+
+def test_bwd_packed_qkv_strides():
+    """q, k and v as views of one packed [B][L][3][H][d_h] tensor: the gradients
+    take the views' strides and equal those of the contiguous call bit for bit."""
+    import torch
+    w = Workload(name="bwd_packed", B=2, H=4, L=150, d_h=64, m=64, r=32, dtype="bf16", causal=True, seed=21,
+                 mask_kind="tail", max_pad=40)
+    inp = make_inputs(w)
+    dev = device_inputs(w, inp)
+    packed = torch.empty((2, 150, 3, 4, 64), dtype=torch.bfloat16, device="cuda:0")
+    views = [packed[:, :, i].permute(0, 2, 1, 3) for i in range(3)]   # [B][H][L][d_h], rows 3*H*d_h apart
+    for vw, n in zip(views, ("q", "k", "v")):
+        vw.copy_(dev[n])
+    g = to_dev(_dout(w, inp["q"].shape), torch.bfloat16)
+    got = bd.prf_attention_backward(*views, dev["M"], dev["omega"], g, mask=dev["mask"], causal=True)
+    ref = bd.prf_attention_backward(dev["q"], dev["k"], dev["v"], dev["M"], dev["omega"], g, mask=dev["mask"],
+                                    causal=True)
+    torch.cuda.synchronize()
+    assert got[0].stride() == views[0].stride() and got[2].stride() == views[2].stride()
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
