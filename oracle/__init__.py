@@ -9,6 +9,7 @@ from .prf_oracle import (  # noqa: F401
     attend_noncausal,
     attention,
     attention_backward,
+    attention_backward_noncausal_head,
     context_state,
     cross_attention,
     decode_step,

@@ -334,3 +334,66 @@ def attention_backward(q, k, v, M, omega, dout, mask: Optional[np.ndarray] = Non
             else:
                 dM += dM_h
     return dq, dk, dv, dM
+
+
+def attention_backward_noncausal_head(q, k, v, M_h, omega, dout, key_mask=None, block: int = 4096):
+    """Gradients of one non-causal (b, h) slice in linear time, for long inputs.
+
+    The same chain rule as attention_backward, with the sums over the other
+    side taken through totals instead of the quadratic weights (section
+    "Kernel", attention equation, associative order): S = Phi(K)^T V and
+    z = Phi(K)^T 1 for the outputs and dPhi(Q) = dN S^T + dD z^T; then
+    G = Phi(Q)^T dN and g = Phi(Q)^T dD for dPhi(K) = V G^T + 1 g^T and
+    dV = Phi(K) G.  Rows are processed in blocks of `block`.  q, k, v, dout are
+    [L][d_h], M_h [r][d_h], key_mask [L] or None.  Returns (dq, dk, dv, dM_h),
+    where dk, dv, dM_h are this head's contributions.
+    """
+    q, k, v, dout, omega, M_h = f64(q), f64(k), f64(v), f64(dout), f64(omega), f64(M_h)
+    L, d = q.shape
+    m = omega.shape[0]
+    s = qk_scale(d)
+    valid = np.ones(L) if key_mask is None else (np.asarray(key_mask) != 0).astype(np.float64)
+
+    def feats(X, lo, hi):
+        return prf_features(X[lo:hi], M_h, omega), project(X[lo:hi], M_h)
+
+    def through_features(dP, P, U, X):
+        dE = dP * P
+        dU = dE @ omega - U * dE.sum(axis=1, keepdims=True)
+        return s * (dU @ M_h), s * (dU.T @ X)
+
+    S = np.zeros((m, d))
+    z = np.zeros(m)
+    for lo in range(0, L, block):
+        PK, _ = feats(k, lo, lo + block)
+        PK = PK * valid[lo:lo + block, None]
+        S += PK.T @ v[lo:lo + block]
+        z += PK.sum(axis=0)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dM = np.zeros_like(M_h)
+    G = np.zeros((m, d))
+    g = np.zeros(m)
+    for lo in range(0, L, block):
+        hi = min(L, lo + block)
+        PQ, UQ = feats(q, lo, hi)
+        N, D = PQ @ S, PQ @ z
+        O = _ratio(N, D)
+        ok = D > 0
+        dN = np.zeros_like(N)
+        dD = np.zeros(hi - lo)
+        dN[ok] = dout[lo:hi][ok] / D[ok, None]
+        dD[ok] = -np.sum(dout[lo:hi][ok] * O[ok], axis=1) / D[ok]
+        G += PQ.T @ dN
+        g += PQ.T @ dD
+        dq[lo:hi], dMq = through_features(dN @ S.T + dD[:, None] * z[None, :], PQ, UQ, q[lo:hi])
+        dM += dMq
+    for lo in range(0, L, block):
+        hi = min(L, lo + block)
+        PK, UK = feats(k, lo, hi)
+        PK = PK * valid[lo:hi, None]
+        dv[lo:hi] = PK @ G
+        dk[lo:hi], dMk = through_features(v[lo:hi] @ G.T + g[None, :], PK, UK, k[lo:hi])
+        dM += dMk
+    return dq, dk, dv, dM

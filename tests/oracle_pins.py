@@ -474,8 +474,38 @@ def check_backward_finite_differences(seed=81, eps=1e-5, n_dir=3):
                     assert np.all(grads["q"][0, :, 0] == 0)
 
 
+def check_backward_linear_form(seed=82, eps=1e-5):
+    """The linear-time non-causal backward of one head: central finite
+    differences of the oracle's forward, with a masked key and blocks shorter
+    than the sequence; dk and dv of the masked key are exactly 0."""
+    rng = np.random.default_rng(seed)
+    L, d, m, r = 13, 4, 8, 3
+    q, k, v, M, om = _random_case(rng, B=1, H=1, H_kv=1, Lq=L, d=d, m=m, r=r, per_head=False)
+    q, k = 0.7 * q, 0.7 * k
+    mask = np.ones((1, L), np.uint8)
+    mask[0, [2, 8]] = 0
+    dout = rng.standard_normal((1, 1, L, d))
+    grads = dict(zip("qkvM", po.attention_backward_noncausal_head(q[0, 0], k[0, 0], v[0, 0], M, om, dout[0, 0],
+                                                                  key_mask=mask[0], block=5)))
+    base = dict(q=q, k=k, v=v, M=M)
+
+    def f(**over):
+        a = dict(base, **over)
+        return float(np.sum(dout * po.attention(a["q"], a["k"], a["v"], a["M"], om, mask=mask)))
+
+    for name, x in base.items():
+        g = grads[name] if name == "M" else grads[name][None, None]
+        for _ in range(3):
+            dirn = rng.standard_normal(x.shape)
+            fd = (f(**{name: x + eps * dirn}) - f(**{name: x - eps * dirn})) / (2 * eps)
+            an = float(np.sum(g * dirn))
+            assert abs(an - fd) <= 1e-6 * max(1.0, abs(fd)), f"linear-form d{name}: {an:.9e} vs {fd:.9e}"
+    assert np.all(grads["k"][[2, 8]] == 0) and np.all(grads["v"][[2, 8]] == 0)
+
+
 ALL_CHECKS = [
     check_backward_finite_differences,
+    check_backward_linear_form,
     check_closed_form_features,
     check_closed_form_attention,
     check_associative_vs_explicit,

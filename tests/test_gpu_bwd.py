@@ -162,3 +162,47 @@ def test_bwd_packed_qkv_strides():
     assert got[0].stride() == views[0].stride() and got[2].stride() == views[2].stride()
     for a, b in zip(got, ref):
         assert torch.equal(a, b)
+
+
+def test_bwd_c3_full_size():
+    """The L=64K non-causal workload at its full size: every (b, h) on the
+    device; the oracle's linear-time form checks dq, dk, dv of heads 0 and 5 and
+    the shared dM, which sums all eight heads."""
+    w = CONFIGS["c3_long_L64K"]
+    assert not w.causal and not w.per_head_geometry and w.hkv == w.H and w.B == 1
+    inp = make_inputs(w)
+    dout = _dout(w, inp["q"].shape)
+    got = _run(w, inp, dout)
+    om = oracle_omega(w)
+    key_mask = None if inp["mask"] is None else inp["mask"][0]
+    dM = np.zeros_like(got[3])
+    for h in range(w.H):
+        ref = oracle.attention_backward_noncausal_head(inp["q"][0, h], inp["k"][0, h], inp["v"][0, h], inp["M"], om,
+                                                       dout[0, h], key_mask=key_mask)
+        dM += ref[3]
+        if h in (0, 5):
+            floor = 1e-4 * max(float(np.max(np.abs(r))) for r in ref[:3])
+            errs = [_err(got[i][0, h], ref[i], floor) for i in range(3)]
+            say(f"[bwd] c3 head {h}: dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
+            assert max(errs) <= TOL[w.dtype], errs
+    e = normwise_rel_err(got[3], dM)
+    say(f"[bwd] c3 dM over all heads: {e:.2e}")
+    assert e <= TOL[w.dtype]
+
+
+def test_bwd_c4_batch_row():
+    """The L=8192 GQA workload at its full size: all (b, h) on the device; the
+    dense oracle checks batch row 0 (its eight query heads share one key/value
+    head, so dk and dv of that row sum all eight)."""
+    w = CONFIGS["c4_gqa_L8192"]
+    assert w.hkv == 1 and w.causal
+    inp = make_inputs(w)
+    dout = _dout(w, inp["q"].shape)
+    got = _run(w, inp, dout)
+    sl = lambda x: x[0:1]
+    ref = oracle.attention_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), inp["M"], oracle_omega(w), sl(dout),
+                                    mask=None if inp["mask"] is None else sl(inp["mask"]), causal=True)
+    floor = 1e-4 * max(float(np.max(np.abs(r))) for r in ref[:3])
+    errs = [max(_err(sl(got[i])[0, j], ref[i][0, j], floor) for j in range(ref[i].shape[1])) for i in range(3)]
+    say(f"[bwd] c4 batch row 0: dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
+    assert max(errs) <= TOL[w.dtype], errs

@@ -56,3 +56,7 @@ def test_cross_vs_explicit():
 
 def test_backward_finite_differences():
     pins.check_backward_finite_differences()
+
+
+def test_backward_linear_form():
+    pins.check_backward_linear_form()
