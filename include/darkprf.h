@@ -300,7 +300,8 @@ dark_status dark_prf_projection_fix(dark_prf_projection* p, int32_t fixed);
  * (out fixed at 0) gets no gradient; a masked key gets dk = dv = 0.
  *
  * dark_prf_bwd_workspace_bytes - device workspace dark_prf_bwd needs for
- * desc; 0 for an invalid descriptor.  It holds the fp32 features, the
+ * desc; 0 for an invalid descriptor, and 0 for B = 0 (dark_prf_bwd then
+ * only zeroes dM and takes no workspace).  It holds the fp32 features, the
  * per-chunk states and the intermediate gradients: about
  * 4*B*H*Lp*(4*m + 4*r + 6*d_h + 135) + 8*B*H*(Lp/64)*m*(d_h+1) bytes, with Lp
  * the sequence length rounded up to a multiple of 64, plus at most

@@ -351,7 +351,7 @@ BwdLayout bwd_layout(const dark_prf_desc& d) {
   o.Lp = o.NC * o.C;
   // dM = s sum_t dU_t^T x_t is split over runs of KC tokens (a multiple of 64)
   // so that the partial products fill about kMTarget workgroups
-  const int64_t mtiles = (int64_t)d.B * d.H * cdiv64(d.r, 64) * cdiv64(d.d_h, 64);
+  const int64_t mtiles = std::max<int64_t>(1, (int64_t)d.B * d.H * cdiv64(d.r, 64) * cdiv64(d.d_h, 64));
   const int64_t nkc = std::max<int64_t>(1, cdiv64(kMTarget, mtiles));
   o.KC = (int)std::max<int64_t>(64, cdiv64(cdiv64(L, nkc), 64) * 64);
   o.NKC = (int)cdiv64(L, o.KC);
@@ -362,7 +362,7 @@ BwdLayout bwd_layout(const dark_prf_desc& d) {
   if (d.causal) {
     o.CS = o.C;
   } else {
-    const int64_t stiles = (int64_t)d.B * d.H * cdiv64(d.m, 64) * cdiv64(d.d_h + 1, 64);
+    const int64_t stiles = std::max<int64_t>(1, (int64_t)d.B * d.H * cdiv64(d.m, 64) * cdiv64(d.d_h + 1, 64));
     const int64_t ncs = std::max<int64_t>(1, cdiv64(kSTarget, stiles));
     o.CS = (int)std::max<int64_t>(64, cdiv64(cdiv64(o.Lp, ncs), 64) * 64);
   }

@@ -319,3 +319,12 @@ def test_bwd_argument_checks():
     assert call(dd=_desc(o_str=[0, 0, 3])) == bd.DARK_ERR_INVALID_ARG
     assert bd.dark_prf_bwd_workspace_bytes(_desc(d_h=48)) == 0
     assert bd.dark_prf_bwd_workspace_bytes(_desc(L=4096)) >= nb
+
+
+def test_bwd_workspace_for_empty_calls():
+    # an empty batch is sized without dividing by its (zero) tile count: it
+    # needs no workspace; neither call below may fault on the host
+    for kw in (dict(B=0), dict(B=0, causal=0)):
+        assert bd.dark_prf_bwd_workspace_bytes(_desc(**kw)) == 0, kw
+    for kw in (dict(L=0), dict(L=0, causal=0)):
+        assert bd.dark_prf_bwd_workspace_bytes(_desc(**kw)) > 0, kw

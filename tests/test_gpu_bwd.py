@@ -31,6 +31,8 @@ CASES = [
     ("bwd_bf16_L700_c",   "bf16", 1, 2, 1,   700, 64,  64,  32,  True,  False, True,  "tail"),
     ("bwd_f32_m512_nc",   "f32",  1, 1, 1,   260, 64,  512, 64,  False, True,  True,  "none"),
     ("bwd_f32_d16_gqa4",  "f32",  1, 8, 2,   90,  16,  32,  8,   True,  False, True,  "random"),
+    ("bwd_f32_r1_m16",    "f32",  2, 2, 2,   75,  32,  16,  1,   True,  True,  False, "tail"),
+    ("bwd_c1_shape",      "f32",  1, 1, 1,   128, 16,  32,  16,  False, True,  False, "none"),
 ]
 
 
@@ -128,6 +130,11 @@ def test_bwd_fully_masked_and_empty():
     g = bd.prf_attention_backward(e, e, e, dev["M"], dev["omega"], e, causal=True)
     torch.cuda.synchronize()
     assert float(g[3].abs().max()) == 0.0 and g[0].numel() == 0
+    # B = 0: likewise
+    e0 = torch.zeros((0, 2, 70, 64), dtype=torch.bfloat16, device="cuda:0")
+    g0 = bd.prf_attention_backward(e0, e0, e0, dev["M"], dev["omega"], e0, causal=False)
+    torch.cuda.synchronize()
+    assert float(g0[3].abs().max()) == 0.0
 
 
 def test_bwd_single_token():
