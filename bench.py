@@ -65,9 +65,14 @@ def nominal_flops(w) -> int:
 
 
 def source_digest() -> str:
+    """Digest of the sources the forward, cross-attention and decode kernels
+    are built and planned from (the kernels whose HBM bytes are recorded)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "random_feature_linear_amd", "csrc")
+    mine = ("common.h", "prf_kernels.cuh", "decode_kernels.cuh", "api.hip")
     for f in sorted(os.listdir(csrc)):
+        if not (f in mine or f.startswith("fwd_") or f.startswith("dec_")):
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
