@@ -102,7 +102,10 @@ struct GemmArgs {
 
 constexpr int kKT = 32;   // K depth of one LDS slice
 
-template <typename TA, typename TB, bool PROD>
+// XC: the last output column N - 1 is not tiled; it is accumulated on the
+// vector ALUs from the A values each thread stages (A(i, k) * B(k, N - 1)) and
+// reduced at the end, so an odd width such as d_h + 1 needs no extra tile.
+template <typename TA, typename TB, bool PROD, bool XC = false>
 __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
   constexpr int KT = kKT, NE = 64 * KT / 256;   // elements of each operand per thread and slice
   __shared__ float As[64][KT + 1];   // [i][k]
@@ -127,6 +130,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
   const bool b_jrow = a.B.sk == 1;   // j contiguous in B: threads walk j
   // offsets inside one batch fit in 32 bits (checked on the host)
   const int asi = (int)a.A.si, ask = (int)a.A.sk, bsi = (int)a.B.si, bsk = (int)a.B.sk;
+  const int NT = XC ? a.N - 1 : a.N;   // tiled columns
   f32x16 acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
@@ -149,7 +153,22 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
       int kb, j;
       if (b_jrow) { kb = e >> 6; j = e & 63; } else { kb = e % KT; j = e / KT; }
       const int gkb = k0 + kb, gj = j0 + j;
-      rb[e8] = (gkb < K && gj < a.N) ? ld_f(Bp + (gkb * bsi + gj * bsk)) : 0.f;
+      rb[e8] = (gkb < K && gj < NT) ? ld_f(Bp + (gkb * bsi + gj * bsk)) : 0.f;
+    }
+  };
+  // the last column: k contiguous in A puts row tid / KT + (256 / KT) e8 and
+  // column k = tid % KT in element e8; otherwise row tid & 63 and column
+  // tid / 64 + 4 e8.  rbx holds B(k, N - 1) for the thread's columns.
+  float xacc[NE], rbx[NE];
+#pragma unroll
+  for (int e8 = 0; e8 < NE; ++e8) xacc[e8] = rbx[e8] = 0.f;
+  auto fetch_x = [&](int k0) {
+    if (!XC) return;
+#pragma unroll
+    for (int e8 = 0; e8 < NE; ++e8) {
+      const int k = k0 + (a_krow ? tid % KT : (tid >> 6) + 4 * e8);
+      rbx[e8] = k < K ? ld_f(Bp + (k * bsi + (a.N - 1) * bsk)) : 0.f;
+      if (a_krow) break;   // one column per thread
     }
   };
   // with k contiguous in A, thread tid holds rows tid / KT + (256 / KT) e8 in every slice
@@ -157,18 +176,23 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int e8 = 0; e8 < NE; ++e8) rsum[e8] = 0.f;
   fetch(0);
+  fetch_x(0);
   for (int k0 = 0; k0 < K; k0 += KT) {
 #pragma unroll
     for (int e8 = 0; e8 < NE; ++e8) {
       const int e = tid + 256 * e8;
       if (PROD) rsum[e8] += ra[e8];
+      if (XC) xacc[e8] = fmaf(ra[e8], a_krow ? rbx[0] : rbx[e8], xacc[e8]);
       if (a_krow) As[e / KT][e % KT] = ra[e8];
       else As[e & 63][e >> 6] = ra[e8];
       if (b_jrow) Bs[e >> 6][e & 63] = rb[e8];
       else Bs[e % KT][e / KT] = rb[e8];
     }
     __syncthreads();
-    if (k0 + KT < K) fetch(k0 + KT);
+    if (k0 + KT < K) {
+      fetch(k0 + KT);
+      fetch_x(k0 + KT);
+    }
 #pragma unroll
     for (int kk = 0; kk < KT; kk += 8)
 #pragma unroll
@@ -187,8 +211,34 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
       if ((tid % KT) == 0 && row < a.M) a.rowsum[bh * a.rs_sbh + row] = v;
     }
   }
+  if (XC && tn == 0) {
+    // the last column, written like the tiled ones (plain or accumulate)
+    auto put = [&](int row, float v) {
+      if (row >= a.M) return;
+      float* cp = C + row * a.C.si + (a.N - 1);
+      const float x = a.alpha * v;
+      *cp = a.accumulate ? *cp + x : x;
+    };
+    if (a_krow) {   // KT lanes share each row
+#pragma unroll
+      for (int e8 = 0; e8 < NE; ++e8) {
+        float v = xacc[e8];
+#pragma unroll
+        for (int o = KT / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        if ((tid % KT) == 0) put(i0 + tid / KT + (256 / KT) * e8, v);
+      }
+    } else {        // the four waves share each row: sum through LDS
+      float v = 0.f;
+#pragma unroll
+      for (int e8 = 0; e8 < NE; ++e8) v += xacc[e8];
+      float* red = &As[0][0];   // free after the last slice's barrier
+      red[tid] = v;
+      __syncthreads();
+      if (tid < 64) put(i0 + tid, red[tid] + red[tid + 64] + red[tid + 128] + red[tid + 192]);
+    }
+  }
   const int col = j0 + wj + l32;
-  if (col >= a.N) return;
+  if (col >= NT) return;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int row = i0 + wi + 8 * (e >> 2) + 4 * g + (e & 3);
@@ -431,7 +481,7 @@ struct Launcher {
   double flops = 0.0;
   dark_status status = DARK_OK;
 
-  template <typename TA, typename TB, bool PROD = false>
+  template <typename TA, typename TB, bool PROD = false, bool XC = false>
   void gemm(GOp A, GOp B, GOut C, int M, int N, int K, int batches, int NCB, float alpha = 1.f, int accumulate = 0,
             int epi = kEpiPlain, int Ktot = 0, int Arows = -1, const float* nrm = nullptr, int64_t nrm_sbh = 0,
             const uint8_t* mask = nullptr, int L = 0, float* rowsum = nullptr, int64_t rs_sbh = 0) {
@@ -447,11 +497,12 @@ struct Launcher {
     a.Arows = Arows < 0 ? M : Arows;
     a.H = H;
     a.NCB = NCB;
-    a.tiles_n = (N + 63) / 64;
+    a.tiles_n = (N - (XC ? 1 : 0) + 63) / 64;
     a.tiles = ((M + 63) / 64) * a.tiles_n;
     a.rowsum = rowsum;
     a.rs_sbh = rs_sbh;
-    if (rowsum != nullptr && (!PROD || A.sk != 1 || NCB != 1)) {
+    if ((rowsum != nullptr && (!PROD || A.sk != 1 || NCB != 1)) ||
+        (XC && (N < 2 || PROD || epi != kEpiPlain || (A.sk != 1 && A.si != 1)))) {
       status = DARK_ERR_UNSUPPORTED;
       return;
     }
@@ -473,7 +524,7 @@ struct Launcher {
     const int64_t kt = Ktot > 0 ? (int64_t)Ktot * (batches / NCB) : (int64_t)K * batches;
     flops += 2.0 * M * N * (double)kt;
     KernelTimer tm(kBwdGemm, st);
-    hipLaunchKernelGGL((bgemm_kernel<TA, TB, PROD>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bgemm_kernel<TA, TB, PROD, XC>), dim3((unsigned)grid), dim3(256), 0, st, a);
     if (hipGetLastError() != hipSuccess) status = DARK_ERR_HIP;
   }
 
@@ -544,26 +595,32 @@ dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStrea
   // 3. [V, 1] per query head
   ln.aux(vx_kernel<T>, BH * Lp * D1, 256, (const T*)p.v, d.v_str[0], d.v_str[1], d.v_str[2], Vx, H, G, L, Lp, dh,
          BH * Lp * D1);
+  // products of width d_h + 1: the last column on the vector ALUs when d_h + 1
+  // would otherwise start a 64-wide tile of its own
+  auto gemm_d1 = [&](GOp A, GOp B, GOut Cc, int M, int K, int batches, int NCB, int accumulate, int Ktot) {
+    if (dh % 64 == 0)
+      ln.gemm<float, float, false, true>(A, B, Cc, M, D1, K, batches, NCB, 1.f, accumulate, kEpiPlain, Ktot);
+    else
+      ln.gemm<float, float>(A, B, Cc, M, D1, K, batches, NCB, 1.f, accumulate, kEpiPlain, Ktot);
+  };
   // 4. key-side state partials Phi(K_c)^T [V, 1]_c
-  ln.gemm<float, float>(runT(Pk, m), run(Vx, D1), ostates(Sx), m, D1, CS, (int)(BH * NCS), NCS, 1.f, 0, kEpiPlain,
-                        Lp);
+  gemm_d1(runT(Pk, m), run(Vx, D1), ostates(Sx), m, CS, (int)(BH * NCS), NCS, 0, Lp);
   const int NB = (int)(BH * NC);
   if (d.causal) {
     ln.aux(chunk_scan_kernel, BH * X, 256, Sx, NC, X, BH * X, 0);
     // 5. [N, D] = Phi(Q_c) Sx_c + tril(Phi(Q_c) Phi(K_c)^T) [V, 1]_c
     ln.gemm<float, float>(rows(Pq, m), rowsT(Pk, m), oblk(Wc), C, C, m, NB, NC, 1.f, 0, kEpiTril);
-    ln.gemm<float, float>(rows(Pq, m), states(Sx), orows(ND, D1), C, D1, m, NB, NC);
-    ln.gemm<float, float>(blk(Wc), rows(Vx, D1), orows(ND, D1), C, D1, C, NB, NC, 1.f, 1);
+    gemm_d1(rows(Pq, m), states(Sx), orows(ND, D1), C, m, NB, NC, 0, 0);
+    gemm_d1(blk(Wc), rows(Vx, D1), orows(ND, D1), C, C, NB, NC, 1, 0);
   } else {
     ln.aux(chunk_sum_kernel, BH * X, 256, (const float*)Sx, St, NCS, X, BH * X);
-    ln.gemm<float, float>(rows(Pq, m), tot(St), orows(ND, D1), Lp, D1, m, (int)BH, 1);
+    gemm_d1(rows(Pq, m), tot(St), orows(ND, D1), Lp, m, (int)BH, 1, 0, 0);
   }
   // 6. Gd = [dO / D, -(dO . O) / D]
   ln.aux(gd_kernel<T>, BH * Lp * 64, 256, (const T*)p.dout, d.o_str[0], d.o_str[1], d.o_str[2], (const float*)ND, Gd,
          H, L, Lp, dh, BH * Lp);
   // 7. dPhi(Q), the query-side state partials Phi(Q_c)^T Gd_c, dPhi(K) and dV
-  ln.gemm<float, float>(runT(Pq, m), run(Gd, D1), ostates(Gx), m, D1, CS, (int)(BH * NCS), NCS, 1.f, 0, kEpiPlain,
-                        Lp);
+  gemm_d1(runT(Pq, m), run(Gd, D1), ostates(Gx), m, CS, (int)(BH * NCS), NCS, 0, Lp);
   if (d.causal) {
     ln.aux(chunk_scan_kernel, BH * X, 256, Gx, NC, X, BH * X, 1);
     ln.gemm<float, float>(rows(Gd, D1), rowsT(Vx, D1), oblk(A2), C, C, D1, NB, NC, 1.f, 0, kEpiTril);
