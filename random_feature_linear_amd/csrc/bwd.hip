@@ -93,10 +93,12 @@ struct GemmArgs {
   int accumulate;   // C += result instead of C = result
   int epi;
   // kEpiFeature: C = valid ? exp(acc - nrm[bh*nrm_sbh + i]) * alpha : 0, valid =
-  // i < L and (mask == null or mask[b*L + i] != 0)
+  // i < L and (mask == null or b < mask_b0 or mask[(b - mask_b0)*L + i] != 0)
+  // (a launch over queries then keys masks the batch rows from mask_b0 on)
   const float* nrm;
   int64_t nrm_sbh;
   const uint8_t* mask;
+  int mask_b0;
   int L;
 };
 
@@ -247,7 +249,8 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
     if (a.epi == kEpiTril) {
       if (col > row) x = 0.f;
     } else if (a.epi == kEpiFeature) {
-      const bool ok = row < a.L && (a.mask == nullptr || a.mask[(int64_t)b * a.L + row] != 0);
+      const bool ok = row < a.L && (a.mask == nullptr || b < a.mask_b0 ||
+                                    a.mask[(int64_t)(b - a.mask_b0) * a.L + row] != 0);
       x = ok ? __expf(acc[e] - a.nrm[bh * a.nrm_sbh + row]) * a.alpha : 0.f;
     }
     float* cp = C + row * a.C.si + col;
@@ -417,7 +420,7 @@ BwdLayout bwd_layout(const dark_prf_desc& d) {
     o.CS = (int)std::max<int64_t>(64, cdiv64(cdiv64(o.Lp, ncs), 64) * 64);
   }
   o.NCS = (int)cdiv64(o.Lp, o.CS);
-  const size_t BH = (size_t)d.B * d.H, Lp = o.Lp, m = d.m, r = d.r, dh = d.d_h, D1 = o.D1, NC = o.NC;
+  const size_t BH = (size_t)d.B * d.H, Lp = o.Lp, m = d.m, r = d.r, dh = d.d_h, D1 = o.D1;
   size_t off = 0;
   auto take = [&](size_t floats) {
     const size_t at = off;
@@ -484,7 +487,8 @@ struct Launcher {
   template <typename TA, typename TB, bool PROD = false, bool XC = false>
   void gemm(GOp A, GOp B, GOut C, int M, int N, int K, int batches, int NCB, float alpha = 1.f, int accumulate = 0,
             int epi = kEpiPlain, int Ktot = 0, int Arows = -1, const float* nrm = nullptr, int64_t nrm_sbh = 0,
-            const uint8_t* mask = nullptr, int L = 0, float* rowsum = nullptr, int64_t rs_sbh = 0) {
+            const uint8_t* mask = nullptr, int L = 0, float* rowsum = nullptr, int64_t rs_sbh = 0,
+            int mask_b0 = 0) {
     if (status != DARK_OK || M <= 0 || N <= 0 || batches <= 0) return;
     GemmArgs a;
     a.A = A;
@@ -512,6 +516,7 @@ struct Launcher {
     a.nrm = nrm;
     a.nrm_sbh = nrm_sbh;
     a.mask = mask;
+    a.mask_b0 = mask_b0;
     a.L = L;
     const int64_t grid = (int64_t)batches * a.tiles;
     const int64_t amax = (int64_t)(a.Arows - 1) * A.si + (int64_t)(K - 1) * A.sk;
@@ -583,15 +588,20 @@ dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStrea
                     kEpiPlain, 0, L);
   ln.gemm<T, float>(op(p.k, d.k_str[0], d.k_str[1], 0, d.k_str[2], 1, G), Mt, orows(Uk, r), Lp, r, dh, (int)BH, 1, s,
                     0, kEpiPlain, 0, L);
-  ln.aux(halfnorm_kernel, BH * Lp * 64, 256, (const float*)Uq, nq, r, BH * Lp);
-  ln.aux(halfnorm_kernel, BH * Lp * 64, 256, (const float*)Uk, nk, r, BH * Lp);
+  // The query and key buffers of each kind are adjacent in the workspace (every
+  // size is a multiple of 256 bytes), so one launch over 2 B batch rows covers
+  // queries (rows b < B) and keys (rows B + b).
+  const bool paired = Uk == Uq + BH * Lp * r && nk == nq + BH * Lp && Pk == Pq + BH * Lp * m &&
+                      dPk == dPq + BH * Lp * m && dUk == dUq + BH * Lp * r && rsk == rsq + BH * Lp &&
+                      dKh == dQh + BH * Lp * dh;
+  if (!paired) return DARK_ERR_UNSUPPORTED;
+  const int BH2 = (int)(2 * BH);
+  ln.aux(halfnorm_kernel, 2 * BH * Lp * 64, 256, (const float*)Uq, nq, r, 2 * BH * Lp);
   // 2. features phi = exp(u . omega_j - |u|^2 / 2) / sqrt(m); keys masked, rows t >= L zero
   const GOp OmT = op(p.omega, 0, 0, 0, 1, r);   // (k, j) = omega[j][k]
   const float inv_sqrt_m = 1.0f / sqrtf((float)m);
-  ln.gemm<float, float>(rows(Uq, r), OmT, orows(Pq, m), Lp, m, r, (int)BH, 1, inv_sqrt_m, 0, kEpiFeature, 0, -1, nq,
-                        Lp, nullptr, L);
-  ln.gemm<float, float>(rows(Uk, r), OmT, orows(Pk, m), Lp, m, r, (int)BH, 1, inv_sqrt_m, 0, kEpiFeature, 0, -1, nk,
-                        Lp, p.mask, L);
+  ln.gemm<float, float>(rows(Uq, r), OmT, orows(Pq, m), Lp, m, r, BH2, 1, inv_sqrt_m, 0, kEpiFeature, 0, -1, nq, Lp,
+                        p.mask, L, nullptr, 0, p.mask ? d.B : 0);
   // 3. [V, 1] per query head
   ln.aux(vx_kernel<T>, BH * Lp * D1, 256, (const T*)p.v, d.v_str[0], d.v_str[1], d.v_str[2], Vx, H, G, L, Lp, dh,
          BH * Lp * D1);
@@ -639,19 +649,14 @@ dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStrea
   // 8. through the feature map: dU = (dPhi * Phi) Omega - U * rowsum(dPhi * Phi)
   // (the A operand dPhi * Phi is formed in the loads, which also sum its rows)
   const GOp Om = op(p.omega, 0, 0, 0, r, 1);   // (k, j) = omega[k][j]
-  GOp dEq = rows(dPq, m), dEk = rows(dPk, m);
+  GOp dEq = rows(dPq, m);   // and dPk, Pk from batch row B on
   dEq.p2 = Pq;
-  dEk.p2 = Pk;
-  ln.gemm<float, float, true>(dEq, Om, orows(dUq, r), Lp, r, m, (int)BH, 1, 1.f, 0, kEpiPlain, 0, -1, nullptr, 0,
-                              nullptr, 0, rsq, Lp);
-  ln.gemm<float, float, true>(dEk, Om, orows(dUk, r), Lp, r, m, (int)BH, 1, 1.f, 0, kEpiPlain, 0, -1, nullptr, 0,
-                              nullptr, 0, rsk, Lp);
-  ln.aux(fixdu_kernel, BH * Lp * r, 256, dUq, (const float*)Uq, (const float*)rsq, r, BH * Lp * r);
-  ln.aux(fixdu_kernel, BH * Lp * r, 256, dUk, (const float*)Uk, (const float*)rsk, r, BH * Lp * r);
+  ln.gemm<float, float, true>(dEq, Om, orows(dUq, r), Lp, r, m, BH2, 1, 1.f, 0, kEpiPlain, 0, -1, nullptr, 0, nullptr,
+                              0, rsq, Lp);
+  ln.aux(fixdu_kernel, 2 * BH * Lp * r, 256, dUq, (const float*)Uq, (const float*)rsq, r, 2 * BH * Lp * r);
   // 9. dX = s dU M_h, dM_h = s sum dU^T X
   const GOp Mh = op(p.M, 0, hM, 0, dh, 1);
-  ln.gemm<float, float>(rows(dUq, r), Mh, orows(dQh, dh), Lp, dh, r, (int)BH, 1, s);
-  ln.gemm<float, float>(rows(dUk, r), Mh, orows(dKh, dh), Lp, dh, r, (int)BH, 1, s);
+  ln.gemm<float, float>(rows(dUq, r), Mh, orows(dQh, dh), Lp, dh, r, BH2, 1, s);
   const int KC = o.KC, NKC = o.NKC;
   const int64_t RD = (int64_t)r * dh;
   const GOut oMp = out(dMp, (int64_t)H * NKC * RD, (int64_t)NKC * RD, RD, dh);
