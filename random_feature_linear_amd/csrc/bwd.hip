@@ -44,7 +44,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // write fewer m x (d_h + 1) states but do more intra-chunk work: 128 tokens pay
 // off once the state is wide (d_h >= 128), 64 below.
 inline int bwd_chunk(const dark_prf_desc& d) { return d.causal && d.d_h >= 128 ? 128 : 64; }
-constexpr int kMTarget = 2048; // workgroups the split dM reduction aims for
+constexpr int kMTarget = 1024; // workgroups the split dM reduction aims for
 constexpr int kSTarget = 4096; // workgroups the non-causal state partials aim for
 
 __device__ __forceinline__ float ld_f(const float* p) { return *p; }
