@@ -4,15 +4,18 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one dark_prf_fwd call over one batch (every kernel of the path:
-operand preparation, key-side state, state sum / prefix scan, query-side
-output), on seeded synthetic inputs already resident in HBM.  The timed region
-replays a HIP graph of back-to-back forwards that rotate over enough input
-copies to touch more memory than the 256 MB Infinity Cache holds.  Prints one
-JSON line.  The default workload is the causal L=2048 attention core
-(B=2, H=8, d_h=64, m=256, r=64); the L=64K non-causal workload
-(B=1, H=8, d_h=64, m=1024, r=16) is measured in the same run and reported
-under "secondary".  `--workload c4_gqa_L8192` or `c5_decode` prints the line
-for those workloads instead.
+operand preparation, key-side state, state prefix, query-side output), on
+seeded synthetic inputs already resident in HBM.  The timed region replays a
+HIP graph of back-to-back forwards that rotate over enough input copies to
+touch more memory than the 256 MB Infinity Cache holds; the step time is the
+median over several timed replays.  Prints one JSON line.  Its headline is the
+causal L=2048 attention core (B=2, H=8, d_h=64, m=256, r=64); the other
+workloads are measured in the same run and reported under "workloads": the
+L=64K non-causal one (B=1, H=8, d_h=64, m=1024, r=16), the L=8192 GQA prefill
+(B=4, 8 query heads on 1 K/V head, d_h=256, m=512, r=256), the decode step
+(256 sequences x 8 heads) and the tiny fp32 call (as a latency).  Each carries
+the roofline of its dominant kernel and the fp64 oracle timed on a bounded
+sample.  `--workload NAME` prints the line of one workload only.
 """
 from __future__ import annotations
 
@@ -41,17 +44,35 @@ def log(msg: str) -> None:
 # ---------------------------------------------------------------------------
 # algorithmic work per kernel (method steps only; no recomputation counted)
 # ---------------------------------------------------------------------------
-def kernel_flops(w, chunk: int) -> dict:
-    """Algorithmic flops per launch of each kernel, from the method's steps:
-    projection 2 r d_h and exponent 2 r m per token and tensor, state and output
-    contractions 2 m (d_h + 1) per token, and for the causal form the masked
-    intra-chunk block 2 C (m + d_h + 1) per token (C = chunk length)."""
-    th = w.B * w.H * w.L
-    proj = 2 * w.r * w.d_h
-    expo = 2 * w.r * w.m
+CHUNK_ALG = 64   # causal chunk length of the algorithmic count (fixed; not the implementation's)
+
+
+def folded_queries(w) -> bool:
+    """Whether the query feature map counts as the folded product x W_h^T
+    (W_h = Omega M_h, m x d_h): when m d_h < r d_h + m r."""
+    return w.m * w.d_h < w.r * w.d_h + w.m * w.r
+
+
+def alg_flops_per_token_head(w) -> dict:
+    """Algorithmic flops per (token, query head) of each side of the forward:
+    key feature map 2 r (d_h + m); query feature map 2 m d_h when folded, else
+    2 r (d_h + m); each feature-space contraction 2 m (d_h + 1); causal adds the
+    masked C x C block 2 C (m + d_h + 1) with C = 64."""
+    fmap = 2 * w.r * (w.d_h + w.m)
+    qmap = 2 * w.m * w.d_h if folded_queries(w) else fmap
     contr = 2 * w.m * (w.d_h + 1)
-    intra = 2 * chunk * (w.m + w.d_h + 1) if w.causal else 0
-    return {"kstate": th * (proj + expo + contr), "qout": th * (proj + expo + contr + intra)}
+    intra = 2 * CHUNK_ALG * (w.m + w.d_h + 1) if w.causal else 0
+    return {"kstate": fmap + contr, "qout": qmap + contr + intra}
+
+
+def kernel_flops(w) -> dict:
+    """Algorithmic flops per launch of the key-side and query-side kernels."""
+    th = w.B * w.H * w.L
+    return {k: th * v for k, v in alg_flops_per_token_head(w).items()}
+
+
+def alg_flops(w) -> int:
+    return sum(kernel_flops(w).values())
 
 
 def io_bytes(w) -> int:
@@ -68,12 +89,10 @@ def source_digest() -> str:
     """Digest of the sources the forward, cross-attention and decode kernels
     are built and planned from (the kernels whose HBM bytes are recorded)."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "random_feature_linear_amd", "csrc")
-    mine = ("common.h", "prf_kernels.cuh", "decode_kernels.cuh", "api.hip")
-    for f in sorted(os.listdir(csrc)):
-        if not (f in mine or f.startswith("fwd_") or f.startswith("dec_")):
-            continue
-        with open(os.path.join(csrc, f), "rb") as fh:
+    pkg = os.path.join(ROOT, "random_feature_linear_amd")
+    # the kernel sources, the host planner and the generator of the instantiation units
+    for f in ("csrc/common.h", "csrc/prf_kernels.h", "csrc/decode_kernels.h", "csrc/api.hip", "build.py"):
+        with open(os.path.join(pkg, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -139,12 +158,30 @@ class Forward:
             raise self.bd.DarkPrfError(st, "dark_prf_fwd")
 
 
-def chunk_len(w) -> int:
-    """Causal chunk the library plans (the query-side tile): 128 tokens."""
-    return 128 if w.causal else 0
+def timed_replays(g, replays: int) -> list:
+    """Milliseconds of each of `replays` replays of graph g, timed with events on the
+    current stream (one untimed replay first)."""
+    import torch
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(replays):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1))
+    return times
 
 
-def measure(w, steps: int, warmup: int, eager: bool = False) -> dict:
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def measure(w, steps: int, warmup: int, eager: bool = False, replays: int = 5) -> dict:
     import torch
     per_copy = io_bytes(w)
     copies = max(2, min(32, -(-(MALL_BYTES + (64 << 20)) // per_copy)))
@@ -164,7 +201,7 @@ def measure(w, steps: int, warmup: int, eager: bool = False) -> dict:
         return {"ms": t0.elapsed_time(t1) / steps, "n_fwd": steps, "copies": copies, "kernels": {},
                 "launch": "eager"}
     # Timed region: one HIP graph of `steps` forwards that rotate over the input
-    # copies, replayed once after an untimed first replay.
+    # copies; the per-forward time is the median over `replays` timed replays.
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
@@ -173,15 +210,11 @@ def measure(w, steps: int, warmup: int, eager: bool = False) -> dict:
             for i in range(steps):
                 fwd(i)
     torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    g.replay()
-    t1.record()
+    reps = timed_replays(g, replays)
     # Per-kernel times: the same `steps` forwards launched one by one right behind
-    # the replay (the GPU stays busy), with the library's HIP events recorded
+    # the replays (the GPU stays busy), with the library's HIP events recorded
     # around every kernel launch on the stream the kernel runs on.
+    g.replay()
     fwd.bd.dark_prf_timing_begin()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -190,18 +223,19 @@ def measure(w, steps: int, warmup: int, eager: bool = False) -> dict:
     e1.record()
     per = fwd.bd.dark_prf_timing_end()
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    ms = median(reps) / steps
     ms_eager = e0.elapsed_time(e1) / steps
     del g
     kern = {k: {"avg_us": 1e3 * v[0] / v[1], "launches": v[1]} for k, v in per.items() if v[1] > 0}
-    n_fwd = steps
-    return {"ms": ms, "ms_eager": ms_eager, "n_fwd": n_fwd, "copies": copies, "kernels": kern}
+    return {"ms": ms, "ms_eager": ms_eager, "n_fwd": steps, "copies": copies, "kernels": kern,
+            "replay_ms": [round(t / steps, 6) for t in reps]}
 
 
 def roofline(w, res: dict) -> dict:
-    """Roofline of the dominant kernel (largest average duration)."""
-    C = chunk_len(w)
-    flops = kernel_flops(w, C)
+    """Roofline of the dominant kernel (largest average live duration): its
+    algorithmic flops per launch over that duration, against the dense MFMA peak
+    of the input type."""
+    flops = kernel_flops(w)
     dom = max(res["kernels"], key=lambda k: res["kernels"][k]["avg_us"])
     avg_s = res["kernels"][dom]["avg_us"] * 1e-6
     traffic = traffic_from_profiles(dom, w.name)
@@ -210,7 +244,9 @@ def roofline(w, res: dict) -> dict:
         ach = flops[dom] / avg_s / 1e12
         return {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
-                "flops_per_launch": flops[dom], "avg_launch_us": round(res["kernels"][dom]["avg_us"], 3)}
+                "flops_per_launch": flops[dom],
+                "flops_per_token_head": alg_flops_per_token_head(w)[dom],
+                "avg_launch_us": round(res["kernels"][dom]["avg_us"], 3)}
     return {"bound": "hbm", "kernel": dom, "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": None, "traffic": traffic, "avg_launch_us": round(res["kernels"][dom]["avg_us"], 3)}
 
@@ -258,30 +294,40 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 4) -> None:
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def line_for(w, res: dict, steps: int, warmup: int) -> dict:
+def line_for(w, res: dict) -> dict:
     tokens = w.B * w.L
-    value = tokens / (res["ms"] * 1e-3)
-    nom = nominal_flops(w) / (res["ms"] * 1e-3) / 1e12
+    sec = res["ms"] * 1e-3
+    value = tokens / sec
+    nom = nominal_flops(w) / sec / 1e12
+    alg = alg_flops(w) / sec / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     return {
-        "value": round(value, 1), "ms_per_step": round(res["ms"], 6),
+        "value": round(value, 1), "unit": "tokens/s", "ms_per_step": round(res["ms"], 6),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.hkv, "L": w.L, "d_h": w.d_h,
                    "m": w.m, "r": w.r, "causal": w.causal, "mask": w.mask_kind,
-                   "launch": "one hipGraph of %d forwards over %d rotating input copies" % (res["n_fwd"], res["copies"])},
+                   "launch": "one hipGraph of %d forwards over %d rotating input copies, median of %d replays"
+                             % (res["n_fwd"], res["copies"], len(res["replay_ms"]))},
         "roofline": roofline(w, res),
-        "nominal_tflops": round(nom, 2), "nominal_frac_bf16": round(nom / PEAK_BF16_TFLOPS, 4),
-        "io_GBps": round(io_bytes(w) / (res["ms"] * 1e-3) / 1e9, 1),
+        "forward_frac": {"alg_tflops": round(alg, 2), "alg_frac": round(alg / peak, 4),
+                         "nominal_tflops": round(nom, 2), "nominal_frac": round(nom / peak, 4),
+                         "io_GBps": round(io_bytes(w) / sec / 1e9, 1),
+                         "io_frac_hbm": round(io_bytes(w) / sec / 1e9 / PEAK_HBM_GBS, 4)},
+        "replay_ms_per_step": res["replay_ms"],
         "kernels_us": {k: round(v["avg_us"], 3) for k, v in res["kernels"].items()},
         "kernel_timing": "HIP events around each launch, eager pass of the same forwards "
-                         "right behind the timed replay (%.4f ms per forward)" % res["ms_eager"],
+                         "right behind the timed replays (%.4f ms per forward)" % res["ms_eager"],
     }
 
 
-def decode_line(steps: int) -> dict:
-    """Workload 5: 512 one-token steps over 256 sequences x 8 heads (fp32 state)."""
+def decode_line(steps: int, replays: int = 3) -> dict:
+    """Workload 5: `steps` one-token steps over 256 sequences x 8 heads (fp32
+    state, updated in place), captured in one HIP graph; median of `replays`
+    replays.  The state holds seeded random values of the shape a 4096-token
+    prefill leaves (a step's work and bytes do not depend on the values)."""
     import torch
 
     from random_feature_linear_amd import binding as bd
-    from random_feature_linear_amd.workloads import CONFIGS, make_decode_tokens
+    from random_feature_linear_amd.workloads import CONFIGS, make_decode_tokens, make_inputs
     w = CONFIGS["c5_decode"]
     g = torch.Generator(device="cuda:0").manual_seed(w.seed)
     dt = torch.bfloat16
@@ -289,7 +335,6 @@ def decode_line(steps: int) -> dict:
     z = torch.rand((w.B, w.H, w.m), generator=g, device="cuda:0", dtype=torch.float32) * 4096
     tok = make_decode_tokens(w, steps)
     tq, tk, tv = (torch.from_numpy(tok[n]).to(dt).to("cuda:0") for n in ("q", "k", "v"))
-    from random_feature_linear_amd.workloads import make_inputs
     M = torch.from_numpy(make_inputs(w.with_(B=1, L=1))["M"]).to("cuda:0")
     om = torch.from_numpy(bd.dark_prf_omega(w.seed, w.m, w.r, w.orthogonal)).to("cuda:0")
     tag = bd.dark_prf_proj_tag(w.seed, w.m, w.r, w.orthogonal)
@@ -297,27 +342,66 @@ def decode_line(steps: int) -> dict:
     for t in range(4):
         bd.decode_step(tq[t], tk[t], tv[t], M, om, S, z, tag, tag, out=out)
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for t in range(steps):
-        bd.decode_step(tq[t], tk[t], tv[t], M, om, S, z, tag, tag, out=out)
-    t1.record()
+    sm = torch.cuda.Stream()
+    sm.wait_stream(torch.cuda.current_stream())
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(sm):
+        with torch.cuda.graph(gr, stream=sm):
+            for t in range(steps):
+                bd.decode_step(tq[t], tk[t], tv[t], M, om, S, z, tag, tag, out=out)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    reps = timed_replays(gr, replays)
+    ms = median(reps) / steps
+    del gr
     bd.dark_prf_timing_begin()
     for t in range(min(steps, 64)):
         bd.decode_step(tq[t], tk[t], tv[t], M, om, S, z, tag, tag, out=out)
     per = bd.dark_prf_timing_end()
     avg_us = 1e3 * per["decode"][0] / per["decode"][1]
+    # algorithmic bytes of one step: S and z read and written once (fp32), plus
+    # q, k, v and out (bf16)
     state_bytes = 2 * (w.B * w.H * w.m * (w.d_h + 1) * 4)
-    ach = state_bytes / (avg_us * 1e-6) / 1e9
+    tok_bytes = 2 * w.d_h * (2 * w.B * w.H + 2 * w.B * w.hkv)
+    ach = (state_bytes + tok_bytes) / (avg_us * 1e-6) / 1e9
     return {"value": round(w.B / (ms * 1e-3), 1), "ms_per_step": round(ms, 6), "unit": "tokens/s",
             "config": {"workload": w.name, "N": w.B, "H": w.H, "d_h": w.d_h, "m": w.m, "r": w.r,
-                       "steps": steps, "launch": "eager, one launch per step"},
+                       "steps": steps, "state": "seeded random fp32 of the prefilled state's shape",
+                       "launch": "one hipGraph of %d decode steps, median of %d replays" % (steps, replays)},
+            "replay_ms_per_step": [round(t / steps, 6) for t in reps],
             "roofline": {"bound": "hbm", "kernel": "decode", "achieved": round(ach, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                          "traffic": traffic_from_profiles("decode", w.name),
-                         "bytes_per_launch": state_bytes, "avg_launch_us": round(avg_us, 3)}}
+                         "bytes_per_launch": state_bytes + tok_bytes, "avg_launch_us": round(avg_us, 3)}}
+
+
+def cpu_baseline_decode(w, seqs: int = 16, min_seconds: float = 10.0) -> dict:
+    """The fp64 oracle's recurrence (oracle.decode_step, vectorised over sequences
+    and heads) on `seqs` of the 256 sequences, one token per step, repeated until
+    `min_seconds` have passed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from random_feature_linear_amd.workloads import make_decode_tokens, make_inputs
+    om = oracle.omega(w.seed, w.m, w.r, w.orthogonal)
+    M = make_inputs(w.with_(B=1, L=1))["M"]
+    rng = np.random.default_rng(w.seed)
+    S = rng.standard_normal((seqs, w.H, w.m, w.d_h))
+    z = rng.random((seqs, w.H, w.m)) * 4096
+    tok = make_decode_tokens(w.with_(B=seqs), 64)
+    steps, t = 0, time.perf_counter()
+    while True:
+        i = steps % 64
+        _, S, z = oracle.decode_step(S, z, tok["q"][i], tok["k"][i], tok["v"][i], M, om)
+        steps += 1
+        dt = time.perf_counter() - t
+        if dt >= min_seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("internal_api") in
+                   ("openblas", "mkl", "blis")] or [1])
+    return {"value": round(seqs * steps / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{seqs} of {w.B} sequences x {w.H} heads, {steps} one-token steps in {dt:.1f} s, fp64",
+            "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def cross_line(steps: int, eager: bool = False) -> dict:
@@ -631,8 +715,9 @@ def main() -> int:
     ap.add_argument("--workload", default="c2_causal_L2048")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the L=64K and the cross-attention measurements")
-    ap.add_argument("--no-cross", action="store_true", help="skip the cross-attention measurement")
+                    help="measure only the chosen workload (no other workloads, no cross-attention)")
+    ap.add_argument("--no-cross", action="store_true",
+                    help="skip the cross-attention, exact-path and backward measurements")
     ap.add_argument("--eager", action="store_true",
                     help="plain launches instead of a HIP graph, no per-kernel timing (for profilers)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -699,7 +784,7 @@ def main() -> int:
                           "launch": "eager"}), flush=True)
         return 0
     res = measure(w, args.steps, args.warmup)
-    main_line = line_for(w, res, args.steps, args.warmup)
+    main_line = line_for(w, res)
     rec = {"metric": METRIC, "value": main_line["value"], "unit": "tokens/s", "n_gpus": 1,
            "steps": res["n_fwd"], "warmup": args.warmup, "ms_per_step": main_line["ms_per_step"],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -707,17 +792,35 @@ def main() -> int:
     rec.update({k: v for k, v in main_line.items() if k not in ("value", "ms_per_step")})
     if not args.no_cpu and torch.cuda.current_device() == 0:
         log("[bench] timing the fp64 oracle on the host")
-        rec["cpu_baseline"] = cpu_baseline(w)
-    if args.workload == "c2_causal_L2048" and not args.no_secondary:
-        w3 = CONFIGS["c3_long_L64K"]
-        res3 = measure(w3, max(20, args.steps // 8), min(args.warmup, 5))
-        sec = line_for(w3, res3, args.steps, args.warmup)
-        if not args.no_cpu:
-            log("[bench] timing the fp64 oracle on one head of the L=64K workload")
-            sec["cpu_baseline"] = cpu_baseline(w3, max_heads=1)
-        sec["steps"] = res3["n_fwd"]
-        rec["secondary"] = sec
-    if args.workload == "c2_causal_L2048" and not args.no_secondary and not args.no_cross:
+        rec["cpu_baseline"] = cpu_baseline(w, max_heads=1 if w.L * w.B * w.H > 1 << 17 else None)
+    if args.workload != "c2_causal_L2048" or args.no_secondary:
+        print(json.dumps(rec), flush=True)
+        return 0
+    # the other workloads, measured in the same run
+    others = {}
+    w3 = CONFIGS["c3_long_L64K"]
+    res3 = measure(w3, max(10, args.steps // 2), min(args.warmup, 5))
+    others[w3.name] = line_for(w3, res3)
+    w4 = CONFIGS["c4_gqa_L8192"]
+    res4 = measure(w4, max(5, args.steps // 4), min(args.warmup, 3))
+    others[w4.name] = line_for(w4, res4)
+    log("[bench] decode steps")
+    others["c5_decode"] = decode_line(512)
+    w1 = CONFIGS["c1_tiny_f32"]
+    res1 = measure(w1, max(100, args.steps * 5), args.warmup)
+    l1 = line_for(w1, res1)
+    l1["latency_us"] = round(1e3 * res1["ms"], 3)
+    l1["note"] = "launch-bound (36 KB of data, 0.6 MFLOP): reported as an absolute latency per forward"
+    others[w1.name] = l1
+    if not args.no_cpu:
+        log("[bench] timing the fp64 oracle on samples of the other workloads")
+        others[w3.name]["cpu_baseline"] = cpu_baseline(w3, max_heads=1)
+        others[w4.name]["cpu_baseline"] = cpu_baseline(w4, max_heads=1)
+        others["c5_decode"]["cpu_baseline"] = cpu_baseline_decode(CONFIGS["c5_decode"])
+        others[w1.name]["cpu_baseline"] = cpu_baseline(w1, min_seconds=3.0)
+    rec["workloads"] = others
+    if not args.no_cross:
+        log("[bench] cross-attention, exact path and backward")
         rec["cross"] = cross_line(max(20, args.steps // 4))
         rec["cross_step"] = cross_step_line(256)
         rec["exact"] = exact_line(w, max(20, args.steps // 4))
