@@ -153,6 +153,29 @@ dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k
                          void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * dark_prf_fwd_noalloc - dark_prf_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, with the workspace taken from a
+ * static device array of DARK_PRF_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends.  Arguments as for dark_prf_fwd
+ * without workspace and ws_bytes.  The call allocates and frees nothing.
+ *   - The first call on a device looks up that device's copy of the array
+ *     (hipGetSymbolAddress); `stream` must belong to the current device, else
+ *     DARK_ERR_INVALID_ARG.
+ *   - A call whose dark_prf_workspace_bytes(desc) exceeds
+ *     DARK_PRF_SCRATCH_BYTES returns DARK_ERR_WORKSPACE and queues nothing.
+ *   - Every call on one GPU shares that GPU's array, whose contents persist
+ *     between calls and need no initialisation: calls that overlap in time on
+ *     one GPU (several streams, several host threads) race on it and must be
+ *     serialised by the caller, e.g. by queueing them on one stream.
+ */
+#define DARK_PRF_SCRATCH_BYTES (64u << 20)
+dark_status dark_prf_fwd_noalloc(const dark_prf_desc* desc, const void* q, const void* k,
+                                 const void* v, const float* M, const float* omega,
+                                 const uint8_t* mask, void* out, float* S_out, float* z_out,
+                                 void* stream);
+
+/*
  * dark_prf_decode_step - append one token to every sequence and emit its
  * output (README section "Encoder-decoder model and generation": recurrent
  * statistics updated per appended token).  desc->B = N sequences, desc->L = 1,

@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.dark_prf_fwd.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P, P, P, P,
                                    ctypes.c_size_t, P]
         L.dark_prf_fwd.restype = ctypes.c_int
+        L.dark_prf_fwd_noalloc.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P, P, P, P]
+        L.dark_prf_fwd_noalloc.restype = ctypes.c_int
         L.dark_prf_decode_step.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P,
                                            ctypes.c_uint64, P, P]
         L.dark_prf_decode_step.restype = ctypes.c_int
@@ -198,6 +200,18 @@ def dark_prf_fwd(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, omega: int, 
     return lib().dark_prf_fwd(ctypes.byref(desc), q or None, k or None, v or None, M or None,
                               omega or None, mask or None, out or None, S_out or None,
                               z_out or None, workspace or None, ws_bytes, stream or None)
+
+
+DARK_PRF_SCRATCH_BYTES = 64 << 20   # the static workspace of dark_prf_fwd_noalloc
+
+
+def dark_prf_fwd_noalloc(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, omega: int, mask: int,
+                         out: int, S_out: int, z_out: int, stream: int) -> int:
+    """Raw call of the forward that takes its workspace from the library's static
+    per-GPU buffer (no workspace argument); returns the status."""
+    return lib().dark_prf_fwd_noalloc(ctypes.byref(desc), q or None, k or None, v or None, M or None,
+                                      omega or None, mask or None, out or None, S_out or None,
+                                      z_out or None, stream or None)
 
 
 def dark_prf_context_state(desc: DarkPrfDesc, k: int, v: int, M: int, omega: int, context_mask: int,

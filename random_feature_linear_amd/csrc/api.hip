@@ -133,7 +133,7 @@ static void make_plan(const dark_prf_desc& d, Plan& p, int mode = kPlanForward) 
     p.span1 = cdiv(cdiv(L, splits), tile1) * tile1;
     p.NU = cdiv(L, p.span1);
   }
-  // operand copies of M' and omega' (bf16: hi and lo parts; see prf_kernels.cuh)
+  // operand copies of M' and omega' (bf16: hi and lo parts; see prf_kernels.h)
   const int NM = d.dtype == DARK_BF16 ? 2 : 1;
   const int R32 = (p.R16 + 1) / 2;
   const int DB = (d.d_h + 31) / 32;      // 32-column blocks of V
@@ -280,6 +280,34 @@ static void drop_records(TimingState& t) {
     (void)hipEventDestroy(r.second.second);
   }
   t.recs.clear();
+}
+
+// dark_prf_fwd_noalloc: the forward's workspace taken from a static device
+// array instead of the caller.  The array exists once per GPU (each device
+// holds its own copy at its own address).  Host code never uses its name as an
+// address, only the device pointer that hipGetSymbolAddress returns for the
+// current device, looked up on the first call on that device and kept.
+static __device__ __align__(256) unsigned char scratch[DARK_PRF_SCRATCH_BYTES];
+
+static dark_status scratch_address(void* stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DARK_ERR_HIP;
+  if (stream != nullptr) {   // the kernels run on the stream's device: it must be the current one
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &sdev) != hipSuccess) return DARK_ERR_HIP;
+    if (sdev != dev) return DARK_ERR_INVALID_ARG;
+  }
+  static std::mutex mu;
+  static std::vector<void*> ptr;   // per device; null until looked up
+  std::lock_guard<std::mutex> g(mu);
+  if ((int)ptr.size() <= dev) ptr.resize(dev + 1, nullptr);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DARK_ERR_HIP;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return DARK_OK;
 }
 
 }  // namespace dk
@@ -467,6 +495,21 @@ dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k
   a.causal = d.causal;
   a.m_per_head = d.m_per_head;
   return fn(a, p, workspace, stream);
+}
+
+dark_status dark_prf_fwd_noalloc(const dark_prf_desc* desc, const void* q, const void* k, const void* v,
+                                 const float* M, const float* omega, const uint8_t* mask, void* out, float* S_out,
+                                 float* z_out, void* stream) {
+  dark_status st = check_desc(desc, false);
+  if (st != DARK_OK) return st;
+  Plan p;
+  make_plan(*desc, p);
+  if (p.total > (size_t)DARK_PRF_SCRATCH_BYTES) return DARK_ERR_WORKSPACE;   // more than the static buffer holds
+  void* ws = nullptr;
+  st = scratch_address(stream, &ws);
+  if (st != DARK_OK) return st;
+  return dark_prf_fwd(desc, q, k, v, M, omega, mask, out, S_out, z_out, ws, (size_t)DARK_PRF_SCRATCH_BYTES,
+                      stream);
 }
 
 // Arguments common to the forward-chain calls (pointers the call does not use stay null).

@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     L = bd.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -76,6 +76,18 @@ def test_workspace_checks():
     assert _fwd(d, ws=0) == bd.DARK_ERR_WORKSPACE
     # more tokens never need less workspace
     assert bd.dark_prf_workspace_bytes(_desc(L=4096)) >= nb
+
+
+def test_noalloc_rejects_before_touching_a_device():
+    # an invalid descriptor, and a call whose workspace exceeds the static buffer,
+    # return before the library looks up its buffer or queues anything
+    assert bd.dark_prf_fwd_noalloc(_desc(d_h=48), FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0, 0, 0) == \
+        bd.DARK_ERR_INVALID_ARG
+    big = _desc(B=64, L=8192)
+    assert bd.dark_prf_workspace_bytes(big) > bd.DARK_PRF_SCRATCH_BYTES
+    assert bd.dark_prf_fwd_noalloc(big, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0, 0, 0) == bd.DARK_ERR_WORKSPACE
+    # the two L=64K-sized and L=2048-sized workloads fit
+    assert bd.dark_prf_workspace_bytes(_desc(B=2, L=2048)) <= bd.DARK_PRF_SCRATCH_BYTES
 
 
 def test_state_export_rules():
