@@ -71,7 +71,8 @@ typedef struct {
   int64_t k_str[3];   /* element strides of k over (b, h_kv, l) */
   int64_t v_str[3];   /* element strides of v over (b, h_kv, l) */
   int64_t o_str[3];   /* element strides of out over (b, h, l) */
-  uint64_t proj_tag;  /* identifies omega; see dark_prf_proj_tag */
+  uint64_t proj_tag;  /* identifies omega; see dark_prf_proj_tag and dark_prf_proj_tag_per_head */
+  int32_t omega_per_head; /* 1: omega is [H][m][r], one projection per query head; 0: one [m][r] shared */
 } dark_prf_desc;
 
 /*
@@ -92,6 +93,32 @@ typedef struct {
  */
 dark_status dark_prf_omega(uint64_t seed, int32_t m, int32_t r, int32_t orthogonal,
                            float* omega_host);
+
+/*
+ * Per-head projections (the projection drawn once per query head instead of
+ * once per module; the README keeps the projection a library choice next to
+ * the per-head geometry of section "Self-attention").  Head h uses the
+ * projection of seed dark_prf_head_seed(seed, h), built exactly as
+ * dark_prf_omega builds it, so one seed still makes every head reproducible
+ * (section "Projection lifecycle").
+ *   dark_prf_head_seed: SplitMix64's finaliser over seed + (h + 1) *
+ *     0xD1B54A32D192ED03 (an odd constant other than the redraw sequence's).
+ *   dark_prf_omega_per_head: omega_host [H][m][r] (fp32, host memory), head h
+ *     equal to dark_prf_omega(dark_prf_head_seed(seed, h), m, r, orthogonal).
+ *     DARK_ERR_INVALID_ARG for H < 1, m < 1, r < 1 or omega_host == NULL.
+ *   dark_prf_proj_tag_per_head: the tag of the H projections together; it
+ *     differs from dark_prf_proj_tag(seed, ...) and between head counts, so a
+ *     state made with shared projections is rejected by per-head calls and
+ *     the other way round.
+ * A call uses per-head projections when desc->omega_per_head = 1: omega is
+ * then [H][m][r] contiguous and every query head h uses omega[h] for its
+ * queries and for the keys it reads (with GQA, the keys of K/V head
+ * h*H_kv/H as seen by h, as with per-head geometry).
+ */
+uint64_t dark_prf_head_seed(uint64_t seed, int32_t h);
+dark_status dark_prf_omega_per_head(uint64_t seed, int32_t H, int32_t m, int32_t r, int32_t orthogonal,
+                                    float* omega_host);
+uint64_t dark_prf_proj_tag_per_head(uint64_t seed, int32_t H, int32_t m, int32_t r, int32_t orthogonal);
 
 /*
  * dark_prf_omega_device - the same projection as dark_prf_omega, generated on
@@ -133,7 +160,8 @@ size_t dark_prf_workspace_bytes(const dark_prf_desc* desc);
  *   q     [B][H][L][d_h]     (strides q_str), dtype
  *   k, v  [B][H_kv][L][d_h]  (strides k_str, v_str), dtype
  *   M     fp32 [H][r][d_h] when m_per_head, else [r][d_h], contiguous
- *   omega fp32 [m][r], contiguous (e.g. from dark_prf_omega)
+ *   omega fp32 [m][r], contiguous (e.g. from dark_prf_omega), or [H][m][r]
+ *         when desc->omega_per_head (e.g. from dark_prf_omega_per_head)
  *   mask  uint8 [B][L] contiguous, nonzero = valid key, or NULL (all valid);
  *         masked positions are removed as keys; their query rows are still
  *         computed
@@ -267,6 +295,29 @@ size_t dark_prf_exact_workspace_bytes(const dark_prf_desc* desc);
 dark_status dark_prf_exact_fwd(const dark_prf_desc* desc, const void* q, const void* k,
                                const void* v, const float* M, const uint8_t* mask, void* out,
                                void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * "auto" attention mode (README section "Attention modes": exact attention up
+ * to and including a caller-chosen sequence length, linear attention beyond
+ * it).  With L = desc->L:
+ *   L <= exact_threshold: dark_prf_exact_fwd (omega is not used);
+ *   L >  exact_threshold: dark_prf_fwd without state export.
+ * exact_threshold >= 0 (0: always linear).  No recurrent state is exported:
+ * the README keeps full-prefix decoding for the auto and exact modes.
+ *   dark_prf_auto_mode: 1 if the call takes the exact path, 0 if the linear
+ *     one, -1 for an invalid descriptor or a negative threshold.
+ *   dark_prf_auto_workspace_bytes: the workspace of the path taken (0 if
+ *     invalid).
+ *   dark_prf_auto_fwd: arguments as for dark_prf_fwd without S_out and z_out;
+ *     DARK_ERR_INVALID_ARG for a negative threshold; otherwise the status of
+ *     the path taken.
+ */
+int32_t dark_prf_auto_mode(const dark_prf_desc* desc, int32_t exact_threshold);
+size_t dark_prf_auto_workspace_bytes(const dark_prf_desc* desc, int32_t exact_threshold);
+dark_status dark_prf_auto_fwd(const dark_prf_desc* desc, int32_t exact_threshold, const void* q,
+                              const void* k, const void* v, const float* M, const float* omega,
+                              const uint8_t* mask, void* out, void* workspace, size_t ws_bytes,
+                              void* stream);
 
 /*
  * Projection lifecycle (README section "Projection lifecycle"): a projection

@@ -3,7 +3,16 @@
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
 this package.  It shares no code with the HIP library and never calls it.
 """
-from .omega_gen import omega, omega_iid, omega_orthogonal, normals, splitmix64, uniforms  # noqa: F401
+from .omega_gen import (  # noqa: F401
+    head_seed,
+    normals,
+    omega,
+    omega_iid,
+    omega_orthogonal,
+    omega_per_head,
+    splitmix64,
+    uniforms,
+)
 from .prf_oracle import (  # noqa: F401
     attend_causal_blockwise,
     attend_noncausal,
@@ -15,6 +24,7 @@ from .prf_oracle import (  # noqa: F401
     decode_step,
     exact_kernel_attention,
     head_geometry,
+    head_omega,
     kv_head,
     prf_features,
     project,

@@ -89,3 +89,18 @@ def omega(seed: int, m: int, r: int, orthogonal: bool) -> np.ndarray:
     """Omega as float32 [m][r] (the values both sides feed to the attention)."""
     om = omega_orthogonal(seed, m, r) if orthogonal else omega_iid(seed, m, r)
     return om.astype(np.float32)
+
+
+def head_seed(seed: int, h: int) -> int:
+    """Seed of query head h's projection when every head draws its own: SplitMix64's
+    finaliser (the same Mix13 steps as in splitmix64 above) applied to
+    seed + (h + 1) * 0xD1B54A32D192ED03 modulo 2^64.  Written with Python integers."""
+    z = (seed + (h + 1) * 0xD1B54A32D192ED03) & _MASK64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+    return z ^ (z >> 31)
+
+
+def omega_per_head(seed: int, H: int, m: int, r: int, orthogonal: bool) -> np.ndarray:
+    """Per-head projections [H][m][r] (float32): head h is omega(head_seed(seed, h), m, r, orthogonal)."""
+    return np.stack([omega(head_seed(seed, h), m, r, orthogonal) for h in range(H)])

@@ -60,6 +60,12 @@ def head_geometry(M: np.ndarray, h: int) -> np.ndarray:
     return M[h] if M.ndim == 3 else M
 
 
+def head_omega(omega: np.ndarray, h: int) -> np.ndarray:
+    """Omega_h: one projection per query head [H][m][r], or one [m][r] shared by all heads."""
+    omega = np.asarray(omega)
+    return omega[h] if omega.ndim == 3 else omega
+
+
 def kv_head(h: int, H: int, H_kv: int) -> int:
     """Key/value head read by query head h when H_kv heads are shared (GQA)."""
     return (h * H_kv) // H
@@ -132,7 +138,8 @@ def attention(q, k, v, M, omega, mask: Optional[np.ndarray] = None, causal: bool
     """DARKFormer linear-mode attention core.
 
     q [B][H][L][d_h], k and v [B][H_kv][L][d_h], M [H][r][d_h] or [r][d_h],
-    omega [m][r], mask [B][L] (nonzero = valid key) or None.
+    omega [m][r] or [H][m][r] (one projection per query head), mask [B][L]
+    (nonzero = valid key) or None.
     `heads` restricts the work to a list of (b, h) pairs (other outputs stay 0).
     Returns O [B][H][L][d_h] (fp64) and, if return_state, S [B][H][m][d_h] and
     z [B][H][m]: the state after the last token.
@@ -140,16 +147,16 @@ def attention(q, k, v, M, omega, mask: Optional[np.ndarray] = None, causal: bool
     q, k, v = f64(q), f64(k), f64(v)
     B, H, L, d = q.shape
     H_kv = k.shape[1]
-    m = np.asarray(omega).shape[0]
+    m = np.asarray(omega).shape[-2]
     O = np.zeros((B, H, L, d))
     S_all = np.zeros((B, H, m, d)) if return_state else None
     z_all = np.zeros((B, H, m)) if return_state else None
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in pairs:
         g = kv_head(h, H, H_kv)
-        M_h = head_geometry(M, h)
-        PQ = prf_features(q[b, h], M_h, omega)
-        PK = prf_features(k[b, g], M_h, omega)
+        M_h, om_h = head_geometry(M, h), head_omega(omega, h)
+        PQ = prf_features(q[b, h], M_h, om_h)
+        PK = prf_features(k[b, g], M_h, om_h)
         if mask is not None:
             PK = PK * (np.asarray(mask[b]) != 0)[:, None]
         if causal:
@@ -180,8 +187,8 @@ def decode_step(S, z, q, k, v, M, omega):
     for h in range(H):
         g = kv_head(h, H, H_kv)
         M_h = head_geometry(M, h)
-        pq = prf_features(q[:, h], M_h, omega)      # [N][m]
-        pk = prf_features(k[:, g], M_h, omega)      # [N][m]
+        pq = prf_features(q[:, h], M_h, head_omega(omega, h))      # [N][m]
+        pk = prf_features(k[:, g], M_h, head_omega(omega, h))      # [N][m]
         S[:, h] += pk[:, :, None] * v[:, g][:, None, :]
         z[:, h] += pk
         num = np.einsum("nm,nmd->nd", pq, S[:, h])
@@ -202,13 +209,13 @@ def context_state(k, v, M, omega, H: int, context_mask: Optional[np.ndarray] = N
     """
     k, v = f64(k), f64(v)
     B, H_kv, L_k, d = k.shape
-    m = np.asarray(omega).shape[0]
+    m = np.asarray(omega).shape[-2]
     S = np.zeros((B, H, m, d))
     z = np.zeros((B, H, m))
     for b in range(B):
         for h in range(H):
             g = kv_head(h, H, H_kv)
-            PK = prf_features(k[b, g], head_geometry(M, h), omega)
+            PK = prf_features(k[b, g], head_geometry(M, h), head_omega(omega, h))
             if context_mask is not None:
                 PK = PK * (np.asarray(context_mask[b]) != 0)[:, None]
             S[b, h] = PK.T @ v[b, g]
@@ -230,7 +237,7 @@ def cross_attention(q, S, z, M, omega, query_mask: Optional[np.ndarray] = None):
     O = np.zeros((B, H, L_q, d))
     for b in range(B):
         for h in range(H):
-            PQ = prf_features(q[b, h], head_geometry(M, h), omega)
+            PQ = prf_features(q[b, h], head_geometry(M, h), head_omega(omega, h))
             O[b, h] = _ratio(PQ @ S[b, h], PQ @ z[b, h])
             if query_mask is not None:
                 O[b, h][np.asarray(query_mask[b]) == 0] = 0.0
@@ -307,10 +314,10 @@ def attention_backward(q, k, v, M, omega, dout, mask: Optional[np.ndarray] = Non
         visb = vis if mask is None else vis * (np.asarray(mask[b]) != 0)[None, :]
         for h in range(H):
             g = kv_head(h, H, H_kv)
-            M_h = head_geometry(M, h)
+            M_h, om_h = head_geometry(M, h), head_omega(omega, h)
             UQ, UK = project(q[b, h], M_h), project(k[b, g], M_h)
-            PQ = prf_features(q[b, h], M_h, omega)
-            PK = prf_features(k[b, g], M_h, omega)
+            PQ = prf_features(q[b, h], M_h, om_h)
+            PK = prf_features(k[b, g], M_h, om_h)
             W = (PQ @ PK.T) * visb
             D = W.sum(axis=1)
             O = _ratio(W @ v[b, g], D)
@@ -324,7 +331,7 @@ def attention_backward(q, k, v, M, omega, dout, mask: Optional[np.ndarray] = Non
             grads = []
             for P, U, dP in ((PQ, UQ, dW @ PK), (PK, UK, dW.T @ PQ)):
                 dE = dP * P
-                grads.append(dE @ omega - U * dE.sum(axis=1, keepdims=True))
+                grads.append(dE @ om_h - U * dE.sum(axis=1, keepdims=True))
             dUQ, dUK = grads
             dq[b, h] += s * (dUQ @ M_h)
             dk[b, g] += s * (dUK @ M_h)

@@ -33,7 +33,7 @@ class DarkPrfDesc(ctypes.Structure):
         ("m_per_head", ctypes.c_int32),
         ("q_str", ctypes.c_int64 * 3), ("k_str", ctypes.c_int64 * 3),
         ("v_str", ctypes.c_int64 * 3), ("o_str", ctypes.c_int64 * 3),
-        ("proj_tag", ctypes.c_uint64),
+        ("proj_tag", ctypes.c_uint64), ("omega_per_head", ctypes.c_int32),
     ]
 
 
@@ -78,6 +78,14 @@ def lib() -> ctypes.CDLL:
         L.dark_prf_omega_device.restype = ctypes.c_int
         L.dark_prf_proj_tag.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         L.dark_prf_proj_tag.restype = ctypes.c_uint64
+        L.dark_prf_head_seed.argtypes = [ctypes.c_uint64, ctypes.c_int32]
+        L.dark_prf_head_seed.restype = ctypes.c_uint64
+        L.dark_prf_omega_per_head.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, P]
+        L.dark_prf_omega_per_head.restype = ctypes.c_int
+        L.dark_prf_proj_tag_per_head.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int32]
+        L.dark_prf_proj_tag_per_head.restype = ctypes.c_uint64
         L.dark_prf_workspace_bytes.argtypes = [ctypes.POINTER(DarkPrfDesc)]
         L.dark_prf_workspace_bytes.restype = ctypes.c_size_t
         L.dark_prf_fwd.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P, P, P, P,
@@ -98,6 +106,13 @@ def lib() -> ctypes.CDLL:
         L.dark_prf_exact_workspace_bytes.restype = ctypes.c_size_t
         L.dark_prf_exact_fwd.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.dark_prf_exact_fwd.restype = ctypes.c_int
+        L.dark_prf_auto_mode.argtypes = [ctypes.POINTER(DarkPrfDesc), ctypes.c_int32]
+        L.dark_prf_auto_mode.restype = ctypes.c_int32
+        L.dark_prf_auto_workspace_bytes.argtypes = [ctypes.POINTER(DarkPrfDesc), ctypes.c_int32]
+        L.dark_prf_auto_workspace_bytes.restype = ctypes.c_size_t
+        L.dark_prf_auto_fwd.argtypes = [ctypes.POINTER(DarkPrfDesc), ctypes.c_int32, P, P, P, P, P, P, P, P,
+                                        ctypes.c_size_t, P]
+        L.dark_prf_auto_fwd.restype = ctypes.c_int
         L.dark_prf_bwd_workspace_bytes.argtypes = [ctypes.POINTER(DarkPrfDesc)]
         L.dark_prf_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.dark_prf_bwd.argtypes = [ctypes.POINTER(DarkPrfDesc), P, P, P, P, P, P, P, P, P, P, P, P,
@@ -138,6 +153,24 @@ def dark_prf_omega(seed: int, m: int, r: int, orthogonal: bool) -> np.ndarray:
     if st != DARK_OK:
         raise DarkPrfError(st, "dark_prf_omega")
     return out
+
+
+def dark_prf_head_seed(seed: int, h: int) -> int:
+    return int(lib().dark_prf_head_seed(ctypes.c_uint64(seed), h))
+
+
+def dark_prf_omega_per_head(seed: int, H: int, m: int, r: int, orthogonal: bool) -> np.ndarray:
+    """Per-head projections [H][m][r]: head h is dark_prf_omega(dark_prf_head_seed(seed, h), ...)."""
+    out = np.empty((H, m, r), dtype=np.float32)
+    st = lib().dark_prf_omega_per_head(ctypes.c_uint64(seed), H, m, r, int(bool(orthogonal)),
+                                       out.ctypes.data_as(ctypes.c_void_p))
+    if st != DARK_OK:
+        raise DarkPrfError(st, "dark_prf_omega_per_head")
+    return out
+
+
+def dark_prf_proj_tag_per_head(seed: int, H: int, m: int, r: int, orthogonal: bool) -> int:
+    return int(lib().dark_prf_proj_tag_per_head(ctypes.c_uint64(seed), H, m, r, int(bool(orthogonal))))
 
 
 def dark_prf_omega_device_workspace_bytes(m: int, r: int, orthogonal: bool) -> int:
@@ -239,6 +272,21 @@ def dark_prf_exact_fwd(desc: DarkPrfDesc, q: int, k: int, v: int, M: int, mask: 
                                     mask or None, out or None, workspace or None, ws_bytes, stream or None)
 
 
+def dark_prf_auto_mode(desc: DarkPrfDesc, exact_threshold: int) -> int:
+    return int(lib().dark_prf_auto_mode(ctypes.byref(desc), exact_threshold))
+
+
+def dark_prf_auto_workspace_bytes(desc: DarkPrfDesc, exact_threshold: int) -> int:
+    return int(lib().dark_prf_auto_workspace_bytes(ctypes.byref(desc), exact_threshold))
+
+
+def dark_prf_auto_fwd(desc: DarkPrfDesc, exact_threshold: int, q: int, k: int, v: int, M: int, omega: int,
+                      mask: int, out: int, workspace: int, ws_bytes: int, stream: int) -> int:
+    return lib().dark_prf_auto_fwd(ctypes.byref(desc), exact_threshold, q or None, k or None, v or None,
+                                   M or None, omega or None, mask or None, out or None, workspace or None,
+                                   ws_bytes, stream or None)
+
+
 def dark_prf_bwd_workspace_bytes(desc: DarkPrfDesc) -> int:
     return int(lib().dark_prf_bwd_workspace_bytes(ctypes.byref(desc)))
 
@@ -291,7 +339,8 @@ def make_desc(q, k, v, out, M, omega, causal: bool, proj_tag: int = 0) -> DarkPr
     B, H, L, d_h = q.shape
     d = DarkPrfDesc()
     d.B, d.H, d.H_kv, d.L, d.d_h = B, H, k.shape[1], L, d_h
-    d.m, d.r = omega.shape[0], omega.shape[1]
+    d.m, d.r = omega.shape[-2], omega.shape[-1]
+    d.omega_per_head = int(omega.dim() == 3)
     d.dtype = _dtype_code(q)
     d.causal = int(bool(causal))
     d.m_per_head = int(M.dim() == 3)
@@ -341,7 +390,8 @@ def decode_step(q, k, v, M, omega, S, z, state_tag: int, proj_tag: int, out=None
     N, H, d_h = q.shape
     d = DarkPrfDesc()
     d.B, d.H, d.H_kv, d.L, d.d_h = N, H, k.shape[1], 1, d_h
-    d.m, d.r = omega.shape[0], omega.shape[1]
+    d.m, d.r = omega.shape[-2], omega.shape[-1]
+    d.omega_per_head = int(omega.dim() == 3)
     d.dtype = _dtype_code(q)
     d.causal = 1
     d.m_per_head = int(M.dim() == 3)
@@ -374,7 +424,8 @@ def context_state(k, v, M, omega, H: int, context_mask=None, proj_tag: int = 0, 
     B, H_kv, L_k, d_h = k.shape
     d = DarkPrfDesc()
     d.B, d.H, d.H_kv, d.L, d.d_h = B, H, H_kv, L_k, d_h
-    d.m, d.r = omega.shape[0], omega.shape[1]
+    d.m, d.r = omega.shape[-2], omega.shape[-1]
+    d.omega_per_head = int(omega.dim() == 3)
     d.dtype = _dtype_code(k)
     d.causal = 0
     d.m_per_head = int(M.dim() == 3)
@@ -408,7 +459,8 @@ def cross_attention(q, M, omega, S, z, state_tag: int, proj_tag: int, query_mask
     B, H, L_q, d_h = q.shape
     d = DarkPrfDesc()
     d.B, d.H, d.H_kv, d.L, d.d_h = B, H, H_kv, L_q, d_h
-    d.m, d.r = omega.shape[0], omega.shape[1]
+    d.m, d.r = omega.shape[-2], omega.shape[-1]
+    d.omega_per_head = int(omega.dim() == 3)
     d.dtype = _dtype_code(q)
     d.causal = 0
     d.m_per_head = int(M.dim() == 3)
@@ -428,6 +480,25 @@ def cross_attention(q, M, omega, S, z, state_tag: int, proj_tag: int, query_mask
                             workspace.data_ptr(), workspace.numel(), stream)
     if st != DARK_OK:
         raise DarkPrfError(st, "dark_prf_cross_fwd")
+    return out
+
+
+def auto_attention(q, k, v, M, omega, exact_threshold: int, mask=None, causal: bool = False, proj_tag: int = 0,
+                   out=None, workspace=None):
+    """dark_prf_auto_fwd: exact attention for L <= exact_threshold, linear attention above."""
+    import torch
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    desc = make_desc(q, k, v, out, M, omega, causal, proj_tag)
+    nbytes = dark_prf_auto_workspace_bytes(desc, exact_threshold)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = dark_prf_auto_fwd(desc, exact_threshold, q.data_ptr(), k.data_ptr(), v.data_ptr(), M.data_ptr(),
+                           omega.data_ptr(), _mask_ptr(mask, "mask"), out.data_ptr(), workspace.data_ptr(),
+                           workspace.numel(), stream)
+    if st != DARK_OK:
+        raise DarkPrfError(st, "dark_prf_auto_fwd")
     return out
 
 

@@ -105,6 +105,8 @@ static void make_plan(const dark_prf_desc& d, Plan& p, int mode = kPlanForward) 
   p.R16 = rank_blocks(d.r);
   p.FB = cdiv(d.m, 32);
   p.HM = d.m_per_head ? d.H : 1;
+  p.HO = d.omega_per_head ? d.H : 1;
+  p.HW = (d.m_per_head || d.omega_per_head) ? d.H : 1;
   p.fold = fold_exponent(d.dtype == DARK_BF16 ? 2 : 4, d.d_h, p.R16);
   p.BH = d.B * d.H;
   p.elem = d.dtype == DARK_BF16 ? 2 : 4;
@@ -144,10 +146,10 @@ static void make_plan(const dark_prf_desc& d, Plan& p, int mode = kPlanForward) 
   p.off_mfrag = off;
   off = align256(off + (size_t)p.HM * R32 * (d.d_h / 16) * NM * frag * p.elem);
   p.off_ofrag = off;
-  if (p.fold)   // W' fragments per geometry matrix, K-steps over d_h
-    off = align256(off + (size_t)p.HM * p.FB * (d.d_h / 16) * NM * frag * p.elem);
-  else          // omega' fragments, K-steps over the rank
-    off = align256(off + (size_t)p.FB * p.R16 * NM * frag * p.elem);
+  if (p.fold)   // W' fragments per folded operand, K-steps over d_h
+    off = align256(off + (size_t)p.HW * p.FB * (d.d_h / 16) * NM * frag * p.elem);
+  else          // omega' fragments per projection, K-steps over the rank
+    off = align256(off + (size_t)p.HO * p.FB * p.R16 * NM * frag * p.elem);
   p.off_sdelta = off;
   off = align256(off + (size_t)p.BH * p.NU * state_frags * frag * p.elem);
   p.off_sfrag = off;
@@ -157,13 +159,13 @@ static void make_plan(const dark_prf_desc& d, Plan& p, int mode = kPlanForward) 
   off = align256(off + (size_t)p.BH * p.NU * p.FB * 32 * sizeof(float));
   p.off_zsum = off;
   off = align256(off + (size_t)p.BH * nout * p.FB * 32 * sizeof(float));
-  // keys and queries are projected once up front (for |u|^2) when several
-  // feature slices, or the causal query side, would otherwise repeat it
-  // (the cross-attention calls have one side each: each side projects its own shifts)
+  // keys are projected once up front (for |u|^2) when several feature slices,
+  // or the causal query side, would otherwise repeat it (a context summary
+  // projects its own keys; queries need no such shift)
   p.mode = mode;
   p.kshift = mode == kPlanForward && p.fold && (p.NF > 1 || (d.causal && d.d_h >= 128));
   p.off_kshift = off;
-  if (p.kshift) off = align256(off + 2 * (size_t)p.BH * L * sizeof(float));   // key, then query shifts
+  if (p.kshift) off = align256(off + (size_t)p.BH * L * sizeof(float));
   p.total = off;
 }
 
@@ -180,6 +182,7 @@ static dark_status check_desc(const dark_prf_desc* d, bool decode, int tensors =
   if (d->dtype != DARK_F32 && d->dtype != DARK_BF16) return DARK_ERR_INVALID_ARG;
   if (d->causal != 0 && d->causal != 1) return DARK_ERR_INVALID_ARG;
   if (d->m_per_head != 0 && d->m_per_head != 1) return DARK_ERR_INVALID_ARG;
+  if (d->omega_per_head != 0 && d->omega_per_head != 1) return DARK_ERR_INVALID_ARG;
   if (decode && (d->L != 1 || d->causal != 1)) return DARK_ERR_INVALID_ARG;
   const int64_t elem = d->dtype == DARK_BF16 ? 2 : 4;
   const int64_t* strides[4] = {d->q_str, d->k_str, d->v_str, d->o_str};
@@ -359,6 +362,25 @@ dark_status dark_prf_omega(uint64_t seed, int32_t m, int32_t r, int32_t orthogon
   return DARK_OK;
 }
 
+uint64_t dark_prf_head_seed(uint64_t seed, int32_t h) {
+  return mix64(seed + (uint64_t)((int64_t)h + 1) * 0xD1B54A32D192ED03ULL);
+}
+
+dark_status dark_prf_omega_per_head(uint64_t seed, int32_t H, int32_t m, int32_t r, int32_t orthogonal,
+                                    float* omega_host) {
+  if (H < 1 || m < 1 || r < 1 || omega_host == nullptr) return DARK_ERR_INVALID_ARG;
+  for (int32_t h = 0; h < H; ++h) {
+    const dark_status st = dark_prf_omega(dark_prf_head_seed(seed, h), m, r, orthogonal,
+                                          omega_host + (int64_t)h * m * r);
+    if (st != DARK_OK) return st;
+  }
+  return DARK_OK;
+}
+
+uint64_t dark_prf_proj_tag_per_head(uint64_t seed, int32_t H, int32_t m, int32_t r, int32_t orthogonal) {
+  return mix64(dark_prf_proj_tag(seed, m, r, orthogonal) ^ mix64((uint64_t)(uint32_t)H + 0x5851F42D4C957F2DULL));
+}
+
 static uint64_t draw_seed(uint64_t base, int64_t draw) {
   return draw == 0 ? base : mix64(base + (uint64_t)draw * 0x9E3779B97F4A7C15ULL);
 }
@@ -482,7 +504,6 @@ dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k
   a.S_out = S_out;
   a.z_out = z_out;
   a.kshift = nullptr;   // set by the launcher from the workspace
-  a.qshift = nullptr;
   a.qmask = nullptr;
   a.S_in = nullptr;
   a.z_in = nullptr;
@@ -494,6 +515,7 @@ dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k
   a.r = d.r;
   a.causal = d.causal;
   a.m_per_head = d.m_per_head;
+  a.omega_per_head = d.omega_per_head;
   return fn(a, p, workspace, stream);
 }
 
@@ -530,6 +552,7 @@ static FwdArgs fwd_args(const dark_prf_desc& d) {
   a.r = d.r;
   a.causal = d.causal;
   a.m_per_head = d.m_per_head;
+  a.omega_per_head = d.omega_per_head;
   return a;
 }
 
@@ -638,6 +661,28 @@ dark_status dark_prf_exact_fwd(const dark_prf_desc* desc, const void* q, const v
   a.mask = mask;
   a.M = M;
   return fn(a, workspace, stream);
+}
+
+int32_t dark_prf_auto_mode(const dark_prf_desc* desc, int32_t exact_threshold) {
+  if (exact_threshold < 0 || check_desc(desc, false) != DARK_OK) return -1;
+  return desc->L <= exact_threshold ? 1 : 0;
+}
+
+size_t dark_prf_auto_workspace_bytes(const dark_prf_desc* desc, int32_t exact_threshold) {
+  const int32_t mode = dark_prf_auto_mode(desc, exact_threshold);
+  if (mode < 0) return 0;
+  return mode == 1 ? dark_prf_exact_workspace_bytes(desc) : dark_prf_workspace_bytes(desc);
+}
+
+dark_status dark_prf_auto_fwd(const dark_prf_desc* desc, int32_t exact_threshold, const void* q, const void* k,
+                              const void* v, const float* M, const float* omega, const uint8_t* mask, void* out,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  if (exact_threshold < 0) return DARK_ERR_INVALID_ARG;
+  const dark_status st = check_desc(desc, false);
+  if (st != DARK_OK) return st;
+  if (desc->L <= exact_threshold)
+    return dark_prf_exact_fwd(desc, q, k, v, M, mask, out, workspace, ws_bytes, stream);
+  return dark_prf_fwd(desc, q, k, v, M, omega, mask, out, nullptr, nullptr, workspace, ws_bytes, stream);
 }
 
 size_t dark_prf_bwd_workspace_bytes(const dark_prf_desc* desc) {

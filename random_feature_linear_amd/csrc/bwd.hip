@@ -560,6 +560,7 @@ dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStrea
   float *Wc = F(o.Wc), *A2 = F(o.A2), *dQh = F(o.dQh), *dKh = F(o.dKh), *dVh = F(o.dVh), *dMp = F(o.dMp);
   const float s = 1.0f / sqrtf(sqrtf((float)dh));
   const int64_t hM = d.m_per_head ? (int64_t)r * dh : 0;   // M_h offset per head
+  const int64_t hO = d.omega_per_head ? (int64_t)m * r : 0;   // omega_h offset per head
   Launcher ln{st, H};
 
   // per-(b, h) row-major fp32 buffers [BH][Lp][w]: operand and output strides
@@ -598,7 +599,7 @@ dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStrea
   const int BH2 = (int)(2 * BH);
   ln.aux(halfnorm_kernel, 2 * BH * Lp * 64, 256, (const float*)Uq, nq, r, 2 * BH * Lp);
   // 2. features phi = exp(u . omega_j - |u|^2 / 2) / sqrt(m); keys masked, rows t >= L zero
-  const GOp OmT = op(p.omega, 0, 0, 0, 1, r);   // (k, j) = omega[j][k]
+  const GOp OmT = op(p.omega, 0, hO, 0, 1, r);   // (k, j) = omega_h[j][k]
   const float inv_sqrt_m = 1.0f / sqrtf((float)m);
   ln.gemm<float, float>(rows(Uq, r), OmT, orows(Pq, m), Lp, m, r, BH2, 1, inv_sqrt_m, 0, kEpiFeature, 0, -1, nq, Lp,
                         p.mask, L, nullptr, 0, p.mask ? d.B : 0);
@@ -648,7 +649,7 @@ dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStrea
   }
   // 8. through the feature map: dU = (dPhi * Phi) Omega - U * rowsum(dPhi * Phi)
   // (the A operand dPhi * Phi is formed in the loads, which also sum its rows)
-  const GOp Om = op(p.omega, 0, 0, 0, r, 1);   // (k, j) = omega[k][j]
+  const GOp Om = op(p.omega, 0, hO, 0, r, 1);   // (k, j) = omega_h[k][j]
   GOp dEq = rows(dPq, m);   // and dPk, Pk from batch row B on
   dEq.p2 = Pq;
   ln.gemm<float, float, true>(dEq, Om, orows(dUq, r), Lp, r, m, BH2, 1, 1.f, 0, kEpiPlain, 0, -1, nullptr, 0, nullptr,

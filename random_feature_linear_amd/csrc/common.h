@@ -20,11 +20,10 @@ struct FwdArgs {
   float* S_out;
   float* z_out;
   float* kshift;   // per-key shifts in the workspace (folded path), or null
-  float* qshift;   // per-query shifts, likewise
   const uint8_t* qmask;   // cross-attention query mask [B][L] (nonzero = valid), or null
   const float* S_in;      // cross-attention context summary S [B][H][m][d_h], z [B][H][m]
   const float* z_in;
-  int B, H, H_kv, L, m, r, causal, m_per_head;
+  int B, H, H_kv, L, m, r, causal, m_per_head, omega_per_head;
 };
 
 // The exponent omega_j . u of a feature can be formed from the projected token
@@ -44,7 +43,9 @@ struct Plan {
   int DH;      // head dimension (template value)
   int R16;     // geometry rank in 16-wide blocks, rounded up to 1, 2, 4, 8 or 16
   int FB;      // 32-feature blocks (ceil(m / 32))
-  int HM;      // number of geometry matrices (H or 1)
+  int HM;      // number of geometry matrices M (H or 1)
+  int HO;      // number of projections omega (H or 1)
+  int HW;      // number of folded operands W' = omega' M' (H if either is per head, else 1)
   int fold;    // exponent from W' x (see fold_exponent)
   int kshift;  // folded path with per-key shifts precomputed once (kshift_kernel)
   int mode;    // kPlanForward, kPlanContext (key side and sum only) or kPlanCross (query side on a given state)

@@ -30,7 +30,7 @@ struct DecodeArgs {
   float* S;
   float* z;
   const uint8_t* qmask;   // read-only pass: query mask [N] (nonzero = valid), or null
-  int N, H, H_kv, m, r, m_per_head, NS;
+  int N, H, H_kv, m, r, m_per_head, omega_per_head, NS;
 };
 
 __device__ __forceinline__ float ld_elem(const __bf16* p, int i) { return (float)p[i]; }
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   // ---- phi_j = exp(omega_j . u - |u|^2 / 2) / sqrt(m) for every vector ----
   const float half_log2m = 0.5f * log2f((float)a.m);
   for (int j = tid; j < a.m; j += kDecThreads) {
-    const float* om = a.omega + (long)j * a.r;
+    const float* om = a.omega + ((long)(a.omega_per_head ? h : 0) * a.m + j) * a.r;
     float e[NV * NS];
 #pragma unroll
     for (int vi = 0; vi < NV * NS; ++vi) e[vi] = 0.f;
@@ -299,6 +299,7 @@ dark_status launch_decode_impl(const dark_prf_desc& d, const void* q, const void
   a.m = d.m;
   a.r = d.r;
   a.m_per_head = d.m_per_head;
+  a.omega_per_head = d.omega_per_head;
   auto lds = [&](int ns) { return dec_lds_bytes(ns, DH, d.r, d.m); };
   // two sequences per workgroup (the feature maps share the M and omega reads)
   // when there are enough of them and the LDS allows it

@@ -21,9 +21,12 @@
 // same order.
 //
 // exp is evaluated as exp2: omega is pre-scaled by log2(e) and the accumulator
-// of the exponent product starts at -(log2(e) |u|^2 / 2 + log2(m) / 2), so the
-// shift and the 1/sqrt(m) factor cost nothing.  A masked key, and a padding
-// feature past m, starts at -inf and gives exactly 0.
+// of a key's exponent product starts at -(log2(e) |u|^2 / 2 + log2(m) / 2), so
+// the shift and the 1/sqrt(m) factor cost nothing.  A masked key, and a padding
+// feature past m, starts at -inf and gives exactly 0.  A query's features need
+// neither term: any factor per query row cancels in N / D (section "Kernel",
+// attention equation), so the query side subtracts instead its largest
+// exponent over the first 32 features, which keeps the exp2 arguments near 0.
 //
 // Precision of the bf16 path.  The exponent omega_j . u reaches magnitudes of
 // ten and more, and a weight error of e per key shows up as a relative output
@@ -379,14 +382,15 @@ __device__ __forceinline__ void mfrag_lane(long idx, const float* __restrict__ M
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict__ omega,
-                            T* __restrict__ mfrag, T* __restrict__ ofrag, int HM, int r, int d_h, int m,
-                            int R16, int FB, float s, int fold) {
+                            T* __restrict__ mfrag, T* __restrict__ ofrag, int HM, int HO, int HW, int r, int d_h,
+                            int m, int R16, int FB, float s, int fold) {
   constexpr int NM = kParts<T>;
   const int R32 = (R16 + 1) / 2;
   const int KD = d_h / 16;
   const long nM = (long)HM * R32 * KD * NM * 64;
-  // fold: 0 omega' fragments, 1 W' fragments here, 2 W' fragments by fold_kernel
-  const long nO = fold == 2 ? 0 : fold ? (long)HM * FB * KD * 64 : (long)FB * R16 * NM * 64;
+  // fold: 0 omega' fragments (HO projections), 1 W' fragments here (HW
+  // operands), 2 W' fragments by fold_kernel
+  const long nO = fold == 2 ? 0 : fold ? (long)HW * FB * KD * 64 : (long)HO * FB * R16 * NM * 64;
   for (long idx = blockIdx.x * (long)blockDim.x + threadIdx.x; idx < nM + nO;
        idx += (long)gridDim.x * blockDim.x) {
     float v[8];
@@ -399,13 +403,13 @@ __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict
     if (!m_side && fold) {
       const int kd = (int)(f % KD);
       const int fb = (int)((f / KD) % FB);
-      const int hm = (int)(f / ((long)KD * FB));
+      const int hw = (int)(f / ((long)KD * FB));   // operand hw: M of head hw (or shared), omega likewise
       const int row = fb * 32 + c;
       const int col0 = kd * 16 + 8 * g;
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (row < m) {
-        const float* orow = omega + (long)row * r;
-        const float* Mh = M + (long)hm * r * d_h + col0;
+        const float* orow = omega + ((long)(HO > 1 ? hw : 0) * m + row) * r;
+        const float* Mh = M + (long)(HM > 1 ? hw : 0) * r * d_h + col0;
         for (int a = 0; a < r; ++a) {
           const float w = orow[a];
           const float4 m0 = *reinterpret_cast<const float4*>(Mh + (long)a * d_h);
@@ -440,12 +444,14 @@ __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict
       continue;
     } else {
       const int k = (int)((f / NM) % R16);
-      const int fb = (int)(f / ((long)NM * R16));
+      const int fb = (int)((f / ((long)NM * R16)) % FB);
+      const int ho = (int)(f / ((long)NM * R16 * FB));
       const int row = fb * 32 + c;
+      const float* om = omega + (long)ho * m * r;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int a = 16 * k + 8 * (e >> 2) + 4 * g + (e & 3);
-        const float x = (row < m && a < r) ? kLog2e * omega[(long)row * r + a] : 0.f;
+        const float x = (row < m && a < r) ? kLog2e * om[(long)row * r + a] : 0.f;
         const float hi = NM == 2 ? bf16_hi(x) : x;
         v[e] = part == 0 ? hi : x - hi;
       }
@@ -468,11 +474,12 @@ __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict
 constexpr int kFoldRC = 64;   // rank indices per chunk
 template <typename T>
 __global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict__ M, const float* __restrict__ omega,
-                                                        T* __restrict__ ofrag, T* __restrict__ mfrag, int HM, int R16,
-                                                        int r, int d_h, int m, int FB, float s, float scale) {
+                                                        T* __restrict__ ofrag, T* __restrict__ mfrag, int HM, int HO,
+                                                        int HW, int R16, int r, int d_h, int m, int FB, float s,
+                                                        float scale) {
   static_assert(sizeof(T) == 2, "the folded operands are bf16");
   {  // blocks past the W' tiles write the M' fragments (used for |u|^2)
-    const int nW = HM * FB * ((d_h / 32 + 3) / 4);
+    const int nW = HW * FB * ((d_h / 32 + 3) / 4);
     if ((int)blockIdx.x >= nW) {
       const long nM = (long)HM * ((R16 + 1) / 2) * (d_h / 16) * kParts<T> * 64;
       const long idx = (long)(blockIdx.x - nW) * kThreads + threadIdx.x;
@@ -487,9 +494,10 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict_
   const int NG = (DT + 3) / 4;                 // groups of four column tiles
   const int grp = blockIdx.x % NG;
   const int fb = (blockIdx.x / NG) % FB;
-  const int hm = blockIdx.x / (NG * FB);
+  const int hw = blockIdx.x / (NG * FB);       // operand hw: M and omega of head hw (or the shared ones)
   const int col0 = grp * 128;                  // first column of the group
-  const float* Mh = M + (long)hm * r * d_h;
+  const float* Mh = M + (long)(HM > 1 ? hw : 0) * r * d_h;
+  omega += (long)(HO > 1 ? hw : 0) * m * r;
   // this thread's loads of one chunk: 8 float4 of M (row a, 4 columns), 2 float4 of omega
   float4 vm[8], vo[2];
   auto fetch = [&](int a0) {
@@ -562,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict_
       hi[e] = bf16_hi(x);
       lo[e] = x - hi[e];
     }
-    const long f = ((long)hm * FB + fb) * KD + 2 * dt + h;
+    const long f = ((long)hw * FB + fb) * KD + 2 * dt + h;
     typename FragOf<T>::type fr;
     make_frag(fr, hi);
     st8(ofrag + ((f * NM) * 64 + lane) * 8, fr);
@@ -572,22 +580,23 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Token shifts for the folded path: log2(e) |M'_h x|^2 / 2 + log2(m) / 2 of
-// every query row (qshift[bh][t]) and every key row as seen by query head h
-// (kshift[bh][t] = minus that, or -inf for a masked key).  They replace the
-// projections in the key-side kernel (once per feature slice) and in the query
-// side.  Workgroup: 4 waves over 256 rows (fp32: 128) of q (first half of the
-// grid) or of k (second half); wave w keeps its two 32-row blocks (fp32: one)
-// in registers while M' streams through LDS one 32-row slice at a time
-// (double-buffered, the next slice fetched during the products), so that every
-// slice fragment read from LDS feeds two products.
+// Key shifts for the folded path: kshift[bh][t] = -(log2(e) |M'_h k_t|^2 / 2 +
+// log2(m) / 2) of every key row as seen by query head h, or -inf for a masked
+// key.  They replace the projection in the key-side kernel (once per feature
+// slice) and in the causal query side.  (Queries need no such shift: a factor
+// per query row cancels in N / D.)  Workgroup: 4 waves over 256 key rows
+// (fp32: 128); wave w keeps its two 32-row blocks (fp32: one) in registers
+// while M' streams through LDS one 32-row slice at a time (double-buffered,
+// the next slice fetched during the products), so that every slice fragment
+// read from LDS feeds two products.  The query heads that share a K/V head
+// take consecutive workgroups (one L2).
 // ---------------------------------------------------------------------------
 // 32-row blocks per wave (fp32: one, for registers) and rows per workgroup
 template <typename T> constexpr int shift_rb() { return sizeof(T) == 2 ? 2 : 1; }
 template <typename T> constexpr int shift_tile() { return shift_rb<T>() * kTile; }
 template <typename T, int DH, int R16>
 __global__ __launch_bounds__(kThreads, 2) void shift_kernel(FwdArgs a, const T* __restrict__ mfrag,
-                                                          float* __restrict__ qshift, float* __restrict__ kshift) {
+                                                          float* __restrict__ kshift) {
   typedef typename FragOf<T>::type F;
   constexpr int KD = DH / 16;
   constexpr int NM = kParts<T>;
@@ -599,17 +608,13 @@ __global__ __launch_bounds__(kThreads, 2) void shift_kernel(FwdArgs a, const T* 
   __shared__ __attribute__((aligned(16))) T s_m[2][SL * 64 * 8];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
   const int ntile = (a.L + kShiftTile - 1) / kShiftTile;
-  const int lb = xcd_block();
-  const int half = lb / (int)(gridDim.x / 2);   // 0: queries, 1: keys
-  const int blk = lb % (int)(gridDim.x / 2);
-  // keys: the heads that share a K/V head take consecutive blocks (one L2)
-  const int tile = half == 0 ? blk % ntile : (blk / a.H) % ntile;
-  const int bh = half == 0 ? blk / ntile : (blk / (a.H * ntile)) * a.H + blk % a.H;
+  const int blk = xcd_block();
+  const int tile = (blk / a.H) % ntile;
+  const int bh = (blk / (a.H * ntile)) * a.H + blk % a.H;
   const int b = bh / a.H, h = bh % a.H;
   const int hk = (h * a.H_kv) / a.H;
-  const T* base = half == 0 ? reinterpret_cast<const T*>(a.q) + b * a.qs[0] + h * a.qs[1]
-                            : reinterpret_cast<const T*>(a.k) + b * a.ks[0] + hk * a.ks[1];
-  const int64_t stride = half == 0 ? a.qs[2] : a.ks[2];
+  const T* base = reinterpret_cast<const T*>(a.k) + b * a.ks[0] + hk * a.ks[1];
+  const int64_t stride = a.ks[2];
   const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * R32 * SL * 64 * 8;
   const int t0 = tile * kShiftTile + RB * 32 * w + c;   // row of block 0 of this lane
   F stage[PS];
@@ -664,12 +669,8 @@ __global__ __launch_bounds__(kThreads, 2) void shift_kernel(FwdArgs a, const T* 
     const float sh = 0.5f * kLog2e * sq + hl;
     const int t = t0 + 32 * j;
     if (g == 0 && t < a.L) {
-      if (half == 0) {
-        qshift[(long)bh * a.L + t] = sh;
-      } else {
-        const bool valid = a.mask == nullptr || a.mask[(long)b * a.L + t] != 0;
-        kshift[(long)bh * a.L + t] = valid ? -sh : -INFINITY;
-      }
+      const bool valid = a.mask == nullptr || a.mask[(long)b * a.L + t] != 0;
+      kshift[(long)bh * a.L + t] = valid ? -sh : -INFINITY;
     }
   }
 }
@@ -812,8 +813,8 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
   const T* vbase = reinterpret_cast<const T*>(a.v) + b * a.vs[0] + hk * a.vs[1];
   const uint8_t* mrow = a.mask ? a.mask + (long)b * a.L : nullptr;
   const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * ((R16 + 1) / 2) * KD * NM * 64 * 8;
-  // omega' (shared), or W' of this head's geometry when folded
-  const T* of = ofrag + (FOLD ? (long)(a.m_per_head ? h : 0) * pl.FB * UK * NM * 64 * 8 : 0);
+  // omega' of this head's projection (or the shared one), or W' of its folded operand
+  const T* of = ofrag + (long)((FOLD ? pl.HW : pl.HO) > 1 ? h : 0) * pl.FB * UK * NM * 64 * 8;
   const float half_log2m = 0.5f * log2f((float)a.m);
   const int t_begin = unit * pl.span1;
   const int t_end = min(a.L, t_begin + pl.span1);
@@ -1034,6 +1035,7 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
   const T* vbase = reinterpret_cast<const T*>(a.v) + b * a.vs[0] + hk * a.vs[1];
   const uint8_t* mrow = a.mask ? a.mask + (long)b * a.L : nullptr;
   const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * R32 * KD * NM * 64 * 8;
+  const T* of = ofrag + (long)(pl.HO > 1 ? h : 0) * pl.FB * R16 * NM * 64 * 8;   // this head's omega'
   const float half_log2m = 0.5f * log2f((float)a.m);
   const int t_begin = unit * pl.span1;
   const int t_end = min(a.L, t_begin + pl.span1);
@@ -1098,8 +1100,8 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
       F ohi[R16], olo[R16];
 #pragma unroll
       for (int k = 0; k < R16; ++k) {
-        ohi[k] = ld8(ofrag + (((long)(fbc * R16 + k) * NM) * 64 + lane) * 8);
-        olo[k] = ld8(ofrag + (((long)(fbc * R16 + k) * NM + NM - 1) * 64 + lane) * 8);
+        ohi[k] = ld8(of + (((long)(fbc * R16 + k) * NM) * 64 + lane) * 8);
+        olo[k] = ld8(of + (((long)(fbc * R16 + k) * NM + NM - 1) * 64 + lane) * 8);
       }
       f32x16 e = ini;
       if constexpr (PAD)
@@ -1368,7 +1370,7 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   T* obase = reinterpret_cast<T*>(a.out) + b * a.os[0] + h * a.os[1];
   const uint8_t* mrow = a.mask ? a.mask + (long)b * a.L : nullptr;
   const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * ((R16 + 1) / 2) * KD * NM * 64 * 8;
-  const T* of = ofrag + (FOLD ? (long)(a.m_per_head ? h : 0) * pl.FB * UK * NM * 64 * 8 : 0);
+  const T* of = ofrag + (long)((FOLD ? pl.HW : pl.HO) > 1 ? h : 0) * pl.FB * UK * NM * 64 * 8;
   const float half_log2m = 0.5f * log2f((float)a.m);
   const int t0 = tile * TT;
   const long FK = 2L * pl.FB;
@@ -1401,7 +1403,10 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
 
   // ---- exponent operands of this wave's query (and key) blocks: u = M' x as
   // hi/lo fragments, or (folded) the token rows x themselves.  Rows and the
-  // V tile are requested first, the projections run once they are in. ----
+  // V tile are requested first, the projections run once they are in.  The
+  // queries need no |u|^2 / 2: any factor per query row cancels in N / D, and
+  // the exponent of query t is shifted by shq, its largest exponent over the
+  // first 32 features (set before the first feature step). ----
   F uqh[NQB][UK], uql[NQB][FOLD ? 1 : UK];
   float shq[NQB];
   F ukh[CAUSAL ? NQB : 1][UK], ukl[CAUSAL ? NQB : 1][FOLD ? 1 : UK];
@@ -1429,14 +1434,10 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   for (int j = 0; j < NQB; ++j) {
     const int t = t0 + 32 * (w * NQB + j) + c;
     const bool ok = t < a.L;
-    if (FOLD && pl.kshift) {   // shifts precomputed
-      shq[j] = ok ? a.qshift[(long)bh * a.L + t] : 0.f;
-    } else if constexpr (FOLD) {
-      shq[j] = project_shift<T, DH, R16>(*reinterpret_cast<F(*)[KD]>(uqh[j]), msrc, lane, half_log2m);
-    } else {
-      shq[j] = project_block<T, DH, R16>(*reinterpret_cast<F(*)[R16]>(uqh[j]), *reinterpret_cast<F(*)[R16]>(uql[j]),
-                                         xq[FOLD ? 0 : j], msrc, lane, half_log2m);
-    }
+    shq[j] = 0.f;
+    if constexpr (!FOLD)
+      (void)project_block<T, DH, R16>(*reinterpret_cast<F(*)[R16]>(uqh[j]), *reinterpret_cast<F(*)[R16]>(uql[j]),
+                                      xq[FOLD ? 0 : j], msrc, lane, half_log2m);
     if constexpr (CAUSAL) {
       float sh = 0.f;
       if (FOLD && pl.kshift) {
@@ -1504,6 +1505,30 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
     return *reinterpret_cast<const float4*>(zb + 8 * jj + 4 * g);
   };
 
+  // shq[j]: the largest exponent of query block j's rows over the first 32
+  // features (lanes c and c + 32 hold the two halves of query c's features);
+  // the first block always holds at least 16 real features
+  auto set_query_shift = [&](int buf) {
+    auto oload = [&](int k, int part) -> F { return op(0, buf, k * NM + (part ? NM - 1 : 0)); };
+#pragma unroll
+    for (int j = 0; j < NQB; ++j) {
+      f32x16 e = zero16();
+      if constexpr (PAD) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (crow(i, g) >= a.m) e[i] = -INFINITY;
+      }
+      if constexpr (FOLD)
+        e = exponent_stream<T, UK, false, false>([&](int k, int) -> F { return uqh[j][k]; }, oload, e);
+      else
+        e = exponent_stream<T, UK, false, true>(
+            [&](int k, int part) -> F { return part ? uql[j][k] : uqh[j][k]; }, oload, e);
+      float mx = e[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, e[i]);
+      shq[j] = fmaxf(mx, __shfl_xor(mx, 32));
+    }
+  };
   // one 32-feature step; the operands of the next step are fetched before it runs
   auto step = [&](int fb, int buf) {
     auto oload = [&](int k, int part) -> F { return op(fb, buf, k * NM + (part ? NM - 1 : 0)); };
@@ -1595,11 +1620,13 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   if constexpr (ALL) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed
     __syncthreads();                      // and everyone else's
+    set_query_shift(0);
     for (int fb = 0; fb < pl.FB; ++fb) step(fb, 0);
   } else {
     load_step(0);
     store_step(0);
     __syncthreads();
+    set_query_shift(0);
     for (int fb = 0; fb < pl.FB; ++fb) {
       const int buf = OPB == 2 ? (fb & 1) : 0;
       if constexpr (EARLY)
@@ -1690,7 +1717,6 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
   char* base = reinterpret_cast<char*>(ws);
   FwdArgs a = a_in;
   a.kshift = pl.kshift ? reinterpret_cast<float*>(base + pl.off_kshift) : nullptr;
-  a.qshift = pl.kshift ? a.kshift + (long)pl.BH * a.L : nullptr;
   T* mfrag = reinterpret_cast<T*>(base + pl.off_mfrag);
   T* ofrag = reinterpret_cast<T*>(base + pl.off_ofrag);
   T* sdelta = reinterpret_cast<T*>(base + pl.off_sdelta);
@@ -1707,15 +1733,16 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
     KernelTimer tm(kPrep, stream);
     if (fmode == 2) {
       if constexpr (sizeof(T) == 2 && DH >= 32) {
-        const int nW = pl.HM * pl.FB * ((DH / 32 + 3) / 4);
+        const int nW = pl.HW * pl.FB * ((DH / 32 + 3) / 4);
         hipLaunchKernelGGL(fold_kernel<T>, dim3(nW + (int)((nM + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
-                           a.M, a.omega, ofrag, mfrag, pl.HM, R16, a.r, DH, a.m, pl.FB, s, kLog2e * s);
+                           a.M, a.omega, ofrag, mfrag, pl.HM, pl.HO, pl.HW, R16, a.r, DH, a.m, pl.FB, s,
+                           kLog2e * s);
       }
     } else {
-      const long n = nM + (fmode ? (long)pl.HM * pl.FB * (DH / 16) * 64 : (long)pl.FB * R16 * NM * 64);
+      const long n = nM + (fmode ? (long)pl.HW * pl.FB * (DH / 16) * 64 : (long)pl.HO * pl.FB * R16 * NM * 64);
       const int blocks = (int)((n + 255) / 256);
-      hipLaunchKernelGGL(prep_kernel<T>, dim3(blocks), dim3(256), 0, st, a.M, a.omega, mfrag, ofrag, pl.HM, a.r, DH,
-                         a.m, R16, pl.FB, s, fmode);
+      hipLaunchKernelGGL(prep_kernel<T>, dim3(blocks), dim3(256), 0, st, a.M, a.omega, mfrag, ofrag, pl.HM, pl.HO,
+                         pl.HW, a.r, DH, a.m, R16, pl.FB, s, fmode);
     }
   }
   if (pl.mode == kPlanCross) {   // the caller's summary as the query side's operands
@@ -1726,8 +1753,8 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
   if (pl.kshift) {
     const int ntile = (a.L + shift_tile<T>() - 1) / shift_tile<T>();
     KernelTimer tm(kShift, stream);
-    hipLaunchKernelGGL((shift_kernel<T, DH, R16>), dim3(2 * pl.BH * ntile), dim3(kThreads), 0, st, a, mfrag,
-                       a.qshift, a.kshift);
+    hipLaunchKernelGGL((shift_kernel<T, DH, R16>), dim3(pl.BH * ntile), dim3(kThreads), 0, st, a, mfrag,
+                       a.kshift);
   }
   if (pl.mode != kPlanCross) {
     KernelTimer tm(kKState, stream);

@@ -136,7 +136,8 @@ def explicit_attention(q, k, v, M, om, mask=None, causal=False):
         for h in range(H):
             g = (h * H_kv) // H
             M_h = M[h] if M.ndim == 3 else M
-            K = explicit_kernel_matrix(q[b, h], k[b, g], M_h, om)
+            om_h = om[h] if np.ndim(om) == 3 else om
+            K = explicit_kernel_matrix(q[b, h], k[b, g], M_h, om_h)
             if mask is not None:
                 K = K * (np.asarray(mask[b]) != 0)[None, :]
             if causal:
@@ -503,7 +504,55 @@ def check_backward_linear_form(seed=82, eps=1e-5):
     assert np.all(grads["k"][[2, 8]] == 0) and np.all(grads["v"][[2, 8]] == 0)
 
 
+# ----------------------------------------------------------------------------
+# one projection per query head: every head against the explicit form with its
+# own omega, a shared omega replicated, the recurrence and the gradients
+# ----------------------------------------------------------------------------
+def check_per_head_projection(seed=91, eps=1e-5):
+    rng = np.random.default_rng(seed)
+    B, H, H_kv, L, d, m, r = 2, 4, 2, 19, 8, 16, 8
+    q, k, v, M, _ = _random_case(rng, B=B, H=H, H_kv=H_kv, Lq=L, d=d, m=m, r=r)
+    om = rng.standard_normal((H, m, r))
+    mask = (rng.random((B, L)) < 0.7).astype(np.uint8)
+    mask[:, 0] = 1
+    for causal in (False, True):
+        _close(po.attention(q, k, v, M, om, mask=mask, causal=causal),
+               explicit_attention(q, k, v, M, om, mask=mask, causal=causal), 1e-12,
+               f"per-head omega vs explicit (causal={causal})")
+    # a shared omega equals the same omega given to every head
+    _close(po.attention(q, k, v, M, om[1], mask=mask, causal=True),
+           po.attention(q, k, v, M, np.stack([om[1]] * H), mask=mask, causal=True), 1e-13,
+           "shared omega == replicated")
+    # the recurrence with per-head projections
+    P = 11
+    full, S_full, z_full = po.attention(q, k, v, M, om, causal=True, return_state=True)
+    _, S, z = po.attention(q[:, :, :P], k[:, :, :P], v[:, :, :P], M, om, causal=True, return_state=True)
+    outs = []
+    for t in range(P, L):
+        o, S, z = po.decode_step(S, z, q[:, :, t], k[:, :, t], v[:, :, t], M, om)
+        outs.append(o)
+    _close(np.stack(outs, axis=2), full[:, :, P:], 1e-12, "per-head decode vs causal")
+    _close(S, S_full, 1e-12, "per-head decode final S")
+    # gradients: central finite differences of the forward
+    qs, ks = 0.7 * q[:, :2, :9, :4], 0.7 * k[:, :1, :9, :4]
+    vs, Ms, oms = v[:, :1, :9, :4], M[:2, :3, :4], om[:2, :8, :3]
+    dout = rng.standard_normal(qs.shape)
+    grads = dict(zip("qkvM", po.attention_backward(qs, ks, vs, Ms, oms, dout, causal=True)))
+    base = dict(q=qs, k=ks, v=vs, M=Ms)
+
+    def f(**over):
+        a = dict(base, **over)
+        return float(np.sum(dout * po.attention(a["q"], a["k"], a["v"], a["M"], oms, causal=True)))
+
+    for name, x in base.items():
+        dirn = rng.standard_normal(x.shape)
+        fd = (f(**{name: x + eps * dirn}) - f(**{name: x - eps * dirn})) / (2 * eps)
+        an = float(np.sum(grads[name] * dirn))
+        assert abs(an - fd) <= 1e-6 * max(1.0, abs(fd)), f"per-head d{name}: {an:.9e} vs {fd:.9e}"
+
+
 ALL_CHECKS = [
+    check_per_head_projection,
     check_backward_finite_differences,
     check_backward_linear_form,
     check_closed_form_features,

@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 27, names
     L = bd.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -200,6 +200,56 @@ def test_proj_tag():
     others = {bd.dark_prf_proj_tag(6, 256, 64, True), bd.dark_prf_proj_tag(5, 512, 64, True),
               bd.dark_prf_proj_tag(5, 256, 32, True), bd.dark_prf_proj_tag(5, 256, 64, False)}
     assert a not in others and len(others) == 4
+
+
+@pytest.mark.parametrize("seed,H,m,r,orth", [(1002, 8, 256, 64, True), (9, 3, 48, 16, False)])
+def test_library_per_head_omega_matches_oracle(seed, H, m, r, orth):
+    lib_om = bd.dark_prf_omega_per_head(seed, H, m, r, orth)
+    ref = oo.omega_per_head(seed, H, m, r, orth)
+    assert lib_om.shape == ref.shape == (H, m, r)
+    ulp = np.spacing(np.abs(ref).astype(np.float32))
+    assert np.mean(lib_om == ref) >= 0.999
+    assert np.all(np.abs(lib_om - ref) <= ulp)
+    for h in range(H):
+        assert bd.dark_prf_head_seed(seed, h) == oo.head_seed(seed, h)
+
+
+def test_per_head_tag_differs_from_shared_and_other_head_counts():
+    shared = bd.dark_prf_proj_tag(5, 256, 64, True)
+    t8 = bd.dark_prf_proj_tag_per_head(5, 8, 256, 64, True)
+    assert t8 == bd.dark_prf_proj_tag_per_head(5, 8, 256, 64, True)
+    assert len({shared, t8, bd.dark_prf_proj_tag_per_head(5, 4, 256, 64, True),
+                bd.dark_prf_proj_tag_per_head(6, 8, 256, 64, True)}) == 4
+    assert bd.lib().dark_prf_omega_per_head(1, 0, 16, 16, 1, None) == bd.DARK_ERR_INVALID_ARG
+
+
+def test_per_head_omega_flag_is_validated_and_sizes_the_workspace():
+    d = _desc(omega_per_head=2)
+    assert bd.dark_prf_workspace_bytes(d) == 0
+    shared = bd.dark_prf_workspace_bytes(_desc(m_per_head=0, r=16))          # unfolded: omega' once
+    per_head = bd.dark_prf_workspace_bytes(_desc(m_per_head=0, r=16, omega_per_head=1))
+    assert per_head > shared
+
+
+def test_auto_mode_choice():
+    # exact attention through the threshold (inclusive), linear beyond it
+    for L, thr, want in ((256, 256, 1), (257, 256, 0), (1, 0, 0), (2048, 4096, 1), (2048, 1024, 0)):
+        d = _desc(L=L)
+        assert bd.dark_prf_auto_mode(d, thr) == want, (L, thr)
+        ws = bd.dark_prf_exact_workspace_bytes(d) if want else bd.dark_prf_workspace_bytes(d)
+        assert bd.dark_prf_auto_workspace_bytes(d, thr) == ws
+    assert bd.dark_prf_auto_mode(_desc(), -1) == -1
+    assert bd.dark_prf_auto_mode(_desc(d_h=48), 100) == -1
+    assert bd.dark_prf_auto_workspace_bytes(_desc(), -1) == 0
+    d = _desc(L=300)
+    call = lambda thr, q=FAKE, ws=FAKE, n=None: bd.dark_prf_auto_fwd(  # noqa: E731
+        d, thr, q, FAKE, FAKE, FAKE, FAKE, 0, FAKE, ws, bd.dark_prf_auto_workspace_bytes(d, thr) if n is None else n, 0)
+    assert call(-5) == bd.DARK_ERR_INVALID_ARG
+    # argument errors of either path come back before anything is queued
+    assert call(1000, q=0) == bd.DARK_ERR_INVALID_ARG          # exact path
+    assert call(10, q=0) == bd.DARK_ERR_INVALID_ARG            # linear path
+    assert call(1000, n=bd.dark_prf_exact_workspace_bytes(d) - 1) == bd.DARK_ERR_WORKSPACE
+    assert call(10, n=bd.dark_prf_workspace_bytes(d) - 1) == bd.DARK_ERR_WORKSPACE
 
 
 def test_omega_argument_checks():

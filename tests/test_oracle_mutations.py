@@ -151,6 +151,8 @@ MUTATIONS = {
     "bwd_dPK_untransposed": ("attention_backward", _bwd(dpk_untransposed=True)),
     "bwd_dM_unscaled": ("attention_backward", _bwd(dM_scale=False)),
     "bwd_gqa_overwrite": ("attention_backward", _bwd(gqa_overwrite=True)),
+    "per_head_omega_ignored": ("head_omega", lambda omega, h: np.asarray(omega)[0] if np.ndim(omega) == 3
+                               else np.asarray(omega)),
 }
 
 QUICK = pins.ALL_CHECKS + [pins.check_mc_kernel]

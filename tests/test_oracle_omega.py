@@ -87,3 +87,28 @@ def test_determinism_and_seed_sensitivity():
         assert a.dtype == np.float32
         assert np.array_equal(a, b)
         assert not np.array_equal(a, c)
+
+
+def test_head_seed_is_the_splitmix64_finaliser():
+    # output 0 of the stream of seed s is the finaliser applied to s + gamma, so the
+    # finaliser of x is output 0 of the stream of x - gamma: head_seed uses the
+    # same known-answer-pinned finaliser on seed + (h + 1) * 0xD1B54A32D192ED03
+    gamma, c = 0x9E3779B97F4A7C15, 0xD1B54A32D192ED03
+    for seed in (0, 1, 1004, (1 << 64) - 1):
+        for h in range(5):
+            x = (seed + (h + 1) * c) & ((1 << 64) - 1)
+            assert oo.head_seed(seed, h) == int(oo.splitmix64((x - gamma) & ((1 << 64) - 1), 0, 1)[0])
+
+
+def test_omega_per_head_draws_each_head_from_its_seed():
+    om = oo.omega_per_head(1004, 3, 96, 32, True)
+    assert om.shape == (3, 96, 32) and om.dtype == np.float32
+    for h in range(3):
+        assert np.array_equal(om[h], oo.omega(oo.head_seed(1004, h), 96, 32, True))
+    # distinct heads, each orthogonal within its blocks
+    assert not np.allclose(om[0], om[1])
+    for h in range(3):
+        blk = om[h][:32].astype(np.float64)
+        g = blk @ blk.T
+        off = g - np.diag(np.diag(g))
+        assert np.max(np.abs(off)) < 1e-4 * np.max(np.diag(g))

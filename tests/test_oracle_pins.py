@@ -60,3 +60,7 @@ def test_backward_finite_differences():
 
 def test_backward_linear_form():
     pins.check_backward_linear_form()
+
+
+def test_per_head_projection():
+    pins.check_per_head_projection()
