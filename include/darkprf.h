@@ -376,10 +376,10 @@ dark_status dark_prf_projection_fix(dark_prf_projection* p, int32_t fixed);
  * dark_prf_bwd_workspace_bytes - device workspace dark_prf_bwd needs for
  * desc; 0 for an invalid descriptor, and 0 for B = 0 (dark_prf_bwd then
  * only zeroes dM and takes no workspace).  It holds the fp32 features, the
- * per-chunk states and the intermediate gradients: about
- * 4*B*H*Lp*(4*m + 4*r + 6*d_h + 135) + 8*B*H*(Lp/64)*m*(d_h+1) bytes, with Lp
- * the sequence length rounded up to a multiple of 64, plus at most
- * 4*B*H*r*d_h*(Lp/64) bytes of partial sums of dM.
+ * per-chunk states and the intermediate gradients, and grows linearly in
+ * B*H*L (with the chunk length C = 64, or 128 for causal calls with
+ * d_h >= 128, and L rounded up to a multiple of C); size the workspace with
+ * this call rather than from a formula.
  *
  * dark_prf_bwd - arguments as for dark_prf_fwd, plus:
  *   dout  [B][H][L][d_h] (strides o_str), dtype

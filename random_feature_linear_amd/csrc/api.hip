@@ -111,6 +111,7 @@ static void make_plan(const dark_prf_desc& d, Plan& p, int mode = kPlanForward) 
   p.BH = d.B * d.H;
   p.elem = d.dtype == DARK_BF16 ? 2 : 4;
   p.FBW = feature_blocks_per_wave(d.d_h);
+  int units_ws = 0;   // units the workspace is sized for (>= NU; grows with L, so the workspace never shrinks)
   p.NF = cdiv(p.FB, 4 * p.FBW);
   const int L = d.L > 0 ? d.L : 1;
   const int tile1 = 128;                 // key-side tile: 4 waves x 32 tokens
@@ -122,18 +123,20 @@ static void make_plan(const dark_prf_desc& d, Plan& p, int mode = kPlanForward) 
     p.span1 = p.tile2;
     p.NU = cdiv(L, p.span1);
     p.NT2 = p.NU;
+    units_ws = p.NU;
   } else {
     // two query blocks per wave (d_h <= 64) when that still leaves at least
     // two workgroups per compute unit
     p.NQB = (d.d_h <= 64 && (long)p.BH * cdiv(L, 256) >= 512) ? 2 : 1;
     p.tile2 = 128 * p.NQB;
     p.NT2 = cdiv(L, p.tile2);
-    int splits = cdiv(512, (long)p.BH * p.NF);
+    int splits = cdiv(512, (long)(p.BH > 0 ? p.BH : 1) * p.NF);   // B = 0 plans as B = 1
     splits = splits < 1 ? 1 : splits;
     const int max_splits = cdiv(L, tile1);
     if (splits > max_splits) splits = max_splits;
     p.span1 = cdiv(cdiv(L, splits), tile1) * tile1;
     p.NU = cdiv(L, p.span1);
+    units_ws = splits;   // NU <= splits, and splits never decreases as L grows
   }
   // operand copies of M' and omega' (bf16: hi and lo parts; see prf_kernels.h)
   const int NM = d.dtype == DARK_BF16 ? 2 : 1;
@@ -142,6 +145,7 @@ static void make_plan(const dark_prf_desc& d, Plan& p, int mode = kPlanForward) 
   const size_t frag = 64 * 8;            // elements per operand fragment
   const size_t state_frags = (size_t)DB * 2 * p.FB;   // fragments of one unit state S
   const int nout = d.causal ? p.NU : 1;
+  const int units = units_ws > p.NU ? units_ws : p.NU;
   size_t off = 0;
   p.off_mfrag = off;
   off = align256(off + (size_t)p.HM * R32 * (d.d_h / 16) * NM * frag * p.elem);
@@ -151,12 +155,15 @@ static void make_plan(const dark_prf_desc& d, Plan& p, int mode = kPlanForward) 
   else          // omega' fragments per projection, K-steps over the rank
     off = align256(off + (size_t)p.HO * p.FB * p.R16 * NM * frag * p.elem);
   p.off_sdelta = off;
-  off = align256(off + (size_t)p.BH * p.NU * state_frags * frag * p.elem);
+  off = align256(off + (size_t)p.BH * units * state_frags * frag * p.elem);
+  // the per-unit states stay in L2 between the key side and the sum (same XCD)
+  // unless they are larger than about half of the 8 x 4 MB of L2
+  p.stream_states = (size_t)p.BH * p.NU * state_frags * frag * p.elem > ((size_t)16 << 20);
   p.off_sfrag = off;
   off = align256(off + (size_t)p.BH * nout * state_frags * frag * p.elem);
   // normaliser states z (fp32, 32 FB per unit): per unit, then combined
   p.off_zdelta = off;
-  off = align256(off + (size_t)p.BH * p.NU * p.FB * 32 * sizeof(float));
+  off = align256(off + (size_t)p.BH * units * p.FB * 32 * sizeof(float));
   p.off_zsum = off;
   off = align256(off + (size_t)p.BH * nout * p.FB * 32 * sizeof(float));
   // keys are projected once up front (for |u|^2) when several feature slices,

@@ -62,6 +62,7 @@ struct Plan {
   // workspace (bytes from the base pointer)
   size_t off_mfrag, off_ofrag, off_sdelta, off_sfrag, off_zdelta, off_zsum, off_kshift, total;
   int elem;    // bytes per element of q/k/v (2 or 4)
+  int stream_states;   // per-unit states too large for L2: accessed non-temporally
 };
 
 // Workspace of the exact-attention path: the M' fragments, the projected rows
@@ -90,12 +91,21 @@ inline ExactLayout exact_layout(int B, int H, int L, int d_h, int R16, int HM, i
   off += (size_t)2 * B * H * e.NBLK * R16 * NM * frag * elem;
   off = (off + 255) & ~(size_t)255;
   const int NT = (L + 127) / 128;
-  e.KS = ((long)B * H * NT < 512 && NT > 4) ? kExactKS : 0;
-  e.splits_per_head = 0;
-  if (e.KS > 0)
-    for (int t = 0; t < NT; ++t) e.splits_per_head += causal ? t / e.KS + 1 : (NT + e.KS - 1) / e.KS;
+  const long BH = (long)B * H;
+  e.KS = (BH * NT < 512 && NT > 4) ? kExactKS : 0;
+  auto runs = [&](int nt) {   // runs of kExactKS key tiles over all query tiles of one (b, h)
+    int n = 0;
+    for (int t = 0; t < nt; ++t) n += causal ? t / kExactKS + 1 : (nt + kExactKS - 1) / kExactKS;
+    return n;
+  };
+  e.splits_per_head = e.KS > 0 ? runs(NT) : 0;
+  // partials reserved for the longest split plan up to this length (equal to the
+  // plan's own when it splits), so that the workspace never shrinks as L grows
+  const long nt_split = BH > 0 ? (511 / BH < NT ? 511 / BH : NT) : 0;
+  const int reserve = nt_split > 4 ? runs((int)nt_split) : 0;
   e.off_part = off;
-  off += (size_t)B * H * e.splits_per_head * (128 * d_h + 2 * 128) * sizeof(float);
+  off += (size_t)BH * (reserve > e.splits_per_head ? reserve : e.splits_per_head) * (128 * d_h + 2 * 128) *
+         sizeof(float);
   e.total = (off + 255) & ~(size_t)255;
   return e;
 }

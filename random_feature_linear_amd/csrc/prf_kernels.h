@@ -172,6 +172,19 @@ __device__ __forceinline__ void st8(float* p, const f32x8& f) {
   *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
 }
+// The per-unit states between the key side and the sum: streamed past the
+// caches (non-temporal) when they are too large to stay in L2, else ordinary
+// accesses, so that the sum, which runs on the XCD that wrote them, finds them
+// in its L2.
+template <typename F, typename T> __device__ __forceinline__ F ld8_state(const T* p, int stream) {
+  return stream ? ld8_stream(p) : ld8(p);
+}
+template <typename T, typename F> __device__ __forceinline__ void st8_state(T* p, const F& f, int stream) {
+  if (stream)
+    st8_stream(p, f);
+  else
+    st8(p, f);
+}
 // One 16-byte element per lane from global memory straight into LDS (the
 // global_load_lds path, no registers): lane l writes bytes [16 l, 16 l + 16) of
 // the 1 KB at lds_dst, which must be the same for the whole wave.  Counted by
@@ -988,7 +1001,8 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int k = 0; k < 2; ++k) st8_stream(sd + ((db * FK + 2 * fb + k) * 64 + lane) * 8, acc_frag<F>(acc[f][db], k));
+      for (int k = 0; k < 2; ++k)
+        st8_state(sd + ((db * FK + 2 * fb + k) * 64 + lane) * 8, acc_frag<F>(acc[f][db], k), pl.stream_states);
     if constexpr (ZMMA) {   // column d_h: lane d_h % 32 of each half holds rows crow(i, g)
       if (c == DH % 32) {
 #pragma unroll
@@ -1129,7 +1143,8 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int k = 0; k < 2; ++k) st8_stream(sd + ((db * FK + 2 * fb + k) * 64 + lane) * 8, acc_frag<F>(acc[f][db], k));
+      for (int k = 0; k < 2; ++k)
+        st8_state(sd + ((db * FK + 2 * fb + k) * 64 + lane) * 8, acc_frag<F>(acc[f][db], k), pl.stream_states);
     if (c == DH % 32) {   // column d_h: lane d_h % 32 of each half holds rows crow(i, g)
 #pragma unroll
       for (int i = 0; i < 16; ++i) zd[fb * 32 + crow(i, g)] = acc[f][DBK - 1][i];
@@ -1157,7 +1172,16 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
   const long nZ = (long)pl.BH * z_unit;
   const int nout = a.causal ? pl.NU : 1;
   constexpr int UB = 16;                       // units whose loads are in flight together
-  for (long idx = blockIdx.x * (long)blockDim.x + threadIdx.x; idx < nS + nZ; idx += (long)gridDim.x * blockDim.x) {
+  // Work items in (b, h)-major order, S lanes then z values of each (b, h), and
+  // blocks taken in XCD order: the (b, h) ranges that one XCD sums are the ones
+  // its key side wrote and its query side reads (one L2).
+  (void)nS;
+  (void)nZ;
+  const long per_bh = per_unit + z_unit;
+  const long idx_all = (long)xcd_block() * blockDim.x + threadIdx.x;
+  if (idx_all < (long)pl.BH * per_bh) {
+    const long bh_i = idx_all / per_bh, r_i = idx_all % per_bh;
+    const long idx = r_i < per_unit ? bh_i * per_unit + r_i : nS + bh_i * z_unit + (r_i - per_unit);
     if (idx >= nS) {   // z: one feature per thread
       const long zi = idx - nS;
       const long bh = zi / z_unit, j = zi % z_unit;
@@ -1178,7 +1202,7 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
       }
       if (!a.causal) dst[0] = run;
       if (a.z_out && j < a.m) a.z_out[bh * a.m + j] = run;
-      continue;
+      return;
     }
     const long bh = idx / per_unit;
     const long rem = idx % per_unit;
@@ -1189,7 +1213,7 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
     for (; u + UB <= pl.NU; u += UB) {
       F x[UB];
 #pragma unroll
-      for (int q = 0; q < UB; ++q) x[q] = ld8_stream(src + (long)(u + q) * per_unit * 8);
+      for (int q = 0; q < UB; ++q) x[q] = ld8_state<F>(src + (long)(u + q) * per_unit * 8, pl.stream_states);
 #pragma unroll
       for (int q = 0; q < UB; ++q) {
         if (a.causal) {
@@ -1204,7 +1228,7 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
     for (; u + 4 <= pl.NU; u += 4) {       // four loads in flight
       F x[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] = ld8_stream(src + (long)(u + q) * per_unit * 8);
+      for (int q = 0; q < 4; ++q) x[q] = ld8_state<F>(src + (long)(u + q) * per_unit * 8, pl.stream_states);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (a.causal) {
@@ -1217,7 +1241,7 @@ __global__ void scan_kernel(FwdArgs a, Plan pl, const T* __restrict__ sdelta, T*
       }
     }
     for (; u < pl.NU; ++u) {
-      const F x = ld8_stream(src + (long)u * per_unit * 8);
+      const F x = ld8_state<F>(src + (long)u * per_unit * 8, pl.stream_states);
       if (a.causal) {
         F o;
         make_frag(o, run);

@@ -213,3 +213,11 @@ def test_bwd_c4_batch_row():
     errs = [max(_err(sl(got[i])[0, j], ref[i][0, j], floor) for j in range(ref[i].shape[1])) for i in range(3)]
     say(f"[bwd] c4 batch row 0: dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
     assert max(errs) <= TOL[w.dtype], errs
+    # dM sums the batch: the device backward of batch row 0 alone against the oracle's
+    # (the same launch shape per row: r = d_h = 256, 128-token chunks, per-head M)
+    one = {n: sl(inp[n]) for n in ("q", "k", "v")}
+    one.update(M=inp["M"], mask=None if inp["mask"] is None else sl(inp["mask"]))
+    got1 = _run(w.with_(B=1), one, sl(dout))
+    e = normwise_rel_err(got1[3], ref[3])
+    say(f"[bwd] c4 batch row 0: dM {e:.2e}")
+    assert e <= TOL[w.dtype], e
