@@ -1,0 +1,541 @@
+"""A host-side model of the LDS schedules of the attention kernels.
+
+The query-side, key-side and shift kernels stage operands in LDS and hand
+data between the four waves of a workgroup across barriers: the ring of
+feature-step operand buffers (s_op) with the z values in the last slot of a
+step, the key-feature buffers (s_kf), the operands copied global -> LDS by the
+DMA path (all steps, and M' in the key-feature buffers), the V^T tile, and on
+the key side the double-buffered tile state.  This module replays, wave by
+wave and barrier phase by barrier phase, every LDS access these kernels make
+(the same index arithmetic, the same constexpr choices of buffering, derived
+here from the same formulas), and checks at byte granularity:
+
+  * every access lies inside its array;
+  * every byte read was written before and is visible to the reader: by the
+    same wave earlier in program order, or by any wave in an earlier barrier
+    phase (DMA copies count as written when the issuing wave waits for its
+    vector-memory counter);
+  * no byte written by one wave in a phase is read or written by another
+    wave in the same phase.
+
+A read of LDS that the launch never wrote would return whatever an earlier
+workgroup or launch left there; this is the failure that shows on a process's
+first launch and hides on later ones.  The model is checked against planted
+mistakes (a barrier removed, a buffer index changed) in test_lds_schedule.py.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+WAVES = 4
+LANES = np.arange(64)
+C = LANES & 31
+G = LANES >> 5
+MAX_LDS = 160 * 1024
+
+
+class Violation(AssertionError):
+    pass
+
+
+@dataclass
+class Tracker:
+    sizes: dict                                # array name -> bytes
+    mutate: set = field(default_factory=set)   # planted mistakes (tests of the model itself)
+
+    def __post_init__(self):
+        self.epoch = 0
+        self.w_epoch = {n: np.full(s, -1, np.int64) for n, s in self.sizes.items()}
+        self.w_wave = {n: np.full(s, -1, np.int64) for n, s in self.sizes.items()}
+        self.r_epoch = {n: np.full(s, -1, np.int64) for n, s in self.sizes.items()}
+        self.r_mask = {n: np.zeros(s, np.int64) for n, s in self.sizes.items()}
+        self.pending = {w: [] for w in range(WAVES)}   # DMA copies in flight per wave
+        self.total = sum(self.sizes.values())
+
+    def _bytes(self, name, starts, width):
+        idx = (np.asarray(starts, np.int64)[:, None] + np.arange(width)[None, :]).ravel()
+        if idx.size and (idx.min() < 0 or idx.max() >= self.sizes[name]):
+            raise Violation(f"{name}: access [{idx.min()}, {idx.max()}] outside [0, {self.sizes[name]})")
+        return np.unique(idx)
+
+    def write(self, wave, name, starts, width):
+        b = self._bytes(name, starts, width)
+        other_r = (self.r_epoch[name][b] == self.epoch) & ((self.r_mask[name][b] & ~(1 << wave)) != 0)
+        if other_r.any():
+            raise Violation(f"{name}: wave {wave} writes byte {b[other_r][0]} that another wave reads in phase "
+                            f"{self.epoch}")
+        other_w = (self.w_epoch[name][b] == self.epoch) & (self.w_wave[name][b] != wave) & (self.w_wave[name][b] >= 0)
+        if other_w.any():
+            raise Violation(f"{name}: waves {wave} and {self.w_wave[name][b][other_w][0]} write byte "
+                            f"{b[other_w][0]} in phase {self.epoch}")
+        self.w_epoch[name][b] = self.epoch
+        self.w_wave[name][b] = wave
+
+    def read(self, wave, name, starts, width):
+        b = self._bytes(name, starts, width)
+        we, ww = self.w_epoch[name][b], self.w_wave[name][b]
+        never = we < 0
+        if never.any():
+            raise Violation(f"{name}: wave {wave} reads byte {b[never][0]} that was never written (phase {self.epoch})")
+        same_phase_other = (ww != wave) & (we == self.epoch)
+        if same_phase_other.any():
+            raise Violation(f"{name}: wave {wave} reads byte {b[same_phase_other][0]} written by wave "
+                            f"{ww[same_phase_other][0]} in the same phase {self.epoch}")
+        fresh = self.r_epoch[name][b] != self.epoch
+        self.r_mask[name][b[fresh]] = 0
+        self.r_epoch[name][b] = self.epoch
+        self.r_mask[name][b] |= 1 << wave
+
+    def dma(self, wave, name, start):
+        """One global -> LDS copy by a wave: lane l fills bytes [16 l, 16 l + 16) of the 1 KB at start."""
+        self._bytes(name, [start], 1024)
+        self.pending[wave].append((name, start))
+
+    def waitcnt(self, wave):
+        """The wave waits for its vector-memory counter: its DMA copies have landed."""
+        for name, start in self.pending[wave]:
+            self.write(wave, name, [start], 1024)
+        self.pending[wave] = []
+
+
+def run_waves(tr: Tracker, programs):
+    """programs[w] is a generator yielding at each barrier; phases advance together."""
+    gens = [p for p in programs]
+    alive = [True] * WAVES
+    while any(alive):
+        hits = 0
+        for w in range(WAVES):
+            if not alive[w]:
+                continue
+            try:
+                next(gens[w])
+                hits += 1
+            except StopIteration:
+                alive[w] = False
+        if hits not in (0, WAVES) or (hits == 0 and any(alive)):
+            raise Violation("waves reach different numbers of barriers")
+        tr.epoch += 1
+
+
+# ---------------------------------------------------------------------------
+# shared definitions (the kernels' constants)
+# ---------------------------------------------------------------------------
+def fold_exponent(elem, d_h, r16):
+    return elem == 2 and 2 * d_h < 3 * 16 * r16
+
+
+def vblocks(dh):
+    return (dh + 31) // 32
+
+
+def vblocks_ones(dh):
+    return (dh + 1 + 31) // 32
+
+
+def vloads_per_thread(dh, tt):
+    return (tt * (dh // 8) + 256 - 1) // 256
+
+
+def vt_pos(t):
+    return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1)
+
+
+def frag_lanes(base_elem, elem):
+    """Byte starts of the 64 lanes of one 8-element operand fragment at element base_elem."""
+    return (base_elem + LANES * 8) * elem
+
+
+def store_vt(tr, w, name, base, dh, tt, vst, elem):
+    """store_vt: rows t0 .. t0 + TT - 1 of V into s_vt[d][vt_pos(t)] (every thread of wave w)."""
+    for p in range(vloads_per_thread(dh, tt)):
+        e = 64 * w + LANES + p * 256
+        ok = e < tt * (dh // 8)
+        e = e[ok]
+        tl, d8 = e % tt, (e // tt) * 8
+        pos = np.array([vt_pos(int(t)) for t in tl], np.int64)
+        for i in range(8):
+            tr.write(w, name, (base + (d8 + i) * vst + pos) * elem, elem)
+
+
+def v_frag_read(tr, w, name, base, dh, vst, db, tb0, k, elem, ones=False):
+    d = db * 32 + C
+    ok = ~(((ones or dh % 32 != 0)) & (d >= dh))
+    starts = (base + d[ok] * vst + tb0 + 16 * k + 8 * G[ok]) * elem
+    if starts.size:
+        tr.read(w, name, starts, 8 * elem)
+
+
+# ---------------------------------------------------------------------------
+# query side (qout_kernel)
+# ---------------------------------------------------------------------------
+@dataclass
+class QoutConfig:
+    elem: int          # 2 (bf16) or 4 (fp32)
+    dh: int
+    r16: int
+    nqb: int
+    causal: bool
+    allfb: int         # > 0: all steps staged by DMA (bf16, causal, FB <= allfb)
+    fb: int            # feature blocks of the call
+    m: int             # features (m <= 32 fb)
+    kshift: bool = False
+
+    def derived(self):
+        e, dh = self.elem, self.dh
+        kd, nm, db = dh // 16, (2 if e == 2 else 1), vblocks(dh)
+        nb = WAVES * self.nqb
+        tt = 32 * nb
+        vst = tt + 8
+        fold = fold_exponent(e, dh, self.r16)
+        uk = kd if fold else self.r16
+        nof = uk * nm
+        nstep = nof + 2 * db + 1
+        vt_elems = dh * vst if self.causal else 8
+        k_base = vt_elems * e
+        k_op = nstep * 512 * e
+        k_kf = nb * 2 * 512 * e if self.causal else 0
+        stage = k_base + k_op + k_kf <= MAX_LDS
+        opb = 0 if not stage else (2 if k_base + 2 * k_op + 2 * k_kf <= MAX_LDS else 1)
+        kbuf = 2 if k_base + opb * k_op + 2 * k_kf <= MAX_LDS else 1
+        kf_elems = kbuf * nb * 2 * 512 if self.causal else 8
+        all_ = self.allfb > 0
+        op_elems = self.allfb * nstep * 512 if all_ else (opb * nstep * 512 if stage else 8)
+        mfrg = ((self.r16 + 1) // 2) * kd * nm
+        m_lds = all_ and self.causal and mfrg * 512 <= kf_elems
+        return dict(kd=kd, nm=nm, db=db, nb=nb, tt=tt, vst=vst, fold=fold, uk=uk, nof=nof, nstep=nstep,
+                    zs=nstep - 1, zw=8 * e // 4, perw=(nstep + WAVES - 1) // WAVES, vt_elems=vt_elems,
+                    stage=stage, opb=opb, kbuf=kbuf, kf_elems=kf_elems, all=all_, op_elems=op_elems,
+                    mfrg=mfrg, m_lds=m_lds, r32=(self.r16 + 1) // 2)
+
+
+def qout_model(cfg: QoutConfig, mutate=frozenset()):
+    D = cfg.derived()
+    e = cfg.elem
+    sizes = {"s_vt": D["vt_elems"] * e, "s_kf": D["kf_elems"] * e, "s_op": D["op_elems"] * e}
+    if sum(sizes.values()) > MAX_LDS:
+        raise Violation(f"LDS {sum(sizes.values())} bytes > {MAX_LDS}")
+    tr = Tracker(sizes, set(mutate))
+    nstep, nm, uk, zs = D["nstep"], D["nm"], D["uk"], D["zs"]
+
+    def op_read(w, fb, buf, f):
+        if D["all"]:
+            tr.read(w, "s_op", frag_lanes((fb * nstep + f) * 512, e), 8 * e)
+        elif D["stage"]:
+            tr.read(w, "s_op", frag_lanes((buf * nstep + f) * 512, e), 8 * e)
+
+    def zrow4(w, fb, buf, jj):
+        if D["all"]:
+            zb = (fb * nstep + zs) * 512 * e
+        elif D["stage"]:
+            zb = (buf * nstep + zs) * 512 * e
+        else:
+            return
+        tr.read(w, "s_op", zb + (8 * jj + 4 * G) * 4, 16)
+
+    def exponent_reads(w, fb, buf):
+        for k in range(uk):
+            for part in (0, 1):
+                op_read(w, fb, buf, k * nm + (nm - 1 if part else 0))
+
+    def store_step(w, buf):
+        if D["stage"] and not D["all"]:
+            for q in range(D["perw"]):
+                f = w + WAVES * q
+                if f < nstep:
+                    tr.write(w, "s_op", frag_lanes((buf * nstep + f) * 512, e), 8 * e)
+
+    def wave(w):
+        # DMA staging of all steps and M'
+        if D["all"]:
+            for idx in range(w, cfg.fb * nstep, WAVES):
+                tr.dma(w, "s_op", idx * 512 * e)
+            if D["m_lds"]:
+                for idx in range(w, D["mfrg"], WAVES):
+                    tr.dma(w, "s_kf", idx * 512 * e)
+            if "no_wait_before_vt" not in tr.mutate:
+                tr.waitcnt(w)
+        if cfg.causal:
+            store_vt(tr, w, "s_vt", 0, cfg.dh, D["tt"], D["vst"], e)
+        if D["m_lds"]:
+            yield                                            # M' and every wave's copies visible
+        # projections (key shifts and unfolded u) read M' from LDS when staged there
+        if D["m_lds"]:
+            nproj = cfg.nqb * (0 if D["fold"] else 1) + (cfg.nqb if cfg.causal and not cfg.kshift else 0)
+            for _ in range(nproj):
+                for rb in range(D["r32"]):
+                    for kd in range(D["kd"]):
+                        for part in range(nm):
+                            tr.read(w, "s_kf", frag_lanes((((rb * D["kd"] + kd) * nm + part) * 64) * 8, e), 8 * e)
+        if D["all"]:
+            tr.waitcnt(w)
+            yield
+            exponent_reads(w, 0, 0)                          # the query shift from feature block 0
+            fbs = range(cfg.fb)
+        else:
+            store_step(w, 0)
+            yield
+            exponent_reads(w, 0, 0)
+            fbs = range(cfg.fb)
+        for fb in fbs:
+            buf = 0 if D["all"] else (fb & 1 if D["opb"] == 2 else 0)
+            # step(fb, buf)
+            if not D["fold"]:
+                for k in range(uk):
+                    op_read(w, fb, buf, k * nm)
+                    op_read(w, fb, buf, k * nm + nm - 1)
+            for _j in range(cfg.nqb):
+                if D["fold"]:
+                    exponent_reads(w, fb, buf)
+                for jj in range(4):
+                    zrow4(w, fb, buf, jj)
+            for db in range(D["db"]):
+                for k in range(2):
+                    op_read(w, fb, buf, D["nof"] + 2 * db + k)
+            if cfg.causal:
+                kb = (fb & 1 if D["kbuf"] == 2 else 0)
+                if "kbuf_index_fixed" in tr.mutate:
+                    kb = 0
+                kbase = kb * D["nb"] * 2 * 512
+                for j in range(cfg.nqb):
+                    if D["fold"]:
+                        exponent_reads(w, fb, buf)
+                    for k in range(2):
+                        tr.write(w, "s_kf", frag_lanes(kbase + ((w * cfg.nqb + j) * 2 + k) * 512, e), 8 * e)
+                if "no_kbuf_barrier" not in tr.mutate:
+                    yield
+                for j in range(cfg.nqb):
+                    gq = w * cfg.nqb + j
+                    for kb2 in range(D["nb"]):
+                        if kb2 <= gq:
+                            for k in range(2):
+                                tr.read(w, "s_kf", frag_lanes(kbase + (kb2 * 2 + k) * 512, e), 8 * e)
+                if D["kbuf"] == 1 and "no_kbuf1_barrier" not in tr.mutate:
+                    yield
+            if not D["all"] and D["stage"]:
+                if fb + 1 < cfg.fb:
+                    if D["opb"] == 1 and "no_opb1_barrier" not in tr.mutate:
+                        yield
+                    nbuf = (fb + 1) & 1 if D["opb"] == 2 else 0
+                    if "ring_same_buffer" in tr.mutate:
+                        nbuf = buf
+                    store_step(w, nbuf)
+                if "no_step_barrier" not in tr.mutate:
+                    yield
+        # epilogue: the intra-chunk products read the V^T tile
+        if cfg.causal:
+            for j in range(cfg.nqb):
+                gq = w * cfg.nqb + j
+                for kb2 in range(D["nb"]):
+                    if kb2 > gq:
+                        continue
+                    for k in range(2):
+                        for db in range(D["db"]):
+                            v_frag_read(tr, w, "s_vt", 0, cfg.dh, D["vst"], db, 32 * kb2, k, e)
+
+    run_waves(tr, [wave(w) for w in range(WAVES)])
+    return tr
+
+
+# ---------------------------------------------------------------------------
+# key side (kstate_kernel, the tiled form)
+# ---------------------------------------------------------------------------
+@dataclass
+class KstateConfig:
+    elem: int
+    dh: int
+    r16: int
+    fbw: int
+    tiles: int         # tiles of 128 tokens in the unit
+    kshift: bool = False
+
+    def derived(self):
+        e, dh = self.elem, self.dh
+        kd, nm = dh // 16, (2 if e == 2 else 1)
+        tt = 128
+        vst = tt + 8
+        fold = fold_exponent(e, dh, self.r16)
+        uk = kd if fold else self.r16
+        up = 1 if fold else nm
+        zmma = (not fold) or dh % 32 != 0
+        dbk = vblocks_ones(dh) if zmma else vblocks(dh)
+        mfr = ((self.r16 + 1) // 2) * kd * nm
+        m_lds = mfr * 512 * e <= 32 * 1024
+        tile_state = (WAVES * up * uk * 512 + dh * vst) * e + tt * 4
+        nbuf = 2 if 2 * tile_state + (mfr * 512 * e if m_lds else 0) <= MAX_LDS else 1
+        return dict(kd=kd, nm=nm, tt=tt, vst=vst, fold=fold, uk=uk, up=up, zmma=zmma, dbk=dbk, mfr=mfr,
+                    m_lds=m_lds, nbuf=nbuf, r32=(self.r16 + 1) // 2, vhold=dbk <= 4)
+
+
+def kstate_tile_lds_bytes(elem, dh, r16):
+    fold = fold_exponent(elem, dh, r16)
+    uk = dh // 16 if fold else r16
+    up = 1 if fold else (2 if elem == 2 else 1)
+    mbytes = ((r16 + 1) // 2) * (dh // 16) * (2 if elem == 2 else 1) * 512 * elem
+    return (WAVES * up * uk * 512 + dh * 136) * elem + 128 * 4 + (mbytes if mbytes <= 32 * 1024 else 16)
+
+
+def kstate_model(cfg: KstateConfig, mutate=frozenset()):
+    D = cfg.derived()
+    e = cfg.elem
+    nb, up, uk = D["nbuf"], D["up"], D["uk"]
+    u_slot = lambda buf, w, part, k: ((((buf * WAVES + w) * up + part) * uk + k) * 512)  # noqa: E731
+    sizes = {"s_u": nb * WAVES * up * uk * 512 * e, "s_init": nb * 128 * 4, "s_vt": nb * cfg.dh * D["vst"] * e,
+             "s_m": (D["mfr"] * 512 if D["m_lds"] else 8) * e}
+    if sum(sizes.values()) > MAX_LDS:
+        raise Violation(f"LDS {sum(sizes.values())} bytes > {MAX_LDS}")
+    tr = Tracker(sizes, set(mutate))
+
+    def project_tile(w, buf):
+        if D["m_lds"] and (not D["fold"] or not cfg.kshift):
+            for rb in range(D["r32"]):
+                for kd in range(D["kd"]):
+                    for part in range(D["nm"]):
+                        tr.read(w, "s_m", frag_lanes(((rb * D["kd"] + kd) * D["nm"] + part) * 512, e), 8 * e)
+        if D["fold"]:
+            for k in range(uk):
+                tr.write(w, "s_u", frag_lanes(u_slot(buf, w, 0, k), e), 8 * e)
+        else:
+            for k in range(cfg.r16):
+                tr.write(w, "s_u", frag_lanes(u_slot(buf, w, 0, k), e), 8 * e)
+                if D["nm"] == 2:
+                    tr.write(w, "s_u", frag_lanes(u_slot(buf, w, D["nm"] - 1, k), e), 8 * e)
+        tr.write(w, "s_init", (buf * 128 + 32 * w + C[G == 0]) * 4, 4)
+        store_vt(tr, w, "s_vt", buf * cfg.dh * D["vst"], cfg.dh, 128, D["vst"], e)
+
+    def compute_tile(w, buf):
+        for tb in range(WAVES):
+            for jj in range(4):
+                tr.read(w, "s_init", (buf * 128 + 32 * tb + 8 * jj + 4 * G) * 4, 16)
+            if D["vhold"]:
+                for db in range(D["dbk"]):
+                    for k in range(2):
+                        v_frag_read(tr, w, "s_vt", buf * cfg.dh * D["vst"], cfg.dh, D["vst"], db, 32 * tb, k, e,
+                                    ones=D["zmma"])
+            for _f in range(cfg.fbw):
+                for k in range(uk):
+                    tr.read(w, "s_u", frag_lanes(u_slot(buf, tb, 0, k), e), 8 * e)
+                    if not D["fold"]:
+                        tr.read(w, "s_u", frag_lanes(u_slot(buf, tb, up - 1, k), e), 8 * e)
+                if not D["vhold"]:
+                    for db in range(D["dbk"]):
+                        for k in range(2):
+                            v_frag_read(tr, w, "s_vt", buf * cfg.dh * D["vst"], cfg.dh, D["vst"], db, 32 * tb, k, e,
+                                        ones=D["zmma"])
+
+    def wave(w):
+        if D["m_lds"]:
+            pm = (D["mfr"] * 64 + 255) // 256
+            for p in range(pm):
+                idx = 64 * w + LANES + p * 256
+                ok = idx < D["mfr"] * 64
+                tr.write(w, "s_m", idx[ok] * 8 * e, 8 * e)
+        if nb == 2:
+            yield                                   # M' in LDS
+            project_tile(w, 0)
+            yield
+            for it in range(cfg.tiles):
+                more = it + 1 < cfg.tiles
+                compute_tile(w, it & 1)
+                if more:
+                    project_tile(w, (it + 1) & 1 if "tile_same_buffer" not in tr.mutate else it & 1)
+                yield
+        else:
+            yield
+            for _ in range(cfg.tiles):
+                project_tile(w, 0)
+                yield
+                compute_tile(w, 0)
+                if "no_tile_end_barrier" not in tr.mutate:
+                    yield
+
+    run_waves(tr, [wave(w) for w in range(WAVES)])
+    return tr
+
+
+# ---------------------------------------------------------------------------
+# key shifts (shift_kernel): M' slices double-buffered through LDS
+# ---------------------------------------------------------------------------
+def shift_model(elem, dh, r16, mutate=frozenset()):
+    kd, nm = dh // 16, (2 if elem == 2 else 1)
+    sl = kd * nm
+    ps = (sl * 64 + 255) // 256
+    r32 = (r16 + 1) // 2
+    tr = Tracker({"s_m": 2 * sl * 512 * elem}, set(mutate))
+
+    def put(w, buf):
+        for p in range(ps):
+            idx = 64 * w + LANES + p * 256
+            ok = idx < sl * 64
+            tr.write(w, "s_m", (buf * sl * 512 + idx[ok] * 8) * elem, 8 * elem)
+
+    def wave(w):
+        put(w, 0)
+        yield
+        for rb in range(r32):
+            for kd_ in range(kd):
+                for part in range(nm):
+                    tr.read(w, "s_m", frag_lanes((rb & 1) * sl * 512 + ((kd_ * nm + part) * 64) * 8, elem), 8 * elem)
+            if rb + 1 < r32:
+                put(w, (rb + 1) & 1 if "shift_same_buffer" not in tr.mutate else rb & 1)
+            yield
+
+    run_waves(tr, [wave(w) for w in range(WAVES)])
+    return tr
+
+
+# ---------------------------------------------------------------------------
+# every instantiation the library builds, with the launch choices of the host
+# ---------------------------------------------------------------------------
+DTYPES = (2, 4)
+HEAD_DIMS = (16, 32, 64, 128, 256)
+RANK_BLOCKS = (1, 2, 4, 8, 16)
+
+
+def qout_all_fits(elem, dh, r16, allfb=8):
+    kd, nm, db = dh // 16, (2 if elem == 2 else 1), vblocks(dh)
+    uk = kd if fold_exponent(elem, dh, r16) else r16
+    nstep = uk * nm + 2 * db + 1
+    vt = dh * (128 + 8) * elem
+    return elem == 2 and vt + allfb * nstep * 512 * elem + 2 * 4 * 2 * 512 * elem <= MAX_LDS
+
+
+def qout_cases():
+    """(QoutConfig, label) for every launched query-side variant and a few feature counts."""
+    out = []
+    for elem in DTYPES:
+        for dh in HEAD_DIMS:
+            for r16 in RANK_BLOCKS:
+                fold = fold_exponent(elem, dh, r16)
+                for fb in (1, 2, 3, 9):
+                    m = 32 * fb - (16 if fb > 1 else 0)
+                    # non-causal: one or two query blocks per wave (two only for d_h <= 128)
+                    for nqb in ((1, 2) if dh <= 128 else (1,)):
+                        out.append((QoutConfig(elem, dh, r16, nqb, False, 0, fb, m), f"nc e{elem} d{dh} r{r16} "
+                                    f"nqb{nqb} fb{fb}"))
+                    # causal: one query block per wave, all-step staging when it fits and FB <= 8
+                    if (dh * (128 + 8) + 4 * 2 * 512) * elem <= MAX_LDS:
+                        allfb = 8 if (qout_all_fits(elem, dh, r16) and fb <= 8) else 0
+                        fbw = 2 if dh <= 64 else 1
+                        nf = -(-fb // (4 * fbw))
+                        kshift = fold and (nf > 1 or dh >= 128)
+                        out.append((QoutConfig(elem, dh, r16, 1, True, allfb, fb, m, kshift),
+                                    f"c e{elem} d{dh} r{r16} fb{fb} all{allfb}"))
+    return out
+
+
+def kstate_cases():
+    out = []
+    for elem in DTYPES:
+        for dh in HEAD_DIMS:
+            for r16 in RANK_BLOCKS:
+                if kstate_tile_lds_bytes(elem, dh, r16) > MAX_LDS:
+                    continue   # the one-block-at-a-time key side runs instead
+                fbw = 2 if dh <= 64 else 1
+                fold = fold_exponent(elem, dh, r16)
+                for tiles in (1, 3):
+                    for kshift in ((False, True) if fold else (False,)):
+                        out.append((KstateConfig(elem, dh, r16, fbw, tiles, kshift=kshift),
+                                    f"e{elem} d{dh} r{r16} t{tiles} kshift{int(kshift)}"))
+    return out

@@ -1,0 +1,71 @@
+"""The LDS schedules of the query-side, key-side and shift kernels, replayed on
+the host for every instantiation the library builds (tests/lds_model.py):
+accesses in bounds, every byte read written before and visible to its reader,
+no two waves touching a byte in one barrier phase with a write.  Planted
+mistakes (a barrier removed, a buffer index frozen) must be caught."""
+import pytest
+
+from tests import lds_model as lm
+
+QOUT = lm.qout_cases()
+KSTATE = lm.kstate_cases()
+
+
+@pytest.mark.parametrize("cfg", [c for c, _ in QOUT], ids=[n for _, n in QOUT])
+def test_query_side_schedule(cfg):
+    lm.qout_model(cfg)
+
+
+@pytest.mark.parametrize("cfg", [c for c, _ in KSTATE], ids=[n for _, n in KSTATE])
+def test_key_side_schedule(cfg):
+    lm.kstate_model(cfg)
+
+
+@pytest.mark.parametrize("elem", lm.DTYPES)
+@pytest.mark.parametrize("dh", lm.HEAD_DIMS)
+@pytest.mark.parametrize("r16", lm.RANK_BLOCKS)
+def test_shift_schedule(elem, dh, r16):
+    lm.shift_model(elem, dh, r16)
+
+
+def _first_caught(model, cases, mutation):
+    for cfg, name in cases:
+        try:
+            model(cfg, mutate={mutation})
+        except lm.Violation:
+            return name
+    return None
+
+
+@pytest.mark.parametrize("mutation", ["no_kbuf_barrier", "no_kbuf1_barrier", "no_step_barrier", "ring_same_buffer",
+                                      "kbuf_index_fixed"])
+def test_model_catches_planted_query_side_mistakes(mutation):
+    cases = QOUT
+    if mutation == "no_kbuf1_barrier":
+        cases = [(c, n) for c, n in QOUT if c.causal and c.derived()["kbuf"] == 1 and c.fb > 1]
+    if not cases:
+        pytest.skip(f"no instantiation exercises {mutation}")
+    assert _first_caught(lm.qout_model, cases, mutation), f"{mutation} not caught"
+
+
+@pytest.mark.parametrize("mutation", ["tile_same_buffer", "no_tile_end_barrier"])
+def test_model_catches_planted_key_side_mistakes(mutation):
+    cases = [(c, n) for c, n in KSTATE if c.tiles > 1]
+    if mutation == "no_tile_end_barrier":
+        cases = [(c, n) for c, n in cases if c.derived()["nbuf"] == 1]
+        if not cases:
+            pytest.skip("every key-side instantiation double-buffers its tiles")
+    assert _first_caught(lm.kstate_model, cases, mutation), f"{mutation} not caught"
+
+
+def test_model_catches_shift_buffer_reuse():
+    assert any(_raises(lambda: lm.shift_model(e, d, r, mutate={"shift_same_buffer"}))
+               for e in lm.DTYPES for d in lm.HEAD_DIMS for r in (2, 4, 16))
+
+
+def _raises(fn):
+    try:
+        fn()
+    except lm.Violation:
+        return True
+    return False
