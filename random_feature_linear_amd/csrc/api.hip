@@ -463,6 +463,28 @@ __global__ void dk_fill_zero(float* p, long n) {
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) p[i] = 0.f;
 }
 
+// Arguments common to the forward-chain calls (pointers the call does not use stay null).
+static FwdArgs fwd_args(const dark_prf_desc& d) {
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = d.q_str[i];
+    a.ks[i] = d.k_str[i];
+    a.vs[i] = d.v_str[i];
+    a.os[i] = d.o_str[i];
+  }
+  a.B = d.B;
+  a.H = d.H;
+  a.H_kv = d.H_kv;
+  a.L = d.L;
+  a.m = d.m;
+  a.r = d.r;
+  a.causal = d.causal;
+  a.m_per_head = d.m_per_head;
+  a.omega_per_head = d.omega_per_head;
+  return a;
+}
+
 dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k, const void* v,
                          const float* M, const float* omega, const uint8_t* mask, void* out, float* S_out,
                          float* z_out, void* workspace, size_t ws_bytes, void* stream) {
@@ -494,35 +516,16 @@ dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k
   fwd_launcher fn = find_fwd_launcher(d.dtype, d.d_h, p.R16);
   if (!fn) return DARK_ERR_UNSUPPORTED;
   (void)hipGetLastError();   // launch errors below are ours, not an earlier caller's
-  FwdArgs a;
+  FwdArgs a = fwd_args(d);   // every field set; kshift comes from the workspace in the launcher
   a.q = q;
   a.k = k;
   a.v = v;
   a.out = out;
-  for (int i = 0; i < 3; ++i) {
-    a.qs[i] = d.q_str[i];
-    a.ks[i] = d.k_str[i];
-    a.vs[i] = d.v_str[i];
-    a.os[i] = d.o_str[i];
-  }
   a.mask = mask;
   a.M = M;
   a.omega = omega;
   a.S_out = S_out;
   a.z_out = z_out;
-  a.kshift = nullptr;   // set by the launcher from the workspace
-  a.qmask = nullptr;
-  a.S_in = nullptr;
-  a.z_in = nullptr;
-  a.B = d.B;
-  a.H = d.H;
-  a.H_kv = d.H_kv;
-  a.L = d.L;
-  a.m = d.m;
-  a.r = d.r;
-  a.causal = d.causal;
-  a.m_per_head = d.m_per_head;
-  a.omega_per_head = d.omega_per_head;
   return fn(a, p, workspace, stream);
 }
 
@@ -539,28 +542,6 @@ dark_status dark_prf_fwd_noalloc(const dark_prf_desc* desc, const void* q, const
   if (st != DARK_OK) return st;
   return dark_prf_fwd(desc, q, k, v, M, omega, mask, out, S_out, z_out, ws, (size_t)DARK_PRF_SCRATCH_BYTES,
                       stream);
-}
-
-// Arguments common to the forward-chain calls (pointers the call does not use stay null).
-static FwdArgs fwd_args(const dark_prf_desc& d) {
-  FwdArgs a;
-  memset(&a, 0, sizeof(a));
-  for (int i = 0; i < 3; ++i) {
-    a.qs[i] = d.q_str[i];
-    a.ks[i] = d.k_str[i];
-    a.vs[i] = d.v_str[i];
-    a.os[i] = d.o_str[i];
-  }
-  a.B = d.B;
-  a.H = d.H;
-  a.H_kv = d.H_kv;
-  a.L = d.L;
-  a.m = d.m;
-  a.r = d.r;
-  a.causal = d.causal;
-  a.m_per_head = d.m_per_head;
-  a.omega_per_head = d.omega_per_head;
-  return a;
 }
 
 static dark_status zero_state(const dark_prf_desc& d, float* S, float* z, void* stream) {

@@ -695,14 +695,14 @@ __device__ __forceinline__ void stage_vt(T* s_vt, const T* vb, int64_t vstride, 
 
 // The same staging in two halves: global loads into registers (issued a tile
 // ahead of their use) and the transposed LDS stores.
-template <int DH, int TT> constexpr int vloads_per_thread() { return (TT * (DH / 8) + kThreads - 1) / kThreads; }
-template <typename T, int DH, int TT>
+template <int DH, int TT, int NT = kThreads> constexpr int vloads_per_thread() { return (TT * (DH / 8) + NT - 1) / NT; }
+template <typename T, int DH, int TT, int NT = kThreads>
 __device__ __forceinline__ void load_v(typename FragOf<T>::type* vr, const T* vb, int64_t vstride, int t0, int t_end,
                                        int tid) {
   typedef typename FragOf<T>::type F;
 #pragma unroll
-  for (int p = 0; p < vloads_per_thread<DH, TT>(); ++p) {
-    const int e = tid + p * kThreads;
+  for (int p = 0; p < vloads_per_thread<DH, TT, NT>(); ++p) {
+    const int e = tid + p * NT;
     const int tl = e % TT, d8 = ((e / TT) * 8) % DH;   // consecutive lanes: consecutive tokens
     const int t = t0 + tl;
     // clamped (always valid) address, so that all loads are in flight at once
@@ -714,11 +714,11 @@ __device__ __forceinline__ void load_v(typename FragOf<T>::type* vr, const T* vb
 // the 8 tokens one lane of a V operand fragment holds (16k + 8(e / 4) + 4g + e % 4,
 // the operand order of the feature products) are 8 consecutive elements.
 __device__ __forceinline__ int vt_pos(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
-template <typename T, int DH, int TT, int VST>
+template <typename T, int DH, int TT, int VST, int NT = kThreads>
 __device__ __forceinline__ void store_vt(T* s_vt, const typename FragOf<T>::type* vr, int tid) {
 #pragma unroll
-  for (int p = 0; p < vloads_per_thread<DH, TT>(); ++p) {
-    const int e = tid + p * kThreads;
+  for (int p = 0; p < vloads_per_thread<DH, TT, NT>(); ++p) {
+    const int e = tid + p * NT;
     if (e >= TT * (DH / 8)) break;
     const int tl = e % TT, d8 = (e / TT) * 8;
 #pragma unroll
@@ -856,16 +856,17 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
     }
   }
 
-  // M' of this head in LDS when it is small: every token block of every tile reads it
-  if constexpr (M_LDS) {   // all loads in flight, then the stores
-    constexpr int PM = (MFR * 64 + kThreads - 1) / kThreads;
-    F mreg[PM];
-#pragma unroll
-    for (int p = 0; p < PM; ++p) mreg[p] = ld8(mf + (long)min(tid + p * kThreads, MFR * 64 - 1) * 8);
-#pragma unroll
-    for (int p = 0; p < PM; ++p)
-      if (tid + p * kThreads < MFR * 64) st8(s_m + (tid + p * kThreads) * 8, mreg[p]);
-  }
+  // M' of this head in LDS when it is small (every token block of every tile
+  // reads it): copied global -> LDS by the DMA path, 1 KB per wave instruction,
+  // issued behind the first tile's K and V loads so that all are in flight
+  // together; the caller waits for vmcnt(0) and a barrier.
+  auto stage_m = [&]() {
+    if constexpr (M_LDS) {
+      constexpr int NKB = MFR * 64 * 8 * (int)sizeof(T) / 1024;
+      for (int i = w; i < NKB; i += kWaves)
+        dma16(reinterpret_cast<const char*>(mf) + i * 1024 + lane * 16, reinterpret_cast<char*>(s_m) + i * 1024);
+    }
+  };
   const T* msrc = M_LDS ? s_m : mf;
   // K rows of block w and the V rows of a tile are loaded one tile ahead of their use
   // (d_h = 256: no register prefetch, the registers go to the accumulators)
@@ -961,7 +962,9 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
   };
   if constexpr (NBUF == 2) {
     prefetch(t_begin);
-    __syncthreads();   // M' in LDS
+    stage_m();
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the tile's rows and this wave's copies of M'
+    __syncthreads();                      // M' in LDS
     project_tile(t_begin, 0, msrc);
     __syncthreads();
     int it = 0;
@@ -976,7 +979,9 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
     }
   } else {
     if constexpr (PREF) prefetch(t_begin);
-    __syncthreads();
+    stage_m();
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();                      // M' in LDS
     for (int t0 = t_begin; t0 < t_end; t0 += TT) {
       const T* of_t = opaque(of, !kHoist);
       const T* msrc_t = opaque(msrc, !M_LDS);
@@ -1716,6 +1721,303 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
 }
 
 // ---------------------------------------------------------------------------
+// Causal query side with eight waves per workgroup (bf16, every step's
+// operands staged in LDS at once).  The same sums as qout_kernel, with the
+// feature steps split in two halves: waves w and w + 4 both own query block
+// w % 4 (and key block w % 4 of the chunk); wave w takes the first half of the
+// 32-feature steps, wave w + 4 the second.  N and D are sums over features, so
+// each half forms its own part of Phi(Q) S, of the masked scores
+// Phi(Q) Phi(K_chunk)^T and of their products with V, and the two parts are
+// added at the end through LDS.  Both halves shift their queries by the same
+// value (the largest exponent over the first 32 features, from the first
+// step's operands).  Two waves per SIMD let one wave's exp and LDS latencies
+// overlap the other's matrix products.
+// ---------------------------------------------------------------------------
+constexpr int kWaves8 = 2 * kWaves;
+constexpr int kThreads8 = 64 * kWaves8;
+template <typename T, int DH, int R16, int ALLFB> constexpr bool qout8_fits() {
+  constexpr size_t vt = (size_t)DH * (128 + 8) * sizeof(T);
+  constexpr size_t op = (size_t)ALLFB * qout_nstep<T, DH, R16>() * 64 * 8 * sizeof(T);
+  constexpr size_t kf = 2 * 2 * kWaves * 2 * 64 * 8 * sizeof(T);
+  constexpr size_t xch = (size_t)kWaves * (vblocks<DH>() * 16 + 1) * 64 * sizeof(float);   // the halves' hand-over
+  constexpr size_t ost = (size_t)kWaves * 32 * (DH + 8) * sizeof(T);                      // output staging
+  return sizeof(T) == 2 && vt + op + kf <= 160 * 1024 && xch <= op && (ost <= kf || ost <= vt);
+}
+template <typename T, int DH, int R16, bool PAD, int ALLFB>
+__global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
+                                                          const T* __restrict__ ofrag, const T* __restrict__ sfrag,
+                                                          const float* __restrict__ zsum) {
+  typedef typename FragOf<T>::type F;
+  static_assert(sizeof(T) == 2, "bf16 only");
+  constexpr int KD = DH / 16;
+  constexpr int NM = kParts<T>;
+  constexpr int DB = vblocks<DH>();
+  constexpr int NB = kWaves;               // 32-token blocks per chunk
+  constexpr int TT = 32 * NB;              // tokens per chunk
+  constexpr int VST = TT + 8;
+  constexpr bool FOLD = fold_exponent(sizeof(T), DH, R16);
+  constexpr int UK = FOLD ? KD : R16;      // K-steps of the exponent
+  constexpr int NOF = UK * NM;             // omega' (W') fragments per feature step
+  constexpr int NSTEP = qout_nstep<T, DH, R16>();
+  constexpr int ZS = NSTEP - 1;            // the z slot
+  constexpr int ZW = 8 * (int)sizeof(T) / 4;
+  constexpr int VT_ELEMS = DH * VST;
+  constexpr int KFH = 2 * NB * 2 * 64 * 8;   // key-feature buffers of one half (two)
+  constexpr int KF_ELEMS = 2 * KFH;
+  constexpr int OP_ELEMS = ALLFB * NSTEP * 64 * 8;
+  static_assert(qout8_fits<T, DH, R16, ALLFB>(), "LDS");
+  __shared__ __attribute__((aligned(16))) T s_vt[VT_ELEMS];
+  __shared__ __attribute__((aligned(16))) T s_kf[KF_ELEMS];
+  __shared__ __attribute__((aligned(16))) T s_op[OP_ELEMS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, c = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qb = w & (NB - 1), half = w / NB;
+  const int lb = xcd_block();
+  const int tile = lb % pl.NT2;
+  const int bh = lb / pl.NT2;
+  const int b = bh / a.H, h = bh % a.H;
+  const int hk = (h * a.H_kv) / a.H;
+  const T* qbase = reinterpret_cast<const T*>(a.q) + b * a.qs[0] + h * a.qs[1];
+  const T* kbase = reinterpret_cast<const T*>(a.k) + b * a.ks[0] + hk * a.ks[1];
+  const T* vbase = reinterpret_cast<const T*>(a.v) + b * a.vs[0] + hk * a.vs[1];
+  T* obase = reinterpret_cast<T*>(a.out) + b * a.os[0] + h * a.os[1];
+  const uint8_t* mrow = a.mask ? a.mask + (long)b * a.L : nullptr;
+  const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * ((R16 + 1) / 2) * KD * NM * 64 * 8;
+  const T* of = ofrag + (long)((FOLD ? pl.HW : pl.HO) > 1 ? h : 0) * pl.FB * UK * NM * 64 * 8;
+  const float half_log2m = 0.5f * log2f((float)a.m);
+  const int t0 = tile * TT;
+  const long FK = 2L * pl.FB;
+  const long unit_s = (long)bh * pl.NU + tile;
+  const T* sf = sfrag + unit_s * DB * FK * 64 * 8;
+  const float* zs = zsum + unit_s * pl.FB * 32;
+
+  // step operands as in qout_kernel: W' (omega') fragments, state fragments, z slot
+  auto gsrc = [&](int fb, int f) -> const T* {
+    if (f < NOF) return of + (((long)(fb * UK + f / NM) * NM + f % NM) * 64 + lane) * 8;
+    if (f == ZS) return reinterpret_cast<const T*>(zs + fb * 32 + min(lane, 32 / ZW - 1) * ZW);
+    f -= NOF;
+    return sf + (((f >> 1) * FK + 2 * fb + (f & 1)) * 64 + lane) * 8;
+  };
+  // M' (in the key-feature buffers, free until the first step) and every
+  // step's operands go to LDS by DMA before the rows are loaded.
+  constexpr int MFRG = ((R16 + 1) / 2) * KD * NM;
+  constexpr bool M_LDS = MFRG * 64 * 8 <= KF_ELEMS;
+  if constexpr (M_LDS)
+    for (int idx = w; idx < MFRG; idx += kWaves8) dma16(mf + ((long)idx * 64 + lane) * 8, s_kf + idx * 64 * 8);
+  for (int idx = w; idx < pl.FB * NSTEP; idx += kWaves8) {
+    const int fb = idx / NSTEP, f = idx - fb * NSTEP;
+    dma16(gsrc(fb, f), s_op + idx * 64 * 8);
+  }
+
+  // ---- exponent operands of query block qb and key block qb ----
+  const int t = t0 + 32 * qb + c;
+  const bool ok = t < a.L;
+  F uqh[UK], uql[FOLD ? 1 : UK];
+  F ukh[UK], ukl[FOLD ? 1 : UK];
+  F xq[FOLD ? 1 : KD], xk[FOLD ? 1 : KD];
+  load_rows<T, DH>(*reinterpret_cast<F(*)[KD]>(FOLD ? uqh : xq), qbase + (long)t * a.qs[2], ok, g);
+  load_rows<T, DH>(*reinterpret_cast<F(*)[KD]>(FOLD ? ukh : xk), kbase + (long)t * a.ks[2], ok, g);
+  constexpr int VPT = vloads_per_thread<DH, TT, kThreads8>();
+  F vr[VPT];
+  load_v<T, DH, TT, kThreads8>(vr, vbase, a.vs[2], t0, a.L, tid);
+  float initk = -INFINITY;
+  bool kvalid = ok;
+  if (FOLD && pl.kshift) {
+    if (ok) initk = a.kshift[(long)bh * a.L + t];
+  } else {
+    kvalid = ok && (mrow == nullptr || mrow[t] != 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): rows, V and this wave's copies
+  store_vt<T, DH, TT, VST, kThreads8>(s_vt, vr, tid);
+  __syncthreads();                      // M', V^T and every wave's copies visible
+  const T* msrc = M_LDS ? s_kf : mf;
+  if constexpr (!FOLD)
+    (void)project_block<T, DH, R16>(*reinterpret_cast<F(*)[R16]>(uqh), *reinterpret_cast<F(*)[R16]>(uql), xq, msrc,
+                                    lane, half_log2m);
+  if (!(FOLD && pl.kshift)) {
+    float sh;
+    if constexpr (FOLD)
+      sh = project_shift<T, DH, R16>(*reinterpret_cast<F(*)[KD]>(ukh), msrc, lane, half_log2m);
+    else
+      sh = project_block<T, DH, R16>(*reinterpret_cast<F(*)[R16]>(ukh), *reinterpret_cast<F(*)[R16]>(ukl), xk, msrc,
+                                     lane, half_log2m);
+    initk = kvalid ? -sh : -INFINITY;
+  }
+
+  auto op = [&](int fb, int f) { return ld8(s_op + ((fb * NSTEP + f) * 64 + lane) * 8); };
+  auto zrow4 = [&](int fb, int jj) -> float4 {
+    const float* zb = reinterpret_cast<const float*>(s_op + (fb * NSTEP + ZS) * 64 * 8);
+    return *reinterpret_cast<const float4*>(zb + 8 * jj + 4 * g);
+  };
+  // the query shift: largest exponent of query c over the first 32 features
+  float shq;
+  {
+    auto oload = [&](int k, int part) -> F { return op(0, k * NM + (part ? NM - 1 : 0)); };
+    f32x16 e = zero16();
+    if constexpr (PAD) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (crow(i, g) >= a.m) e[i] = -INFINITY;
+    }
+    if constexpr (FOLD)
+      e = exponent_stream<T, UK, false, false>([&](int k, int) -> F { return uqh[k]; }, oload, e);
+    else
+      e = exponent_stream<T, UK, false, true>([&](int k, int part) -> F { return part ? uql[k] : uqh[k]; }, oload,
+                                              e);
+    float mx = e[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, e[i]);
+    shq = fmaxf(mx, __shfl_xor(mx, 32));
+  }
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = zero16();
+  float den = 0.f;
+  f32x16 at[NB];   // A^T[key block][query block qb], this half's features
+  // every wave's projections are done reading M' from the key-feature buffers
+  // before the first step writes key features there
+  if constexpr (M_LDS) __syncthreads();
+#pragma unroll
+  for (int kb2 = 0; kb2 < NB; ++kb2) at[kb2] = zero16();
+
+  const int nit = (pl.FB + 1) >> 1;   // steps per half (the second half may have one fewer)
+  for (int it = 0; it < nit; ++it) {
+    const int fb = half * nit + it;
+    const bool live = fb < pl.FB;
+    T* kbuf = s_kf + half * KFH + (it & 1) * NB * 2 * 64 * 8;
+    F pq[2];
+    if (live) {
+      auto oload = [&](int k, int part) -> F { return op(fb, k * NM + (part ? NM - 1 : 0)); };
+      F ohi[FOLD ? 1 : UK], olo[FOLD ? 1 : UK];
+      if constexpr (!FOLD) {
+#pragma unroll
+        for (int k = 0; k < UK; ++k) {
+          ohi[k] = op(fb, k * NM);
+          olo[k] = op(fb, k * NM + NM - 1);
+        }
+      }
+      const bool partial = PAD && (fb + 1) * 32 > a.m;
+      {
+        f32x16 e = splat16(-shq);
+        if (partial) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (fb * 32 + crow(i, g) >= a.m) e[i] = -INFINITY;
+        }
+        if constexpr (FOLD)
+          e = exponent_stream<T, UK, false, false>([&](int k, int) -> F { return uqh[k]; }, oload, e);
+        else
+          e = exponent<T, UK, false, true>(uqh, uql, ohi, olo, e);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {   // D += phi(q) . z
+          const float4 z = zrow4(fb, jj);
+          den += e[4 * jj] * z.x + e[4 * jj + 1] * z.y + e[4 * jj + 2] * z.z + e[4 * jj + 3] * z.w;
+        }
+        pq[0] = acc_frag<F>(e, 0);
+        pq[1] = acc_frag<F>(e, 1);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) acc[db] = mma(pq[k], op(fb, NOF + 2 * db + k), acc[db]);
+      {
+        f32x16 e = splat16(initk);
+        if (partial) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (fb * 32 + crow(i, g) >= a.m) e[i] = -INFINITY;
+        }
+        if constexpr (FOLD)
+          e = exponent_stream<T, UK, false, false>([&](int k, int) -> F { return ukh[k]; }, oload, e);
+        else
+          e = exponent<T, UK, false, true>(ukh, ukl, ohi, olo, e);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) st8(kbuf + ((qb * 2 + k) * 64 + lane) * 8, acc_frag<F>(e, k));
+      }
+    }
+    __syncthreads();   // this step's key features of the half's four blocks are in
+    if (live) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < NB; ++kb2)
+        if (kb2 <= qb)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) at[kb2] = mma(ld8(kbuf + ((kb2 * 2 + k) * 64 + lane) * 8), pq[k], at[kb2]);
+    }
+  }
+
+  // intra-chunk part with this half's scores: key R(i, g) of the diagonal block
+  // is visible to query c iff R(i, g) <= c
+#pragma unroll
+  for (int kb2 = 0; kb2 < NB; ++kb2) {
+    if (kb2 > qb) continue;
+    if (kb2 == qb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (crow(i, g) > c) at[kb2][i] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const F pf = acc_frag<F>(at[kb2], k);
+      den = frag_sum(pf, den);   // the rounded scores the products use
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] = mma(pf, v_frag<T, DH, VST>(s_vt, db, 32 * kb2, k, c, g), acc[db]);
+    }
+  }
+
+  // ---- the second half's N and D added to the first's through LDS; out = N / D
+  // staged per wave and stored as 16-byte pieces of whole rows ----
+  constexpr int XW = DB * 16 + 1;   // floats per lane handed over
+  static_assert((size_t)kWaves * XW * 64 * sizeof(float) <= (size_t)OP_ELEMS * sizeof(T), "exchange buffer");
+  constexpr int OST = DH + 8;
+  constexpr bool OST_KF = kWaves * 32 * OST <= KF_ELEMS;   // else the V^T tile's buffer (d_h >= 128)
+  static_assert(OST_KF || kWaves * 32 * OST <= VT_ELEMS, "output staging buffer");
+  float* xch = reinterpret_cast<float*>(s_op) + qb * XW * 64;
+  // (no barrier needed first: the step operands in s_op were last read before
+  // the last key-feature barrier, which every wave has passed)
+  if (half == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xch[(db * 16 + i) * 64 + lane] = acc[db][i];
+    xch[DB * 16 * 64 + lane] = den;
+  }
+  __syncthreads();   // the hand-over is in; s_kf and s_vt are no longer read
+  if (half == 1) return;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] += xch[(db * 16 + i) * 64 + lane];
+  den += xch[DB * 16 * 64 + lane];
+  T* const ostage = (OST_KF ? s_kf : s_vt) + qb * 32 * OST;
+  const float dq = den + __shfl_xor(den, 32);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float dd = __shfl(dq, crow(i, g));
+    const float inv = dd > 0.f ? __builtin_amdgcn_rcpf(dd) : 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = db * 32 + c;
+      if (d < DH) store_out(ostage + crow(i, g) * OST + d, acc[db][i] * inv);
+    }
+  }
+  constexpr int CPR = DH / 8;   // 16-byte pieces per row
+#pragma unroll
+  for (int q = lane; q < 32 * CPR; q += 64) {
+    const int row = q / CPR, col = (q - row * CPR) * 8;
+    const int tr = t0 + 32 * qb + row;
+    if (tr < a.L)
+      *reinterpret_cast<uint4*>(obase + (long)tr * a.os[2] + col) = *reinterpret_cast<const uint4*>(ostage + row * OST + col);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host launch of one forward call for (T, DH, R16).
 // ---------------------------------------------------------------------------
 constexpr size_t kMaxLds = 160 * 1024;
@@ -1806,8 +2108,12 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
       if (pl.NQB != 1) return DARK_ERR_UNSUPPORTED;
       if constexpr (qout_all_fits<T, DH, R16, kAllFB>()) {   // few feature blocks: all steps staged at once
         if (pl.FB <= kAllFB) {
-          hipLaunchKernelGGL((qout_kernel<T, DH, R16, 1, true, PAD, kAllFB>), grid, dim3(kThreads), 0, st, a, pl,
-                             mfrag, ofrag, sfrag, zsum);
+          if constexpr (!PAD && qout8_fits<T, DH, R16, kAllFB>())   // eight waves, feature steps in two halves
+            hipLaunchKernelGGL((qout8_kernel<T, DH, R16, PAD, kAllFB>), grid, dim3(kThreads8), 0, st, a, pl, mfrag,
+                               ofrag, sfrag, zsum);
+          else
+            hipLaunchKernelGGL((qout_kernel<T, DH, R16, 1, true, PAD, kAllFB>), grid, dim3(kThreads), 0, st, a, pl,
+                               mfrag, ofrag, sfrag, zsum);
           return hipGetLastError() == hipSuccess ? DARK_OK : DARK_ERR_HIP;
         }
       }

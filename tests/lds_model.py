@@ -1,7 +1,8 @@
 """A host-side model of the LDS schedules of the attention kernels.
 
 The query-side, key-side and shift kernels stage operands in LDS and hand
-data between the four waves of a workgroup across barriers: the ring of
+data between the waves of a workgroup (four, or eight in the causal query
+side that splits the feature steps in two halves) across barriers: the ring of
 feature-step operand buffers (s_op) with the z values in the last slot of a
 step, the key-feature buffers (s_kf), the operands copied global -> LDS by the
 DMA path (all steps, and M' in the key-feature buffers), the V^T tile, and on
@@ -44,6 +45,7 @@ class Violation(AssertionError):
 class Tracker:
     sizes: dict                                # array name -> bytes
     mutate: set = field(default_factory=set)   # planted mistakes (tests of the model itself)
+    waves: int = WAVES
 
     def __post_init__(self):
         self.epoch = 0
@@ -51,7 +53,7 @@ class Tracker:
         self.w_wave = {n: np.full(s, -1, np.int64) for n, s in self.sizes.items()}
         self.r_epoch = {n: np.full(s, -1, np.int64) for n, s in self.sizes.items()}
         self.r_mask = {n: np.zeros(s, np.int64) for n, s in self.sizes.items()}
-        self.pending = {w: [] for w in range(WAVES)}   # DMA copies in flight per wave
+        self.pending = {w: [] for w in range(self.waves)}   # DMA copies in flight per wave
         self.total = sum(self.sizes.values())
 
     def _bytes(self, name, starts, width):
@@ -101,12 +103,16 @@ class Tracker:
 
 
 def run_waves(tr: Tracker, programs):
-    """programs[w] is a generator yielding at each barrier; phases advance together."""
-    gens = [p for p in programs]
-    alive = [True] * WAVES
+    """programs[w] is a generator yielding at each barrier; phases advance together.
+    In each round every wave still running must reach the same barrier, or all
+    of them must finish (a wave that leaves early may do so only after the last
+    barrier)."""
+    gens = list(programs)
+    alive = [True] * len(gens)
     while any(alive):
+        running = sum(alive)
         hits = 0
-        for w in range(WAVES):
+        for w in range(len(gens)):
             if not alive[w]:
                 continue
             try:
@@ -114,7 +120,7 @@ def run_waves(tr: Tracker, programs):
                 hits += 1
             except StopIteration:
                 alive[w] = False
-        if hits not in (0, WAVES) or (hits == 0 and any(alive)):
+        if hits not in (0, running):
             raise Violation("waves reach different numbers of barriers")
         tr.epoch += 1
 
@@ -134,8 +140,8 @@ def vblocks_ones(dh):
     return (dh + 1 + 31) // 32
 
 
-def vloads_per_thread(dh, tt):
-    return (tt * (dh // 8) + 256 - 1) // 256
+def vloads_per_thread(dh, tt, nt=256):
+    return (tt * (dh // 8) + nt - 1) // nt
 
 
 def vt_pos(t):
@@ -147,10 +153,10 @@ def frag_lanes(base_elem, elem):
     return (base_elem + LANES * 8) * elem
 
 
-def store_vt(tr, w, name, base, dh, tt, vst, elem):
-    """store_vt: rows t0 .. t0 + TT - 1 of V into s_vt[d][vt_pos(t)] (every thread of wave w)."""
-    for p in range(vloads_per_thread(dh, tt)):
-        e = 64 * w + LANES + p * 256
+def store_vt(tr, w, name, base, dh, tt, vst, elem, nt=256):
+    """store_vt: rows t0 .. t0 + TT - 1 of V into s_vt[d][vt_pos(t)] (every thread of wave w, nt threads)."""
+    for p in range(vloads_per_thread(dh, tt, nt)):
+        e = 64 * w + LANES + p * nt
         ok = e < tt * (dh // 8)
         e = e[ok]
         tl, d8 = e % tt, (e // tt) * 8
@@ -339,6 +345,144 @@ def qout_model(cfg: QoutConfig, mutate=frozenset()):
 
 
 # ---------------------------------------------------------------------------
+# causal query side with eight waves (qout8_kernel): the feature steps in two
+# halves, each half with its own pair of key-feature buffers; the halves' N and
+# D meet in s_op at the end, and the output rows are staged in s_kf (or s_vt)
+# ---------------------------------------------------------------------------
+WAVES8 = 8
+
+
+def qout8_fits(elem, dh, r16, allfb=8):
+    kd, nm, db = dh // 16, (2 if elem == 2 else 1), vblocks(dh)
+    uk = kd if fold_exponent(elem, dh, r16) else r16
+    nstep = uk * nm + 2 * db + 1
+    vt = dh * 136 * elem
+    op = allfb * nstep * 512 * elem
+    kf = 2 * 2 * WAVES * 2 * 512 * elem
+    xch = WAVES * (db * 16 + 1) * 64 * 4
+    ost = WAVES * 32 * (dh + 8) * elem
+    return elem == 2 and vt + op + kf <= MAX_LDS and xch <= op and (ost <= kf or ost <= vt)
+
+
+def qout8_model(cfg: QoutConfig, mutate=frozenset()):
+    e, dh = cfg.elem, cfg.dh
+    kd, nm, db = dh // 16, (2 if e == 2 else 1), vblocks(dh)
+    fold = fold_exponent(e, dh, cfg.r16)
+    uk = kd if fold else cfg.r16
+    nof = uk * nm
+    nstep = nof + 2 * db + 1
+    zs = nstep - 1
+    vst = 136
+    kfh = 2 * WAVES * 2 * 512                  # elements: the two key-feature buffers of one half
+    kf_elems, op_elems, vt_elems = 2 * kfh, cfg.allfb * nstep * 512, dh * vst
+    mfrg = ((cfg.r16 + 1) // 2) * kd * nm
+    m_lds = mfrg * 512 <= kf_elems
+    xw = db * 16 + 1
+    ost = dh + 8
+    ost_kf = WAVES * 32 * ost <= kf_elems
+    sizes = {"s_vt": vt_elems * e, "s_kf": kf_elems * e, "s_op": op_elems * e}
+    if sum(sizes.values()) > MAX_LDS:
+        raise Violation(f"LDS {sum(sizes.values())} bytes > {MAX_LDS}")
+    tr = Tracker(sizes, set(mutate), waves=WAVES8)
+    op_read = lambda w, fb, f: tr.read(w, "s_op", frag_lanes((fb * nstep + f) * 512, e), 8 * e)  # noqa: E731
+
+    def exponent_reads(w, fb):
+        for k in range(uk):
+            op_read(w, fb, k * nm)
+            op_read(w, fb, k * nm + nm - 1)
+
+    def wave(w):
+        qb, half = w % WAVES, w // WAVES
+        if m_lds:
+            for idx in range(w, mfrg, WAVES8):
+                tr.dma(w, "s_kf", idx * 512 * e)
+        for idx in range(w, cfg.fb * nstep, WAVES8):
+            tr.dma(w, "s_op", idx * 512 * e)
+        if "no_wait8" not in tr.mutate:
+            tr.waitcnt(w)
+        store_vt(tr, w, "s_vt", 0, dh, 128, vst, e, nt=64 * WAVES8)
+        yield                                            # M', V^T and every copy visible
+        if m_lds:
+            nproj = (0 if fold else 1) + (0 if (fold and cfg.kshift) else 1)
+            for _ in range(nproj):
+                for rb in range((cfg.r16 + 1) // 2):
+                    for kd_ in range(kd):
+                        for part in range(nm):
+                            tr.read(w, "s_kf", frag_lanes(((rb * kd + kd_) * nm + part) * 512, e), 8 * e)
+        exponent_reads(w, 0)                             # the query shift
+        if m_lds and "no_m_barrier8" not in tr.mutate:
+            yield                                        # M' no longer read
+        nit = (cfg.fb + 1) // 2
+        for it in range(nit):
+            fb = half * nit + it
+            live = fb < cfg.fb
+            kbase = half * kfh + ((it & 1) if "kbuf8_index_fixed" not in tr.mutate else 0) * WAVES * 2 * 512
+            if live:
+                exponent_reads(w, fb)                    # queries (unfolded: the step's omega' read once)
+                for jj in range(4):
+                    tr.read(w, "s_op", (fb * nstep + zs) * 512 * e + (8 * jj + 4 * G) * 4, 16)
+                for d in range(db):
+                    for k in range(2):
+                        op_read(w, fb, nof + 2 * d + k)
+                if fold:
+                    exponent_reads(w, fb)                # keys
+                for k in range(2):
+                    tr.write(w, "s_kf", frag_lanes(kbase + (qb * 2 + k) * 512, e), 8 * e)
+            if "no_kbuf8_barrier" not in tr.mutate:
+                yield
+            if live:
+                for kb2 in range(qb + 1):
+                    for k in range(2):
+                        tr.read(w, "s_kf", frag_lanes(kbase + (kb2 * 2 + k) * 512, e), 8 * e)
+        for kb2 in range(qb + 1):                        # this half's scores times V
+            for k in range(2):
+                for d in range(db):
+                    v_frag_read(tr, w, "s_vt", 0, dh, vst, d, 32 * kb2, k, e)
+        xbase = qb * xw * 64 * 4
+        xbytes = xbase + (np.arange(xw)[:, None] * 64 + LANES[None, :]).ravel() * 4
+        if half == 1:
+            tr.write(w, "s_op", xbytes, 4)
+        if "no_exchange_barrier" not in tr.mutate:
+            yield                                        # the hand-over is in
+        if half == 1:
+            return
+        tr.read(w, "s_op", xbytes, 4)
+        buf = "s_kf" if ost_kf else "s_vt"
+        base = qb * 32 * ost
+        for i in range(16):
+            row = 8 * (i >> 2) + 4 * G + (i & 3)
+            for d in range(db):
+                dd = d * 32 + C
+                ok = dd < dh
+                tr.write(w, buf, (base + row[ok] * ost + dd[ok]) * e, e)
+        cpr = dh // 8
+        for q0 in range(0, 32 * cpr, 64):
+            q = q0 + LANES
+            q = q[q < 32 * cpr]
+            row, col = q // cpr, (q % cpr) * 8
+            tr.read(w, buf, (base + row * ost + col) * e, 16)
+
+    run_waves(tr, [wave(w) for w in range(WAVES8)])
+    return tr
+
+
+def qout8_cases():
+    """The eight-wave query side: bf16, causal, every step staged, m a multiple of 32."""
+    out = []
+    for dh in HEAD_DIMS:
+        for r16 in RANK_BLOCKS:
+            if not (qout_all_fits(2, dh, r16) and qout8_fits(2, dh, r16)):
+                continue
+            fold = fold_exponent(2, dh, r16)
+            for fb in (1, 2, 3, 8):
+                fbw = 2 if dh <= 64 else 1
+                nf = -(-fb // (4 * fbw))
+                kshift = fold and (nf > 1 or dh >= 128)
+                out.append((QoutConfig(2, dh, r16, 1, True, 8, fb, 32 * fb, kshift), f"q8 d{dh} r{r16} fb{fb}"))
+    return out
+
+
+# ---------------------------------------------------------------------------
 # key side (kstate_kernel, the tiled form)
 # ---------------------------------------------------------------------------
 @dataclass
@@ -425,12 +569,11 @@ def kstate_model(cfg: KstateConfig, mutate=frozenset()):
                                         ones=D["zmma"])
 
     def wave(w):
-        if D["m_lds"]:
-            pm = (D["mfr"] * 64 + 255) // 256
-            for p in range(pm):
-                idx = 64 * w + LANES + p * 256
-                ok = idx < D["mfr"] * 64
-                tr.write(w, "s_m", idx[ok] * 8 * e, 8 * e)
+        if D["m_lds"]:   # M' by the DMA path, 1 KB per wave instruction, then vmcnt(0)
+            for i in range(w, D["mfr"] * 512 * e // 1024, WAVES):
+                tr.dma(w, "s_m", i * 1024)
+            if "no_m_wait" not in tr.mutate:
+                tr.waitcnt(w)
         if nb == 2:
             yield                                   # M' in LDS
             project_tile(w, 0)
