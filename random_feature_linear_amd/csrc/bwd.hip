@@ -107,7 +107,12 @@ constexpr int kKT = 32;   // K depth of one LDS slice
 // XC: the last output column N - 1 is not tiled; it is accumulated on the
 // vector ALUs from the A values each thread stages (A(i, k) * B(k, N - 1)) and
 // reduced at the end, so an odd width such as d_h + 1 needs no extra tile.
-template <typename TA, typename TB, bool PROD, bool XC = false>
+// HILO (bf16 inputs): the fp32 operands staged in LDS are split into bf16
+// hi + lo parts and multiplied on the bf16 matrix cores (32x32x16), as
+// A_hi B_hi + A_lo B_hi + A_hi B_lo with fp32 accumulation: about 16
+// significant bits per operand, at a fraction of the fp32 products' cost.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+template <typename TA, typename TB, bool PROD, bool XC = false, bool HILO = false>
 __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
   constexpr int KT = kKT, NE = 64 * KT / 256;   // elements of each operand per thread and slice
   __shared__ float As[64][KT + 1];   // [i][k]
@@ -195,12 +200,32 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
       fetch(k0 + KT);
       fetch_x(k0 + KT);
     }
+    if constexpr (HILO) {
+      // operand fragments: row (column) l32 of the wave's block at K-slots 8g .. 8g + 7
 #pragma unroll
-    for (int kk = 0; kk < KT; kk += 8)
+      for (int kk = 0; kk < KT; kk += 16) {
+        bf16x8_t ah, al, bh, bl;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[wi + l32][kk + 4 * g + s], Bs[kk + 4 * g + s][wj + l32],
-                                                   acc, 0, 0, 0);
+        for (int e = 0; e < 8; ++e) {
+          const float x = As[wi + l32][kk + 8 * g + e], y = Bs[kk + 8 * g + e][wj + l32];
+          const __bf16 xh = (__bf16)x, yh = (__bf16)y;
+          ah[e] = xh;
+          al[e] = (__bf16)(x - (float)xh);
+          bh[e] = yh;
+          bl[e] = (__bf16)(y - (float)yh);
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KT; kk += 8)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[wi + l32][kk + 4 * g + s], Bs[kk + 4 * g + s][wj + l32],
+                                                     acc, 0, 0, 0);
+    }
     __syncthreads();
   }
   if (PROD && a.rowsum != nullptr && tn == 0) {   // KT lanes share a row
@@ -481,6 +506,7 @@ GOut out(float* p, int64_t sb, int64_t sh, int64_t sc, int64_t si) {
 struct Launcher {
   hipStream_t st;
   int H;
+  bool hilo = false;   // bf16 inputs: products on the bf16 matrix cores (hi/lo parts)
   double flops = 0.0;
   dark_status status = DARK_OK;
 
@@ -529,7 +555,13 @@ struct Launcher {
     const int64_t kt = Ktot > 0 ? (int64_t)Ktot * (batches / NCB) : (int64_t)K * batches;
     flops += 2.0 * M * N * (double)kt;
     KernelTimer tm(kBwdGemm, st);
-    hipLaunchKernelGGL((bgemm_kernel<TA, TB, PROD, XC>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    // the feature exponents and the intra-chunk score gradients (whose sums
+    // cancel exactly where the output does not depend on q and k) keep the
+    // fp32 products
+    if (hilo && epi == kEpiPlain)
+      hipLaunchKernelGGL((bgemm_kernel<TA, TB, PROD, XC, true>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((bgemm_kernel<TA, TB, PROD, XC>), dim3((unsigned)grid), dim3(256), 0, st, a);
     if (hipGetLastError() != hipSuccess) status = DARK_ERR_HIP;
   }
 
@@ -562,6 +594,7 @@ dark_status run_bwd(const dark_prf_desc& d, const BwdPtrs& p, char* ws, hipStrea
   const int64_t hM = d.m_per_head ? (int64_t)r * dh : 0;   // M_h offset per head
   const int64_t hO = d.omega_per_head ? (int64_t)m * r : 0;   // omega_h offset per head
   Launcher ln{st, H};
+  ln.hilo = sizeof(T) == 2;   // bf16 inputs
 
   // per-(b, h) row-major fp32 buffers [BH][Lp][w]: operand and output strides
   auto rows = [&](const float* p, int w) { return op(p, (int64_t)H * Lp * w, (int64_t)Lp * w, (int64_t)C * w, w, 1); };
