@@ -1773,7 +1773,11 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
   const int tid = threadIdx.x;
   const int lane = tid & 63, c = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qb = w & (NB - 1), half = w / NB;
+  // Waves w and w + 4 share a SIMD.  The causal products grow with the query
+  // block (block qb visits qb + 1 key blocks), so the second half takes the
+  // blocks in reverse order and every SIMD gets one block of each weight.
+  const int half = w / NB;
+  const int qb = half == 0 ? (w & (NB - 1)) : NB - 1 - (w & (NB - 1));
   const int lb = xcd_block();
   const int tile = lb % pl.NT2;
   const int bh = lb / pl.NT2;

@@ -392,7 +392,8 @@ def qout8_model(cfg: QoutConfig, mutate=frozenset()):
             op_read(w, fb, k * nm + nm - 1)
 
     def wave(w):
-        qb, half = w % WAVES, w // WAVES
+        half = w // WAVES
+        qb = w % WAVES if half == 0 else WAVES - 1 - w % WAVES   # reversed in the second half
         if m_lds:
             for idx in range(w, mfrg, WAVES8):
                 tr.dma(w, "s_kf", idx * 512 * e)
