@@ -389,8 +389,12 @@ dark_status dark_prf_projection_fix(dark_prf_projection* p, int32_t fixed);
  *   dM    fp32, shaped like M ([H][r][d_h] or [r][d_h], contiguous),
  *         overwritten; a shared M sums over heads; summed over the batch
  *   workspace, ws_bytes: at least dark_prf_bwd_workspace_bytes(desc)
- * Computed in fp32 throughout (fp32 matrix cores); dq, dk and dv are rounded
- * to the input dtype once at the end.  Error codes as for dark_prf_fwd.
+ * Intermediates are fp32.  The products run on the fp32 matrix cores, except
+ * that for bf16 inputs the plain matrix products (not the feature exponents
+ * and not the intra-chunk scores) run on the bf16 matrix cores with each fp32
+ * operand split into a bf16 high part and a bf16 remainder (three products,
+ * about 16 significant bits per operand).  dq, dk and dv are rounded to the
+ * input dtype once at the end.  Error codes as for dark_prf_fwd.
  */
 size_t dark_prf_bwd_workspace_bytes(const dark_prf_desc* desc);
 dark_status dark_prf_bwd(const dark_prf_desc* desc, const void* q, const void* k, const void* v,

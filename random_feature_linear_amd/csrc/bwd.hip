@@ -23,11 +23,14 @@
 //   dV_c = Phi(K_c) Gx_c[:, :d] + tril(Phi(Q_c) Phi(K_c)^T)^T dN_c.
 // Without causality the states are the plain totals and the tril terms vanish.
 //
-// Every product runs through one batched GEMM kernel on the fp32 matrix cores
-// (v_mfma_f32_32x32x2_f32): 64 x 64 output tiles, 32-deep K slices staged
-// through LDS, operands addressed by strides so that transposed operands need
-// no copies.  Features, states and intermediate gradients are fp32 in the
-// workspace.
+// Every product runs through one batched GEMM kernel: 64 x 64 output tiles,
+// 32-deep K slices staged through LDS, operands addressed by strides so that
+// transposed operands need no copies.  Features, states and intermediate
+// gradients are fp32 in the workspace.  The products run on the fp32 matrix
+// cores (v_mfma_f32_32x32x2_f32); for bf16 inputs the plain products (not the
+// feature exponents or the intra-chunk scores) run on the bf16 matrix cores
+// instead, each staged fp32 operand split into a bf16 high part and a bf16
+// remainder and the three products hi*hi + lo*hi + hi*lo summed in fp32.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -705,9 +705,12 @@ __device__ __forceinline__ void load_v(typename FragOf<T>::type* vr, const T* vb
     const int e = tid + p * NT;
     const int tl = e % TT, d8 = ((e / TT) * 8) % DH;   // consecutive lanes: consecutive tokens
     const int t = t0 + tl;
-    // clamped (always valid) address, so that all loads are in flight at once
-    const F x = ld8(vb + (long)min(t, t_end - 1) * vstride + d8);
-    vr[p] = (e < TT * (DH / 8) && t < t_end) ? x : zero_frag<F>();
+    // rows past t_end are zero: a load under the lane mask into a zeroed
+    // register (a select after an unconditional load would make every use of
+    // vr, and the code before it, wait for the load)
+    F x = zero_frag<F>();
+    if (e < TT * (DH / 8) && t < t_end) x = ld8(vb + (long)t * vstride + d8);
+    vr[p] = x;
   }
 }
 // Position of token t in a row of the V^T tile: bits 2 and 3 swapped, so that
@@ -786,8 +789,17 @@ __device__ __forceinline__ float frag_sum(const f32x8& f, float s) {
 // publishes its rank-index fragments and shifts in LDS; then every wave maps
 // its own FBW x 32 features over the whole tile.
 // ---------------------------------------------------------------------------
+// The key side's feature steps run as a software pipeline (see compute_tile)
+// in the unfolded bf16 form with few accumulator and omega' registers; there
+// the kernel is held to two workgroups per compute unit.  (Elsewhere the extra
+// exponent registers cost occupancy or spills.)
+template <typename T, int DH, int R16, int FBW> constexpr bool kstate_pipe() {
+  return sizeof(T) == 2 && !fold_exponent(sizeof(T), DH, R16) &&
+         FBW * vblocks_ones<DH>() * 16 + FBW * R16 * kParts<T> * 4 <= 112;
+}
 template <typename T, int DH, int R16, int FBW, bool PAD>
-__global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
+__global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1)) void kstate_kernel(
+    FwdArgs a, Plan pl, const T* __restrict__ mfrag,
                                                            const T* __restrict__ ofrag, T* __restrict__ sdelta,
                                                            float* __restrict__ zdelta) {
   typedef typename FragOf<T>::type F;
@@ -901,55 +913,71 @@ __global__ __launch_bounds__(kThreads) void kstate_kernel(FwdArgs a, Plan pl, co
                                                      : (valid ? -shift : -INFINITY);
     store_vt<T, DH, TT, VST>(s_vt[buf], vpre, tid);
   };
-  // the products of one tile from buffer buf
+  // the products of one tile from buffer buf, in (token block, feature block)
+  // steps.  Pipelined (kstate_pipe), the exponent products of step s + 1 are
+  // issued before the exp2 of step s, so that the matrix cores work on them
+  // while the vector ALUs take the exponentials.
   auto compute_tile = [&](int buf, const T* of_t) {
-#pragma unroll
-    for (int tb = 0; tb < kWaves; ++tb) {
-      f32x16 ini;
+    constexpr int NS = kWaves * FBW;
+    constexpr bool PIPE = kstate_pipe<T, DH, R16, FBW>();
+    auto exponent_of = [&](int s) -> f32x16 {
+      const int tb = s / FBW, f = s % FBW;
+      f32x16 e;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {   // rows 8 jj + 4g .. 8 jj + 4g + 3 are contiguous
         const float4 x = *reinterpret_cast<const float4*>(&s_init[buf][32 * tb + 8 * jj + 4 * g]);
-        ini[4 * jj] = x.x;
-        ini[4 * jj + 1] = x.y;
-        ini[4 * jj + 2] = x.z;
-        ini[4 * jj + 3] = x.w;
+        e[4 * jj] = x.x;
+        e[4 * jj + 1] = x.y;
+        e[4 * jj + 2] = x.z;
+        e[4 * jj + 3] = x.w;
       }
+      // a block past the last one (last slice only) runs on clamped operands
+      // and is never stored: no branch in the loop
+      const int fb = fb0 + f;
+      const int fbc = min(fb, pl.FB - 1);
       auto uload = [&](int k, int part) -> F { return ld8(&s_u[buf][tb][part ? UP - 1 : 0][k][lane * 8]); };
-      // V (and ones) fragments of the block: held across the feature blocks
-      // when few, else read from LDS at each use
-      constexpr bool VHOLD = DBK <= 4;
-      F vf[VHOLD ? DBK : 1][2];
+      auto oload = [&](int k, int part) -> F {
+        if constexpr (kHoist) return part ? olr[f][k] : ohr[f][k];
+        else return ld8(of_t + (((long)(fbc * UK + k) * NM + (part ? NM - 1 : 0)) * 64 + lane) * 8);
+      };
+      if constexpr (PAD)   // m is not a multiple of 32: features past m give 0
+        if (fb * 32 + c >= a.m) e = splat16(-INFINITY);
+      return exponent_stream<T, UK, true, !FOLD>(uload, oload, e);
+    };
+    // V (and ones) fragments of a token block: held across the feature blocks
+    // when few, else read from LDS at each use
+    constexpr bool VHOLD = DBK <= 4;
+    F vf[VHOLD ? DBK : 1][2];
+    f32x16 en;
+    if constexpr (PIPE) en = exponent_of(0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int tb = s / FBW, f = s % FBW;
+      f32x16 e;
+      if constexpr (PIPE) {
+        e = en;
+        if (s + 1 < NS) en = exponent_of(s + 1);
+      } else {
+        e = exponent_of(s);
+      }
       if constexpr (VHOLD) {
+        if (f == 0) {
 #pragma unroll
-        for (int db = 0; db < DBK; ++db)
+          for (int db = 0; db < DBK; ++db)
 #pragma unroll
-          for (int k = 0; k < 2; ++k) vf[db][k] = v_frag<T, DH, VST, ZMMA>(s_vt[buf], db, 32 * tb, k, c, g);
+            for (int k = 0; k < 2; ++k) vf[db][k] = v_frag<T, DH, VST, ZMMA>(s_vt[buf], db, 32 * tb, k, c, g);
+        }
       }
 #pragma unroll
-      for (int f = 0; f < FBW; ++f) {
-        // a block past the last one (last slice only) runs on clamped operands
-        // and is never stored: no branch in the loop
-        const int fb = fb0 + f;
-        const int fbc = min(fb, pl.FB - 1);
-        auto oload = [&](int k, int part) -> F {
-          if constexpr (kHoist) return part ? olr[f][k] : ohr[f][k];
-          else return ld8(of_t + (((long)(fbc * UK + k) * NM + (part ? NM - 1 : 0)) * 64 + lane) * 8);
-        };
-        f32x16 e = ini;
-        if constexpr (PAD)   // m is not a multiple of 32: features past m give 0
-          if (fb * 32 + c >= a.m) e = splat16(-INFINITY);
-        e = exponent_stream<T, UK, true, !FOLD>(uload, oload, e);
+      for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
+      const F p0 = acc_frag<F>(e, 0), p1 = acc_frag<F>(e, 1);
+      if constexpr (!ZMMA) zacc[f] = frag_sum(p1, frag_sum(p0, zacc[f]));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
-        const F p0 = acc_frag<F>(e, 0), p1 = acc_frag<F>(e, 1);
-        if constexpr (!ZMMA) zacc[f] = frag_sum(p1, frag_sum(p0, zacc[f]));
-#pragma unroll
-        for (int db = 0; db < DBK; ++db) {
-          const F v0 = VHOLD ? vf[VHOLD ? db : 0][0] : v_frag<T, DH, VST, ZMMA>(s_vt[buf], db, 32 * tb, 0, c, g);
-          const F v1 = VHOLD ? vf[VHOLD ? db : 0][1] : v_frag<T, DH, VST, ZMMA>(s_vt[buf], db, 32 * tb, 1, c, g);
-          acc[f][db] = mma(p0, v0, acc[f][db]);
-          acc[f][db] = mma(p1, v1, acc[f][db]);
-        }
+      for (int db = 0; db < DBK; ++db) {
+        const F v0 = VHOLD ? vf[VHOLD ? db : 0][0] : v_frag<T, DH, VST, ZMMA>(s_vt[buf], db, 32 * tb, 0, c, g);
+        const F v1 = VHOLD ? vf[VHOLD ? db : 0][1] : v_frag<T, DH, VST, ZMMA>(s_vt[buf], db, 32 * tb, 1, c, g);
+        acc[f][db] = mma(p0, v0, acc[f][db]);
+        acc[f][db] = mma(p1, v1, acc[f][db]);
       }
     }
   };
