@@ -1398,7 +1398,11 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   // Operands staged in LDS when one step buffer fits beside the V^T tile (else
   // each wave reads them from L2 itself); double buffers (one barrier per
   // feature step) unless LDS is short.
-  constexpr bool STAGE = kBase + kOpStep + kKfStep <= 160 * 1024;
+  // Non-causal with few operands per step (at most 8 slots): no staging and no
+  // barrier per step, each wave reads them from L2 itself (L=64K, 16-rank
+  // geometry: 150 against 155 us; a register prefetch one step ahead, 152).
+  constexpr bool SELF = !CAUSAL && ALLFB == 0 && NSTEP <= 8;
+  constexpr bool STAGE = !SELF && kBase + kOpStep + kKfStep <= 160 * 1024;
   constexpr int OPB = !STAGE ? 0 : kBase + 2 * kOpStep + 2 * kKfStep <= 160 * 1024 ? 2 : 1;
   constexpr int KBUF = kBase + OPB * kOpStep + 2 * kKfStep <= 160 * 1024 ? 2 : 1;
   constexpr int KF_ELEMS = CAUSAL ? KBUF * NB * 2 * 64 * 8 : 8;

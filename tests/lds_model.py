@@ -202,7 +202,10 @@ class QoutConfig:
         k_base = vt_elems * e
         k_op = nstep * 512 * e
         k_kf = nb * 2 * 512 * e if self.causal else 0
-        stage = k_base + k_op + k_kf <= MAX_LDS
+        # non-causal with at most 8 operand slots per step: each wave reads them
+        # from L2 itself, nothing staged
+        self_read = not self.causal and self.allfb == 0 and nstep <= 8
+        stage = not self_read and k_base + k_op + k_kf <= MAX_LDS
         opb = 0 if not stage else (2 if k_base + 2 * k_op + 2 * k_kf <= MAX_LDS else 1)
         kbuf = 2 if k_base + opb * k_op + 2 * k_kf <= MAX_LDS else 1
         kf_elems = kbuf * nb * 2 * 512 if self.causal else 8
