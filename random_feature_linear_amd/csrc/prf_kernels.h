@@ -696,21 +696,41 @@ __device__ __forceinline__ void stage_vt(T* s_vt, const T* vb, int64_t vstride, 
 // The same staging in two halves: global loads into registers (issued a tile
 // ahead of their use) and the transposed LDS stores.
 template <int DH, int TT, int NT = kThreads> constexpr int vloads_per_thread() { return (TT * (DH / 8) + NT - 1) / NT; }
+// Thread tid takes token tid % TT of the tile and the 8-column pieces
+// 8 (tid / TT) + p VSTEP, p = 0 .. VPT - 1 (consecutive lanes: consecutive
+// tokens); when the thread count is a multiple of TT every piece of a thread
+// is one token row, at offsets fixed at compile time.
+template <int DH, int TT, int NT> constexpr int vstep() { return NT / TT * 8; }
+template <int DH, int TT, int NT> constexpr bool vpieces_in_range() {   // no piece past column DH
+  return NT % TT == 0 && (vloads_per_thread<DH, TT, NT>() - 1) * vstep<DH, TT, NT>() + (NT / TT - 1) * 8 < DH;
+}
 template <typename T, int DH, int TT, int NT = kThreads>
 __device__ __forceinline__ void load_v(typename FragOf<T>::type* vr, const T* vb, int64_t vstride, int t0, int t_end,
                                        int tid) {
   typedef typename FragOf<T>::type F;
+  constexpr int VPT = vloads_per_thread<DH, TT, NT>();
+  // rows past t_end are zero: loads under the lane mask into zeroed registers
+  // (a select after an unconditional load would make every use of vr, and the
+  // code before it, wait for the load)
+  if constexpr (vpieces_in_range<DH, TT, NT>()) {
+    const int t = t0 + tid % TT;
+    const T* row = vb + (long)t * vstride + (tid / TT) * 8;
 #pragma unroll
-  for (int p = 0; p < vloads_per_thread<DH, TT, NT>(); ++p) {
-    const int e = tid + p * NT;
-    const int tl = e % TT, d8 = ((e / TT) * 8) % DH;   // consecutive lanes: consecutive tokens
-    const int t = t0 + tl;
-    // rows past t_end are zero: a load under the lane mask into a zeroed
-    // register (a select after an unconditional load would make every use of
-    // vr, and the code before it, wait for the load)
-    F x = zero_frag<F>();
-    if (e < TT * (DH / 8) && t < t_end) x = ld8(vb + (long)t * vstride + d8);
-    vr[p] = x;
+    for (int p = 0; p < VPT; ++p) vr[p] = zero_frag<F>();
+    if (t < t_end) {
+#pragma unroll
+      for (int p = 0; p < VPT; ++p) vr[p] = ld8(row + p * vstep<DH, TT, NT>());
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < VPT; ++p) {
+      const int e = tid + p * NT;
+      const int tl = e % TT, d8 = (e / TT) * 8;
+      const int t = t0 + tl;
+      F x = zero_frag<F>();
+      if (e < TT * (DH / 8) && t < t_end) x = ld8(vb + (long)t * vstride + d8);
+      vr[p] = x;
+    }
   }
 }
 // Position of token t in a row of the V^T tile: bits 2 and 3 swapped, so that
@@ -719,13 +739,22 @@ __device__ __forceinline__ void load_v(typename FragOf<T>::type* vr, const T* vb
 __device__ __forceinline__ int vt_pos(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
 template <typename T, int DH, int TT, int VST, int NT = kThreads>
 __device__ __forceinline__ void store_vt(T* s_vt, const typename FragOf<T>::type* vr, int tid) {
+  constexpr int VPT = vloads_per_thread<DH, TT, NT>();
+  if constexpr (vpieces_in_range<DH, TT, NT>()) {
+    T* dst = s_vt + (tid / TT) * 8 * VST + vt_pos(tid % TT);
 #pragma unroll
-  for (int p = 0; p < vloads_per_thread<DH, TT, NT>(); ++p) {
-    const int e = tid + p * NT;
-    if (e >= TT * (DH / 8)) break;
-    const int tl = e % TT, d8 = (e / TT) * 8;
+    for (int p = 0; p < VPT; ++p)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s_vt[(d8 + i) * VST + vt_pos(tl)] = vr[p][i];
+      for (int i = 0; i < 8; ++i) dst[(p * vstep<DH, TT, NT>() + i) * VST] = vr[p][i];
+  } else {
+#pragma unroll
+    for (int p = 0; p < VPT; ++p) {
+      const int e = tid + p * NT;
+      if (e >= TT * (DH / 8)) break;
+      const int tl = e % TT, d8 = (e / TT) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s_vt[(d8 + i) * VST + vt_pos(tl)] = vr[p][i];
+    }
   }
 }
 
