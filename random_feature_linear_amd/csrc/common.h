@@ -55,6 +55,7 @@ struct Plan {
   int NU;      // units per (b, h)
   int FBW;     // 32-feature blocks per wave
   int NF;      // feature slices per unit (each slice = 4 waves * FBW blocks)
+  int UPW;     // consecutive units per key-side workgroup (tiled kernel; states stored unit by unit)
   // query-side output kernel
   int NQB;     // 32-token query blocks per wave
   int tile2;   // queries per workgroup (4 waves * 32 * NQB); equals span1 when causal

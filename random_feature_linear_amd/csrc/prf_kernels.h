@@ -857,10 +857,12 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
+  // workgroup: feature slice fslice of units u0 .. u0 + UPW - 1 of (b, h)
   const int lb = xcd_block();
+  const int NUG = (pl.NU + pl.UPW - 1) / pl.UPW;
   const int fslice = lb % pl.NF;
-  const int unit = (lb / pl.NF) % pl.NU;
-  const int bh = lb / (pl.NF * pl.NU);
+  const int u0 = ((lb / pl.NF) % NUG) * pl.UPW;
+  const int bh = lb / (pl.NF * NUG);
   const int b = bh / a.H, h = bh % a.H;
   const int hk = (h * a.H_kv) / a.H;
   const T* kbase = reinterpret_cast<const T*>(a.k) + b * a.ks[0] + hk * a.ks[1];
@@ -870,8 +872,8 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
   // omega' of this head's projection (or the shared one), or W' of its folded operand
   const T* of = ofrag + (long)((FOLD ? pl.HW : pl.HO) > 1 ? h : 0) * pl.FB * UK * NM * 64 * 8;
   const float half_log2m = 0.5f * log2f((float)a.m);
-  const int t_begin = unit * pl.span1;
-  const int t_end = min(a.L, t_begin + pl.span1);
+  const int t_begin = u0 * pl.span1;   // the tiles of all the workgroup's units, in order
+  const int t_end = min(a.L, min(u0 + pl.UPW, pl.NU) * pl.span1);
   const int fb0 = (fslice * kWaves + w) * FBW;     // first 32-feature block of this wave
 
   f32x16 acc[FBW][DBK];
@@ -1017,6 +1019,44 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
     if (hide) asm volatile("" : "+s"(p));
     return p;
   };
+  // ---- write this wave's part of the unit state (the accumulators are then
+  // cleared for the workgroup's next unit) ----
+  auto store_unit = [&](int unit) {
+    const long FK = 2L * pl.FB;     // 16-feature fragments per d-block
+    T* sd = sdelta + ((long)bh * pl.NU + unit) * DB * FK * 64 * 8;
+    float* zd = zdelta + ((long)bh * pl.NU + unit) * pl.FB * 32;
+#pragma unroll
+    for (int f = 0; f < FBW; ++f) {
+      const int fb = fb0 + f;
+      if (fb < pl.FB) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+            st8_state(sd + ((db * FK + 2 * fb + k) * 64 + lane) * 8, acc_frag<F>(acc[f][db], k), pl.stream_states);
+        if constexpr (ZMMA) {   // column d_h: lane d_h % 32 of each half holds rows crow(i, g)
+          if (c == DH % 32) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) zd[fb * 32 + crow(i, g)] = acc[f][DBK - 1][i];
+          }
+        } else {
+          const float z = zacc[f] + __shfl_xor(zacc[f], 32);   // the two token halves
+          if (g == 0) zd[fb * 32 + c] = z;
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DBK; ++db) acc[f][db] = zero16();
+      zacc[f] = 0.f;
+    }
+  };
+  // after the tile at t0: the unit ends there (units are whole tiles).  Only
+  // the folded form takes several units per workgroup (the plan keeps one
+  // otherwise); the others store their one unit after the loop, which keeps
+  // the store's registers out of the loop.
+  auto flush = [&](int t0) {
+    if constexpr (FOLD)
+      if (t0 + TT >= t_end || (t0 + TT - t_begin) % pl.span1 == 0) store_unit(u0 + (t0 - t_begin) / pl.span1);
+  };
   if constexpr (NBUF == 2) {
     prefetch(t_begin);
     stage_m();
@@ -1032,6 +1072,7 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
       if (more) prefetch(t0 + TT);
       compute_tile(it & 1, of_t);
       if (more) project_tile(t0 + TT, (it + 1) & 1, msrc_t);
+      flush(t0);
       __syncthreads();
     }
   } else {
@@ -1048,34 +1089,13 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
       if constexpr (PREF)
         if (t0 + TT < t_end) prefetch(t0 + TT);
       compute_tile(0, of_t);
+      flush(t0);
       __syncthreads();
     }
   }
-
-  // ---- write this wave's part of the unit state ----
-  const long FK = 2L * pl.FB;     // 16-feature fragments per d-block
-  T* sd = sdelta + ((long)bh * pl.NU + unit) * DB * FK * 64 * 8;
-  float* zd = zdelta + ((long)bh * pl.NU + unit) * pl.FB * 32;
-#pragma unroll
-  for (int f = 0; f < FBW; ++f) {
-    const int fb = fb0 + f;
-    if (fb >= pl.FB) continue;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        st8_state(sd + ((db * FK + 2 * fb + k) * 64 + lane) * 8, acc_frag<F>(acc[f][db], k), pl.stream_states);
-    if constexpr (ZMMA) {   // column d_h: lane d_h % 32 of each half holds rows crow(i, g)
-      if (c == DH % 32) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) zd[fb * 32 + crow(i, g)] = acc[f][DBK - 1][i];
-      }
-    } else {
-      const float z = zacc[f] + __shfl_xor(zacc[f], 32);   // the two token halves
-      if (g == 0) zd[fb * 32 + c] = z;
-    }
-  }
+  if constexpr (!FOLD) store_unit(u0);
 }
+
 
 // ---------------------------------------------------------------------------
 // Key side for large ranks (the u fragments of a whole tile do not fit in LDS):
@@ -2153,8 +2173,8 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
     static_assert(!fold_exponent(sizeof(T), DH, R16) || kstate_tile_lds_bytes<T, DH, R16>() <= kMaxLds,
                   "the folded key side runs on the tiled kernel");
     if constexpr (kstate_tile_lds_bytes<T, DH, R16>() <= kMaxLds)
-      hipLaunchKernelGGL((kstate_kernel<T, DH, R16, FBW, PAD>), grid1, dim3(kThreads), 0, st, a, pl, mfrag, ofrag,
-                         sdelta, zdelta);
+      hipLaunchKernelGGL((kstate_kernel<T, DH, R16, FBW, PAD>), dim3(pl.BH * ((pl.NU + pl.UPW - 1) / pl.UPW) * pl.NF),
+                         dim3(kThreads), 0, st, a, pl, mfrag, ofrag, sdelta, zdelta);
     else
       hipLaunchKernelGGL((kstate_seq_kernel<T, DH, R16, FBW, PAD>), grid1, dim3(kThreads), 0, st, a, pl, mfrag,
                          ofrag, sdelta, zdelta);
