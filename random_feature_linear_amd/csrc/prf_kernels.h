@@ -475,14 +475,17 @@ __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Folded operand W'_hm = omega' M'_hm (m x d_h) for the bf16 path, with fp32
-// matrix products (32x32x2) so that the hi/lo split sees the exact product.
-// Workgroup: 4 waves, one 32-feature block and up to four 32-column tiles (one
-// per wave).  The rank index runs in chunks of 64: the chunk's M columns and
-// omega rows are fetched into registers one chunk ahead (all loads of a chunk
-// in flight together) and staged in LDS.  Each wave's transposed tile
-// W'^T = M'^T omega'^T (features in the lane index) goes back through LDS to
-// the fragment order of prep_kernel's folded layout.
+// Folded operand W'_hm = omega' M'_hm (m x d_h) for the bf16 path.  The
+// products run on the bf16 matrix cores with each fp32 operand split into a
+// bf16 high part and a bf16 remainder (hi hi + lo hi + hi lo, about 16
+// significant bits per operand), so that W' is as exact as its own hi/lo
+// parts.  Workgroup: 4 waves, one 32-feature block and up to four 32-column
+// tiles (one per wave).  The rank index runs in chunks of 64: the chunk's M
+// columns and omega rows are fetched into registers one chunk ahead (all loads
+// of a chunk in flight together), split, and staged in LDS as bf16 parts.
+// Each wave's transposed tile W'^T = M'^T omega'^T (features in the lane
+// index) goes back through LDS to the fragment order of prep_kernel's folded
+// layout.
 // ---------------------------------------------------------------------------
 constexpr int kFoldRC = 64;   // rank indices per chunk
 template <typename T>
@@ -500,8 +503,11 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict_
       return;
     }
   }
-  __shared__ float s_m[kFoldRC][4 * 32 + 1];   // M[a][col], 128 columns of the group
-  __shared__ float s_o[32][kFoldRC + 1];       // omega[32 fb + row][a]
+  constexpr int MST = 4 * 32 + 8;   // row stride of the M parts (bf16)
+  constexpr int OST = kFoldRC + 8;  // row stride of the omega parts (bf16; 16-byte aligned rows)
+  __shared__ float s_m[32][4 * 32 + 1];                                  // transpose buffer of the result
+  __shared__ __attribute__((aligned(16))) bf16 s_mp[2][kFoldRC][MST];   // M[a][col] hi / lo, 128 columns
+  __shared__ __attribute__((aligned(16))) bf16 s_op[2][32][OST];        // omega[32 fb + row][a] hi / lo
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
   const int DT = d_h / 32;
   const int NG = (DT + 3) / 4;                 // groups of four column tiles
@@ -538,6 +544,21 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict_
                           okr && a + 3 < r ? x.w : 0.f);
     }
   };
+  // four values as bf16 high parts and remainders at dst_hi / dst_lo
+  auto split4 = [](const float4& x, bf16* dst_hi, bf16* dst_lo) {
+    typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 h, l;
+    h[0] = (bf16)x.x;
+    h[1] = (bf16)x.y;
+    h[2] = (bf16)x.z;
+    h[3] = (bf16)x.w;
+    l[0] = (bf16)(x.x - (float)h[0]);
+    l[1] = (bf16)(x.y - (float)h[1]);
+    l[2] = (bf16)(x.z - (float)h[2]);
+    l[3] = (bf16)(x.w - (float)h[3]);
+    *reinterpret_cast<bf16x4*>(dst_hi) = h;
+    *reinterpret_cast<bf16x4*>(dst_lo) = l;
+  };
   f32x16 acc = zero16();
   fetch(0);
   for (int a0 = 0; a0 < r; a0 += kFoldRC) {
@@ -545,24 +566,31 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict_
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int e = tid + p * kThreads, row = e >> 5, cc = 4 * (e & 31);
-      s_m[row][cc] = vm[p].x;
-      s_m[row][cc + 1] = vm[p].y;
-      s_m[row][cc + 2] = vm[p].z;
-      s_m[row][cc + 3] = vm[p].w;
+      split4(vm[p], &s_mp[0][row][cc], &s_mp[1][row][cc]);
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int e = tid + p * kThreads, row = e >> 4, a = 4 * (e & 15);
-      s_o[row][a] = vo[p].x;
-      s_o[row][a + 1] = vo[p].y;
-      s_o[row][a + 2] = vo[p].z;
-      s_o[row][a + 3] = vo[p].w;
+      split4(vo[p], &s_op[0][row][a], &s_op[1][row][a]);
     }
     __syncthreads();
     if (a0 + kFoldRC < r) fetch(a0 + kFoldRC);
-#pragma unroll 8
-    for (int k = 0; k < kFoldRC; k += 2)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(s_m[k + g][32 * w + c], s_o[c][k + g], acc, 0, 0, 0);
+    // K-step ks: A = M'^T (row = column 32 w + c of the group, rank 16 ks + 8 g + e),
+    // B = omega'^T (column = feature c, the same ranks)
+#pragma unroll
+    for (int ks = 0; ks < kFoldRC / 16; ++ks) {
+      bf16x8 ah, al;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ah[e] = s_mp[0][16 * ks + 8 * g + e][32 * w + c];
+        al[e] = s_mp[1][16 * ks + 8 * g + e][32 * w + c];
+      }
+      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&s_op[0][c][16 * ks + 8 * g]);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&s_op[1][c][16 * ks + 8 * g]);
+      acc = mma(ah, bh, acc);
+      acc = mma(al, bh, acc);
+      acc = mma(ah, bl, acc);
+    }
   }
   __syncthreads();
   // acc[i]: W'^T[column 32 w + 8(i/4) + 4g + i%4 of the group][feature c]; s_m is the transpose buffer
