@@ -810,6 +810,58 @@ __device__ __forceinline__ typename FragOf<T>::type v_frag(const T* s_vt, int db
   }
   return ld8(s_vt + d * VST + tb0 + 16 * k + 8 * g);   // tokens in vt_pos order
 }
+// bf16: V staged in its own row layout, s_v[t][d] with rows DH + 8 elements
+// apart (16-byte aligned; eight consecutive rows then fall on distinct 16-byte
+// bank groups), written as 16-byte pieces and read into operand fragments by
+// the LDS transpose loads (ds_read_b64_tr_b16).  Within each group of 16 lanes
+// such a load returns to lane 4a + b the b-th 16-bit element of the 8-byte
+// pieces addressed by lanes a, a + 4, a + 8 and a + 12 of the group.  So lanes
+// 16q + x address row tb0 + 16k + 4g + x / 4 (+ 8 for the second load),
+// columns 32 db + 16 (q % 2) + 4 (x % 4) .. + 3, and lane l receives column
+// 32 db + l % 32 at tokens tb0 + 16k + 8 (e / 4) + 4g + e % 4: the operand
+// order of the feature products.
+template <int DH> constexpr int vsn() { return DH + 8; }
+template <typename T, int DH, int TT, int NT = kThreads>
+__device__ __forceinline__ void store_v(T* s_v, const typename FragOf<T>::type* vr, int tid) {
+  static_assert(sizeof(T) == 2 && vpieces_in_range<DH, TT, NT>(), "bf16 row pieces");
+  T* dst = s_v + (tid % TT) * vsn<DH>() + (tid / TT) * 8;
+#pragma unroll
+  for (int p = 0; p < vloads_per_thread<DH, TT, NT>(); ++p)
+    *reinterpret_cast<typename FragOf<T>::type*>(dst + p * vstep<DH, TT, NT>()) = vr[p];
+}
+template <int DH, bool ONES = false>
+__device__ __forceinline__ bf16x8 v_frag_tr(const bf16* s_v, int db, int tb0, int k, int lane) {
+  const int c = lane & 31;
+  const int d = db * 32 + c;
+  if ((ONES || DH % 32 != 0) && db * 32 >= DH) {   // the whole block past the columns of V
+    const float o = ONES && d == DH ? 1.0f : 0.0f;
+    float v[8] = {o, o, o, o, o, o, o, o};
+    bf16x8 f;
+    make_frag(f, v);
+    return f;
+  }
+  const int x = lane & 15, q = lane >> 4, g = lane >> 5;
+  const int row = tb0 + 16 * k + 4 * g + (x >> 2);
+  const int col = min(db * 32 + 16 * (q & 1) + 4 * (x & 3), DH - 4);   // groups past DH: any valid address
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const bf16* p0 = s_v + row * vsn<DH>() + col;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(__attribute__((address_space(3))) bf16*)p0);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)(__attribute__((address_space(3))) bf16*)(p0 + 8 * vsn<DH>()));
+  typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x8 f = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4,
+                                     5, 6, 7);
+  if constexpr (ONES || DH % 32 != 0) {   // columns past DH in a partly filled block
+    if (d >= DH) {
+      const float o = ONES && d == DH ? 1.0f : 0.0f;
+      float v[8] = {o, o, o, o, o, o, o, o};
+      make_frag(f, v);
+    }
+  }
+  return f;
+}
+
 // 32-column blocks of V (of the state S).  The normaliser z (the sums of the
 // features) is kept apart in fp32: the key side takes it from a column of
 // ones beside V on the matrix cores, or sums the rounded features on the
@@ -876,11 +928,14 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
   constexpr int VPT = vloads_per_thread<DH, TT>();
   // Double-buffered tile state (one barrier per tile; the next tile is
   // projected right behind the current tile's products) when it fits.
-  constexpr size_t kTileState = (size_t)(kWaves * UP * UK * 64 * 8 + DH * VST) * sizeof(T) + TT * sizeof(float);
+  // bf16: V in its row layout (transpose loads); fp32: V^T
+  constexpr bool VTR = sizeof(T) == 2;
+  constexpr int V_ELEMS = VTR ? TT * vsn<DH>() : DH * VST;
+  constexpr size_t kTileState = (size_t)(kWaves * UP * UK * 64 * 8 + V_ELEMS) * sizeof(T) + TT * sizeof(float);
   constexpr int NBUF = 2 * kTileState + (M_LDS ? MFR * 64 * 8 * sizeof(T) : 0) <= 160 * 1024 ? 2 : 1;
   __shared__ __attribute__((aligned(16))) T s_u[NBUF][kWaves][UP][UK][64 * 8];
   __shared__ __attribute__((aligned(16))) float s_init[NBUF][TT];
-  __shared__ __attribute__((aligned(16))) T s_vt[NBUF][DH * VST];
+  __shared__ __attribute__((aligned(16))) T s_vt[NBUF][V_ELEMS];
   __shared__ __attribute__((aligned(16))) T s_m[M_LDS ? MFR * 64 * 8 : 8];
 
   const int tid = threadIdx.x;
@@ -970,7 +1025,12 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
     if (g == 0)
       s_init[buf][32 * w + c] = (FOLD && pl.kshift) ? (ok ? a.kshift[(long)bh * a.L + t] : -INFINITY)
                                                      : (valid ? -shift : -INFINITY);
-    store_vt<T, DH, TT, VST>(s_vt[buf], vpre, tid);
+    if constexpr (VTR) store_v<T, DH, TT>(s_vt[buf], vpre, tid);
+    else store_vt<T, DH, TT, VST>(s_vt[buf], vpre, tid);
+  };
+  auto vfrag = [&](int buf, int db, int tb0, int k) -> F {
+    if constexpr (VTR) return v_frag_tr<DH, ZMMA>(s_vt[buf], db, tb0, k, lane);
+    else return v_frag<T, DH, VST, ZMMA>(s_vt[buf], db, tb0, k, c, g);
   };
   // the products of one tile from buffer buf, in (token block, feature block)
   // steps.  Pipelined (kstate_pipe), the exponent products of step s + 1 are
@@ -1024,7 +1084,7 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
 #pragma unroll
           for (int db = 0; db < DBK; ++db)
 #pragma unroll
-            for (int k = 0; k < 2; ++k) vf[db][k] = v_frag<T, DH, VST, ZMMA>(s_vt[buf], db, 32 * tb, k, c, g);
+            for (int k = 0; k < 2; ++k) vf[db][k] = vfrag(buf, db, 32 * tb, k);
         }
       }
 #pragma unroll
@@ -1033,8 +1093,8 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
       if constexpr (!ZMMA) zacc[f] = frag_sum(p1, frag_sum(p0, zacc[f]));
 #pragma unroll
       for (int db = 0; db < DBK; ++db) {
-        const F v0 = VHOLD ? vf[VHOLD ? db : 0][0] : v_frag<T, DH, VST, ZMMA>(s_vt[buf], db, 32 * tb, 0, c, g);
-        const F v1 = VHOLD ? vf[VHOLD ? db : 0][1] : v_frag<T, DH, VST, ZMMA>(s_vt[buf], db, 32 * tb, 1, c, g);
+        const F v0 = VHOLD ? vf[VHOLD ? db : 0][0] : vfrag(buf, db, 32 * tb, 0);
+        const F v1 = VHOLD ? vf[VHOLD ? db : 0][1] : vfrag(buf, db, 32 * tb, 1);
         acc[f][db] = mma(p0, v0, acc[f][db]);
         acc[f][db] = mma(p1, v1, acc[f][db]);
       }
@@ -2141,7 +2201,8 @@ template <typename T, int DH, int R16> constexpr size_t kstate_tile_lds_bytes() 
   constexpr int UK = FOLD ? DH / 16 : R16;
   constexpr int UP = FOLD ? 1 : kParts<T>;
   constexpr size_t mbytes = (size_t)((R16 + 1) / 2) * (DH / 16) * kParts<T> * 64 * 8 * sizeof(T);
-  return (size_t)(kWaves * UP * UK * 64 * 8 + DH * (kTile + 8)) * sizeof(T) + kTile * sizeof(float) +
+  constexpr size_t v_elems = sizeof(T) == 2 ? (size_t)kTile * vsn<DH>() : (size_t)DH * (kTile + 8);
+  return (size_t)(kWaves * UP * UK * 64 * 8 + v_elems) * sizeof(T) + kTile * sizeof(float) +
          (mbytes <= 32 * 1024 ? mbytes : 16);
 }
 // Least LDS of the causal query-side kernel: the V^T tile and one key-feature

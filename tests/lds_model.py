@@ -165,6 +165,29 @@ def store_vt(tr, w, name, base, dh, tt, vst, elem, nt=256):
             tr.write(w, name, (base + (d8 + i) * vst + pos) * elem, elem)
 
 
+def store_v(tr, w, name, base, dh, tt, elem, nt=256):
+    """store_v (bf16): token row tid % TT, 16-byte pieces at columns 8 (tid / TT) + p (nt / TT) 8,
+    in s_v[t][d] with rows dh + 8 elements apart."""
+    vsn, step = dh + 8, nt // tt * 8
+    tid = 64 * w + LANES
+    for p in range(vloads_per_thread(dh, tt, nt)):
+        col = (tid // tt) * 8 + p * step
+        assert np.all(col < dh)   # the kernel asserts every piece is inside the row
+        tr.write(w, name, (base + (tid % tt) * vsn + col) * elem, 16)
+
+
+def v_frag_read_tr(tr, w, name, base, dh, db, tb0, k, elem, ones=False):
+    """v_frag_tr (bf16): two transpose loads; each lane reads 8 bytes at its own address."""
+    if (ones or dh % 32 != 0) and db * 32 >= dh:
+        return
+    vsn = dh + 8
+    x, q = LANES & 15, LANES >> 4
+    row = tb0 + 16 * k + 4 * G + (x >> 2)
+    col = np.minimum(db * 32 + 16 * (q & 1) + 4 * (x & 3), dh - 4)
+    for half in range(2):
+        tr.read(w, name, (base + (row + 8 * half) * vsn + col) * elem, 8)
+
+
 def v_frag_read(tr, w, name, base, dh, vst, db, tb0, k, elem, ones=False):
     d = db * 32 + C
     ok = ~(((ones or dh % 32 != 0)) & (d >= dh))
@@ -510,10 +533,12 @@ class KstateConfig:
         dbk = vblocks_ones(dh) if zmma else vblocks(dh)
         mfr = ((self.r16 + 1) // 2) * kd * nm
         m_lds = mfr * 512 * e <= 32 * 1024
-        tile_state = (WAVES * up * uk * 512 + dh * vst) * e + tt * 4
+        vtr = e == 2                    # bf16: V in its row layout, read by transpose loads
+        v_elems = tt * (dh + 8) if vtr else dh * vst
+        tile_state = (WAVES * up * uk * 512 + v_elems) * e + tt * 4
         nbuf = 2 if 2 * tile_state + (mfr * 512 * e if m_lds else 0) <= MAX_LDS else 1
         return dict(kd=kd, nm=nm, tt=tt, vst=vst, fold=fold, uk=uk, up=up, zmma=zmma, dbk=dbk, mfr=mfr,
-                    m_lds=m_lds, nbuf=nbuf, r32=(self.r16 + 1) // 2, vhold=dbk <= 4)
+                    m_lds=m_lds, nbuf=nbuf, r32=(self.r16 + 1) // 2, vhold=dbk <= 4, vtr=vtr, v_elems=v_elems)
 
 
 def kstate_tile_lds_bytes(elem, dh, r16):
@@ -521,7 +546,8 @@ def kstate_tile_lds_bytes(elem, dh, r16):
     uk = dh // 16 if fold else r16
     up = 1 if fold else (2 if elem == 2 else 1)
     mbytes = ((r16 + 1) // 2) * (dh // 16) * (2 if elem == 2 else 1) * 512 * elem
-    return (WAVES * up * uk * 512 + dh * 136) * elem + 128 * 4 + (mbytes if mbytes <= 32 * 1024 else 16)
+    v_elems = 128 * (dh + 8) if elem == 2 else dh * 136
+    return (WAVES * up * uk * 512 + v_elems) * elem + 128 * 4 + (mbytes if mbytes <= 32 * 1024 else 16)
 
 
 def kstate_model(cfg: KstateConfig, mutate=frozenset()):
@@ -529,7 +555,7 @@ def kstate_model(cfg: KstateConfig, mutate=frozenset()):
     e = cfg.elem
     nb, up, uk = D["nbuf"], D["up"], D["uk"]
     u_slot = lambda buf, w, part, k: ((((buf * WAVES + w) * up + part) * uk + k) * 512)  # noqa: E731
-    sizes = {"s_u": nb * WAVES * up * uk * 512 * e, "s_init": nb * 128 * 4, "s_vt": nb * cfg.dh * D["vst"] * e,
+    sizes = {"s_u": nb * WAVES * up * uk * 512 * e, "s_init": nb * 128 * 4, "s_vt": nb * D["v_elems"] * e,
              "s_m": (D["mfr"] * 512 if D["m_lds"] else 8) * e}
     if sum(sizes.values()) > MAX_LDS:
         raise Violation(f"LDS {sum(sizes.values())} bytes > {MAX_LDS}")
@@ -550,7 +576,16 @@ def kstate_model(cfg: KstateConfig, mutate=frozenset()):
                 if D["nm"] == 2:
                     tr.write(w, "s_u", frag_lanes(u_slot(buf, w, D["nm"] - 1, k), e), 8 * e)
         tr.write(w, "s_init", (buf * 128 + 32 * w + C[G == 0]) * 4, 4)
-        store_vt(tr, w, "s_vt", buf * cfg.dh * D["vst"], cfg.dh, 128, D["vst"], e)
+        if D["vtr"]:
+            store_v(tr, w, "s_vt", buf * D["v_elems"], cfg.dh, 128, e)
+        else:
+            store_vt(tr, w, "s_vt", buf * cfg.dh * D["vst"], cfg.dh, 128, D["vst"], e)
+
+    def vread(w, buf, db, tb0, k):
+        if D["vtr"]:
+            v_frag_read_tr(tr, w, "s_vt", buf * D["v_elems"], cfg.dh, db, tb0, k, e, ones=D["zmma"])
+        else:
+            v_frag_read(tr, w, "s_vt", buf * cfg.dh * D["vst"], cfg.dh, D["vst"], db, tb0, k, e, ones=D["zmma"])
 
     def compute_tile(w, buf):
         for tb in range(WAVES):
@@ -559,8 +594,7 @@ def kstate_model(cfg: KstateConfig, mutate=frozenset()):
             if D["vhold"]:
                 for db in range(D["dbk"]):
                     for k in range(2):
-                        v_frag_read(tr, w, "s_vt", buf * cfg.dh * D["vst"], cfg.dh, D["vst"], db, 32 * tb, k, e,
-                                    ones=D["zmma"])
+                        vread(w, buf, db, 32 * tb, k)
             for _f in range(cfg.fbw):
                 for k in range(uk):
                     tr.read(w, "s_u", frag_lanes(u_slot(buf, tb, 0, k), e), 8 * e)
@@ -569,8 +603,7 @@ def kstate_model(cfg: KstateConfig, mutate=frozenset()):
                 if not D["vhold"]:
                     for db in range(D["dbk"]):
                         for k in range(2):
-                            v_frag_read(tr, w, "s_vt", buf * cfg.dh * D["vst"], cfg.dh, D["vst"], db, 32 * tb, k, e,
-                                        ones=D["zmma"])
+                            vread(w, buf, db, 32 * tb, k)
 
     def wave(w):
         if D["m_lds"]:   # M' by the DMA path, 1 KB per wave instruction, then vmcnt(0)
