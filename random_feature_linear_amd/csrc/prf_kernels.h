@@ -810,9 +810,10 @@ __device__ __forceinline__ typename FragOf<T>::type v_frag(const T* s_vt, int db
   }
   return ld8(s_vt + d * VST + tb0 + 16 * k + 8 * g);   // tokens in vt_pos order
 }
-// bf16: V staged in its own row layout, s_v[t][d] with rows DH + 8 elements
-// apart (16-byte aligned; eight consecutive rows then fall on distinct 16-byte
-// bank groups), written as 16-byte pieces and read into operand fragments by
+// bf16: V staged in its own row layout, s_v[t][d] with rows DH + 16 elements
+// apart (16-byte aligned; the eight rows of 64 bytes one transpose load reads
+// then cover every 16-byte bank group of a 256-byte bank row exactly twice),
+// written as 16-byte pieces and read into operand fragments by
 // the LDS transpose loads (ds_read_b64_tr_b16).  Within each group of 16 lanes
 // such a load returns to lane 4a + b the b-th 16-bit element of the 8-byte
 // pieces addressed by lanes a, a + 4, a + 8 and a + 12 of the group.  So lanes
@@ -820,7 +821,7 @@ __device__ __forceinline__ typename FragOf<T>::type v_frag(const T* s_vt, int db
 // columns 32 db + 16 (q % 2) + 4 (x % 4) .. + 3, and lane l receives column
 // 32 db + l % 32 at tokens tb0 + 16k + 8 (e / 4) + 4g + e % 4: the operand
 // order of the feature products.
-template <int DH> constexpr int vsn() { return DH + 8; }
+template <int DH> constexpr int vsn() { return DH + 16; }
 template <typename T, int DH, int TT, int NT = kThreads>
 __device__ __forceinline__ void store_v(T* s_v, const typename FragOf<T>::type* vr, int tid) {
   static_assert(sizeof(T) == 2 && vpieces_in_range<DH, TT, NT>(), "bf16 row pieces");

@@ -167,8 +167,8 @@ def store_vt(tr, w, name, base, dh, tt, vst, elem, nt=256):
 
 def store_v(tr, w, name, base, dh, tt, elem, nt=256):
     """store_v (bf16): token row tid % TT, 16-byte pieces at columns 8 (tid / TT) + p (nt / TT) 8,
-    in s_v[t][d] with rows dh + 8 elements apart."""
-    vsn, step = dh + 8, nt // tt * 8
+    in s_v[t][d] with rows dh + 16 elements apart."""
+    vsn, step = dh + 16, nt // tt * 8
     tid = 64 * w + LANES
     for p in range(vloads_per_thread(dh, tt, nt)):
         col = (tid // tt) * 8 + p * step
@@ -180,7 +180,7 @@ def v_frag_read_tr(tr, w, name, base, dh, db, tb0, k, elem, ones=False):
     """v_frag_tr (bf16): two transpose loads; each lane reads 8 bytes at its own address."""
     if (ones or dh % 32 != 0) and db * 32 >= dh:
         return
-    vsn = dh + 8
+    vsn = dh + 16
     x, q = LANES & 15, LANES >> 4
     row = tb0 + 16 * k + 4 * G + (x >> 2)
     col = np.minimum(db * 32 + 16 * (q & 1) + 4 * (x & 3), dh - 4)
@@ -534,7 +534,7 @@ class KstateConfig:
         mfr = ((self.r16 + 1) // 2) * kd * nm
         m_lds = mfr * 512 * e <= 32 * 1024
         vtr = e == 2                    # bf16: V in its row layout, read by transpose loads
-        v_elems = tt * (dh + 8) if vtr else dh * vst
+        v_elems = tt * (dh + 16) if vtr else dh * vst
         tile_state = (WAVES * up * uk * 512 + v_elems) * e + tt * 4
         nbuf = 2 if 2 * tile_state + (mfr * 512 * e if m_lds else 0) <= MAX_LDS else 1
         return dict(kd=kd, nm=nm, tt=tt, vst=vst, fold=fold, uk=uk, up=up, zmma=zmma, dbk=dbk, mfr=mfr,
@@ -546,7 +546,7 @@ def kstate_tile_lds_bytes(elem, dh, r16):
     uk = dh // 16 if fold else r16
     up = 1 if fold else (2 if elem == 2 else 1)
     mbytes = ((r16 + 1) // 2) * (dh // 16) * (2 if elem == 2 else 1) * 512 * elem
-    v_elems = 128 * (dh + 8) if elem == 2 else dh * 136
+    v_elems = 128 * (dh + 16) if elem == 2 else dh * 136
     return (WAVES * up * uk * 512 + v_elems) * elem + 128 * 4 + (mbytes if mbytes <= 32 * 1024 else 16)
 
 
