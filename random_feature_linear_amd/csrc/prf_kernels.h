@@ -28,12 +28,17 @@
 // attention equation), so the query side subtracts instead its largest
 // exponent over the first 32 features, which keeps the exp2 arguments near 0.
 //
-// Precision of the bf16 path.  The exponent omega_j . u reaches magnitudes of
-// ten and more, and a weight error of e per key shows up as a relative output
-// error of about e (outputs are averages of zero-mean values), so the operands
-// of the exponent cannot be plain bf16.  M', u and omega' are each carried as a
-// pair of bf16 values hi + lo (about 16 significant bits): u = M'_hi x + M'_lo x
-// and E = u_hi omega'_hi + u_lo omega'_hi + u_hi omega'_lo.
+// Precision of the bf16 path.  The exponent omega_j . u of the feature map
+// reaches magnitudes of ten and more, and a weight error of e per key shows up
+// as a relative output error of about e (outputs are averages of zero-mean
+// values), so the exponent's operands are not plain bf16 (8 significant
+// bits).  u = M' x is formed from M' as a pair of bf16 values hi + lo (about
+// 16 significant bits: u = M'_hi x + M'_lo x, fp32 accumulate); then u and
+// omega' (or, folded, the token row x and W' = omega' M') enter the exponent
+// as fp16 values (11 significant bits, range clamped to +-65504) in one fp16
+// product per K-step.  The exponent's error is then about 2^-12 of its terms,
+// below the 2^-9 rounding of the features themselves to bf16 for the
+// contractions.
 //
 // The normaliser z = Phi(K)^T 1 is kept apart from the state S in fp32, so S
 // holds only V's column blocks.  The key side forms z as a column of ones
@@ -128,6 +133,33 @@ __device__ __forceinline__ void acc_frag_split(const f32x16& a, int k, typename 
   }
   make_frag(hi, vh);
   make_frag(lo, vl);
+}
+
+// ---- fp16 operands of the feature exponent (bf16 path) ----------------------
+// One fp16 value per slot, carried in a bf16x8 register or memory slot (the
+// bits are fp16) and read by the fp16 32x32x16 MFMA.  Values beyond the fp16
+// range are clamped to +-65504 (the exponent is then far outside the range
+// exp2 resolves in fp32 anyway).  On the fp32 path (kH16 false) the
+// operands stay fp32 and nothing here is used.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <typename T> constexpr bool kH16 = sizeof(T) == 2;
+__device__ __forceinline__ bf16x8 make_frag_h(const float* v) {
+  f16x8 h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (_Float16)fminf(fmaxf(v[i], -65504.f), 65504.f);
+  return __builtin_bit_cast(bf16x8, h);
+}
+// a bf16 fragment (a token row) as an fp16 one
+__device__ __forceinline__ bf16x8 to_h(const bf16x8& x) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
+  return make_frag_h(v);
+}
+__device__ __forceinline__ f32x8 to_h(const f32x8& x) { return x; }
+__device__ __forceinline__ f32x16 mma_h(const bf16x8& a, const bf16x8& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
 }
 
 __device__ __forceinline__ bf16x8 ld8(const bf16* p) {
@@ -227,8 +259,9 @@ __device__ __forceinline__ void load_rows(typename FragOf<T>::type (&xf)[DH / 16
 
 // u^T = M' x^T for a 32-token block (rank index in rows, token c in the lane),
 // returned as hi / lo operand fragments over the rank index (K-steps of 16),
-// plus the exp2-domain shift log2(e) |u|^2 / 2 + log2(m) / 2 of token c.
-template <typename T, int DH, int R16>
+// or (H16, bf16 path) as one fp16 fragment per K-step in uhi, plus the
+// exp2-domain shift log2(e) |u|^2 / 2 + log2(m) / 2 of token c.
+template <typename T, int DH, int R16, bool H16 = false>
 __device__ __forceinline__ float project_block(typename FragOf<T>::type (&uhi)[R16],
                                                typename FragOf<T>::type (&ulo)[R16],
                                                const typename FragOf<T>::type (&xf)[DH / 16],
@@ -249,7 +282,16 @@ __device__ __forceinline__ float project_block(typename FragOf<T>::type (&uhi)[R
     for (int i = 0; i < 16; ++i) ss += acc[i] * acc[i];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      if (2 * rb + h < R16) acc_frag_split<T>(acc, h, uhi[2 * rb + h], ulo[2 * rb + h]);
+      if (2 * rb + h < R16) {
+        if constexpr (H16) {   // one fp16 part (the lo fragment is not read)
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = acc[8 * h + e];
+          uhi[2 * rb + h] = make_frag_h(v);
+        } else {
+          acc_frag_split<T>(acc, h, uhi[2 * rb + h], ulo[2 * rb + h]);
+        }
+      }
     if constexpr (KD * NM > 8) __builtin_amdgcn_sched_barrier(0);
   }
   ss += __shfl_xor(ss, 32);
@@ -259,17 +301,22 @@ __device__ __forceinline__ float project_block(typename FragOf<T>::type (&uhi)[R
 // e += u . omega' over the K-steps of the exponent: u_hi omega'_hi + u_lo
 // omega'_hi + u_hi omega'_lo (bf16), or one fp32 product.  In the folded form
 // (see fold_exponent) u is the token row x itself, which is exact in bf16
-// (ULO false, no u_lo term), and omega' is W'.  U_IS_A: the u fragments are
-// the A operand (result rows = tokens, columns = features); otherwise omega'
-// is (result rows = features, columns = tokens).
-template <typename T, int NK, bool U_IS_A, bool ULO = true>
+// (ULO false, no u_lo term), and omega' is W'.  H16 (the feature map on the
+// bf16 path): u and omega' are one fp16 fragment each, one fp16 product per
+// K-step, the lo fragments unused.  U_IS_A: the u fragments are the A operand
+// (result rows = tokens, columns = features); otherwise omega' is (result rows
+// = features, columns = tokens).
+template <typename T, int NK, bool U_IS_A, bool ULO = true, bool H16 = false>
 __device__ __forceinline__ f32x16 exponent(const typename FragOf<T>::type* uhi,
                                            const typename FragOf<T>::type* ulo,
                                            const typename FragOf<T>::type* ohi,
                                            const typename FragOf<T>::type* olo, f32x16 e) {
 #pragma unroll
   for (int k = 0; k < NK; ++k) {
-    if constexpr (U_IS_A) {
+    if constexpr (H16) {
+      static_assert(sizeof(T) == 2, "fp16 exponent operands: bf16 path");
+      e = U_IS_A ? mma_h(uhi[k], ohi[k], e) : mma_h(ohi[k], uhi[k], e);
+    } else if constexpr (U_IS_A) {
       e = mma(uhi[k], ohi[k], e);
       if constexpr (kParts<T> == 2) {
         if constexpr (ULO) e = mma(ulo[k], ohi[k], e);
@@ -291,30 +338,31 @@ __device__ __forceinline__ f32x16 exponent(const typename FragOf<T>::type* uhi,
 // Long sums (more than 8 K-steps, d_h = 256 folded) run in chunks of 2 steps
 // whose operands are fetched one chunk ahead, with scheduling fences between
 // chunks so that at most two chunks of operands are live in registers.
-template <typename T, int NK, bool U_IS_A, bool ULO, typename UL, typename OL>
+template <typename T, int NK, bool U_IS_A, bool ULO, bool H16 = false, typename UL, typename OL>
 __device__ __forceinline__ f32x16 exponent_stream(UL uload, OL oload, f32x16 e) {
   typedef typename FragOf<T>::type F;
+  constexpr bool LO_U = ULO && !H16, LO_O = !H16;   // lo fragments that are read
   if constexpr (NK <= 8) {
     F uh[NK], ul[NK], oh[NK], ol[NK];
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
       uh[k] = uload(k, 0);
-      if constexpr (ULO) ul[k] = uload(k, 1);
+      if constexpr (LO_U) ul[k] = uload(k, 1);
       oh[k] = oload(k, 0);
-      ol[k] = oload(k, 1);
+      if constexpr (LO_O) ol[k] = oload(k, 1);
     }
-    return exponent<T, NK, U_IS_A, ULO>(uh, ul, oh, ol, e);
+    return exponent<T, NK, U_IS_A, ULO, H16>(uh, ul, oh, ol, e);
   } else {
     constexpr int CH = 2;
     static_assert(NK % CH == 0, "chunked exponent");
-    F uh[2][CH], ul[2][ULO ? CH : 1], oh[2][CH], ol[2][CH];
+    F uh[2][CH], ul[2][LO_U ? CH : 1], oh[2][CH], ol[2][LO_O ? CH : 1];
     auto fetch = [&](int b, int k0) {
 #pragma unroll
       for (int k = 0; k < CH; ++k) {
         uh[b][k] = uload(k0 + k, 0);
-        if constexpr (ULO) ul[b][k] = uload(k0 + k, 1);
+        if constexpr (LO_U) ul[b][k] = uload(k0 + k, 1);
         oh[b][k] = oload(k0 + k, 0);
-        ol[b][k] = oload(k0 + k, 1);
+        if constexpr (LO_O) ol[b][k] = oload(k0 + k, 1);
       }
     };
     fetch(0, 0);
@@ -322,7 +370,7 @@ __device__ __forceinline__ f32x16 exponent_stream(UL uload, OL oload, f32x16 e) 
     for (int c0 = 0; c0 < NK / CH; ++c0) {
       if (c0 + 1 < NK / CH) fetch((c0 + 1) & 1, (c0 + 1) * CH);
       __builtin_amdgcn_sched_barrier(0);
-      e = exponent<T, CH, U_IS_A, ULO>(uh[c0 & 1], ul[c0 & 1], oh[c0 & 1], ol[c0 & 1], e);
+      e = exponent<T, CH, U_IS_A, ULO, H16>(uh[c0 & 1], ul[c0 & 1], oh[c0 & 1], ol[c0 & 1], e);
       __builtin_amdgcn_sched_barrier(0);
     }
     return e;
@@ -389,7 +437,9 @@ __device__ __forceinline__ void mfrag_lane(long idx, const float* __restrict__ M
 //                                16k + 8 (e / 4) + 4g + e % 4
 // or, folded, W'_hm = omega' M'_hm:
 //   ofrag[hm][fb][kd][part][lane][8]: row 32 fb + c of W', columns 16 kd + 8g + e
-// part 0 is the bf16-rounded value, part 1 the rounded remainder (bf16 path).
+// For M' (bf16 path) part 0 is the bf16-rounded value and part 1 the rounded
+// remainder; omega' and W' are read as one fp16 operand from part 0 (bf16
+// path; part 1 is left unwritten and never read).
 // The M' and omega' ranges take one thread per fragment lane and part; the W'
 // range one thread per fragment lane (both parts, r products each).
 // ---------------------------------------------------------------------------
@@ -437,18 +487,15 @@ __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict
           acc[7] += w * m1.w;
         }
       }
-      float lo[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = kLog2e * s * acc[e];
-        v[e] = bf16_hi(x);
-        lo[e] = x - v[e];
+      for (int e = 0; e < 8; ++e) v[e] = kLog2e * s * acc[e];
+      const long base = f * NM * 64 + lane;   // fragment (f, part 0): fp16 (part 1 is not read)
+      if constexpr (kH16<T>) {
+        st8(ofrag + base * 8, make_frag_h(v));
+      } else {   // (the folded form is bf16 only)
+        make_frag(fr, v);
+        st8(ofrag + base * 8, fr);
       }
-      const long base = f * NM * 64 + lane;   // fragment (f, part 0)
-      make_frag(fr, v);
-      st8(ofrag + base * 8, fr);
-      make_frag(fr, lo);
-      st8(ofrag + (base + 64) * 8, fr);
       continue;
     }
     const int part = (int)(f % NM);
@@ -464,13 +511,15 @@ __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int a = 16 * k + 8 * (e >> 2) + 4 * g + (e & 3);
-        const float x = (row < m && a < r) ? kLog2e * om[(long)row * r + a] : 0.f;
-        const float hi = NM == 2 ? bf16_hi(x) : x;
-        v[e] = part == 0 ? hi : x - hi;
+        v[e] = (row < m && a < r) ? kLog2e * om[(long)row * r + a] : 0.f;
+      }
+      if constexpr (kH16<T>) {   // part 0: the fp16 operand; part 1 is not read
+        if (part == 0) st8(ofrag + j * 8, make_frag_h(v));
+        continue;
       }
     }
     make_frag(fr, v);
-    st8((m_side ? mfrag : ofrag) + j * 8, fr);
+    st8(ofrag + j * 8, fr);
   }
 }
 
@@ -478,8 +527,8 @@ __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict
 // Folded operand W'_hm = omega' M'_hm (m x d_h) for the bf16 path.  The
 // products run on the bf16 matrix cores with each fp32 operand split into a
 // bf16 high part and a bf16 remainder (hi hi + lo hi + hi lo, about 16
-// significant bits per operand), so that W' is as exact as its own hi/lo
-// parts.  Workgroup: 4 waves, one 32-feature block and up to four 32-column
+// significant bits per operand), well below the fp16 rounding of the stored
+// W' (part 0 of each fragment, the exponent's operand).  Workgroup: 4 waves, one 32-feature block and up to four 32-column
 // tiles (one per wave).  The rank index runs in chunks of 64: the chunk's M
 // columns and omega rows are fetched into registers one chunk ahead (all loads
 // of a chunk in flight together), split, and staged in LDS as bf16 parts.
@@ -604,19 +653,11 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict_
   const int KD = d_h / 16;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    float hi[8], lo[8];
+    float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = s_m[16 * h + 8 * g + e][32 * w + c];
-      hi[e] = bf16_hi(x);
-      lo[e] = x - hi[e];
-    }
+    for (int e = 0; e < 8; ++e) x[e] = s_m[16 * h + 8 * g + e][32 * w + c];
     const long f = ((long)hw * FB + fb) * KD + 2 * dt + h;
-    typename FragOf<T>::type fr;
-    make_frag(fr, hi);
-    st8(ofrag + ((f * NM) * 64 + lane) * 8, fr);
-    make_frag(fr, lo);
-    st8(ofrag + ((f * NM + 1) * 64 + lane) * 8, fr);
+    st8(ofrag + ((f * NM) * 64 + lane) * 8, make_frag_h(x));   // part 0: fp16 (part 1 is not read)
   }
 }
 
@@ -978,7 +1019,7 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
 #pragma unroll
       for (int k = 0; k < UK; ++k) {
         ohr[f][k] = ld8(of + (((long)(fb * UK + k) * NM) * 64 + lane) * 8);
-        olr[f][k] = ld8(of + (((long)(fb * UK + k) * NM + NM - 1) * 64 + lane) * 8);
+        if constexpr (!kH16<T>) olr[f][k] = ld8(of + (((long)(fb * UK + k) * NM + NM - 1) * 64 + lane) * 8);
       }
     }
   }
@@ -1009,17 +1050,17 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
     const int t = tt + 32 * w + c;
     const bool ok = t < t_end;
     float shift = 0.f;
-    if constexpr (FOLD) {   // the exponent reads the token rows themselves
+    if constexpr (FOLD) {   // the exponent reads the token rows themselves (as fp16)
       if (!pl.kshift) shift = project_shift<T, DH, R16>(xpre, msrc_t, lane, half_log2m);
 #pragma unroll
-      for (int k = 0; k < UK; ++k) st8(&s_u[buf][w][0][k][lane * 8], xpre[k]);
+      for (int k = 0; k < UK; ++k) st8(&s_u[buf][w][0][k][lane * 8], to_h(xpre[k]));
     } else {
       F uhi[R16], ulo[R16];
-      shift = project_block<T, DH, R16>(uhi, ulo, xpre, msrc_t, lane, half_log2m);
+      shift = project_block<T, DH, R16, kH16<T>>(uhi, ulo, xpre, msrc_t, lane, half_log2m);
 #pragma unroll
       for (int k = 0; k < R16; ++k) {
         st8(&s_u[buf][w][0][k][lane * 8], uhi[k]);
-        if constexpr (NM == 2) st8(&s_u[buf][w][NM - 1][k][lane * 8], ulo[k]);
+        if constexpr (NM == 2 && !kH16<T>) st8(&s_u[buf][w][NM - 1][k][lane * 8], ulo[k]);
       }
     }
     const bool valid = ok && (mrow == nullptr || mrow[t] != 0);
@@ -1062,7 +1103,7 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
       };
       if constexpr (PAD)   // m is not a multiple of 32: features past m give 0
         if (fb * 32 + c >= a.m) e = splat16(-INFINITY);
-      return exponent_stream<T, UK, true, !FOLD>(uload, oload, e);
+      return exponent_stream<T, UK, true, !FOLD, kH16<T>>(uload, oload, e);
     };
     // V (and ones) fragments of a token block: held across the feature blocks
     // when few, else read from LDS at each use
@@ -1251,10 +1292,17 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
           if (2 * rb + hh < R16) {
-            F hi, lo;
-            acc_frag_split<T>(u, hh, hi, lo);
-            st8(&s_u[0][2 * rb + hh][lane * 8], hi);
-            if constexpr (NM == 2) st8(&s_u[NM - 1][2 * rb + hh][lane * 8], lo);
+            if constexpr (kH16<T>) {   // the exponent's fp16 operand
+              float v[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] = u[8 * hh + e];
+              st8(&s_u[0][2 * rb + hh][lane * 8], make_frag_h(v));
+            } else {
+              F hi, lo;
+              acc_frag_split<T>(u, hh, hi, lo);
+              st8(&s_u[0][2 * rb + hh][lane * 8], hi);
+              if constexpr (NM == 2) st8(&s_u[NM - 1][2 * rb + hh][lane * 8], lo);
+            }
           }
       }
       ss += __shfl_xor(ss, 32);
@@ -1276,7 +1324,7 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
 #pragma unroll
     for (int k = 0; k < R16; ++k) {
       uhi[k] = ld8(&s_u[0][k][lane * 8]);
-      ulo[k] = ld8(&s_u[NM - 1][k][lane * 8]);
+      if constexpr (!kH16<T>) ulo[k] = ld8(&s_u[NM - 1][k][lane * 8]);
     }
 #pragma unroll
     for (int f = 0; f < FBW; ++f) {
@@ -1286,12 +1334,12 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
 #pragma unroll
       for (int k = 0; k < R16; ++k) {
         ohi[k] = ld8(of + (((long)(fbc * R16 + k) * NM) * 64 + lane) * 8);
-        olo[k] = ld8(of + (((long)(fbc * R16 + k) * NM + NM - 1) * 64 + lane) * 8);
+        if constexpr (!kH16<T>) olo[k] = ld8(of + (((long)(fbc * R16 + k) * NM + NM - 1) * 64 + lane) * 8);
       }
       f32x16 e = ini;
       if constexpr (PAD)
         if (fb * 32 + c >= a.m) e = splat16(-INFINITY);
-      e = exponent<T, R16, true>(uhi, ulo, ohi, olo, e);
+      e = exponent<T, R16, true, true, kH16<T>>(uhi, ulo, ohi, olo, e);
 #pragma unroll
       for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
       const F p0 = acc_frag<F>(e, 0), p1 = acc_frag<F>(e, 1);
@@ -1510,8 +1558,17 @@ template <typename T, int DH, int R16, int ALLFB> constexpr bool qout_all_fits()
   return sizeof(T) == 2 && vt + op + kf <= 160 * 1024;
 }
 
+// Largest number of waves per SIMD the compiler schedules the query side for:
+// two where each wave reads its operands from L2 itself (non-causal, few
+// operand slots).  Left free, the compiler aims at three waves there and, to
+// fit their registers, waits for each operand load before issuing the next
+// (L=64K query side 213 against 150 us).
+template <typename T, int DH, int R16, bool CAUSAL, int ALLFB> constexpr int qout_max_waves() {
+  return (!CAUSAL && ALLFB == 0 && qout_nstep<T, DH, R16>() <= 8) ? 2 : 8;
+}
 template <typename T, int DH, int R16, int NQB, bool CAUSAL, bool PAD, int ALLFB = 0>
-__global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, qout_max_waves<T, DH, R16, CAUSAL, ALLFB>())))
+void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
                                                         const T* __restrict__ ofrag, const T* __restrict__ sfrag,
                                                         const float* __restrict__ zsum) {
   typedef typename FragOf<T>::type F;
@@ -1540,6 +1597,7 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
   // barrier per step, each wave reads them from L2 itself (L=64K, 16-rank
   // geometry: 150 against 155 us; a register prefetch one step ahead, 152).
   constexpr bool SELF = !CAUSAL && ALLFB == 0 && NSTEP <= 8;
+  static_assert(SELF == (qout_max_waves<T, DH, R16, CAUSAL, ALLFB>() == 2), "wave bound of the unstaged form");
   constexpr bool STAGE = !SELF && kBase + kOpStep + kKfStep <= 160 * 1024;
   constexpr int OPB = !STAGE ? 0 : kBase + 2 * kOpStep + 2 * kKfStep <= 160 * 1024 ? 2 : 1;
   constexpr int KBUF = kBase + OPB * kOpStep + 2 * kKfStep <= 160 * 1024 ? 2 : 1;
@@ -1635,8 +1693,9 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
     const bool ok = t < a.L;
     shq[j] = 0.f;
     if constexpr (!FOLD)
-      (void)project_block<T, DH, R16>(*reinterpret_cast<F(*)[R16]>(uqh[j]), *reinterpret_cast<F(*)[R16]>(uql[j]),
-                                      xq[FOLD ? 0 : j], msrc, lane, half_log2m);
+      (void)project_block<T, DH, R16, kH16<T>>(*reinterpret_cast<F(*)[R16]>(uqh[j]),
+                                               *reinterpret_cast<F(*)[R16]>(uql[j]), xq[FOLD ? 0 : j], msrc, lane,
+                                               half_log2m);
     if constexpr (CAUSAL) {
       float sh = 0.f;
       if (FOLD && pl.kshift) {
@@ -1645,10 +1704,18 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
         if constexpr (FOLD)
           sh = project_shift<T, DH, R16>(*reinterpret_cast<F(*)[KD]>(ukh[j]), msrc, lane, half_log2m);
         else
-          sh = project_block<T, DH, R16>(*reinterpret_cast<F(*)[R16]>(ukh[j]), *reinterpret_cast<F(*)[R16]>(ukl[j]),
-                                         xk[FOLD ? 0 : j], msrc, lane, half_log2m);
+          sh = project_block<T, DH, R16, kH16<T>>(*reinterpret_cast<F(*)[R16]>(ukh[j]),
+                                                  *reinterpret_cast<F(*)[R16]>(ukl[j]), xk[FOLD ? 0 : j], msrc, lane,
+                                                  half_log2m);
         const bool valid = ok && (mrow == nullptr || mrow[t] != 0);
         initk[j] = valid ? -sh : -INFINITY;
+      }
+    }
+    if constexpr (FOLD && kH16<T>) {   // the token rows as the exponent's fp16 operands
+#pragma unroll
+      for (int k = 0; k < UK; ++k) {
+        uqh[j][k] = to_h(uqh[j][k]);
+        if constexpr (CAUSAL) ukh[j][k] = to_h(ukh[j][k]);
       }
     }
   }
@@ -1718,9 +1785,9 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
           if (crow(i, g) >= a.m) e[i] = -INFINITY;
       }
       if constexpr (FOLD)
-        e = exponent_stream<T, UK, false, false>([&](int k, int) -> F { return uqh[j][k]; }, oload, e);
+        e = exponent_stream<T, UK, false, false, kH16<T>>([&](int k, int) -> F { return uqh[j][k]; }, oload, e);
       else
-        e = exponent_stream<T, UK, false, true>(
+        e = exponent_stream<T, UK, false, true, kH16<T>>(
             [&](int k, int part) -> F { return part ? uql[j][k] : uqh[j][k]; }, oload, e);
       float mx = e[0];
 #pragma unroll
@@ -1740,7 +1807,7 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
 #pragma unroll
       for (int k = 0; k < UK; ++k) {
         ohi[k] = op(fb, buf, k * NM);
-        olo[k] = op(fb, buf, k * NM + NM - 1);
+        if constexpr (!kH16<T>) olo[k] = op(fb, buf, k * NM + NM - 1);
       }
     }
     const bool partial = PAD && (fb + 1) * 32 > a.m;   // the last block may hold padding features
@@ -1754,9 +1821,9 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
           if (fb * 32 + crow(i, g) >= a.m) e[i] = -INFINITY;
       }
       if constexpr (FOLD)
-        e = exponent_stream<T, UK, false, false>([&](int k, int) -> F { return uqh[j][k]; }, oload, e);
+        e = exponent_stream<T, UK, false, false, kH16<T>>([&](int k, int) -> F { return uqh[j][k]; }, oload, e);
       else
-        e = exponent<T, UK, false, true>(uqh[j], uql[j], ohi, olo, e);
+        e = exponent<T, UK, false, true, kH16<T>>(uqh[j], uql[j], ohi, olo, e);
 #pragma unroll
       for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
 #pragma unroll
@@ -1791,9 +1858,9 @@ __global__ __launch_bounds__(kThreads) void qout_kernel(FwdArgs a, Plan pl, cons
             if (fb * 32 + crow(i, g) >= a.m) e[i] = -INFINITY;
         }
         if constexpr (FOLD)
-          e = exponent_stream<T, UK, false, false>([&](int k, int) -> F { return ukh[j][k]; }, oload, e);
+          e = exponent_stream<T, UK, false, false, kH16<T>>([&](int k, int) -> F { return ukh[j][k]; }, oload, e);
         else
-          e = exponent<T, UK, false, true>(ukh[j], ukl[j], ohi, olo, e);
+          e = exponent<T, UK, false, true, kH16<T>>(ukh[j], ukl[j], ohi, olo, e);
 #pragma unroll
         for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
 #pragma unroll
@@ -2008,16 +2075,23 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
   __syncthreads();                      // M', V^T and every wave's copies visible
   const T* msrc = M_LDS ? s_kf : mf;
   if constexpr (!FOLD)
-    (void)project_block<T, DH, R16>(*reinterpret_cast<F(*)[R16]>(uqh), *reinterpret_cast<F(*)[R16]>(uql), xq, msrc,
-                                    lane, half_log2m);
+    (void)project_block<T, DH, R16, kH16<T>>(*reinterpret_cast<F(*)[R16]>(uqh), *reinterpret_cast<F(*)[R16]>(uql),
+                                             xq, msrc, lane, half_log2m);
   if (!(FOLD && pl.kshift)) {
     float sh;
     if constexpr (FOLD)
       sh = project_shift<T, DH, R16>(*reinterpret_cast<F(*)[KD]>(ukh), msrc, lane, half_log2m);
     else
-      sh = project_block<T, DH, R16>(*reinterpret_cast<F(*)[R16]>(ukh), *reinterpret_cast<F(*)[R16]>(ukl), xk, msrc,
-                                     lane, half_log2m);
+      sh = project_block<T, DH, R16, kH16<T>>(*reinterpret_cast<F(*)[R16]>(ukh), *reinterpret_cast<F(*)[R16]>(ukl),
+                                              xk, msrc, lane, half_log2m);
     initk = kvalid ? -sh : -INFINITY;
+  }
+  if constexpr (FOLD && kH16<T>) {   // the token rows as the exponent's fp16 operands
+#pragma unroll
+    for (int k = 0; k < UK; ++k) {
+      uqh[k] = to_h(uqh[k]);
+      ukh[k] = to_h(ukh[k]);
+    }
   }
 
   auto op = [&](int fb, int f) { return ld8(s_op + ((fb * NSTEP + f) * 64 + lane) * 8); };
@@ -2036,10 +2110,10 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
         if (crow(i, g) >= a.m) e[i] = -INFINITY;
     }
     if constexpr (FOLD)
-      e = exponent_stream<T, UK, false, false>([&](int k, int) -> F { return uqh[k]; }, oload, e);
+      e = exponent_stream<T, UK, false, false, kH16<T>>([&](int k, int) -> F { return uqh[k]; }, oload, e);
     else
-      e = exponent_stream<T, UK, false, true>([&](int k, int part) -> F { return part ? uql[k] : uqh[k]; }, oload,
-                                              e);
+      e = exponent_stream<T, UK, false, true, kH16<T>>(
+          [&](int k, int part) -> F { return part ? uql[k] : uqh[k]; }, oload, e);
     float mx = e[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, e[i]);
@@ -2070,7 +2144,7 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
 #pragma unroll
         for (int k = 0; k < UK; ++k) {
           ohi[k] = op(fb, k * NM);
-          olo[k] = op(fb, k * NM + NM - 1);
+          if constexpr (!kH16<T>) olo[k] = op(fb, k * NM + NM - 1);
         }
       }
       const bool partial = PAD && (fb + 1) * 32 > a.m;
@@ -2082,9 +2156,9 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
             if (fb * 32 + crow(i, g) >= a.m) e[i] = -INFINITY;
         }
         if constexpr (FOLD)
-          e = exponent_stream<T, UK, false, false>([&](int k, int) -> F { return uqh[k]; }, oload, e);
+          e = exponent_stream<T, UK, false, false, kH16<T>>([&](int k, int) -> F { return uqh[k]; }, oload, e);
         else
-          e = exponent<T, UK, false, true>(uqh, uql, ohi, olo, e);
+          e = exponent<T, UK, false, true, kH16<T>>(uqh, uql, ohi, olo, e);
 #pragma unroll
         for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
 #pragma unroll
@@ -2107,9 +2181,9 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
             if (fb * 32 + crow(i, g) >= a.m) e[i] = -INFINITY;
         }
         if constexpr (FOLD)
-          e = exponent_stream<T, UK, false, false>([&](int k, int) -> F { return ukh[k]; }, oload, e);
+          e = exponent_stream<T, UK, false, false, kH16<T>>([&](int k, int) -> F { return ukh[k]; }, oload, e);
         else
-          e = exponent<T, UK, false, true>(ukh, ukl, ohi, olo, e);
+          e = exponent<T, UK, false, true, kH16<T>>(ukh, ukl, ohi, olo, e);
 #pragma unroll
         for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
 #pragma unroll
