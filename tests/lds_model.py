@@ -571,10 +571,9 @@ def kstate_model(cfg: KstateConfig, mutate=frozenset()):
             for k in range(uk):
                 tr.write(w, "s_u", frag_lanes(u_slot(buf, w, 0, k), e), 8 * e)
         else:
+            # u as one fp16 fragment per K-step (bf16 path) or one fp32 fragment
             for k in range(cfg.r16):
                 tr.write(w, "s_u", frag_lanes(u_slot(buf, w, 0, k), e), 8 * e)
-                if D["nm"] == 2:
-                    tr.write(w, "s_u", frag_lanes(u_slot(buf, w, D["nm"] - 1, k), e), 8 * e)
         tr.write(w, "s_init", (buf * 128 + 32 * w + C[G == 0]) * 4, 4)
         if D["vtr"]:
             store_v(tr, w, "s_vt", buf * D["v_elems"], cfg.dh, 128, e)
@@ -598,7 +597,7 @@ def kstate_model(cfg: KstateConfig, mutate=frozenset()):
             for _f in range(cfg.fbw):
                 for k in range(uk):
                     tr.read(w, "s_u", frag_lanes(u_slot(buf, tb, 0, k), e), 8 * e)
-                    if not D["fold"]:
+                    if not D["fold"] and e == 4:   # fp32: the exponent's lo read is part 0 again
                         tr.read(w, "s_u", frag_lanes(u_slot(buf, tb, up - 1, k), e), 8 * e)
                 if not D["vhold"]:
                     for db in range(D["dbk"]):
