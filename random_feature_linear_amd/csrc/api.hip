@@ -146,7 +146,7 @@ static void make_plan(const dark_prf_desc& d, Plan& p, int mode = kPlanForward) 
     p.UPW = 1;
     units_ws = splits;   // NU <= splits, and splits never decreases as L grows
   }
-  // operand copies of M' and omega' (bf16: hi and lo parts; see prf_kernels.h)
+  // operand copies of M' (bf16: hi and lo parts) and omega' (see prf_kernels.h)
   const int NM = d.dtype == DARK_BF16 ? 2 : 1;
   const int R32 = (p.R16 + 1) / 2;
   const int DB = (d.d_h + 31) / 32;      // 32-column blocks of V
@@ -157,11 +157,11 @@ static void make_plan(const dark_prf_desc& d, Plan& p, int mode = kPlanForward) 
   size_t off = 0;
   p.off_mfrag = off;
   off = align256(off + (size_t)p.HM * R32 * (d.d_h / 16) * NM * frag * p.elem);
-  p.off_ofrag = off;
+  p.off_ofrag = off;   // one part (the bf16 path's exponent operands are fp16)
   if (p.fold)   // W' fragments per folded operand, K-steps over d_h
-    off = align256(off + (size_t)p.HW * p.FB * (d.d_h / 16) * NM * frag * p.elem);
+    off = align256(off + (size_t)p.HW * p.FB * (d.d_h / 16) * frag * p.elem);
   else          // omega' fragments per projection, K-steps over the rank
-    off = align256(off + (size_t)p.HO * p.FB * p.R16 * NM * frag * p.elem);
+    off = align256(off + (size_t)p.HO * p.FB * p.R16 * frag * p.elem);
   p.off_sdelta = off;
   off = align256(off + (size_t)p.BH * units * state_frags * frag * p.elem);
   // the per-unit states stay in L2 between the key side and the sum (same XCD)

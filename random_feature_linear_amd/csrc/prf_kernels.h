@@ -433,13 +433,13 @@ __device__ __forceinline__ void mfrag_lane(long idx, const float* __restrict__ M
 // ---------------------------------------------------------------------------
 // Preparation: M' = d_h^(-1/4) M and omega' = log2(e) omega in fragment order.
 //   mfrag[hm][rb][kd][part][lane][8]: row 32 rb + c of M', columns 16 kd + 8g + e
-//   ofrag[fb][k][part][lane][8]: row 32 fb + c of omega', rank index
+//   ofrag[ho][fb][k][lane][8]: row 32 fb + c of omega', rank index
 //                                16k + 8 (e / 4) + 4g + e % 4
 // or, folded, W'_hm = omega' M'_hm:
-//   ofrag[hm][fb][kd][part][lane][8]: row 32 fb + c of W', columns 16 kd + 8g + e
+//   ofrag[hw][fb][kd][lane][8]: row 32 fb + c of W', columns 16 kd + 8g + e
 // For M' (bf16 path) part 0 is the bf16-rounded value and part 1 the rounded
-// remainder; omega' and W' are read as one fp16 operand from part 0 (bf16
-// path; part 1 is left unwritten and never read).
+// remainder.  omega' and W' have one part: fp16 on the bf16 path (the
+// exponent's operand), fp32 otherwise.
 // The M' and omega' ranges take one thread per fragment lane and part; the W'
 // range one thread per fragment lane (both parts, r products each).
 // ---------------------------------------------------------------------------
@@ -453,7 +453,7 @@ __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict
   const long nM = (long)HM * R32 * KD * NM * 64;
   // fold: 0 omega' fragments (HO projections), 1 W' fragments here (HW
   // operands), 2 W' fragments by fold_kernel
-  const long nO = fold == 2 ? 0 : fold ? (long)HW * FB * KD * 64 : (long)HO * FB * R16 * NM * 64;
+  const long nO = fold == 2 ? 0 : fold ? (long)HW * FB * KD * 64 : (long)HO * FB * R16 * 64;
   for (long idx = blockIdx.x * (long)blockDim.x + threadIdx.x; idx < nM + nO;
        idx += (long)gridDim.x * blockDim.x) {
     float v[8];
@@ -489,7 +489,7 @@ __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = kLog2e * s * acc[e];
-      const long base = f * NM * 64 + lane;   // fragment (f, part 0): fp16 (part 1 is not read)
+      const long base = f * 64 + lane;   // fragment f (fp16 on the bf16 path)
       if constexpr (kH16<T>) {
         st8(ofrag + base * 8, make_frag_h(v));
       } else {   // (the folded form is bf16 only)
@@ -498,28 +498,26 @@ __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict
       }
       continue;
     }
-    const int part = (int)(f % NM);
     if (m_side) {
       mfrag_lane<T>(j, M, mfrag, r, d_h, R16, s);
       continue;
-    } else {
-      const int k = (int)((f / NM) % R16);
-      const int fb = (int)((f / ((long)NM * R16)) % FB);
-      const int ho = (int)(f / ((long)NM * R16 * FB));
-      const int row = fb * 32 + c;
-      const float* om = omega + (long)ho * m * r;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int a = 16 * k + 8 * (e >> 2) + 4 * g + (e & 3);
-        v[e] = (row < m && a < r) ? kLog2e * om[(long)row * r + a] : 0.f;
-      }
-      if constexpr (kH16<T>) {   // part 0: the fp16 operand; part 1 is not read
-        if (part == 0) st8(ofrag + j * 8, make_frag_h(v));
-        continue;
-      }
     }
-    make_frag(fr, v);
-    st8(ofrag + j * 8, fr);
+    const int k = (int)(f % R16);
+    const int fb = (int)((f / R16) % FB);
+    const int ho = (int)(f / ((long)R16 * FB));
+    const int row = fb * 32 + c;
+    const float* om = omega + (long)ho * m * r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int a = 16 * k + 8 * (e >> 2) + 4 * g + (e & 3);
+      v[e] = (row < m && a < r) ? kLog2e * om[(long)row * r + a] : 0.f;
+    }
+    if constexpr (kH16<T>) {   // the exponent's fp16 operand
+      st8(ofrag + j * 8, make_frag_h(v));
+    } else {
+      make_frag(fr, v);
+      st8(ofrag + j * 8, fr);
+    }
   }
 }
 
@@ -649,7 +647,6 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict_
   const int dt = grp * 4 + w;
   if (dt >= DT) return;
   // fragment (fb, kd = 2 dt + h): lane (c, g) holds feature c, columns 16 h + 8g + e
-  constexpr int NM = 2;
   const int KD = d_h / 16;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -657,7 +654,7 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict_
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = s_m[16 * h + 8 * g + e][32 * w + c];
     const long f = ((long)hw * FB + fb) * KD + 2 * dt + h;
-    st8(ofrag + ((f * NM) * 64 + lane) * 8, make_frag_h(x));   // part 0: fp16 (part 1 is not read)
+    st8(ofrag + (f * 64 + lane) * 8, make_frag_h(x));   // the exponent's fp16 operand
   }
 }
 
@@ -995,7 +992,7 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
   const uint8_t* mrow = a.mask ? a.mask + (long)b * a.L : nullptr;
   const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * ((R16 + 1) / 2) * KD * NM * 64 * 8;
   // omega' of this head's projection (or the shared one), or W' of its folded operand
-  const T* of = ofrag + (long)((FOLD ? pl.HW : pl.HO) > 1 ? h : 0) * pl.FB * UK * NM * 64 * 8;
+  const T* of = ofrag + (long)((FOLD ? pl.HW : pl.HO) > 1 ? h : 0) * pl.FB * UK * 64 * 8;
   const float half_log2m = 0.5f * log2f((float)a.m);
   const int t_begin = u0 * pl.span1;   // the tiles of all the workgroup's units, in order
   const int t_end = min(a.L, min(u0 + pl.UPW, pl.NU) * pl.span1);
@@ -1010,17 +1007,14 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
 #pragma unroll
   for (int f = 0; f < FBW; ++f) zacc[f] = 0.f;
   // omega' (W') fragments of this wave's features stay in registers when they are few
-  constexpr bool kHoist = FBW * UK * NM <= (FOLD ? 32 : 8);
-  F ohr[kHoist ? FBW : 1][UK], olr[kHoist ? FBW : 1][UK];
+  constexpr bool kHoist = FBW * UK * kParts<T> <= (FOLD ? 32 : 8);
+  F ohr[kHoist ? FBW : 1][UK];
   if constexpr (kHoist) {
 #pragma unroll
     for (int f = 0; f < FBW; ++f) {
       const int fb = min(fb0 + f, pl.FB - 1);
 #pragma unroll
-      for (int k = 0; k < UK; ++k) {
-        ohr[f][k] = ld8(of + (((long)(fb * UK + k) * NM) * 64 + lane) * 8);
-        if constexpr (!kH16<T>) olr[f][k] = ld8(of + (((long)(fb * UK + k) * NM + NM - 1) * 64 + lane) * 8);
-      }
+      for (int k = 0; k < UK; ++k) ohr[f][k] = ld8(of + ((long)(fb * UK + k) * 64 + lane) * 8);
     }
   }
 
@@ -1097,9 +1091,9 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
       const int fb = fb0 + f;
       const int fbc = min(fb, pl.FB - 1);
       auto uload = [&](int k, int part) -> F { return ld8(&s_u[buf][tb][part ? UP - 1 : 0][k][lane * 8]); };
-      auto oload = [&](int k, int part) -> F {
-        if constexpr (kHoist) return part ? olr[f][k] : ohr[f][k];
-        else return ld8(of_t + (((long)(fbc * UK + k) * NM + (part ? NM - 1 : 0)) * 64 + lane) * 8);
+      auto oload = [&](int k, int) -> F {   // omega' (W') has one part
+        if constexpr (kHoist) return ohr[f][k];
+        else return ld8(of_t + ((long)(fbc * UK + k) * 64 + lane) * 8);
       };
       if constexpr (PAD)   // m is not a multiple of 32: features past m give 0
         if (fb * 32 + c >= a.m) e = splat16(-INFINITY);
@@ -1261,7 +1255,7 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
   const T* vbase = reinterpret_cast<const T*>(a.v) + b * a.vs[0] + hk * a.vs[1];
   const uint8_t* mrow = a.mask ? a.mask + (long)b * a.L : nullptr;
   const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * R32 * KD * NM * 64 * 8;
-  const T* of = ofrag + (long)(pl.HO > 1 ? h : 0) * pl.FB * R16 * NM * 64 * 8;   // this head's omega'
+  const T* of = ofrag + (long)(pl.HO > 1 ? h : 0) * pl.FB * R16 * 64 * 8;   // this head's omega'
   const float half_log2m = 0.5f * log2f((float)a.m);
   const int t_begin = unit * pl.span1;
   const int t_end = min(a.L, t_begin + pl.span1);
@@ -1330,16 +1324,13 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
     for (int f = 0; f < FBW; ++f) {
       const int fb = fb0 + f;
       const int fbc = min(fb, pl.FB - 1);   // past the last block: clamped, never stored
-      F ohi[R16], olo[R16];
+      F ohi[R16];   // omega' has one part
 #pragma unroll
-      for (int k = 0; k < R16; ++k) {
-        ohi[k] = ld8(of + (((long)(fbc * R16 + k) * NM) * 64 + lane) * 8);
-        if constexpr (!kH16<T>) olo[k] = ld8(of + (((long)(fbc * R16 + k) * NM + NM - 1) * 64 + lane) * 8);
-      }
+      for (int k = 0; k < R16; ++k) ohi[k] = ld8(of + ((long)(fbc * R16 + k) * 64 + lane) * 8);
       f32x16 e = ini;
       if constexpr (PAD)
         if (fb * 32 + c >= a.m) e = splat16(-INFINITY);
-      e = exponent<T, R16, true, true, kH16<T>>(uhi, ulo, ohi, olo, e);
+      e = exponent<T, R16, true, true, kH16<T>>(uhi, ulo, ohi, ohi, e);
 #pragma unroll
       for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
       const F p0 = acc_frag<F>(e, 0), p1 = acc_frag<F>(e, 1);
@@ -1542,11 +1533,11 @@ __global__ void state_frag_kernel(FwdArgs a, Plan pl, T* __restrict__ sfrag, flo
 // the keys at the same positions are mapped by the same wave and shared with
 // the other waves through LDS, one 32-feature step at a time.
 // ---------------------------------------------------------------------------
-// Operand slots of one 32-feature step: omega' (W') hi/lo fragments, the state
-// fragments, and one slot whose first 128 bytes hold the step's 32 z values.
+// Operand slots of one 32-feature step: omega' (W') fragments (one part), the
+// state fragments, and one slot whose first 128 bytes hold the step's 32 z values.
 template <typename T, int DH, int R16> constexpr int qout_nstep() {
   constexpr int UK = fold_exponent(sizeof(T), DH, R16) ? DH / 16 : R16;
-  return UK * kParts<T> + 2 * vblocks<DH>() + 1;
+  return UK + 2 * vblocks<DH>() + 1;
 }
 // Whether the causal query side can stage the operands of all ALLFB feature
 // steps in LDS at once (bf16): V^T tile, all steps, double key-feature buffers.
@@ -1580,7 +1571,7 @@ void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
   constexpr int VST = TT + 8;
   constexpr bool FOLD = fold_exponent(sizeof(T), DH, R16);
   constexpr int UK = FOLD ? KD : R16;      // K-steps of the exponent
-  constexpr int NOF = UK * NM;             // omega' (W') fragments per feature step
+  constexpr int NOF = UK;                  // omega' (W') fragments per feature step (one part)
   constexpr int NSTEP = qout_nstep<T, DH, R16>();
   constexpr int ZS = NSTEP - 1;            // the z slot
   constexpr int ZW = 8 * (int)sizeof(T) / 4;   // z values per lane of a slot copy
@@ -1627,7 +1618,7 @@ void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
   T* obase = reinterpret_cast<T*>(a.out) + b * a.os[0] + h * a.os[1];
   const uint8_t* mrow = a.mask ? a.mask + (long)b * a.L : nullptr;
   const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * ((R16 + 1) / 2) * KD * NM * 64 * 8;
-  const T* of = ofrag + (long)((FOLD ? pl.HW : pl.HO) > 1 ? h : 0) * pl.FB * UK * NM * 64 * 8;
+  const T* of = ofrag + (long)((FOLD ? pl.HW : pl.HO) > 1 ? h : 0) * pl.FB * UK * 64 * 8;
   const float half_log2m = 0.5f * log2f((float)a.m);
   const int t0 = tile * TT;
   const long FK = 2L * pl.FB;
@@ -1639,7 +1630,7 @@ void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
   // slot: lanes 0 .. 32 / ZW - 1 copy the 32 values (the others repeat the last
   // part, inside the slot).
   auto gsrc = [&](int fb, int f) -> const T* {
-    if (f < NOF) return of + (((long)(fb * UK + f / NM) * NM + f % NM) * 64 + lane) * 8;
+    if (f < NOF) return of + ((long)(fb * UK + f) * 64 + lane) * 8;
     if (f == ZS) return reinterpret_cast<const T*>(zs + fb * 32 + min(lane, 32 / ZW - 1) * ZW);
     f -= NOF;
     return sf + (((f >> 1) * FK + 2 * fb + (f & 1)) * 64 + lane) * 8;
@@ -1775,7 +1766,7 @@ void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
   // features (lanes c and c + 32 hold the two halves of query c's features);
   // the first block always holds at least 16 real features
   auto set_query_shift = [&](int buf) {
-    auto oload = [&](int k, int part) -> F { return op(0, buf, k * NM + (part ? NM - 1 : 0)); };
+    auto oload = [&](int k, int) -> F { return op(0, buf, k); };
 #pragma unroll
     for (int j = 0; j < NQB; ++j) {
       f32x16 e = zero16();
@@ -1797,18 +1788,15 @@ void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
   };
   // one 32-feature step; the operands of the next step are fetched before it runs
   auto step = [&](int fb, int buf) {
-    auto oload = [&](int k, int part) -> F { return op(fb, buf, k * NM + (part ? NM - 1 : 0)); };
+    auto oload = [&](int k, int) -> F { return op(fb, buf, k); };
     // Unfolded: omega' fragments of the step read once into registers and
     // shared by the query and key blocks.  (Fetching them per use with the fp32
     // 32x32x2 products gave a schedule whose first launch in a process
     // returned wrong blocks now and then.)
-    F ohi[FOLD ? 1 : UK], olo[FOLD ? 1 : UK];
+    F ohi[FOLD ? 1 : UK];
     if constexpr (!FOLD) {
 #pragma unroll
-      for (int k = 0; k < UK; ++k) {
-        ohi[k] = op(fb, buf, k * NM);
-        if constexpr (!kH16<T>) olo[k] = op(fb, buf, k * NM + NM - 1);
-      }
+      for (int k = 0; k < UK; ++k) ohi[k] = op(fb, buf, k);
     }
     const bool partial = PAD && (fb + 1) * 32 > a.m;   // the last block may hold padding features
     F pq[NQB][2];
@@ -1823,7 +1811,7 @@ void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
       if constexpr (FOLD)
         e = exponent_stream<T, UK, false, false, kH16<T>>([&](int k, int) -> F { return uqh[j][k]; }, oload, e);
       else
-        e = exponent<T, UK, false, true, kH16<T>>(uqh[j], uql[j], ohi, olo, e);
+        e = exponent<T, UK, false, true, kH16<T>>(uqh[j], uql[j], ohi, ohi, e);
 #pragma unroll
       for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
 #pragma unroll
@@ -1860,7 +1848,7 @@ void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
         if constexpr (FOLD)
           e = exponent_stream<T, UK, false, false, kH16<T>>([&](int k, int) -> F { return ukh[j][k]; }, oload, e);
         else
-          e = exponent<T, UK, false, true, kH16<T>>(ukh[j], ukl[j], ohi, olo, e);
+          e = exponent<T, UK, false, true, kH16<T>>(ukh[j], ukl[j], ohi, ohi, e);
 #pragma unroll
         for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
 #pragma unroll
@@ -1994,7 +1982,7 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
   constexpr int VST = TT + 8;
   constexpr bool FOLD = fold_exponent(sizeof(T), DH, R16);
   constexpr int UK = FOLD ? KD : R16;      // K-steps of the exponent
-  constexpr int NOF = UK * NM;             // omega' (W') fragments per feature step
+  constexpr int NOF = UK;                  // omega' (W') fragments per feature step (one part)
   constexpr int NSTEP = qout_nstep<T, DH, R16>();
   constexpr int ZS = NSTEP - 1;            // the z slot
   constexpr int ZW = 8 * (int)sizeof(T) / 4;
@@ -2026,7 +2014,7 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
   T* obase = reinterpret_cast<T*>(a.out) + b * a.os[0] + h * a.os[1];
   const uint8_t* mrow = a.mask ? a.mask + (long)b * a.L : nullptr;
   const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * ((R16 + 1) / 2) * KD * NM * 64 * 8;
-  const T* of = ofrag + (long)((FOLD ? pl.HW : pl.HO) > 1 ? h : 0) * pl.FB * UK * NM * 64 * 8;
+  const T* of = ofrag + (long)((FOLD ? pl.HW : pl.HO) > 1 ? h : 0) * pl.FB * UK * 64 * 8;
   const float half_log2m = 0.5f * log2f((float)a.m);
   const int t0 = tile * TT;
   const long FK = 2L * pl.FB;
@@ -2036,7 +2024,7 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
 
   // step operands as in qout_kernel: W' (omega') fragments, state fragments, z slot
   auto gsrc = [&](int fb, int f) -> const T* {
-    if (f < NOF) return of + (((long)(fb * UK + f / NM) * NM + f % NM) * 64 + lane) * 8;
+    if (f < NOF) return of + ((long)(fb * UK + f) * 64 + lane) * 8;
     if (f == ZS) return reinterpret_cast<const T*>(zs + fb * 32 + min(lane, 32 / ZW - 1) * ZW);
     f -= NOF;
     return sf + (((f >> 1) * FK + 2 * fb + (f & 1)) * 64 + lane) * 8;
@@ -2102,7 +2090,7 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
   // the query shift: largest exponent of query c over the first 32 features
   float shq;
   {
-    auto oload = [&](int k, int part) -> F { return op(0, k * NM + (part ? NM - 1 : 0)); };
+    auto oload = [&](int k, int) -> F { return op(0, k); };
     f32x16 e = zero16();
     if constexpr (PAD) {
 #pragma unroll
@@ -2138,14 +2126,11 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
     T* kbuf = s_kf + half * KFH + (it & 1) * NB * 2 * 64 * 8;
     F pq[2];
     if (live) {
-      auto oload = [&](int k, int part) -> F { return op(fb, k * NM + (part ? NM - 1 : 0)); };
-      F ohi[FOLD ? 1 : UK], olo[FOLD ? 1 : UK];
+      auto oload = [&](int k, int) -> F { return op(fb, k); };
+      F ohi[FOLD ? 1 : UK];
       if constexpr (!FOLD) {
 #pragma unroll
-        for (int k = 0; k < UK; ++k) {
-          ohi[k] = op(fb, k * NM);
-          if constexpr (!kH16<T>) olo[k] = op(fb, k * NM + NM - 1);
-        }
+        for (int k = 0; k < UK; ++k) ohi[k] = op(fb, k);
       }
       const bool partial = PAD && (fb + 1) * 32 > a.m;
       {
@@ -2158,7 +2143,7 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
         if constexpr (FOLD)
           e = exponent_stream<T, UK, false, false, kH16<T>>([&](int k, int) -> F { return uqh[k]; }, oload, e);
         else
-          e = exponent<T, UK, false, true, kH16<T>>(uqh, uql, ohi, olo, e);
+          e = exponent<T, UK, false, true, kH16<T>>(uqh, uql, ohi, ohi, e);
 #pragma unroll
         for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
 #pragma unroll
@@ -2183,7 +2168,7 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
         if constexpr (FOLD)
           e = exponent_stream<T, UK, false, false, kH16<T>>([&](int k, int) -> F { return ukh[k]; }, oload, e);
         else
-          e = exponent<T, UK, false, true, kH16<T>>(ukh, ukl, ohi, olo, e);
+          e = exponent<T, UK, false, true, kH16<T>>(ukh, ukl, ohi, ohi, e);
 #pragma unroll
         for (int i = 0; i < 16; ++i) e[i] = fast_exp2(e[i]);
 #pragma unroll
@@ -2314,7 +2299,7 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
                            kLog2e * s);
       }
     } else {
-      const long n = nM + (fmode ? (long)pl.HW * pl.FB * (DH / 16) * 64 : (long)pl.HO * pl.FB * R16 * NM * 64);
+      const long n = nM + (fmode ? (long)pl.HW * pl.FB * (DH / 16) * 64 : (long)pl.HO * pl.FB * R16 * 64);
       const int blocks = (int)((n + 255) / 256);
       hipLaunchKernelGGL(prep_kernel<T>, dim3(blocks), dim3(256), 0, st, a.M, a.omega, mfrag, ofrag, pl.HM, pl.HO,
                          pl.HW, a.r, DH, a.m, R16, pl.FB, s, fmode);

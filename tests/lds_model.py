@@ -219,7 +219,7 @@ class QoutConfig:
         vst = tt + 8
         fold = fold_exponent(e, dh, self.r16)
         uk = kd if fold else self.r16
-        nof = uk * nm
+        nof = uk   # omega' (W') fragments per step: one part (fp16 on the bf16 path)
         nstep = nof + 2 * db + 1
         vt_elems = dh * vst if self.causal else 8
         k_base = vt_elems * e
@@ -268,8 +268,7 @@ def qout_model(cfg: QoutConfig, mutate=frozenset()):
 
     def exponent_reads(w, fb, buf):
         for k in range(uk):
-            for part in (0, 1):
-                op_read(w, fb, buf, k * nm + (nm - 1 if part else 0))
+            op_read(w, fb, buf, k)
 
     def store_step(w, buf):
         if D["stage"] and not D["all"]:
@@ -315,8 +314,7 @@ def qout_model(cfg: QoutConfig, mutate=frozenset()):
             # step(fb, buf)
             if not D["fold"]:
                 for k in range(uk):
-                    op_read(w, fb, buf, k * nm)
-                    op_read(w, fb, buf, k * nm + nm - 1)
+                    op_read(w, fb, buf, k)
             for _j in range(cfg.nqb):
                 if D["fold"]:
                     exponent_reads(w, fb, buf)
@@ -381,7 +379,7 @@ WAVES8 = 8
 def qout8_fits(elem, dh, r16, allfb=8):
     kd, nm, db = dh // 16, (2 if elem == 2 else 1), vblocks(dh)
     uk = kd if fold_exponent(elem, dh, r16) else r16
-    nstep = uk * nm + 2 * db + 1
+    nstep = uk + 2 * db + 1
     vt = dh * 136 * elem
     op = allfb * nstep * 512 * elem
     kf = 2 * 2 * WAVES * 2 * 512 * elem
@@ -395,7 +393,7 @@ def qout8_model(cfg: QoutConfig, mutate=frozenset()):
     kd, nm, db = dh // 16, (2 if e == 2 else 1), vblocks(dh)
     fold = fold_exponent(e, dh, cfg.r16)
     uk = kd if fold else cfg.r16
-    nof = uk * nm
+    nof = uk
     nstep = nof + 2 * db + 1
     zs = nstep - 1
     vst = 136
@@ -414,8 +412,7 @@ def qout8_model(cfg: QoutConfig, mutate=frozenset()):
 
     def exponent_reads(w, fb):
         for k in range(uk):
-            op_read(w, fb, k * nm)
-            op_read(w, fb, k * nm + nm - 1)
+            op_read(w, fb, k)
 
     def wave(w):
         half = w // WAVES
@@ -675,7 +672,7 @@ RANK_BLOCKS = (1, 2, 4, 8, 16)
 def qout_all_fits(elem, dh, r16, allfb=8):
     kd, nm, db = dh // 16, (2 if elem == 2 else 1), vblocks(dh)
     uk = kd if fold_exponent(elem, dh, r16) else r16
-    nstep = uk * nm + 2 * db + 1
+    nstep = uk + 2 * db + 1
     vt = dh * (128 + 8) * elem
     return elem == 2 and vt + allfb * nstep * 512 * elem + 2 * 4 * 2 * 512 * elem <= MAX_LDS
 
