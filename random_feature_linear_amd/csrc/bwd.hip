@@ -110,12 +110,13 @@ constexpr int kKT = 32;   // K depth of one LDS slice
 // XC: the last output column N - 1 is not tiled; it is accumulated on the
 // vector ALUs from the A values each thread stages (A(i, k) * B(k, N - 1)) and
 // reduced at the end, so an odd width such as d_h + 1 needs no extra tile.
-// HILO (bf16 inputs): the fp32 operands staged in LDS are split into bf16
-// hi + lo parts and multiplied on the bf16 matrix cores (32x32x16), as
+// PREC kHiLo (bf16 inputs): the fp32 operands staged in LDS are split into
+// bf16 hi + lo parts and multiplied on the bf16 matrix cores (32x32x16), as
 // A_hi B_hi + A_lo B_hi + A_hi B_lo with fp32 accumulation: about 16
 // significant bits per operand, at a fraction of the fp32 products' cost.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-template <typename TA, typename TB, bool PROD, bool XC = false, bool HILO = false>
+enum Prec { kF32 = 0, kHiLo = 1 };
+template <typename TA, typename TB, bool PROD, bool XC = false, int PREC = kF32>
 __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
   constexpr int KT = kKT, NE = 64 * KT / 256;   // elements of each operand per thread and slice
   __shared__ float As[64][KT + 1];   // [i][k]
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(GemmArgs a) {
       fetch(k0 + KT);
       fetch_x(k0 + KT);
     }
-    if constexpr (HILO) {
+    if constexpr (PREC == kHiLo) {
       // operand fragments: row (column) l32 of the wave's block at K-slots 8g .. 8g + 7
 #pragma unroll
       for (int kk = 0; kk < KT; kk += 16) {
@@ -349,18 +350,31 @@ __global__ void fixdu_kernel(float* dU, const float* U, const float* rs, int r, 
 }
 
 // Exclusive prefix (reverse = 0) or suffix (reverse = 1) sums over the NC
-// chunk states of each (b, h), in place; X floats per state.
+// chunk states of each (b, h), in place; X floats per state.  The states are
+// read in groups of 16 whose loads are all in flight together (one memory
+// latency per group instead of one per state).
 __global__ void chunk_scan_kernel(float* buf, int NC, int64_t X, int64_t total, int reverse) {
+  constexpr int G = 16;
   const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int64_t bh = idx / X, x = idx - bh * X;
   float* p = buf + bh * NC * X + x;
   float run = 0.f;
-  for (int i = 0; i < NC; ++i) {
-    const int c = reverse ? NC - 1 - i : i;
-    const float v = p[c * X];
-    p[c * X] = run;
-    run += v;
+  for (int i0 = 0; i0 < NC; i0 += G) {
+    float v[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int i = i0 + j;
+      const int c = reverse ? NC - 1 - i : i;
+      v[j] = i < NC ? p[(int64_t)c * X] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int i = i0 + j;
+      const int c = reverse ? NC - 1 - i : i;
+      if (i < NC) p[(int64_t)c * X] = run;
+      run += v[j];
+    }
   }
 }
 
@@ -558,11 +572,14 @@ struct Launcher {
     const int64_t kt = Ktot > 0 ? (int64_t)Ktot * (batches / NCB) : (int64_t)K * batches;
     flops += 2.0 * M * N * (double)kt;
     KernelTimer tm(kBwdGemm, st);
-    // the feature exponents and the intra-chunk score gradients (whose sums
-    // cancel exactly where the output does not depend on q and k) keep the
-    // fp32 products
+    // bf16 inputs: the plain products from hi/lo parts; the feature exponents
+    // and the intra-chunk score gradients (whose sums cancel exactly where the
+    // output does not depend on q and k) keep the fp32 products.  (One fp16
+    // product for the feature exponents, as in the forward, measured no faster
+    // here: this kernel is bound by staging its fp32 operands, not by the
+    // products.)
     if (hilo && epi == kEpiPlain)
-      hipLaunchKernelGGL((bgemm_kernel<TA, TB, PROD, XC, true>), dim3((unsigned)grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((bgemm_kernel<TA, TB, PROD, XC, kHiLo>), dim3((unsigned)grid), dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((bgemm_kernel<TA, TB, PROD, XC>), dim3((unsigned)grid), dim3(256), 0, st, a);
     if (hipGetLastError() != hipSuccess) status = DARK_ERR_HIP;
