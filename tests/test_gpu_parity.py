@@ -345,3 +345,38 @@ def test_graph_replay_matches_eager():
         assert torch.equal(out, eager), f"replay {rep}"
         run_device(w, dev)                  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ---- key rows far outside the fp16 range of the exponent operands ---------------
+# The bf16 path holds the exponent's operands in fp16, clamped to +-65504.  A key
+# row scaled by 1e6 has |u|^2 / 2 of order 1e12, so its feature is exactly 0 in
+# the oracle; the kernels form |u|^2 / 2 in fp32 from the unclamped projection,
+# so the key gets weight 0 there too and every output stays finite.
+HUGE = [
+    # name,              L,   d_h, m,   r,  causal  (r = 64: folded exponent; r = 16: unfolded)
+    ("huge_fold_c",      200, 64,  128, 64, True),
+    ("huge_fold_nc",     200, 64,  128, 64, False),
+    ("huge_unfold_nc",   300, 64,  256, 16, False),
+]
+
+
+@pytest.mark.parametrize("case", HUGE, ids=[c[0] for c in HUGE])
+def test_huge_key_rows_get_zero_weight(case):
+    from random_feature_linear_amd.workloads import round_bf16
+    name, L, dh, m, r, causal = case
+    w = Workload(name=name, B=2, H=2, H_kv=2, L=L, d_h=dh, m=m, r=r, dtype="bf16", causal=causal,
+                 per_head_geometry=True, orthogonal=True, seed=zlib.crc32(name.encode()) % 100000,
+                 m_kind="eye_noise", m_noise=0.3, x_kind="iid", mask_kind="none")
+    say(f"[parity] {name} L={L} r={r} causal={causal}: key rows scaled by 1e6")
+    inp = make_inputs(w)
+    rows = [3, 77, L - 1]
+    k = inp["k"].astype(np.float64)
+    k[:, :, rows, :] *= 1e6
+    inp["k"] = round_bf16(k.astype(np.float32)).astype(inp["k"].dtype)
+    assert np.max(np.abs(inp["k"])) > 1e5
+    out = host(run_device(w, device_inputs(w, inp)))
+    ref = oracle.attention(inp["q"], inp["k"], inp["v"], inp["M"], oracle_omega(w), mask=inp["mask"], causal=causal)
+    err = normwise_rel_err(out, ref)
+    say(f"[parity] {name}: normwise rel err {err:.3e}")
+    assert np.all(np.isfinite(out))
+    assert err <= TOL["bf16"], err
