@@ -2283,6 +2283,16 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
   T* sfrag = reinterpret_cast<T*>(base + pl.off_sfrag);
   float* zdelta = reinterpret_cast<float*>(base + pl.off_zdelta);
   float* zsum = reinterpret_cast<float*>(base + pl.off_zsum);
+  // Non-causal with one key-side unit per (b, h) and no exported state (short
+  // sequences, such as the tiny fp32 workload): the sum over units is that
+  // unit's state, in the same layout, so the query side reads it where the key
+  // side wrote it and the sum's launch is left out.
+  const bool one_unit = pl.mode == kPlanForward && !a.causal && pl.NU == 1 && a.S_out == nullptr &&
+                        a.z_out == nullptr;
+  if (one_unit) {
+    sfrag = sdelta;
+    zsum = zdelta;
+  }
   constexpr int NM = kParts<T>;
   {
     // Folded with d_h >= 32: W' by matrix products and M' in one launch;
@@ -2328,7 +2338,7 @@ dark_status launch_fwd_pad(const FwdArgs& a_in, const Plan& pl, void* ws, void* 
       hipLaunchKernelGGL((kstate_seq_kernel<T, DH, R16, FBW, PAD>), grid1, dim3(kThreads), 0, st, a, pl, mfrag,
                          ofrag, sdelta, zdelta);
   }
-  if (pl.mode != kPlanCross) {
+  if (pl.mode != kPlanCross && !one_unit) {
     const long n = (long)pl.BH * vblocks<DH>() * 2 * pl.FB * 64 + (long)pl.BH * pl.FB * 32;   // S lanes, z values
     const int blocks = (int)((n + 255) / 256);
     KernelTimer tm(kScan, stream);
