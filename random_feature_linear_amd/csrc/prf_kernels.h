@@ -1108,6 +1108,11 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int tb = s / FBW, f = s % FBW;
+      // fp32: feature blocks past the last one are skipped (a wave-uniform
+      // branch; on the bf16 path they run on clamped operands, no branch in
+      // the loop)
+      if constexpr (sizeof(T) == 4)
+        if (fb0 + f >= pl.FB) continue;
       f32x16 e;
       if constexpr (PIPE) {
         e = en;
