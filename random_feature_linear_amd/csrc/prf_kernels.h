@@ -2403,9 +2403,11 @@ dark_status launch_fwd_impl(const FwdArgs& a, const Plan& pl, void* ws, void* st
 // keys j, with u = d_h^(-1/4) M_h x for queries and keys alike.
 //
 // Workspace: the M' fragments, then ufrag[tensor][b h][32-token block][R16]
-// [part][lane][8]: the hi/lo operand fragments of u for q (tensor 0) and for k
-// as seen by query head h (tensor 1), in the order project_block leaves them
-// (the same for both, so the score sum runs over the same rank permutation).
+// [lane][8]: the operand fragments of u for q (tensor 0) and for k as seen by
+// query head h (tensor 1), in the order project_block leaves them (the same for
+// both, so the score sum runs over the same rank permutation).  On the bf16
+// path u is rounded once to fp16 (11 significant bits, clamped to +-65504) and
+// each score K-step is one fp16 product, as in the feature exponent.
 // ---------------------------------------------------------------------------
 // M' = d_h^(-1/4) M in fragment order (the projection operand).
 template <typename T>
@@ -2438,14 +2440,11 @@ __global__ __launch_bounds__(kThreads) void exact_proj_kernel(FwdArgs a, const T
   F xf[KD];
   load_rows<T, DH>(xf, base + (long)t * stride, t < a.L, g);
   const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * R32 * KD * NM * 64 * 8;
-  F uhi[R16], ulo[R16];
-  (void)project_block<T, DH, R16>(uhi, ulo, xf, mf, lane, 0.f);
-  T* dst = ufrag + (((long)tensor * BH + bh) * NBLK + blk) * R16 * NM * 64 * 8;
+  F uhi[R16], ulo[R16];   // one part: fp16 on the bf16 path (as the feature exponent), fp32 otherwise
+  (void)project_block<T, DH, R16, kH16<T>>(uhi, ulo, xf, mf, lane, 0.f);
+  T* dst = ufrag + (((long)tensor * BH + bh) * NBLK + blk) * R16 * 64 * 8;
 #pragma unroll
-  for (int kr = 0; kr < R16; ++kr) {
-    st8(dst + ((kr * NM) * 64 + lane) * 8, uhi[kr]);
-    if constexpr (NM == 2) st8(dst + ((kr * NM + 1) * 64 + lane) * 8, ulo[kr]);
-  }
+  for (int kr = 0; kr < R16; ++kr) st8(dst + (kr * 64 + lane) * 8, uhi[kr]);
 }
 
 // Softmax attention on the projected rows.  Workgroup: 128 queries of one (b,
@@ -2466,12 +2465,11 @@ template <typename T, int DH, int R16, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __restrict__ ufrag, int NBLK, int KS,
                                                           float* __restrict__ part) {
   typedef typename FragOf<T>::type F;
-  constexpr int NM = kParts<T>;
   constexpr int DB = vblocks<DH>();
   constexpr int TT = kTile;
   constexpr int VST = TT + 8;
   constexpr int VPT = vloads_per_thread<DH, TT>();
-  constexpr int UFR = R16 * NM * 64 * 8;   // elements of one block's u fragments
+  constexpr int UFR = R16 * 64 * 8;   // elements of one block's u fragments (one part)
   // ranks up to 64: a key tile's u fragments are staged in LDS beside V^T (the
   // next tile's fetched into registers during the current one); above, every
   // wave reads them from L2
@@ -2517,13 +2515,10 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
   // ranks up to 64: the query block's u fragments stay in registers; above,
   // both operands of the score products stream from memory (L1)
   constexpr bool QREG = R16 <= 4;
-  F qh[QREG ? R16 : 1], ql[QREG ? R16 : 1];
+  F qh[QREG ? R16 : 1];
   if constexpr (QREG) {
 #pragma unroll
-    for (int kr = 0; kr < R16; ++kr) {
-      qh[kr] = ld8(uq + ((kr * NM) * 64 + lane) * 8);
-      ql[kr] = ld8(uq + ((kr * NM + NM - 1) * 64 + lane) * 8);
-    }
+    for (int kr = 0; kr < R16; ++kr) qh[kr] = ld8(uq + (kr * 64 + lane) * 8);
   }
   const int tiles = kt1;                                // key tiles kt0 .. kt1 - 1
   // last key block this wave uses (a block past the sequence end holds no query
@@ -2561,18 +2556,16 @@ __global__ __launch_bounds__(kThreads) void exact_kernel(FwdArgs a, const T* __r
       s[4 * jj + 2] = x.z;
       s[4 * jj + 3] = x.w;
     }
-    auto kload = [&](int k, int part) -> F { return ld8(uk + ((k * NM + (part ? NM - 1 : 0)) * 64 + lane) * 8); };
+    // one-part operands: one fp16 product per K-step on the bf16 path
+    auto kload = [&](int k, int) -> F { return ld8(uk + (k * 64 + lane) * 8); };
     if constexpr (QREG) {
-      F kh[R16], kl[R16];
+      F kh[R16];
 #pragma unroll
-      for (int kr = 0; kr < R16; ++kr) {
-        kh[kr] = kload(kr, 0);
-        kl[kr] = kload(kr, 1);
-      }
-      s = exponent<T, R16, true, true>(kh, kl, qh, ql, s);
+      for (int kr = 0; kr < R16; ++kr) kh[kr] = kload(kr, 0);
+      s = exponent<T, R16, true, true, kH16<T>>(kh, kh, qh, qh, s);
     } else {
-      auto qload = [&](int k, int part) -> F { return ld8(uq + ((k * NM + (part ? NM - 1 : 0)) * 64 + lane) * 8); };
-      s = exponent_stream<T, R16, true, true>(kload, qload, s);
+      auto qload = [&](int k, int) -> F { return ld8(uq + (k * 64 + lane) * 8); };
+      s = exponent_stream<T, R16, true, true, kH16<T>>(kload, qload, s);
     }
     if (CAUSAL && kb == qb) {   // the diagonal block: key crow(i, g) visible to query c iff crow <= c
 #pragma unroll
