@@ -246,6 +246,27 @@ __device__ __forceinline__ void store_out(bf16* p, float x) { *p = (bf16)x; }
 __device__ __forceinline__ void store_out(float* p, float x) { *p = x; }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc += (fragment of M' at p) x.  bf16 path: with MH (the folded exponent's
+// and the exact path's form) M' is one fp16 part and x is already fp16, one
+// fp16 product; otherwise M' is a bf16 hi part at p and lo part 64 x 8
+// elements further, and x is bf16 (exact), two products.  fp32: one product.
+template <typename T, bool MH>
+__device__ __forceinline__ f32x16 m_product(const T* p, const typename FragOf<T>::type& x, f32x16 acc) {
+  if constexpr (kH16<T> && MH) {
+    return mma_h(ld8(p), x, acc);
+  } else if constexpr (kParts<T> == 2) {
+    acc = mma(ld8(p), x, acc);
+    return mma(ld8(p + 64 * 8), x, acc);
+  } else {
+    return mma(ld8(p), x, acc);
+  }
+}
+// the token rows of a projection in place: fp16 on the bf16 path
+template <typename F, int N> __device__ __forceinline__ void rows_to_h(F (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = to_h(x[i]);
+}
+
 // ---- the feature map of one 32-token block -----------------------------------
 // Token row t as the B-operand fragments X^T of the projection (K-steps of 16
 // over d_h); rows at or past the end are zero.
@@ -260,8 +281,9 @@ __device__ __forceinline__ void load_rows(typename FragOf<T>::type (&xf)[DH / 16
 // u^T = M' x^T for a 32-token block (rank index in rows, token c in the lane),
 // returned as hi / lo operand fragments over the rank index (K-steps of 16),
 // or (H16, bf16 path) as one fp16 fragment per K-step in uhi, plus the
-// exp2-domain shift log2(e) |u|^2 / 2 + log2(m) / 2 of token c.
-template <typename T, int DH, int R16, bool H16 = false>
+// exp2-domain shift log2(e) |u|^2 / 2 + log2(m) / 2 of token c.  MH: M' in
+// its one-part fp16 form, the token rows xf already fp16 (see m_product).
+template <typename T, int DH, int R16, bool H16 = false, bool MH = false>
 __device__ __forceinline__ float project_block(typename FragOf<T>::type (&uhi)[R16],
                                                typename FragOf<T>::type (&ulo)[R16],
                                                const typename FragOf<T>::type (&xf)[DH / 16],
@@ -275,9 +297,7 @@ __device__ __forceinline__ float project_block(typename FragOf<T>::type (&uhi)[R
     f32x16 acc = zero16();
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd)
-#pragma unroll
-      for (int part = 0; part < NM; ++part)
-        acc = mma(ld8(mfrag + (((rb * KD + kd) * NM + part) * 64 + lane) * 8), xf[kd], acc);
+      acc = m_product<T, MH>(mfrag + ((rb * KD + kd) * NM * 64 + lane) * 8, xf[kd], acc);
 #pragma unroll
     for (int i = 0; i < 16; ++i) ss += acc[i] * acc[i];
 #pragma unroll
@@ -378,8 +398,9 @@ __device__ __forceinline__ f32x16 exponent_stream(UL uload, OL oload, f32x16 e) 
 }
 
 // Only the exp2-domain shift log2(e) |u|^2 / 2 + log2(m) / 2 of token c of a
-// 32-token block (the folded exponent does not need u itself).
-template <typename T, int DH, int R16>
+// 32-token block (the folded exponent does not need u itself).  MH as in
+// project_block.
+template <typename T, int DH, int R16, bool MH = false>
 __device__ __forceinline__ float project_shift(const typename FragOf<T>::type (&xf)[DH / 16], const T* mfrag,
                                                int lane, float half_log2m) {
   constexpr int KD = DH / 16;
@@ -390,10 +411,7 @@ __device__ __forceinline__ float project_shift(const typename FragOf<T>::type (&
   for (int rb = 0; rb < R32; ++rb) {
     f32x16 acc = zero16();
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd)
-#pragma unroll
-      for (int part = 0; part < NM; ++part)
-        acc = mma(ld8(mfrag + (((rb * KD + kd) * NM + part) * 64 + lane) * 8), xf[kd], acc);
+    for (int kd = 0; kd < KD; ++kd) acc = m_product<T, MH>(mfrag + ((rb * KD + kd) * NM * 64 + lane) * 8, xf[kd], acc);
 #pragma unroll
     for (int i = 0; i < 16; ++i) ss += acc[i] * acc[i];
     // large M' (d_h = 256): one 32-row slice of operands in flight at a time
@@ -403,16 +421,20 @@ __device__ __forceinline__ float project_shift(const typename FragOf<T>::type (&
   return 0.5f * kLog2e * ss + half_log2m;
 }
 
-// Fragment lane idx of M' = s M (bf16: hi and lo parts; see prep_kernel).
+// Fragment lane idx of M' = s M (see prep_kernel): fp32; on the bf16 path
+// either (h16: the folded exponent and the exact path) one fp16 value in part
+// 0 of each fragment, part 1 neither written nor read, or a bf16 high part and
+// a bf16 remainder (the unfolded exponent, whose token rows stay bf16).
 template <typename T>
 __device__ __forceinline__ void mfrag_lane(long idx, const float* __restrict__ M, T* __restrict__ mfrag, int r,
-                                           int d_h, int R16, float s) {
+                                           int d_h, int R16, float s, bool h16) {
   constexpr int NM = kParts<T>;
   const int R32 = (R16 + 1) / 2;
   const int KD = d_h / 16;
   const int lane = (int)(idx & 63), c = lane & 31, g = lane >> 5;
   const long f = idx >> 6;
   const int part = (int)(f % NM);
+  if (kH16<T> && h16 && part != 0) return;
   const int kd = (int)((f / NM) % KD);
   const int rb = (int)((f / ((long)NM * KD)) % R32);
   const int hm = (int)(f / ((long)NM * KD * R32));
@@ -424,6 +446,13 @@ __device__ __forceinline__ void mfrag_lane(long idx, const float* __restrict__ M
     const float x = (row < r) ? s * M[((long)hm * r + row) * d_h + col] : 0.f;
     const float hi = NM == 2 ? bf16_hi(x) : x;
     v[e] = part == 0 ? hi : x - hi;
+    if (kH16<T> && h16) v[e] = x;
+  }
+  if constexpr (kH16<T>) {
+    if (h16) {
+      st8(mfrag + idx * 8, make_frag_h(v));
+      return;
+    }
   }
   typename FragOf<T>::type fr;
   make_frag(fr, v);
@@ -499,7 +528,7 @@ __global__ void prep_kernel(const float* __restrict__ M, const float* __restrict
       continue;
     }
     if (m_side) {
-      mfrag_lane<T>(j, M, mfrag, r, d_h, R16, s);
+      mfrag_lane<T>(j, M, mfrag, r, d_h, R16, s, fold != 0);
       continue;
     }
     const int k = (int)(f % R16);
@@ -546,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const float* __restrict_
     if ((int)blockIdx.x >= nW) {
       const long nM = (long)HM * ((R16 + 1) / 2) * (d_h / 16) * kParts<T> * 64;
       const long idx = (long)(blockIdx.x - nW) * kThreads + threadIdx.x;
-      if (idx < nM) mfrag_lane<T>(idx, M, mfrag, r, d_h, R16, s);
+      if (idx < nM) mfrag_lane<T>(idx, M, mfrag, r, d_h, R16, s, true);
       return;
     }
   }
@@ -711,6 +740,10 @@ __global__ __launch_bounds__(kThreads, 2) void shift_kernel(FwdArgs a, const T* 
   F xf[RB][KD];
 #pragma unroll
   for (int j = 0; j < RB; ++j) load_rows<T, DH>(xf[j], base + (long)(t0 + 32 * j) * stride, t0 + 32 * j < a.L, g);
+  if constexpr (kH16<T>) {   // fp16 rows against the one-part fp16 M'
+#pragma unroll
+    for (int j = 0; j < RB; ++j) rows_to_h(xf[j]);
+  }
   put(0);
   __syncthreads();
   float ss[RB];
@@ -725,11 +758,13 @@ __global__ __launch_bounds__(kThreads, 2) void shift_kernel(FwdArgs a, const T* 
     for (int j = 0; j < RB; ++j) u[j] = zero16();
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd) {
+      {   // part 0 of the slice: M' (fp16 on the bf16 path; part 1 is not read)
+        const F mfr = ld8(sm + ((kd * NM) * 64 + lane) * 8);
 #pragma unroll
-      for (int part = 0; part < NM; ++part) {
-        const F mfr = ld8(sm + ((kd * NM + part) * 64 + lane) * 8);
-#pragma unroll
-        for (int j = 0; j < RB; ++j) u[j] = mma(mfr, xf[j][kd], u[j]);
+        for (int j = 0; j < RB; ++j) {
+          if constexpr (kH16<T>) u[j] = mma_h(mfr, xf[j][kd], u[j]);
+          else u[j] = mma(mfr, xf[j][kd], u[j]);
+        }
       }
       if constexpr (SL > 8)   // bound the slice fragments in flight
         if (kd % 4 == 3) __builtin_amdgcn_sched_barrier(0);
@@ -1044,10 +1079,11 @@ __global__ __launch_bounds__(kThreads, (kstate_pipe<T, DH, R16, FBW>() ? 2 : 1))
     const int t = tt + 32 * w + c;
     const bool ok = t < t_end;
     float shift = 0.f;
-    if constexpr (FOLD) {   // the exponent reads the token rows themselves (as fp16)
-      if (!pl.kshift) shift = project_shift<T, DH, R16>(xpre, msrc_t, lane, half_log2m);
+    if constexpr (FOLD) {   // the exponent reads the token rows themselves, as fp16
+      rows_to_h(xpre);
+      if (!pl.kshift) shift = project_shift<T, DH, R16, true>(xpre, msrc_t, lane, half_log2m);
 #pragma unroll
-      for (int k = 0; k < UK; ++k) st8(&s_u[buf][w][0][k][lane * 8], to_h(xpre[k]));
+      for (int k = 0; k < UK; ++k) st8(&s_u[buf][w][0][k][lane * 8], xpre[k]);
     } else {
       F uhi[R16], ulo[R16];
       shift = project_block<T, DH, R16, kH16<T>>(uhi, ulo, xpre, msrc_t, lane, half_log2m);
@@ -1283,9 +1319,7 @@ __global__ __launch_bounds__(kThreads) void kstate_seq_kernel(FwdArgs a, Plan pl
         f32x16 u = zero16();
 #pragma unroll
         for (int kd = 0; kd < KD; ++kd)
-#pragma unroll
-          for (int part = 0; part < NM; ++part)
-            u = mma(ld8(mf + (((rb * KD + kd) * NM + part) * 64 + lane) * 8), xf[kd], u);
+          u = m_product<T, false>(mf + ((rb * KD + kd) * NM * 64 + lane) * 8, xf[kd], u);
 #pragma unroll
         for (int i = 0; i < 16; ++i) ss += u[i] * u[i];
 #pragma unroll
@@ -1688,6 +1722,10 @@ void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
     const int t = t0 + 32 * (w * NQB + j) + c;
     const bool ok = t < a.L;
     shq[j] = 0.f;
+    if constexpr (FOLD && kH16<T>) {   // the token rows as fp16 operands of the projection and exponent
+      rows_to_h(*reinterpret_cast<F(*)[KD]>(uqh[j]));
+      if constexpr (CAUSAL) rows_to_h(*reinterpret_cast<F(*)[KD]>(ukh[j]));
+    }
     if constexpr (!FOLD)
       (void)project_block<T, DH, R16, kH16<T>>(*reinterpret_cast<F(*)[R16]>(uqh[j]),
                                                *reinterpret_cast<F(*)[R16]>(uql[j]), xq[FOLD ? 0 : j], msrc, lane,
@@ -1698,20 +1736,13 @@ void qout_kernel(FwdArgs a, Plan pl, const T* __restrict__ mfrag,
         initk[j] = ok ? a.kshift[(long)bh * a.L + t] : -INFINITY;
       } else {
         if constexpr (FOLD)
-          sh = project_shift<T, DH, R16>(*reinterpret_cast<F(*)[KD]>(ukh[j]), msrc, lane, half_log2m);
+          sh = project_shift<T, DH, R16, true>(*reinterpret_cast<F(*)[KD]>(ukh[j]), msrc, lane, half_log2m);
         else
           sh = project_block<T, DH, R16, kH16<T>>(*reinterpret_cast<F(*)[R16]>(ukh[j]),
                                                   *reinterpret_cast<F(*)[R16]>(ukl[j]), xk[FOLD ? 0 : j], msrc, lane,
                                                   half_log2m);
         const bool valid = ok && (mrow == nullptr || mrow[t] != 0);
         initk[j] = valid ? -sh : -INFINITY;
-      }
-    }
-    if constexpr (FOLD && kH16<T>) {   // the token rows as the exponent's fp16 operands
-#pragma unroll
-      for (int k = 0; k < UK; ++k) {
-        uqh[j][k] = to_h(uqh[j][k]);
-        if constexpr (CAUSAL) ukh[j][k] = to_h(ukh[j][k]);
       }
     }
   }
@@ -2067,24 +2098,21 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
   store_vt<T, DH, TT, VST, kThreads8>(s_vt, vr, tid);
   __syncthreads();                      // M', V^T and every wave's copies visible
   const T* msrc = M_LDS ? s_kf : mf;
+  if constexpr (FOLD && kH16<T>) {   // the token rows as fp16 operands of the projection and exponent
+    rows_to_h(*reinterpret_cast<F(*)[KD]>(uqh));
+    rows_to_h(*reinterpret_cast<F(*)[KD]>(ukh));
+  }
   if constexpr (!FOLD)
     (void)project_block<T, DH, R16, kH16<T>>(*reinterpret_cast<F(*)[R16]>(uqh), *reinterpret_cast<F(*)[R16]>(uql),
                                              xq, msrc, lane, half_log2m);
   if (!(FOLD && pl.kshift)) {
     float sh;
     if constexpr (FOLD)
-      sh = project_shift<T, DH, R16>(*reinterpret_cast<F(*)[KD]>(ukh), msrc, lane, half_log2m);
+      sh = project_shift<T, DH, R16, true>(*reinterpret_cast<F(*)[KD]>(ukh), msrc, lane, half_log2m);
     else
       sh = project_block<T, DH, R16, kH16<T>>(*reinterpret_cast<F(*)[R16]>(ukh), *reinterpret_cast<F(*)[R16]>(ukl),
                                               xk, msrc, lane, half_log2m);
     initk = kvalid ? -sh : -INFINITY;
-  }
-  if constexpr (FOLD && kH16<T>) {   // the token rows as the exponent's fp16 operands
-#pragma unroll
-    for (int k = 0; k < UK; ++k) {
-      uqh[k] = to_h(uqh[k]);
-      ukh[k] = to_h(ukh[k]);
-    }
   }
 
   auto op = [&](int fb, int f) { return ld8(s_op + ((fb * NSTEP + f) * 64 + lane) * 8); };
@@ -2414,7 +2442,7 @@ template <typename T>
 __global__ void mfrag_kernel(const float* __restrict__ M, T* __restrict__ mfrag, long n, int r, int d_h, int R16,
                              float s) {
   for (long idx = blockIdx.x * (long)blockDim.x + threadIdx.x; idx < n; idx += (long)gridDim.x * blockDim.x)
-    mfrag_lane<T>(idx, M, mfrag, r, d_h, R16, s);
+    mfrag_lane<T>(idx, M, mfrag, r, d_h, R16, s, true);
 }
 
 // u of every 32-token block of q and of k (one wave per block).
@@ -2439,9 +2467,10 @@ __global__ __launch_bounds__(kThreads) void exact_proj_kernel(FwdArgs a, const T
   const int t = blk * 32 + c;
   F xf[KD];
   load_rows<T, DH>(xf, base + (long)t * stride, t < a.L, g);
+  if constexpr (kH16<T>) rows_to_h(xf);
   const T* mf = mfrag + (long)(a.m_per_head ? h : 0) * R32 * KD * NM * 64 * 8;
   F uhi[R16], ulo[R16];   // one part: fp16 on the bf16 path (as the feature exponent), fp32 otherwise
-  (void)project_block<T, DH, R16, kH16<T>>(uhi, ulo, xf, mf, lane, 0.f);
+  (void)project_block<T, DH, R16, kH16<T>, true>(uhi, ulo, xf, mf, lane, 0.f);
   T* dst = ufrag + (((long)tensor * BH + bh) * NBLK + blk) * R16 * 64 * 8;
 #pragma unroll
   for (int kr = 0; kr < R16; ++kr) st8(dst + (kr * 64 + lane) * 8, uhi[kr]);
