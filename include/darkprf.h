@@ -174,11 +174,11 @@ size_t dark_prf_workspace_bytes(const dark_prf_desc* desc);
  *         dark_prf_decode_step
  *   workspace, ws_bytes: device scratch of at least dark_prf_workspace_bytes
  * All device pointers are read or written on `stream` only.
- * Precision (bf16 inputs): u = d_h^(-1/4) M x from bf16 hi/lo parts of M with
- * fp32 sums; the feature exponent from u and omega (or x and omega M) rounded
- * once to fp16, clamped to +-65504, in fp16 matrix products with fp32
- * accumulation; features rounded to bf16 for the contractions, states and
- * sums fp32.  Inputs whose entries (or projections) exceed the fp16 range are
+ * Precision (bf16 inputs): the feature exponent and |u|^2 from fp16 operands
+ * (u and omega, or x with omega M and M, each rounded once to fp16, clamped to
+ * +-65504; u itself from bf16 hi/lo parts of M where it is formed) in matrix
+ * products with fp32 accumulation; features rounded to bf16 for the
+ * contractions, states and sums fp32.  Inputs whose entries (or projections) exceed the fp16 range are
  * outside the supported range.  fp32 inputs: fp32 throughout.
  */
 dark_status dark_prf_fwd(const dark_prf_desc* desc, const void* q, const void* k,

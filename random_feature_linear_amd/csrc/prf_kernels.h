@@ -32,13 +32,14 @@
 // reaches magnitudes of ten and more, and a weight error of e per key shows up
 // as a relative output error of about e (outputs are averages of zero-mean
 // values), so the exponent's operands are not plain bf16 (8 significant
-// bits).  u = M' x is formed from M' as a pair of bf16 values hi + lo (about
-// 16 significant bits: u = M'_hi x + M'_lo x, fp32 accumulate); then u and
-// omega' (or, folded, the token row x and W' = omega' M') enter the exponent
-// as fp16 values (11 significant bits, range clamped to +-65504) in one fp16
-// product per K-step.  The exponent's error is then about 2^-12 of its terms,
-// below the 2^-9 rounding of the features themselves to bf16 for the
-// contractions.
+// bits).  Unfolded, u = M' x is formed from M' as a pair of bf16 values hi +
+// lo (about 16 significant bits: u = M'_hi x + M'_lo x, fp32 accumulate) with
+// the bf16 rows x as they are; then u and omega' enter the exponent as fp16
+// values (11 significant bits, range clamped to +-65504) in one fp16 product
+// per K-step.  Folded, the token row x (converted once to fp16) meets W' =
+// omega' M' in fp16 for the exponent and M' in fp16 for |u|^2 / 2.  The
+// exponent's error is then about 2^-12 of its terms, below the 2^-9 rounding
+// of the features themselves to bf16 for the contractions.
 //
 // The normaliser z = Phi(K)^T 1 is kept apart from the state S in fp32, so S
 // holds only V's column blocks.  The key side forms z as a column of ones
