@@ -275,8 +275,14 @@ template <typename T, int DH>
 __device__ __forceinline__ void load_rows(typename FragOf<T>::type (&xf)[DH / 16], const T* row, bool ok,
                                           int g) {
   typedef typename FragOf<T>::type F;
+  // loads under the lane mask into zeroed registers: a select after the load
+  // would make the code right behind it wait for the load
 #pragma unroll
-  for (int kd = 0; kd < DH / 16; ++kd) xf[kd] = ok ? ld8(row + kd * 16 + 8 * g) : zero_frag<F>();
+  for (int kd = 0; kd < DH / 16; ++kd) xf[kd] = zero_frag<F>();
+  if (ok) {
+#pragma unroll
+    for (int kd = 0; kd < DH / 16; ++kd) xf[kd] = ld8(row + kd * 16 + 8 * g);
+  }
 }
 
 // u^T = M' x^T for a 32-token block (rank index in rows, token c in the lane),
@@ -2066,15 +2072,29 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
     f -= NOF;
     return sf + (((f >> 1) * FK + 2 * fb + (f & 1)) * 64 + lane) * 8;
   };
-  // M' (in the key-feature buffers, free until the first step) and every
-  // step's operands go to LDS by DMA before the rows are loaded.
+  // M' (in the key-feature buffers, free until the first step) and the
+  // operands of each half's first step (steps 0 and nit) go to LDS by DMA
+  // before the rows are loaded.  The other steps' operands are requested into
+  // registers last, PL per wave (a fixed count, so that one explicit counter
+  // wait covers everything before them), and written to LDS during the first
+  // step: their loads overlap the projections and the first step.
   constexpr int MFRG = ((R16 + 1) / 2) * KD * NM;
   constexpr bool M_LDS = MFRG * 64 * 8 <= KF_ELEMS;
+  const int nit = (pl.FB + 1) >> 1;   // steps per half (the second half may have one fewer)
+  const int nE = pl.FB > 1 ? 2 : 1;   // early steps: 0 and nit
+  const int nLate = (pl.FB - nE) * NSTEP;
+  constexpr int PL = ((ALLFB - 2) * NSTEP + kWaves8 - 1) / kWaves8;   // late slots per wave
+  static_assert(PL <= 15, "one vmcnt immediate");
+  auto late_slot = [&](int l, int& fb, int& f) {   // late slot l: step fb, slot f
+    const int j = l / NSTEP;
+    f = l - j * NSTEP;
+    fb = j < nit - 1 ? 1 + j : nit + 1 + (j - (nit - 1));
+  };
   if constexpr (M_LDS)
     for (int idx = w; idx < MFRG; idx += kWaves8) dma16(mf + ((long)idx * 64 + lane) * 8, s_kf + idx * 64 * 8);
-  for (int idx = w; idx < pl.FB * NSTEP; idx += kWaves8) {
-    const int fb = idx / NSTEP, f = idx - fb * NSTEP;
-    dma16(gsrc(fb, f), s_op + idx * 64 * 8);
+  for (int idx = w; idx < nE * NSTEP; idx += kWaves8) {
+    const int fb = idx < NSTEP ? 0 : nit, f = idx < NSTEP ? idx : idx - NSTEP;
+    dma16(gsrc(fb, f), s_op + (fb * NSTEP + f) * 64 * 8);
   }
 
   // ---- exponent operands of query block qb and key block qb ----
@@ -2088,14 +2108,29 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
   constexpr int VPT = vloads_per_thread<DH, TT, kThreads8>();
   F vr[VPT];
   load_v<T, DH, TT, kThreads8>(vr, vbase, a.vs[2], t0, a.L, tid);
+  // the key's shift (precomputed) or mask byte, read only once the
+  // projections need it (a select here would wait for the load at once)
   float initk = -INFINITY;
-  bool kvalid = ok;
+  int kmask = 1;
   if (FOLD && pl.kshift) {
     if (ok) initk = a.kshift[(long)bh * a.L + t];
-  } else {
-    kvalid = ok && (mrow == nullptr || mrow[t] != 0);
+  } else if (mrow != nullptr && ok) {
+    kmask = mrow[t];
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): rows, V and this wave's copies
+  // the late steps' operands: PL requests per wave, the ones past the last
+  // slot from slot 0's address and never stored
+  F late[PL];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < PL; ++p) {
+    const int l = w + kWaves8 * p;
+    int fb = 0, f = 0;
+    if (l < nLate) late_slot(l, fb, f);
+    late[p] = ld8(gsrc(fb, f));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | PL);   // vmcnt(PL): rows, V and this wave's copies (not the late requests)
+  __builtin_amdgcn_sched_barrier(0);
   store_vt<T, DH, TT, VST, kThreads8>(s_vt, vr, tid);
   __syncthreads();                      // M', V^T and every wave's copies visible
   const T* msrc = M_LDS ? s_kf : mf;
@@ -2113,7 +2148,7 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
     else
       sh = project_block<T, DH, R16, kH16<T>>(*reinterpret_cast<F(*)[R16]>(ukh), *reinterpret_cast<F(*)[R16]>(ukl),
                                               xk, msrc, lane, half_log2m);
-    initk = kvalid ? -sh : -INFINITY;
+    initk = (ok && kmask != 0) ? -sh : -INFINITY;
   }
 
   auto op = [&](int fb, int f) { return ld8(s_op + ((fb * NSTEP + f) * 64 + lane) * 8); };
@@ -2153,7 +2188,6 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
 #pragma unroll
   for (int kb2 = 0; kb2 < NB; ++kb2) at[kb2] = zero16();
 
-  const int nit = (pl.FB + 1) >> 1;   // steps per half (the second half may have one fewer)
   for (int it = 0; it < nit; ++it) {
     const int fb = half * nit + it;
     const bool live = fb < pl.FB;
@@ -2209,7 +2243,18 @@ __global__ __launch_bounds__(kThreads8) void qout8_kernel(FwdArgs a, Plan pl, co
         for (int k = 0; k < 2; ++k) st8(kbuf + ((qb * 2 + k) * 64 + lane) * 8, acc_frag<F>(e, k));
       }
     }
-    __syncthreads();   // this step's key features of the half's four blocks are in
+    if (it == 0) {   // the late steps' operands, read from the next step on
+#pragma unroll
+      for (int p = 0; p < PL; ++p) {
+        const int l = w + kWaves8 * p;
+        if (l < nLate) {
+          int fb2, f2;
+          late_slot(l, fb2, f2);
+          st8(s_op + ((fb2 * NSTEP + f2) * 64 + lane) * 8, late[p]);
+        }
+      }
+    }
+    __syncthreads();   // this step's key features of the half's four blocks (and the late operands) are in
     if (live) {
 #pragma unroll
       for (int kb2 = 0; kb2 < NB; ++kb2)

@@ -414,14 +414,27 @@ def qout8_model(cfg: QoutConfig, mutate=frozenset()):
         for k in range(uk):
             op_read(w, fb, k)
 
+    # each half's first step (0 and nit) is copied by DMA at the start; the
+    # other steps' slots are requested into registers, PL per wave, and
+    # written to LDS in the first step, before its barrier
+    nit = (cfg.fb + 1) // 2
+    early = [0] + ([nit] if cfg.fb > 1 else [])
+    n_late = (cfg.fb - len(early)) * nstep
+    pl = ((cfg.allfb - 2) * nstep + WAVES8 - 1) // WAVES8
+
+    def late_slot(l):
+        j, f = divmod(l, nstep)
+        return (1 + j if j < nit - 1 else nit + 1 + (j - (nit - 1))), f
+
     def wave(w):
         half = w // WAVES
         qb = w % WAVES if half == 0 else WAVES - 1 - w % WAVES   # reversed in the second half
         if m_lds:
             for idx in range(w, mfrg, WAVES8):
                 tr.dma(w, "s_kf", idx * 512 * e)
-        for idx in range(w, cfg.fb * nstep, WAVES8):
-            tr.dma(w, "s_op", idx * 512 * e)
+        for idx in range(w, len(early) * nstep, WAVES8):
+            fb_e, f = early[idx // nstep], idx % nstep
+            tr.dma(w, "s_op", (fb_e * nstep + f) * 512 * e)
         if "no_wait8" not in tr.mutate:
             tr.waitcnt(w)
         store_vt(tr, w, "s_vt", 0, dh, 128, vst, e, nt=64 * WAVES8)
@@ -436,7 +449,6 @@ def qout8_model(cfg: QoutConfig, mutate=frozenset()):
         exponent_reads(w, 0)                             # the query shift
         if m_lds and "no_m_barrier8" not in tr.mutate:
             yield                                        # M' no longer read
-        nit = (cfg.fb + 1) // 2
         for it in range(nit):
             fb = half * nit + it
             live = fb < cfg.fb
@@ -452,8 +464,20 @@ def qout8_model(cfg: QoutConfig, mutate=frozenset()):
                     exponent_reads(w, fb)                # keys
                 for k in range(2):
                     tr.write(w, "s_kf", frag_lanes(kbase + (qb * 2 + k) * 512, e), 8 * e)
+            if it == 0 and "late8_after_barrier" not in tr.mutate:
+                for p_ in range(pl):
+                    l = w + WAVES8 * p_
+                    if l < n_late:
+                        fb2, f2 = late_slot(l)
+                        tr.write(w, "s_op", frag_lanes((fb2 * nstep + f2) * 512, e), 8 * e)
             if "no_kbuf8_barrier" not in tr.mutate:
                 yield
+            if it == 0 and "late8_after_barrier" in tr.mutate:   # planted: the late slots written too late
+                for p_ in range(pl):
+                    l = w + WAVES8 * p_
+                    if l < n_late:
+                        fb2, f2 = late_slot(l)
+                        tr.write(w, "s_op", frag_lanes((fb2 * nstep + f2) * 512, e), 8 * e)
             if live:
                 for kb2 in range(qb + 1):
                     for k in range(2):

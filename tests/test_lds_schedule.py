@@ -61,7 +61,7 @@ def test_model_catches_planted_query_side_mistakes(mutation):
 
 
 @pytest.mark.parametrize("mutation", ["no_wait8", "no_m_barrier8", "kbuf8_index_fixed", "no_kbuf8_barrier",
-                                      "no_exchange_barrier"])
+                                      "no_exchange_barrier", "late8_after_barrier"])
 def test_model_catches_planted_eight_wave_mistakes(mutation):
     assert _first_caught(lm.qout8_model, QOUT8, mutation), f"{mutation} not caught"
 
