@@ -287,8 +287,10 @@ dark_status dark_prf_cross_fwd(const dark_prf_desc* desc, const void* q, const f
  * over the keys j that are valid under `mask` and, when desc->causal, j <= t;
  * a row with no such key is 0.  This is the m -> infinity limit of
  * dark_prf_fwd on the same inputs.  Computed with a row-maximum shift and
- * fp32 accumulation; the weights are rounded to the input dtype for the
- * products with V.  omega and desc->m are not used (m must still be valid).
+ * fp32 accumulation; for bf16 inputs the scores u_t . u_j come from u rounded
+ * once to fp16 (clamped to +-65504) in fp16 matrix products, and the weights
+ * are rounded to the input dtype for the products with V.  omega and desc->m
+ * are not used (m must still be valid).
  *
  * dark_prf_exact_workspace_bytes - device workspace dark_prf_exact_fwd needs
  * (M' and the projected rows of q and k); 0 for an invalid descriptor.
