@@ -515,14 +515,15 @@ def qout8_model(cfg: QoutConfig, mutate=frozenset()):
 
 
 def qout8_cases():
-    """The eight-wave query side: bf16, causal, every step staged, m a multiple of 32."""
+    """The eight-wave query side: bf16, causal, m a multiple of 32; every step
+    count from 1 to 8 (each splits differently into early and late steps)."""
     out = []
     for dh in HEAD_DIMS:
         for r16 in RANK_BLOCKS:
             if not (qout_all_fits(2, dh, r16) and qout8_fits(2, dh, r16)):
                 continue
             fold = fold_exponent(2, dh, r16)
-            for fb in (1, 2, 3, 8):
+            for fb in range(1, 9):
                 fbw = 2 if dh <= 64 else 1
                 nf = -(-fb // (4 * fbw))
                 kshift = fold and (nf > 1 or dh >= 128)

@@ -73,6 +73,11 @@ SMALL = [
     # folded exponent with two feature slices: key shifts computed once up front
     ("bf16_d64_nc_m512", "bf16", 1, 2, 1,  300, 64,  512, 64,  False, True,  True,  "random"),
     ("f32_d256_c",     "f32",  1, 1, 1,   70,  256, 32,  64,  True,  True,  True,  "none"),
+    # the eight-wave causal query side with 1, 5 and 7 feature steps (each half's
+    # first step copied up front, the others staged through registers)
+    ("bf16_d64_c_fb1", "bf16", 1, 2, 2,   300, 64,  32,  64,  True,  True,  True,  "tail"),
+    ("bf16_d64_c_fb5", "bf16", 2, 2, 1,   260, 64,  160, 64,  True,  True,  True,  "tail"),
+    ("bf16_d64_c_fb7", "bf16", 1, 3, 3,   390, 64,  224, 64,  True,  True,  False, "random"),
 ]
 
 
