@@ -90,15 +90,16 @@ class Tracker:
         self.r_epoch[name][b] = self.epoch
         self.r_mask[name][b] |= 1 << wave
 
-    def dma(self, wave, name, start):
-        """One global -> LDS copy by a wave: lane l fills bytes [16 l, 16 l + 16) of the 1 KB at start."""
-        self._bytes(name, [start], 1024)
-        self.pending[wave].append((name, start))
+    def dma(self, wave, name, start, nbytes=1024):
+        """One global -> LDS copy by a wave: lane l fills bytes [16 l, 16 l + 16) of the 1 KB at start
+        (the first nbytes / 16 lanes when the others are idle)."""
+        self._bytes(name, [start], nbytes)
+        self.pending[wave].append((name, start, nbytes))
 
     def waitcnt(self, wave):
         """The wave waits for its vector-memory counter: its DMA copies have landed."""
-        for name, start in self.pending[wave]:
-            self.write(wave, name, [start], 1024)
+        for name, start, nbytes in self.pending[wave]:
+            self.write(wave, name, [start], nbytes)
         self.pending[wave] = []
 
 
@@ -239,13 +240,15 @@ class QoutConfig:
         return dict(kd=kd, nm=nm, db=db, nb=nb, tt=tt, vst=vst, fold=fold, uk=uk, nof=nof, nstep=nstep,
                     zs=nstep - 1, zw=8 * e // 4, perw=(nstep + WAVES - 1) // WAVES, vt_elems=vt_elems,
                     stage=stage, opb=opb, kbuf=kbuf, kf_elems=kf_elems, all=all_, op_elems=op_elems,
-                    mfrg=mfrg, m_lds=m_lds, r32=(self.r16 + 1) // 2)
+                    mfrg=mfrg, m_lds=m_lds, r32=(self.r16 + 1) // 2, self_read=self_read)
 
 
 def qout_model(cfg: QoutConfig, mutate=frozenset()):
     D = cfg.derived()
     e = cfg.elem
-    sizes = {"s_vt": D["vt_elems"] * e, "s_kf": D["kf_elems"] * e, "s_op": D["op_elems"] * e}
+    sizes = {"s_vt": D["vt_elems"] * e, "s_kf": D["kf_elems"] * e, "s_op": D["op_elems"] * e,
+             # unstaged form: z of every feature (dynamic LDS, 4 bytes each)
+             "s_zall": 128 * cfg.fb if D["self_read"] else 0}
     if sum(sizes.values()) > MAX_LDS:
         raise Violation(f"LDS {sum(sizes.values())} bytes > {MAX_LDS}")
     tr = Tracker(sizes, set(mutate))
@@ -263,6 +266,8 @@ def qout_model(cfg: QoutConfig, mutate=frozenset()):
         elif D["stage"]:
             zb = (buf * nstep + zs) * 512 * e
         else:
+            if D["self_read"]:
+                tr.read(w, "s_zall", fb * 128 + (8 * jj + 4 * G) * 4, 16)
             return
         tr.read(w, "s_op", zb + (8 * jj + 4 * G) * 4, 16)
 
@@ -305,7 +310,12 @@ def qout_model(cfg: QoutConfig, mutate=frozenset()):
             exponent_reads(w, 0, 0)                          # the query shift from feature block 0
             fbs = range(cfg.fb)
         else:
+            if D["self_read"]:                               # z copies: 1 KB (256 values) per wave instruction
+                for i in range(w, (cfg.fb * 32 + 255) // 256, WAVES):
+                    tr.dma(w, "s_zall", i * 1024, min(1024, 128 * cfg.fb - 1024 * i))
             store_step(w, 0)
+            if D["self_read"] and "no_z_wait" not in tr.mutate:
+                tr.waitcnt(w)
             yield
             exponent_reads(w, 0, 0)
             fbs = range(cfg.fb)

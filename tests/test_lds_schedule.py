@@ -50,11 +50,13 @@ def _first_caught(model, cases, mutation):
 
 
 @pytest.mark.parametrize("mutation", ["no_kbuf_barrier", "no_kbuf1_barrier", "no_step_barrier", "ring_same_buffer",
-                                      "kbuf_index_fixed"])
+                                      "kbuf_index_fixed", "no_z_wait"])
 def test_model_catches_planted_query_side_mistakes(mutation):
     cases = QOUT
     if mutation == "no_kbuf1_barrier":
         cases = [(c, n) for c, n in QOUT if c.causal and c.derived()["kbuf"] == 1 and c.fb > 1]
+    if mutation == "no_z_wait":
+        cases = [(c, n) for c, n in QOUT if c.derived()["self_read"]]
     if not cases:
         pytest.skip(f"no instantiation exercises {mutation}")
     assert _first_caught(lm.qout_model, cases, mutation), f"{mutation} not caught"
