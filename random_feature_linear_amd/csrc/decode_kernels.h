@@ -55,6 +55,11 @@ constexpr int kDecThreads = 256;
 // leaves fewer registers per wave (measured 28.4 against 33.8 us per step for
 // 256 sequences x 8 heads; 16 is 2% faster for the update)
 template <bool UPD> constexpr int dec_vec() { return UPD ? 16 : 8; }
+// float4 of an omega row requested together in the feature exponent: 8 for
+// the update (with the M rows in pieces: 53.3 against 54.0 us per step for 256
+// sequences x 8 heads, m = 256, r = 64); one at a time in the read-only form,
+// where both changes together measured slower (30.0 against 28.5 us)
+template <bool UPD> constexpr int dec_om_piece() { return UPD ? 8 : 1; }
 
 // LDS carve-up in floats, each array starting on a 16-byte boundary
 __host__ __device__ constexpr int dec_align4(int n) { return (n + 3) & ~3; }
@@ -135,10 +140,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     const float* xr = xs + ((vi % NV) * NS + (vi / NV)) * DH;
     const float* mr = Mh + (long)row * DH;
     float acc = 0.f;
+    if constexpr (UPD) {
+      // the row of M in pieces of up to 64 columns, each piece's loads in flight together
+      constexpr int PC = DH < 64 ? DH : 64;
+#pragma unroll
+      for (int d0 = 0; d0 < DH; d0 += PC) {
+        float4 mv[PC / 4];
+#pragma unroll
+        for (int q = 0; q < PC / 4; ++q) mv[q] = *reinterpret_cast<const float4*>(mr + d0 + 4 * q);
+#pragma unroll
+        for (int q = 0; q < PC / 4; ++q) {
+          const int d = d0 + 4 * q;
+          acc += mv[q].x * xr[d] + mv[q].y * xr[d + 1] + mv[q].z * xr[d + 2] + mv[q].w * xr[d + 3];
+        }
+      }
+    } else {   // read-only form: this loop measured faster there (fewer registers)
 #pragma unroll 4
-    for (int d = 0; d < DH; d += 4) {
-      const float4 mv = *reinterpret_cast<const float4*>(mr + d);
-      acc += mv.x * xr[d] + mv.y * xr[d + 1] + mv.z * xr[d + 2] + mv.w * xr[d + 3];
+      for (int d = 0; d < DH; d += 4) {
+        const float4 mv = *reinterpret_cast<const float4*>(mr + d);
+        acc += mv.x * xr[d] + mv.y * xr[d + 1] + mv.z * xr[d + 2] + mv.w * xr[d + 3];
+      }
     }
     us[vi * a.r + row] = s * acc;
   }
@@ -163,12 +184,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int vi = 0; vi < NV * NS; ++vi) e[vi] = 0.f;
     if (a.r % 4 == 0) {   // rows of omega are 16-byte aligned
-      for (int i = 0; i < a.r; i += 4) {
-        const float4 w = *reinterpret_cast<const float4*>(om + i);
+      // the row in pieces of OP float4, each piece's loads in flight together
+      // (one L2 round trip per piece, not one per float4)
+      constexpr int OP = dec_om_piece<UPD>();
+      for (int i0 = 0; i0 < a.r; i0 += 4 * OP) {
+        float4 w[OP];
 #pragma unroll
-        for (int vi = 0; vi < NV * NS; ++vi) {
-          const float* u = us + vi * a.r + i;
-          e[vi] += w.x * u[0] + w.y * u[1] + w.z * u[2] + w.w * u[3];
+        for (int q = 0; q < OP; ++q)
+          w[q] = i0 + 4 * q < a.r ? *reinterpret_cast<const float4*>(om + i0 + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int q = 0; q < OP; ++q) {
+          const int i = i0 + 4 * q;
+          if (i >= a.r) break;
+#pragma unroll
+          for (int vi = 0; vi < NV * NS; ++vi) {
+            const float* u = us + vi * a.r + i;
+            e[vi] += w[q].x * u[0] + w[q].y * u[1] + w[q].z * u[2] + w[q].w * u[3];
+          }
         }
       }
     } else {
